@@ -1,0 +1,371 @@
+"""Plain CPU oracle for the indexer-selected sparse MLA hot path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports, calls or
+links this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library (no kernels, headers, tables or helpers); the only thing both sides
+consume is the seeded input tensors.
+
+Everything here is written for a reader to check against the pages by eye:
+NumPy in float64, a matmul or a sort as the only library primitives, no
+blocking, fusion or reordering beyond what the definition states.  Inputs that
+the GPU consumes as bf16 are handed in already widened (exactly) to float.
+
+Sources, cited by page title and section:
+  [GLM-5.2 techniques map]  models.inteligile.com "GLM-5.2 / Model techniques
+      map", section "Checked in its code", rows "Multi-head latent attention",
+      "Indexer-selected sparse attention (DeepSeek Sparse Attention)",
+      "Learnable attention sink", "Gated attention output", "QK normalization",
+      "Partial RoPE", "YaRN RoPE scaling".
+  [GLM-5.2 architectures]   llm-architectures-explained "GLM-5.2", section
+      "Every architecture field" (row "layout") and "Modelled costs".
+  [GLM 5.2 hermosaai]       hermosaai "GLM 5.2", sections "78 layers,
+      IndexShare pattern" and "MLA + DSA with IndexShare".
+  [GLM-5.2 llm-atlas]       llm-atlas "GLM-5.2", section "Champs bruts du
+      config.json" (index_topk, index_n_heads, index_head_dim, indexer_types,
+      index_topk_freq, index_skip_topk_offset, kv_lora_rank, qk_rope_head_dim,
+      qk_nope_head_dim, v_head_dim, qk_head_dim).
+
+Where the pages leave a step open, the reading taken is stated next to the
+code that takes it.
+
+Pin status (what checks this module against something other than itself, all
+under ``tests/`` marked ``not gpu``):
+  indexer_scores     closed-form one-hot cases, the non-negative GEMV
+                     reduction, w = 0, causal bound, sequence offsets.
+  topk_select        full-sort brute force, pairwise order invariant, hand
+                     example with ties, degenerate (all equal, n <= k).
+  sparse_mla         dense additive-mask attention, dense causal attention
+                     when k >= n, explicit (non-absorbed) kv_b_proj form,
+                     k_eff = 1, zero query, hand-computed two-row example.
+  layer_pattern      the pages' printed 78-layer layout and the 21/57 counts.
+  score_error_bound  pinned against exhaustive fp32 re-summation orders on
+                     small cases (the bound must cover every order).
+No function is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# --- constants printed on the pages --------------------------------------
+# [GLM-5.2 llm-atlas] config.json fields; [GLM-5.2 techniques map] MLA row.
+INDEX_N_HEADS = 32        # index_n_heads
+INDEX_HEAD_DIM = 128      # index_head_dim
+INDEX_TOPK = 2048         # index_topk
+N_HEADS = 64              # num_attention_heads
+KV_LORA_RANK = 512        # kv_lora_rank (latent width)
+QK_ROPE_DIM = 64          # qk_rope_head_dim
+QK_NOPE_DIM = 192         # qk_nope_head_dim
+V_HEAD_DIM = 256          # v_head_dim
+ROW_DIM = KV_LORA_RANK + QK_ROPE_DIM   # 576: one cache row per token
+N_LAYERS = 78             # num_hidden_layers
+INDEX_TOPK_FREQ = 4       # index_topk_freq
+INDEX_SKIP_TOPK_OFFSET = 3  # index_skip_topk_offset
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+# --- a1: indexer score -----------------------------------------------------
+def indexer_scores(q_idx, w, k_idx, seq_start, q_seq, q_pos, ld=None):
+    """Indexer scores I[t, s] for every query t and every cached position s.
+
+    [GLM-5.2 techniques map] "Indexer-selected sparse attention": a per-query
+    indexer with index_n_heads heads of index_head_dim scores past tokens
+    against one key per token shared by all heads (the key has shape
+    [B, S, 1, D]).  The pages give shapes only; the score taken is
+
+        I[t, s] = sum_h w[t, h] * max(0, q[t, h, :] . k[b_t, s, :])
+
+    for s in the causal set {0 .. q_pos[t]} (diagonal included: the single
+    causal mask of the "layer_types" row), and -inf for s > q_pos[t] so that
+    every row of length ``ld`` is self-contained.
+
+    q_idx [n_q, 32, 128], w [n_q, 32], k_idx [total_tokens, 128] (packed by
+    sequence, row seq_start[b] + s holds position s of sequence b),
+    q_seq / q_pos [n_q].  Returns float64 [n_q, ld].
+    """
+    q_idx, w, k_idx = _f64(q_idx), _f64(w), _f64(k_idx)
+    q_seq = np.asarray(q_seq, dtype=np.int64)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    seq_start = np.asarray(seq_start, dtype=np.int64)
+    n_q = q_idx.shape[0]
+    if ld is None:
+        ld = int(q_pos.max()) + 1 if n_q else 0
+    out = np.full((n_q, ld), -np.inf, dtype=np.float64)
+    for t in range(n_q):
+        n_t = int(q_pos[t]) + 1
+        base = int(seq_start[q_seq[t]])
+        keys = k_idx[base:base + n_t]                 # [n_t, 128]
+        dots = q_idx[t] @ keys.T                      # [32, n_t]: q_h . k_s
+        out[t, :n_t] = w[t] @ np.maximum(dots, 0.0)   # sum_h w_h ReLU(.)
+    return out
+
+
+def indexer_scores_at(q_idx, w, k_idx, seq_start, q_seq, q_pos, t, positions):
+    """The same score as :func:`indexer_scores` for one query t at chosen
+    positions only (used at sizes where a full row is too slow on the CPU).
+    Positions must lie in the causal set of t."""
+    positions = np.asarray(positions, dtype=np.int64)
+    assert positions.size == 0 or (positions.min() >= 0 and positions.max() <= int(q_pos[t]))
+    base = int(seq_start[int(q_seq[t])])
+    keys = _f64(k_idx[base + positions])
+    dots = _f64(q_idx[t]) @ keys.T
+    return _f64(w[t]) @ np.maximum(dots, 0.0)
+
+
+def score_error_bound(q_idx_t, w_t, keys, unit_roundoff=2.0 ** -23):
+    """Rigorous bound on |fp32 score - exact score| for scores computed with
+    exact bf16 products, fp32 sums of the 128 products per head in any order,
+    fp32 ReLU, and an fp32 weighted sum over the 32 heads in any order.
+
+    Standard worst-case summation bound (Higham, "Accuracy and Stability of
+    Numerical Algorithms", ch. 3): a sum of n terms in floating point, any
+    order, has error <= gamma_{n-1} * sum |terms| with
+    gamma_n = n u / (1 - n u).  The per-head dot product d_h gets
+    gamma_127 * sum_i |q_hi k_i|; ReLU is 1-Lipschitz so that error passes
+    through; the weighted sum of 32 products w_h * r_h (each one rounding)
+    adds gamma_33 * sum_h |w_h| |r_h|, and the dot-product errors enter scaled
+    by |w_h|.  unit_roundoff defaults to 2^-23 (covers truncating as well as
+    round-to-nearest accumulators).  Returns float64 [n_keys].
+    """
+    q = np.abs(_f64(q_idx_t))            # [32, 128]
+    wa = np.abs(_f64(w_t))               # [32]
+    k = _f64(keys)                        # [n, 128]
+    u = unit_roundoff
+
+    def gamma(n):
+        return n * u / (1.0 - n * u)
+
+    abs_dots = q @ np.abs(k).T            # [32, n]: sum_i |q_hi k_i|
+    relu = np.maximum(_f64(q_idx_t) @ k.T, 0.0)
+    err_dot = gamma(INDEX_HEAD_DIM) * (wa @ abs_dots)
+    err_sum = gamma(INDEX_N_HEADS + 1) * (wa @ (relu + gamma(INDEX_HEAD_DIM) * abs_dots))
+    return err_dot + err_sum
+
+
+# --- a2: top-k selection -----------------------------------------------------
+def topk_select(scores_row, q_pos_t, k=INDEX_TOPK):
+    """Exact top-k of one indexer row over its causal set.
+
+    [GLM-5.2 techniques map] "Indexer-selected sparse attention": the kept
+    count is min(index_topk, number of scores), returned as int32 positions.
+    The pages do not state a tie order; the reading taken is that equal scores
+    go to the lower position.  Scores of -0.0 and +0.0 compare equal (numeric
+    comparison), so they tie.
+
+    Returns the selected positions in ascending order, padded with -1 to k.
+    """
+    n_t = int(q_pos_t) + 1
+    row = _f64(scores_row)[:n_t]
+    k_eff = min(int(k), n_t)
+    positions = np.arange(n_t)
+    order = np.lexsort((positions, -row))   # primary: score desc; then position asc
+    chosen = np.sort(order[:k_eff])
+    out = np.full(int(k), -1, dtype=np.int64)
+    out[:k_eff] = chosen
+    return out
+
+
+def topk_select_rows(scores, q_pos, k=INDEX_TOPK):
+    return np.stack([topk_select(scores[t], q_pos[t], k) for t in range(scores.shape[0])]) \
+        if scores.shape[0] else np.zeros((0, int(k)), dtype=np.int64)
+
+
+# --- a3 + a4: absorbed sparse MLA and the W_UV up-projection ------------------
+def sparse_mla(q_abs, kv, seq_start, q_seq, idx, w_uv, scale, return_parts=False):
+    """Attention of each query over only its selected cache rows, absorbed
+    form, then the per-head value up-projection.
+
+    [GLM-5.2 techniques map] "Multi-head latent attention": keys and values
+    come from one kv_lora_rank latent per token (after kv_a_layernorm) plus a
+    decoupled qk_rope_head_dim key; kv_b_proj maps the latent to, per head,
+    qk_nope_head_dim key rows and v_head_dim value rows.  Folding the key
+    half of kv_b_proj (W_UK) into the query and applying the value half (W_UV)
+    after attention is the same product re-associated; the cache row is then
+    [latent (512) ; k_rope (64)] and the folded query is 576 wide.
+    "Learnable attention sink" / "Gated attention output": plain softmax with
+    no extra logit and no gate.  "Indexer-selected sparse attention": each
+    query attends only to its selected positions (an additive 0 / -inf mask
+    in the reference code; here the selected rows are gathered).
+
+    For each query t and head h, over the selected rows R_j (slots with
+    idx = -1 are ignored):
+        z_j   = scale * (q_abs[t, h] . R_j)               (all 576 dims)
+        p_j   = exp(z_j - max z) / sum_j exp(z_j - max z)
+        obar  = sum_j p_j * R_j[:512]
+        out[t, h] = W_UV[h] @ obar                          ([256, 512] @ [512])
+
+    Returns out float64 [n_q, 64, 256] (unrounded).  With return_parts also
+    returns obar [n_q, 64, 512], the row max m [n_q, 64], the sum l [n_q, 64],
+    and the per-query gathered rows (list of [k_eff, 576]) and weights (list
+    of [64, k_eff]) for error-bound computations.
+    """
+    q_abs, kv, w_uv = _f64(q_abs), kv, _f64(w_uv)
+    seq_start = np.asarray(seq_start, dtype=np.int64)
+    q_seq = np.asarray(q_seq, dtype=np.int64)
+    idx = np.asarray(idx, dtype=np.int64)
+    n_q, n_h = q_abs.shape[0], q_abs.shape[1]
+    lat = w_uv.shape[2]
+    out = np.zeros((n_q, n_h, w_uv.shape[1]))
+    obar_all = np.zeros((n_q, n_h, lat))
+    m_all = np.zeros((n_q, n_h))
+    l_all = np.zeros((n_q, n_h))
+    rows_all, p_all = [], []
+    for t in range(n_q):
+        sel = idx[t][idx[t] >= 0]
+        rows = _f64(kv[int(seq_start[q_seq[t]]) + sel])      # [k_eff, 576]
+        z = scale * (q_abs[t] @ rows.T)                        # [64, k_eff]
+        m = z.max(axis=1, keepdims=True)
+        e = np.exp(z - m)
+        lsum = e.sum(axis=1, keepdims=True)
+        p = e / lsum
+        obar = p @ rows[:, :lat]                               # [64, 512]
+        for h in range(n_h):
+            out[t, h] = w_uv[h] @ obar[h]
+        obar_all[t], m_all[t], l_all[t] = obar, m[:, 0], lsum[:, 0]
+        rows_all.append(rows)
+        p_all.append(p)
+    if return_parts:
+        return out, obar_all, m_all, l_all, rows_all, p_all
+    return out
+
+
+def round_to_bf16(x):
+    """Round float values to the nearest bfloat16 (ties to even), returned as
+    float64.  bfloat16 keeps the top 16 bits of an IEEE binary32; the value is
+    first rounded to binary32 (exact for inputs that are binary32 already)."""
+    f = np.asarray(x, dtype=np.float32)
+    bits = f.view(np.uint32).astype(np.uint64)
+    lsb = (bits >> 16) & 1
+    rounded = (bits + 0x7FFF + lsb) >> 16
+    nan = np.isnan(f)
+    rounded = np.where(nan, (bits >> 16) | 0x40, rounded)
+    out = (rounded.astype(np.uint32) << 16).view(np.float32)
+    return out.astype(np.float64)
+
+
+def mla_error_bound(out, q_abs, w_uv, rows_list, p_list, scale, n_lat=KV_LORA_RANK,
+                    model="probabilistic", lam=8.0):
+    """Per-element tolerance for the GPU's sparse MLA output, derived from the
+    arithmetic the kernels are allowed (not fitted to results).
+
+    Allowed deviations from the exact value (u32 = 2^-24 with slack 2^-23,
+    ub = 2^-8 is the bf16 unit roundoff):
+      * logits summed in fp32 over 576 products, scaled and moved to base 2 in
+        fp32, exponentiated with a 1-2 ulp exp:
+        |dz_j| <= gamma_576 scale sum_i |q_i R_ji| + 2^-21 (|z_j| + 1);
+        a softmax weight then moves by at most a factor exp(2 max|dz|);
+      * weights fed to the value product in bf16 and the normaliser formed
+        from the unrounded fp32 weights: relative 2 ub per weight;
+      * fp32 accumulation of up to 2048 weighted rows;
+      * the latent average fed to the up-projection in bf16 (relative 2 ub)
+        and summed in fp32 over 512 terms;
+      * the final rounding of the output to bf16 (ub |out|, rigorous).
+
+    model="worst": every rounding error at its worst case and aligned
+    (Higham, "Accuracy and Stability of Numerical Algorithms", ch. 3).  It is
+    rigorous but of the order of the output itself.
+    model="probabilistic": independent, mean-zero rounding errors (Higham and
+    Mary, "A new approach to probabilistic rounding error analysis", SISC
+    2019): a sum of n rounded terms errs by at most lam * u * sqrt(sum of
+    squared terms) (for the per-term roundings) or lam * sqrt(n) * u * sum of
+    |terms| (for the accumulation), each holding with probability at least
+    1 - 2 exp(-lam^2 / 2); lam = 8 makes a false alarm ~1e-14 per element.
+
+    Returns float64 [n_q, 64, 256].
+    """
+    u = 2.0 ** -23
+    ub = 2.0 ** -8
+
+    def gamma(n):
+        return n * u / (1 - n * u)
+
+    w = _f64(w_uv)
+    wa = np.abs(w)
+    q_abs = _f64(q_abs)
+    bound = np.zeros_like(out)
+    for t, (rows, p) in enumerate(zip(rows_list, p_list)):
+        n_sel = rows.shape[0]
+        z = scale * (q_abs[t] @ rows.T)                                # [64, k]
+        dz = gamma(rows.shape[1]) * scale * (np.abs(q_abs[t]) @ np.abs(rows).T) \
+            + 2.0 ** -21 * (np.abs(z) + 1.0)
+        rel_z = 2.2 * dz.max(axis=1, keepdims=True)                  # [64, 1]
+        v = rows[:, :n_lat]
+        pv_abs = p @ np.abs(v)                                        # [64, 512]: sum_j p_j |R_j[c]|
+        obar = p @ v                                                  # [64, 512]
+        if model == "worst":
+            d_obar = (2 * ub + rel_z) * pv_abs + gamma(max(n_sel, 1)) * pv_abs
+            for h in range(out.shape[1]):
+                bound[t, h] = wa[h] @ d_obar[h] + (2 * ub + gamma(n_lat)) * (wa[h] @ np.abs(obar[h])) \
+                    + ub * np.abs(out[t, h])
+        else:
+            pv_sq = np.sqrt((p ** 2) @ (v ** 2))                      # [64, 512]
+            d_obar = lam * 2 * ub * pv_sq + rel_z * pv_abs + lam * np.sqrt(max(n_sel, 1)) * u * pv_abs
+            for h in range(out.shape[1]):
+                prop = np.sqrt((w[h] ** 2) @ (d_obar[h] ** 2))        # errors of obar through W_UV
+                rnd = lam * 2 * ub * np.sqrt((w[h] ** 2) @ (obar[h] ** 2))
+                acc = lam * np.sqrt(n_lat) * u * (wa[h] @ np.abs(obar[h]))
+                bound[t, h] = prop + rnd + acc + ub * np.abs(out[t, h])
+    return bound
+
+
+# --- a5: IndexShare layer stack ----------------------------------------------
+def layer_is_full(layer: int) -> bool:
+    """Whether layer l runs its own indexer.
+
+    [GLM 5.2 hermosaai] "78 layers, IndexShare pattern": 21 of 78 layers run a
+    full indexer, the rest reuse one, in groups of four after the first three.
+    [GLM-5.2 llm-atlas] config fields index_topk_freq = 4 and
+    index_skip_topk_offset = 3.  [GLM-5.2 architectures] "layout" row prints
+    the sequence.  The reading that fits all three: layers 0, 1, 2 are full;
+    after them the layers form groups of four whose last layer is full
+    (layers 6, 10, ..., 74), i.e. l < 3 or l mod 4 == 2.
+    """
+    if layer < INDEX_SKIP_TOPK_OFFSET:
+        return True
+    return (layer - INDEX_SKIP_TOPK_OFFSET) % INDEX_TOPK_FREQ == INDEX_TOPK_FREQ - 1
+
+
+def layer_pattern(n_layers=N_LAYERS):
+    return [layer_is_full(l) for l in range(n_layers)]
+
+
+def shared_source(layer: int) -> int:
+    """The full layer whose selection a layer uses: itself if full, else the
+    latest full layer before it."""
+    l = layer
+    while not layer_is_full(l):
+        l -= 1
+    return l
+
+
+def layer_stack(layers, seq_start, q_seq, q_pos, k=INDEX_TOPK, scale=1.0 / 16, full=None):
+    """Run the hot path over a stack of layers in order.
+
+    ``layers`` is a list of dicts with keys q_idx, w, k_idx (full layers only),
+    q_abs, kv, w_uv.  ``full`` gives each layer's kind (default: the pages'
+    pattern).  Each layer keeps its own queries, cache and W_UV; only the
+    selected positions are shared ([GLM 5.2 hermosaai] "MLA + DSA with
+    IndexShare": the next layers reuse the selection instead of scoring
+    again).  Returns (outs, idxs, scores) with idxs / scores holding an entry
+    for every full layer (None for shared layers).
+    """
+    if full is None:
+        full = layer_pattern(len(layers))
+    if len(layers) and not full[0]:
+        raise ValueError("the first layer of a stack must run its own indexer")
+    outs, idxs, scores_all = [], [], []
+    cur = None
+    for l, L in enumerate(layers):
+        if full[l]:
+            sc = indexer_scores(L["q_idx"], L["w"], L["k_idx"], seq_start, q_seq, q_pos)
+            cur = topk_select_rows(sc, q_pos, k)
+            idxs.append(cur)
+            scores_all.append(sc)
+        else:
+            idxs.append(None)
+            scores_all.append(None)
+        outs.append(sparse_mla(L["q_abs"], L["kv"], seq_start, q_seq, cur, L["w_uv"], scale))
+    return outs, idxs, scores_all

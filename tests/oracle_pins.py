@@ -1,0 +1,451 @@
+"""Pins for the CPU oracle: checks against facts the pages and mathematics fix,
+never against the oracle's own formula retyped.
+
+Each ``check_*`` takes the oracle module (or a stand-in with a planted
+mistake) and raises AssertionError when the oracle disagrees with the fact.
+``tests/test_oracle_pins.py`` runs them on the real oracle;
+``tests/test_oracle_mutations.py`` plants plausible mistakes in copies of the
+oracle's functions and requires some check to fail for each.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _bf16_grid(x):
+    """Snap to values exactly representable in bf16 (8 significant bits) so
+    the oracle sees the same kind of inputs as the GPU."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.round(m * 256) / 256, e)
+
+
+# ----------------------------------------------------------------- indexer
+def check_indexer_one_hot_closed_form(ref):
+    """One head with weight w, query e_i: the score is w * max(0, k_s[i]).
+    Keys are chosen so the expected row is printed below by hand."""
+    n = 8
+    k = np.zeros((n, 128))
+    k[:, 5] = [-2.0, -0.5, 0.0, 0.25, 0.5, 1.0, 3.0, -1.0]
+    q = np.zeros((1, 32, 128))
+    q[0, 7, 5] = 1.0                       # head 7 looks at key dim 5
+    w = np.zeros((1, 32))
+    w[0, 7] = 2.0
+    s = ref.indexer_scores(q, w, k, [0], [0], [n - 1], ld=n + 2)
+    expect = [0.0, 0.0, 0.0, 0.5, 1.0, 2.0, 6.0, 0.0, -np.inf, -np.inf]
+    assert np.array_equal(s[0], expect), s[0]
+    # a negative head weight multiplies after the ReLU: w * ReLU(d), not ReLU(w d)
+    w[0, 7] = -0.5
+    s = ref.indexer_scores(q, w, k, [0], [0], [n - 1])
+    expect = [0.0, 0.0, 0.0, -0.125, -0.25, -0.5, -1.5, 0.0]
+    assert np.array_equal(s[0], expect), s[0]
+
+
+def check_indexer_two_heads_closed_form(ref):
+    """Two heads on opposite signs of the same key coordinate: exactly one
+    of them is active per key, so the score is w_a k or -w_b k."""
+    k = np.zeros((4, 128))
+    k[:, 0] = [1.0, -1.0, 2.0, -3.0]
+    q = np.zeros((1, 32, 128))
+    q[0, 0, 0] = 1.0
+    q[0, 31, 0] = -1.0
+    w = np.zeros((1, 32))
+    w[0, 0], w[0, 31] = 1.0, 10.0
+    s = ref.indexer_scores(q, w, k, [0], [0], [3])
+    assert np.array_equal(s[0], [1.0, 10.0, 2.0, 30.0]), s[0]
+
+
+def check_indexer_gemv_reduction(ref):
+    """With non-negative q and k every ReLU is the identity, so
+    I[t, s] = (sum_h w_h q_h) . k_s: a plain matrix-vector product computed
+    through a different association.  Covers head/dim indexing, w per query,
+    sequence offsets and the causal bound, on two packed sequences."""
+    rng = _rng(11)
+    lens = [37, 53]
+    starts = [0, 37]
+    k = _bf16_grid(np.abs(rng.standard_normal((sum(lens), 128))))
+    queries = [(1, 52), (0, 36), (1, 0), (0, 10)]
+    q = _bf16_grid(np.abs(rng.standard_normal((4, 32, 128))) / 11)
+    w = rng.standard_normal((4, 32))
+    s = ref.indexer_scores(q, w, k, starts, [b for b, _ in queries], [p for _, p in queries], ld=60)
+    for t, (b, p) in enumerate(queries):
+        v = np.einsum("h,hi->i", w[t], q[t])
+        expect = np.matmul(k[starts[b]:starts[b] + p + 1], v)
+        np.testing.assert_allclose(s[t, :p + 1], expect, rtol=1e-12, atol=1e-12)
+        assert np.all(np.isneginf(s[t, p + 1:]))
+
+
+def check_indexer_zero_weights(ref):
+    """w = 0 gives an all-zero row over the causal set."""
+    rng = _rng(3)
+    k = rng.standard_normal((20, 128))
+    q = rng.standard_normal((2, 32, 128))
+    s = ref.indexer_scores(q, np.zeros((2, 32)), k, [0], [0, 0], [19, 4], ld=20)
+    assert np.all(s[0] == 0.0) and np.all(s[1, :5] == 0.0) and np.all(np.isneginf(s[1, 5:]))
+
+
+def check_indexer_sampled_matches_rows(ref):
+    """The sampled-position entry point agrees with the full row."""
+    rng = _rng(5)
+    k = rng.standard_normal((30, 128))
+    q = rng.standard_normal((2, 32, 128))
+    w = rng.standard_normal((2, 32))
+    s = ref.indexer_scores(q, w, k, [0, 10], [1, 0], [19, 9])
+    pos = np.array([0, 3, 19])
+    np.testing.assert_allclose(ref.indexer_scores_at(q, w, k, [0, 10], [1, 0], [19, 9], 0, pos),
+                               s[0, pos], rtol=1e-13, atol=1e-13)
+
+
+def check_score_error_bound_covers_fp32(ref):
+    """The fp32 error bound must cover fp32 evaluations in several summation
+    orders (forward, reverse, pairwise) of a real score row."""
+    rng = _rng(17)
+    k = _bf16_grid(rng.standard_normal((64, 128)))
+    q = _bf16_grid(rng.standard_normal((1, 32, 128)) / 11.3)
+    w = rng.standard_normal((1, 32)).astype(np.float32).astype(np.float64) / 5.7
+    exact = ref.indexer_scores(q, w, k, [0], [0], [63])[0]
+    bound = ref.score_error_bound(q[0], w[0], k)
+    q32, k32, w32 = q[0].astype(np.float32), k.astype(np.float32), w[0].astype(np.float32)
+    prods = q32[:, None, :] * k32[None, :, :]                      # exact in fp32
+    for order in ("fwd", "rev", "pair"):
+        if order == "pair":
+            d = prods
+            while d.shape[-1] > 1:
+                d = (d[..., 0::2] + d[..., 1::2]).astype(np.float32)
+            d = d[..., 0]
+        else:
+            seq = range(128) if order == "fwd" else range(127, -1, -1)
+            d = np.zeros((32, 64), dtype=np.float32)
+            for i in seq:
+                d = (d + prods[:, :, i]).astype(np.float32)
+        r = np.maximum(d, np.float32(0))
+        acc = np.zeros(64, dtype=np.float32)
+        for h in (range(32) if order != "rev" else range(31, -1, -1)):
+            acc = (acc + w32[h] * r[h]).astype(np.float32)
+        assert np.all(np.abs(acc.astype(np.float64) - exact) <= bound), order
+    assert np.all(bound < 1e-3 * (np.abs(exact).max() + 1e-30))
+    # Cancellation: products 512, 2^-16, -512 summed left to right lose the
+    # middle term entirely (fp32 ulp at 512 is 2^-14), so the dot-product
+    # term of the bound must carry the error.
+    kc = np.zeros((1, 128))
+    kc[0, :3] = [512.0, 2.0 ** -16, 512.0]
+    qc = np.zeros((1, 32, 128))
+    qc[0, 0, :3] = [1.0, 1.0, -1.0]
+    wc = np.zeros((1, 32))
+    wc[0, 0] = 1.0
+    exact_c = ref.indexer_scores(qc, wc, kc, [0], [0], [0])[0, 0]
+    fwd = np.float32(np.float32(np.float32(512.0) + np.float32(2.0 ** -16)) - np.float32(512.0))
+    assert exact_c == 2.0 ** -16 and fwd == 0.0
+    assert abs(float(fwd) - exact_c) <= ref.score_error_bound(qc[0], wc[0], kc)[0]
+
+
+# ------------------------------------------------------------------- top-k
+def check_topk_full_sort(ref):
+    """Top-k equals the first k of a full sort by (score desc, position asc),
+    on many tiny rows with forced ties (scores quantised to few levels)."""
+    rng = _rng(23)
+    for trial in range(300):
+        n = int(rng.integers(1, 40))
+        levels = int(rng.integers(1, 6))
+        row = rng.integers(-levels, levels + 1, size=n).astype(np.float64) / 4
+        k = int(rng.integers(1, n + 6))
+        got = ref.topk_select(np.concatenate([row, [-np.inf] * 3]), n - 1, k)
+        brute = sorted(range(n), key=lambda s: (-row[s], s))[:min(k, n)]
+        expect = sorted(brute) + [-1] * (k - min(k, n))
+        assert list(got) == expect, (trial, row, k, got)
+
+
+def check_topk_order_invariant(ref):
+    """Every selected position beats every unselected one: a higher score, or
+    an equal score at a lower position; the set has min(k, n) members."""
+    rng = _rng(29)
+    for trial in range(100):
+        n = int(rng.integers(1, 200))
+        row = np.round(rng.standard_normal(n) * 3) / 2
+        k = int(rng.integers(1, 64))
+        got = ref.topk_select(row, n - 1, k)
+        sel = [int(s) for s in got if s >= 0]
+        assert len(sel) == min(k, n) and len(set(sel)) == len(sel)
+        assert all(got[len(sel):] == -1)
+        uns = sorted(set(range(n)) - set(sel))
+        for s in sel:
+            for u in uns:
+                assert row[s] > row[u] or (row[s] == row[u] and s < u)
+
+
+def check_topk_hand_example(ref):
+    """Hand example: scores at positions 0..5 = [1, 3, 3, 2, 3, -0.0] and
+    k = 2 keep the two lowest positions among the three 3's, {1, 2}; k = 5
+    keeps {0, 1, 2, 3, 4}; -0.0 and +0.0 tie (the +0.0 at position 6 loses
+    to the -0.0 at position 5 when one of them must go)."""
+    row = np.array([1.0, 3.0, 3.0, 2.0, 3.0, -0.0, 0.0])
+    assert list(ref.topk_select(row, 6, 2)) == [1, 2]
+    assert list(ref.topk_select(row, 6, 5)) == [0, 1, 2, 3, 4]
+    assert list(ref.topk_select(row, 6, 6)) == [0, 1, 2, 3, 4, 5]
+    assert list(ref.topk_select(row, 3, 6)) == [0, 1, 2, 3, -1, -1]
+
+
+def check_topk_degenerate(ref):
+    """All-equal rows keep positions 0..k-1; rows no longer than k keep all."""
+    assert list(ref.topk_select(np.zeros(100), 99, 8)) == list(range(8))
+    assert list(ref.topk_select(np.arange(5.0), 4, 8)) == [0, 1, 2, 3, 4, -1, -1, -1]
+    assert list(ref.topk_select(np.array([7.0]), 0, 2048))[:2] == [0, -1]
+
+
+def check_topk_respects_causal_bound(ref):
+    """Only positions <= q_pos are eligible, even if later entries are larger."""
+    row = np.array([0.0, 1.0, 2.0, 100.0, 200.0])
+    assert list(ref.topk_select(row, 2, 2)) == [1, 2]
+
+
+# --------------------------------------------------------------- sparse MLA
+def _mla_inputs(seed, n_q, lens, k, n_heads=64, scale_q=1.0):
+    rng = _rng(seed)
+    T = sum(lens)
+    starts = list(np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(int))
+    kv = _bf16_grid(rng.standard_normal((T, 576)))
+    q = _bf16_grid(rng.standard_normal((n_q, n_heads, 576)) * scale_q / 24)
+    wuv = _bf16_grid(rng.standard_normal((n_heads, 256, 512)) / 22.6)
+    q_seq = [int(rng.integers(0, len(lens))) for _ in range(n_q)]
+    q_pos = [int(rng.integers(0, lens[b])) for b in q_seq]
+    idx = np.full((n_q, k), -1)
+    for t in range(n_q):
+        n = q_pos[t] + 1
+        pick = rng.choice(n, size=min(k, n), replace=False)
+        idx[t, :len(pick)] = pick
+        rng.shuffle(idx[t])                  # padding slots anywhere in the row
+    return q, kv, starts, q_seq, q_pos, idx, wuv
+
+
+def _dense_masked_reference(q, kv, starts, q_seq, q_pos, idx, wuv, scale):
+    """The additive-mask mechanism of the reference code: score every cached
+    position of the sequence, add 0 for selected positions and -inf for the
+    rest, softmax over the whole row in one pass, multiply by all latents."""
+    n_q, n_h = q.shape[0], q.shape[1]
+    out = np.zeros((n_q, n_h, 256))
+    for t in range(n_q):
+        b = q_seq[t]
+        end = starts[b + 1] if b + 1 < len(starts) else kv.shape[0]
+        rows = kv[starts[b]:end]
+        mask = np.full(rows.shape[0], -np.inf)
+        sel = idx[t][idx[t] >= 0]
+        mask[sel] = 0.0
+        logits = scale * np.einsum("hd,sd->hs", q[t], rows) + mask[None, :]
+        z = np.exp(logits - logits.max(axis=1, keepdims=True))
+        attn = z / z.sum(axis=1, keepdims=True)
+        lat = np.einsum("hs,sc->hc", attn, rows[:, :512])
+        out[t] = np.einsum("hvc,hc->hv", wuv, lat)
+    return out
+
+
+def check_mla_equals_dense_masked(ref):
+    q, kv, starts, q_seq, q_pos, idx, wuv = _mla_inputs(31, 5, [40, 70, 9], 16)
+    got = ref.sparse_mla(q, kv, starts, q_seq, idx, wuv, 1.0 / 16)
+    exp = _dense_masked_reference(q, kv, starts, q_seq, q_pos, idx, wuv, 1.0 / 16)
+    np.testing.assert_allclose(got, exp, rtol=1e-10, atol=1e-12)
+
+
+def check_mla_take_all_equals_dense_causal(ref):
+    """k >= n: attention over all of 0..p, i.e. dense causal attention."""
+    q, kv, starts, q_seq, q_pos, _, wuv = _mla_inputs(37, 4, [25, 30], 64)
+    idx = np.full((4, 64), -1)
+    for t in range(4):
+        idx[t, :q_pos[t] + 1] = np.arange(q_pos[t] + 1)[::-1]
+    got = ref.sparse_mla(q, kv, starts, q_seq, idx, wuv, 1.0 / 16)
+    for t in range(4):
+        rows = kv[starts[q_seq[t]]:starts[q_seq[t]] + q_pos[t] + 1]
+        for h in (0, 17, 63):
+            z = (q[t, h] @ rows.T) / 16
+            a = np.exp(z - z.max())
+            a /= a.sum()
+            np.testing.assert_allclose(got[t, h], wuv[h] @ (a @ rows[:, :512]), rtol=1e-10, atol=1e-12)
+
+
+def check_mla_absorbed_equals_explicit(ref):
+    """Draw a kv_b_proj [64 * (192 + 256), 512]; per head its first 192 rows
+    are W_UK and the next 256 are W_UV.  The explicit form computes, per head,
+    keys [W_UK c ; k_rope] (256 wide), values W_UV c and scale 1/sqrt(256);
+    the absorbed oracle gets q_abs = [W_UK^T q_nope ; q_rope] and the cache
+    rows [c ; k_rope]."""
+    rng = _rng(41)
+    n_tok, n_q, k = 50, 3, 20
+    kvb = rng.standard_normal((64 * 448, 512)) / 22.6
+    w_uk = np.stack([kvb[h * 448:h * 448 + 192] for h in range(64)])          # [64, 192, 512]
+    w_uv = np.stack([kvb[h * 448 + 192:(h + 1) * 448] for h in range(64)])    # [64, 256, 512]
+    c = rng.standard_normal((n_tok, 512))
+    kr = rng.standard_normal((n_tok, 64))
+    q_nope = rng.standard_normal((n_q, 64, 192)) / 13.9
+    q_rope = rng.standard_normal((n_q, 64, 64)) / 8
+    q_pos = [49, 30, 19]
+    idx = np.stack([rng.choice(p + 1, size=k, replace=False) for p in q_pos])
+    scale = 1.0 / math.sqrt(192 + 64)
+    explicit = np.zeros((n_q, 64, 256))
+    for t in range(n_q):
+        sel = idx[t]
+        for h in range(64):
+            keys = np.concatenate([c[sel] @ w_uk[h].T, kr[sel]], axis=1)     # [k, 256]
+            vals = c[sel] @ w_uv[h].T                                          # [k, 256]
+            z = scale * (keys @ np.concatenate([q_nope[t, h], q_rope[t, h]]))
+            a = np.exp(z - z.max())
+            explicit[t, h] = (a / a.sum()) @ vals
+    q_abs = np.concatenate([np.einsum("hnc,thn->thc", w_uk, q_nope), q_rope], axis=2)
+    rows = np.concatenate([c, kr], axis=1)
+    got = ref.sparse_mla(q_abs, rows, [0], [0] * n_q, idx, w_uv, scale)
+    np.testing.assert_allclose(got, explicit, rtol=1e-9, atol=1e-12)
+
+
+def check_mla_single_row(ref):
+    """One selected row: its weight is 1, so out = W_UV c_s."""
+    q, kv, starts, q_seq, q_pos, _, wuv = _mla_inputs(43, 3, [30, 12], 4)
+    idx = np.full((3, 4), -1)
+    for t in range(3):
+        idx[t, 2] = q_pos[t] // 2
+    got = ref.sparse_mla(q, kv, starts, q_seq, idx, wuv, 1.0 / 16)
+    for t in range(3):
+        c_s = kv[starts[q_seq[t]] + q_pos[t] // 2, :512]
+        np.testing.assert_allclose(got[t], np.einsum("hvc,c->hv", wuv, c_s), rtol=1e-12, atol=1e-13)
+
+
+def check_mla_zero_query_mean(ref):
+    """q = 0: all logits equal, weights uniform, the latent average is the
+    mean of the selected rows; and the result ignores the order of idx."""
+    q, kv, starts, q_seq, q_pos, idx, wuv = _mla_inputs(47, 3, [64], 10)
+    q[:] = 0.0
+    got = ref.sparse_mla(q, kv, starts, q_seq, idx, wuv, 1.0 / 16)
+    perm = idx[:, ::-1].copy()
+    got2 = ref.sparse_mla(q, kv, starts, q_seq, perm, wuv, 1.0 / 16)
+    np.testing.assert_allclose(got, got2, rtol=1e-12, atol=1e-14)
+    for t in range(3):
+        sel = idx[t][idx[t] >= 0]
+        mean = kv[sel, :512].mean(axis=0)
+        np.testing.assert_allclose(got[t], np.einsum("hvc,c->hv", wuv, mean), rtol=1e-12, atol=1e-13)
+
+
+def check_mla_hand_example(ref):
+    """Two rows, hand-computed.  One head sees dim 0 of the rope part:
+    q = 16 ln 3 at dim 512, row A has 0 there and row B has 1, so the logits
+    are 0 and ln 3 (scale 1/16) and the weights 1/4 and 3/4.  Latents:
+    A = (0, 4, 0, ...), B = (4, 0, 8, ...), so obar = (3, 1, 6, 0, ...).
+    W_UV of that head copies latent dims to value dims (v = c for c < 256),
+    so out = (3, 1, 6, 0, ...)."""
+    q = np.zeros((1, 64, 576))
+    q[0, 5, 512] = 16 * math.log(3.0)
+    kv = np.zeros((2, 576))
+    kv[0, 1] = 4.0
+    kv[1, 0], kv[1, 2], kv[1, 512] = 4.0, 8.0, 1.0
+    wuv = np.zeros((64, 256, 512))
+    wuv[5, np.arange(256), np.arange(256)] = 1.0
+    got = ref.sparse_mla(q, kv, [0], [0], np.array([[1, -1, 0]]), wuv, 1.0 / 16)
+    expect = np.zeros(256)
+    expect[:3] = [3.0, 1.0, 6.0]
+    np.testing.assert_allclose(got[0, 5], expect, rtol=1e-14, atol=1e-14)
+    assert np.all(got[0, :5] == 0.0) and np.all(got[0, 6:] == 0.0)
+
+
+def _simulate_fp32_bf16(ref, q_t, rows, wuv, scale):
+    """One allowed evaluation: fp32 logits and exp, weights rounded to bf16
+    for the value product, fp32 normaliser, latent average rounded to bf16,
+    fp32 up-projection, output rounded to bf16."""
+    r32 = rows.astype(np.float32)
+    z = (q_t.astype(np.float32) @ r32.T) * np.float32(scale)
+    e = np.exp(z - z.max(axis=1, keepdims=True)).astype(np.float32)
+    lsum = e.sum(axis=1, dtype=np.float32)
+    e16 = ref.round_to_bf16(e).astype(np.float32)
+    ob = (e16 @ r32[:, :512]) / lsum[:, None]
+    ob16 = ref.round_to_bf16(ob).astype(np.float32)
+    o = np.einsum("hvc,hc->hv", wuv.astype(np.float32), ob16)
+    return ref.round_to_bf16(o)
+
+
+def check_mla_error_bound_sane(ref):
+    """Both derived tolerances cover an allowed fp32 / bf16 re-evaluation;
+    the probabilistic one is small against the output's scale, so it can see
+    mistakes the worst-case one would hide."""
+    q, kv, starts, q_seq, q_pos, idx, wuv = _mla_inputs(53, 2, [3000], 2048)
+    out, obar, m, l, rows, p = ref.sparse_mla(q, kv, starts, q_seq, idx, wuv, 1.0 / 16, return_parts=True)
+    worst = ref.mla_error_bound(out, q, wuv, rows, p, 1.0 / 16, model="worst")
+    prob = ref.mla_error_bound(out, q, wuv, rows, p, 1.0 / 16)
+    for t in range(2):
+        sim = _simulate_fp32_bf16(ref, q[t], rows[t], wuv, 1.0 / 16)
+        assert np.all(np.abs(sim - out[t]) <= prob[t])
+        assert np.all(np.abs(sim - out[t]) <= worst[t])
+    assert np.all(prob <= worst)
+    assert np.max(prob - 2.0 ** -8 * np.abs(out)) < 0.25 * np.sqrt(np.mean(out ** 2))
+
+
+def check_round_to_bf16(ref):
+    """Round to nearest, ties to even, on hand-picked binary32 values:
+    1 + 2^-8 is a tie between 1 and 1 + 2^-7 and goes to the even 1;
+    1 + 3 * 2^-8 ties between 1 + 2^-7 and 1 + 2^-6 and goes up;
+    1 + 2^-8 + 2^-20 is above the tie and goes up."""
+    vals = np.array([1.0, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -20, -2.5, 0.0])
+    expect = [1.0, 1.0, 1 + 2.0 ** -6, 1 + 2.0 ** -7, -2.5, 0.0]
+    assert list(ref.round_to_bf16(vals)) == expect
+
+
+# --------------------------------------------------------------- layer stack
+def check_layer_pattern_matches_pages(ref):
+    g = json.load(open(os.path.join(GOLDEN, "layer_layout.json")))
+    printed = []
+    for count, flag in g["groups"]:
+        printed += [bool(flag)] * count
+    assert ref.layer_pattern(78) == printed
+    assert sum(printed) == g["indexer_types_full"] and len(printed) - sum(printed) == g["indexer_types_shared"]
+    for l in range(78):
+        src = ref.shared_source(l)
+        assert printed[src] and src <= l and all(not printed[j] for j in range(src + 1, l + 1))
+
+
+def check_cache_bytes_match_modelled_costs(ref):
+    """One 576-wide bf16 row per layer plus one 128-d bf16 indexer key per
+    full layer reproduces the pages' modelled 93 KiB per token and 93 GiB at
+    1M tokens."""
+    g = json.load(open(os.path.join(GOLDEN, "modelled_costs.json")))
+    n_full = sum(ref.layer_pattern(78))
+    per_tok = 78 * ref.ROW_DIM * 2 + n_full * ref.INDEX_HEAD_DIM * 2
+    assert round(per_tok / 1024) == g["kv_cache_per_token_kib"]
+    assert round(per_tok * g["context_tokens"] / 2 ** 30) == g["kv_cache_1m_tokens_gib"]
+
+
+def check_layer_stack_shares_selection(ref):
+    """A 4-layer stack [full, shared, shared, shared]: each shared layer's
+    output equals sparse_mla over the full layer's selection with the shared
+    layer's own inputs; a stack starting with a shared layer is refused."""
+    rng = _rng(59)
+    lens, qs, ps = [40, 33], [0, 1, 1], [39, 32, 20]
+    T = sum(lens)
+    layers = []
+    for l in range(4):
+        L = dict(q_abs=rng.standard_normal((3, 64, 576)) / 24, kv=rng.standard_normal((T, 576)),
+                 w_uv=rng.standard_normal((64, 256, 512)) / 22.6)
+        if l == 0:
+            L.update(q_idx=rng.standard_normal((3, 32, 128)) / 11, w=rng.standard_normal((3, 32)),
+                     k_idx=rng.standard_normal((T, 128)))
+        layers.append(L)
+    outs, idxs, _ = ref.layer_stack(layers, [0, 40], qs, ps, k=16, full=[True, False, False, False])
+    sc = ref.indexer_scores(layers[0]["q_idx"], layers[0]["w"], layers[0]["k_idx"], [0, 40], qs, ps)
+    sel = np.stack([sorted(range(ps[t] + 1), key=lambda s: (-sc[t, s], s))[:16] for t in range(3)])
+    assert np.array_equal(np.sort(sel, axis=1), idxs[0])
+    for l in range(4):
+        np.testing.assert_allclose(outs[l], ref.sparse_mla(layers[l]["q_abs"], layers[l]["kv"], [0, 40], qs, sel,
+                                                           layers[l]["w_uv"], 1.0 / 16), rtol=1e-12, atol=1e-14)
+    try:
+        ref.layer_stack(layers, [0, 40], qs, ps, k=16, full=[False, True, False, False])
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("stack starting with a shared layer accepted")
+
+
+ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

@@ -1,0 +1,70 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and require
+that at least one pin catches each of them.  This shows the pins constrain
+every step of the oracle, not only its happy path."""
+import inspect
+import types
+
+import pytest
+
+from oracle import ref
+from tests import oracle_pins
+
+SOURCE = inspect.getsource(ref)
+
+# (name, original text, planted mistake)
+MUTATIONS = [
+    ("relu_after_weight", "out[t, :n_t] = w[t] @ np.maximum(dots, 0.0)",
+     "out[t, :n_t] = np.maximum(w[t][:, None] * dots, 0.0).sum(axis=0)"),
+    ("no_relu", "out[t, :n_t] = w[t] @ np.maximum(dots, 0.0)", "out[t, :n_t] = w[t] @ dots"),
+    ("causal_excludes_diagonal", "        n_t = int(q_pos[t]) + 1\n        base", "        n_t = int(q_pos[t])\n        base"),
+    ("head_weights_reversed", "out[t, :n_t] = w[t] @ np.maximum(dots, 0.0)",
+     "out[t, :n_t] = w[t][::-1] @ np.maximum(dots, 0.0)"),
+    ("ignores_sequence_offset", "        base = int(seq_start[q_seq[t]])\n        keys", "        base = 0\n        keys"),
+    ("key_dims_reversed", "dots = q_idx[t] @ keys.T ", "dots = q_idx[t] @ keys[:, ::-1].T "),
+    ("query_of_wrong_token", "dots = q_idx[t] @ keys.T ", "dots = q_idx[(t + 1) % n_q] @ keys.T "),
+    ("ties_to_higher_position", "order = np.lexsort((positions, -row))", "order = np.lexsort((-positions, -row))"),
+    ("topk_smallest", "order = np.lexsort((positions, -row))", "order = np.lexsort((positions, row))"),
+    ("topk_ignores_causal_bound", "row = _f64(scores_row)[:n_t]", "row = _f64(scores_row)[:n_t + 1]"),
+    ("topk_off_by_one_k", "k_eff = min(int(k), n_t)", "k_eff = min(int(k) - 1, n_t)"),
+    ("mla_no_scale", "z = scale * (q_abs[t] @ rows.T)  ", "z = (q_abs[t] @ rows.T)  "),
+    ("mla_value_slice_wrong", "obar = p @ rows[:, :lat] ", "obar = p @ rows[:, -lat:] "),
+    ("mla_logits_drop_rope", "z = scale * (q_abs[t] @ rows.T)  ", "z = scale * (q_abs[t][:, :lat] @ rows[:, :lat].T)  "),
+    ("mla_head_mismatch", "out[t, h] = w_uv[h] @ obar[h]", "out[t, h] = w_uv[n_h - 1 - h] @ obar[h]"),
+    ("mla_softmax_over_heads", "m = z.max(axis=1, keepdims=True)\n        e = np.exp(z - m)\n        lsum = e.sum(axis=1, keepdims=True)",
+     "m = z.max(axis=0, keepdims=True)\n        e = np.exp(z - m)\n        lsum = e.sum(axis=0, keepdims=True)"),
+    ("mla_padding_not_skipped", "sel = idx[t][idx[t] >= 0]", "sel = idx[t]"),
+    ("mla_sequence_offset_ignored", "rows = _f64(kv[int(seq_start[q_seq[t]]) + sel])", "rows = _f64(kv[sel])"),
+    ("mla_no_normalisation", "p = e / lsum", "p = e"),
+    ("pattern_offset_wrong", "== INDEX_TOPK_FREQ - 1", "== 0"),
+    ("pattern_no_prefix", "if layer < INDEX_SKIP_TOPK_OFFSET:\n        return True", "if layer < 1:\n        return True"),
+    ("stack_shares_wrong_layer", "            cur = topk_select_rows(sc, q_pos, k)", "            cur = topk_select_rows(sc, q_pos, k - 1)"),
+    ("bf16_truncates", "rounded = (bits + 0x7FFF + lsb) >> 16", "rounded = bits >> 16"),
+    ("bf16_ties_away", "rounded = (bits + 0x7FFF + lsb) >> 16", "rounded = (bits + 0x8000) >> 16"),
+    ("bound_drops_dot_term", "return err_dot + err_sum", "return err_sum"),
+]
+
+
+def mutated_module(orig, new):
+    assert SOURCE.count(orig) >= 1, f"mutation anchor not found: {orig!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(SOURCE.replace(orig, new, 1), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name,orig,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_some_pin_catches(name, orig, new):
+    mod = mutated_module(orig, new)
+    caught = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check(mod)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(check.__name__)
+            break
+    assert caught, f"no pin catches the planted mistake {name}"
+
+
+def test_unmutated_source_passes():
+    mod = mutated_module("import numpy as np", "import numpy as np")
+    for check in oracle_pins.ALL_CHECKS:
+        check(mod)
