@@ -1,0 +1,258 @@
+// Indexer score kernels for gfx950.
+//
+// scores[t, s] = sum_h w[t, h] * max(0, q[t, h, :] . k[seq(t), s, :]) over the
+// causal set s <= q_pos[t], -inf beyond it (models.inteligile.com "GLM-5.2 /
+// Model techniques map", "Checked in its code", row "Indexer-selected sparse
+// attention (DeepSeek Sparse Attention)": 32 heads of 128 against one key per
+// token shared by every head).
+//
+// Both kernels put the 32 heads of one query on the M side of
+// v_mfma_f32_32x32x16_bf16 and 32 keys on the N side, so one accumulator tile
+// holds every head of one query for 32 keys: each lane owns one key column and
+// 16 of the 32 head rows, and the ReLU + weighted head sum is 16 in-lane
+// max/fma pairs plus one exchange with the lane 32 away.  The contraction
+// dimension (128) is consumed in 8 steps of 16; the split of each 16-wide step
+// between the two half-waves is the same for both operands, which is all the
+// sum needs.
+//
+//   indexer_decode_kernel   one query per workgroup column: streams that
+//                           query's keys once (decode: every query has its own
+//                           sequence).  HBM-bound: 256 B of keys per 8 KFLOP.
+//   indexer_prefill_kernel  8 queries of one sequence share each key tile staged
+//                           in LDS: the dense contraction of chunked prefill.
+#include "sa_common.h"
+
+namespace sa {
+
+// ---------------------------------------------------------------- helpers
+// Rows of the 32x32 accumulator owned by a lane: element i of the 16-vector
+// is row 8*(i/4) + 4*(lane/32) + (i%4), column lane%32.
+__device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
+
+__device__ __forceinline__ float relu_weighted_sum(const f32x16& acc, const float (&wr)[16]) {
+  float part = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) part = fmaf(wr[i], fmaxf(acc[i], 0.f), part);
+  return part + __shfl_xor(part, 32, 64);
+}
+
+// ------------------------------------------------------------ decode kernel
+constexpr int kDecWaves = 4;
+constexpr int kDecIters = 4;
+constexpr int kDecChunk = kDecWaves * 32 * kDecIters;   // keys per workgroup
+constexpr int kKeyPitch = 272;                            // LDS bytes per key row (256 + 16 pad)
+
+__global__ __launch_bounds__(256) void indexer_decode_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
+    const int64_t* __restrict__ seq_start, const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos,
+    float* __restrict__ scores, int64_t ld, int n_chunks) {
+  const int t = blockIdx.x / n_chunks;
+  const int chunk = blockIdx.x - t * n_chunks;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t pos = q_pos[t];
+  const int64_t c0 = (int64_t)chunk * kDecChunk;
+  float* srow = scores + (int64_t)t * ld;
+  if (c0 > pos) {
+    const int64_t end = min(c0 + (int64_t)kDecChunk, ld);
+    for (int64_t s = c0 + threadIdx.x; s < end; s += 256) srow[s] = -INFINITY;
+    return;
+  }
+  __shared__ __align__(16) uint8_t lds[kDecWaves][32 * kKeyPitch];
+
+  const uint16_t* qt = q_idx + (int64_t)t * kIdxHeads * kIdxDim;
+  bf16x8 a[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) a[s] = as_bf16x8(ld16(qt + (lane & 31) * kIdxDim + 16 * s + 8 * (lane >> 5)));
+  float wr[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) wr[i] = w[(int64_t)t * kIdxHeads + acc_row(i, lane)];
+  const uint16_t* kbase = k_idx + seq_start[q_seq[t]] * kIdxDim;
+  uint8_t* my = lds[wave];
+
+#pragma unroll 1
+  for (int it = 0; it < kDecIters; ++it) {
+    const int64_t key0 = c0 + (int64_t)(it * kDecWaves + wave) * 32;
+    // 8 KB of keys per wave: load j covers keys key0 + 4j .. +3, 16 B per lane.
+    u32x4 g[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t key = key0 + 4 * j + (lane >> 4);
+      g[j] = key <= pos ? ld16(kbase + key * kIdxDim + (lane & 15) * 8) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<u32x4*>(my + (4 * j + (lane >> 4)) * kKeyPitch + (lane & 15) * 16) = g[j];
+    __syncthreads();
+    f32x16 acc = {};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const u32x4 b = *reinterpret_cast<const u32x4*>(my + (lane & 31) * kKeyPitch + (2 * s + (lane >> 5)) * 16);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], as_bf16x8(b), acc, 0, 0, 0);
+    }
+    __syncthreads();
+    const float sc = relu_weighted_sum(acc, wr);
+    const int64_t key = key0 + (lane & 31);
+    if (lane < 32 && key < ld) srow[key] = key <= pos ? sc : -INFINITY;
+  }
+}
+
+// ----------------------------------------------------------- prefill kernel
+constexpr int kPfQ = 8;            // queries per workgroup (2 per wave)
+constexpr int kPfKT = 64;          // keys per tile
+constexpr int kPfSplit = 8192;     // keys per workgroup
+
+__global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
+    const int64_t* __restrict__ seq_start, const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos,
+    int n_q, float* __restrict__ scores, int64_t ld, int n_splits) {
+  const int qb = blockIdx.x / n_splits;
+  const int split = blockIdx.x - qb * n_splits;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t s0 = (int64_t)split * kPfSplit;
+  const int64_t s1 = min(s0 + (int64_t)kPfSplit, ld);
+  const int t_base = qb * kPfQ;
+
+  __shared__ __align__(16) uint8_t lds[2][kPfKT * kKeyPitch];
+  __shared__ int sh_seq[kPfQ];
+  __shared__ int sh_pos[kPfQ];
+  __shared__ int sh_done[kPfQ];
+  if (threadIdx.x < kPfQ) {
+    const int t = t_base + threadIdx.x;
+    sh_seq[threadIdx.x] = t < n_q ? q_seq[t] : -1;
+    sh_pos[threadIdx.x] = t < n_q ? q_pos[t] : -1;
+    sh_done[threadIdx.x] = t < n_q ? 0 : 1;
+  }
+  __syncthreads();
+
+  // This wave's two queries: A operands in registers, weights per accumulator row.
+  bf16x8 a[2][8];
+  float wr[2][16];
+  int64_t pos[2];
+  int seq[2];
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq) {
+    const int lq = 2 * wave + qq;
+    const int t = min(t_base + lq, n_q - 1);
+    pos[qq] = sh_pos[lq];
+    seq[qq] = sh_seq[lq];
+    const uint16_t* qt = q_idx + (int64_t)t * kIdxHeads * kIdxDim;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) a[qq][s] = as_bf16x8(ld16(qt + (lane & 31) * kIdxDim + 16 * s + 8 * (lane >> 5)));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) wr[qq][i] = w[(int64_t)t * kIdxHeads + acc_row(i, lane)];
+  }
+
+  // Queries of one block may belong to several sequences: handle one sequence
+  // per pass, the others' rows stay untouched in that pass.
+#pragma unroll 1
+  for (int pass = 0; pass < kPfQ; ++pass) {
+    int cur = -1;
+    int64_t maxpos = -1;
+    for (int i = 0; i < kPfQ; ++i)
+      if (!sh_done[i] && cur < 0) cur = sh_seq[i];
+    if (cur < 0) break;
+    for (int i = 0; i < kPfQ; ++i)
+      if (!sh_done[i] && sh_seq[i] == cur) maxpos = max(maxpos, (int64_t)sh_pos[i]);
+    const bool act0 = seq[0] == cur && pos[0] >= 0;
+    const bool act1 = seq[1] == cur && pos[1] >= 0;
+    const uint16_t* kbase = k_idx + seq_start[cur] * kIdxDim;
+    const int64_t cend = min(s1, maxpos + 1);              // keys that need a product
+    const int n_tiles = cend > s0 ? (int)((cend - s0 + kPfKT - 1) / kPfKT) : 0;
+
+    // prologue: tile 0 into buffer 0
+    u32x4 g[4];
+    auto load_tile = [&](int tile) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int flat = j * 256 + threadIdx.x;            // 16-byte piece within the 16 KB tile
+        const int64_t key = s0 + (int64_t)tile * kPfKT + (flat >> 4);
+        g[j] = key <= maxpos ? ld16(kbase + key * kIdxDim + (flat & 15) * 8) : u32x4{0, 0, 0, 0};
+      }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int flat = j * 256 + threadIdx.x;
+        *reinterpret_cast<u32x4*>(lds[buf] + (flat >> 4) * kKeyPitch + (flat & 15) * 16) = g[j];
+      }
+    };
+    if (n_tiles > 0) {
+      load_tile(0);
+      store_tile(0);
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int tile = 0; tile < n_tiles; ++tile) {
+      const int buf = tile & 1;
+      if (tile + 1 < n_tiles) load_tile(tile + 1);
+      const int64_t kt0 = s0 + (int64_t)tile * kPfKT;
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const u32x4 b = *reinterpret_cast<const u32x4*>(lds[buf] + (n * 32 + (lane & 31)) * kKeyPitch +
+                                                          (2 * s + (lane >> 5)) * 16);
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][s], as_bf16x8(b), acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][s], as_bf16x8(b), acc1, 0, 0, 0);
+        }
+        const float sc0 = relu_weighted_sum(acc0, wr[0]);
+        const float sc1 = relu_weighted_sum(acc1, wr[1]);
+        const int64_t key = kt0 + n * 32 + (lane & 31);
+        if (lane < 32 && key < s1) {
+          if (act0) scores[(int64_t)(t_base + 2 * wave) * ld + key] = key <= pos[0] ? sc0 : -INFINITY;
+          if (act1) scores[(int64_t)(t_base + 2 * wave + 1) * ld + key] = key <= pos[1] ? sc1 : -INFINITY;
+        }
+      }
+      if (tile + 1 < n_tiles) store_tile(buf ^ 1);
+      __syncthreads();
+    }
+    // keys of this split past the last needed tile: -inf for the active queries
+    const int64_t fill0 = s0 + (int64_t)n_tiles * kPfKT;
+    for (int64_t s = fill0 + lane; s < s1; s += 64) {
+      if (act0) scores[(int64_t)(t_base + 2 * wave) * ld + s] = -INFINITY;
+      if (act1) scores[(int64_t)(t_base + 2 * wave + 1) * ld + s] = -INFINITY;
+    }
+    __syncthreads();
+    if (threadIdx.x < kPfQ && sh_seq[threadIdx.x] == cur) sh_done[threadIdx.x] = 1;
+    __syncthreads();
+  }
+}
+
+}  // namespace sa
+
+// ------------------------------------------------------------------ launchers
+namespace sa_host {
+
+int32_t launch_indexer(const void* q_idx, const float* w, const void* k_idx, const int64_t* seq_start,
+                       const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, float* scores, int64_t ld,
+                       int algo, hipStream_t stream) {
+  if (algo == 0) algo = n_q >= 64 ? 2 : 1;
+  if (algo == 1) {
+    const int n_chunks = (int)((ld + sa::kDecChunk - 1) / sa::kDecChunk);
+    const int64_t grid = (int64_t)n_chunks * n_q;
+    if (grid > 0x7fffffff) {
+      set_error("indexer: grid of %lld workgroups is too large", (long long)grid);
+      return SA_ERR_UNSUPPORTED;
+    }
+    hipLaunchKernelGGL(sa::indexer_decode_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                       (const uint16_t*)q_idx, w, (const uint16_t*)k_idx, seq_start, q_seq, q_pos, scores, ld,
+                       n_chunks);
+    return check_launch("indexer_decode_kernel");
+  }
+  const int n_splits = (int)((ld + sa::kPfSplit - 1) / sa::kPfSplit);
+  const int n_qb = (n_q + sa::kPfQ - 1) / sa::kPfQ;
+  const int64_t grid = (int64_t)n_splits * n_qb;
+  if (grid > 0x7fffffff) {
+    set_error("indexer: grid of %lld workgroups is too large", (long long)grid);
+    return SA_ERR_UNSUPPORTED;
+  }
+  hipLaunchKernelGGL(sa::indexer_prefill_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                     (const uint16_t*)q_idx, w, (const uint16_t*)k_idx, seq_start, q_seq, q_pos, n_q, scores, ld,
+                     n_splits);
+  return check_launch("indexer_prefill_kernel");
+}
+
+}  // namespace sa_host

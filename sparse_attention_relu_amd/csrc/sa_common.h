@@ -1,0 +1,68 @@
+// Shared device helpers for the gfx950 kernels of libsparse_mla.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/sparse_mla.h"
+
+namespace sa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kIdxHeads = SA_INDEX_HEADS;
+constexpr int kIdxDim = SA_INDEX_DIM;
+constexpr int kMaxTopk = SA_MAX_TOPK;
+constexpr int kHeads = SA_HEADS;
+constexpr int kLatent = SA_LATENT;
+constexpr int kRope = SA_ROPE;
+constexpr int kRow = SA_ROW;
+constexpr int kVdim = SA_VDIM;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ s16x4 as_s16x4(u32x2 v) { return __builtin_bit_cast(s16x4, v); }
+
+// 16-byte global load (plain vector load; the compiler emits global_load_dwordx4).
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// fp32 -> bf16 with round-to-nearest-even; NaN stays NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// Order-preserving map of an fp32 score to uint32: a > b (as floats) iff
+// key(a) > key(b); -0.0 is folded onto +0.0 so equal values tie.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <typename T>
+__device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+}  // namespace sa
+
+// Host-side error plumbing shared by the launchers.
+namespace sa_host {
+void set_error(const char* fmt, ...);
+int32_t check_launch(const char* what);
+}  // namespace sa_host

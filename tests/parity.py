@@ -1,0 +1,108 @@
+"""Parity checks of the HIP path against the CPU oracle (used by the gpu tests).
+
+Tolerances (written here, derived in the oracle):
+  indexer scores   |gpu - exact| <= score_error_bound (worst-case fp32
+                   summation bound over any order), entries past q_pos are -inf.
+  top-k            the oracle's selection run on the GPU's own fp32 scores must
+                   equal the GPU's idx exactly (an integer decision taken in the
+                   kernel's precision); against the oracle's exact scores, every
+                   position in the symmetric difference must score within
+                   1e-3 * |I(sigma_k)| + eps(sigma_k) + eps(s) of the oracle's
+                   k-th pick sigma_k (eps = the score error bound).
+  attention        the benchmark spec bar: |gpu - oracle| <= 2e-2 + 1e-2 |oracle|;
+                   and the derived probabilistic bound of mla_error_bound.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import ref
+from sparse_attention_relu_amd.synth import to_numpy
+
+
+def np_batch(batch):
+    return dict(seq_start=to_numpy(batch.seq_start), q_seq=to_numpy(batch.q_seq), q_pos=to_numpy(batch.q_pos))
+
+
+def check_scores(L, B, scores_gpu, rows=None):
+    """L: numpy layer dict (q_idx, w, k_idx); B: numpy batch dict; scores_gpu float64 [n_q, ld]."""
+    n_q, ld = scores_gpu.shape
+    rows = range(n_q) if rows is None else rows
+    worst = 0.0
+    for t in rows:
+        p = int(B["q_pos"][t])
+        exact = ref.indexer_scores_at(L["q_idx"], L["w"], L["k_idx"], B["seq_start"], B["q_seq"], B["q_pos"], t,
+                                      np.arange(p + 1))
+        base = int(B["seq_start"][B["q_seq"][t]])
+        bound = ref.score_error_bound(L["q_idx"][t], L["w"][t], L["k_idx"][base:base + p + 1])
+        err = np.abs(scores_gpu[t, :p + 1] - exact)
+        bad = np.nonzero(err > bound)[0]
+        assert bad.size == 0, f"row {t}: {bad.size} scores outside the fp32 bound, first at s={bad[0]}: " \
+                              f"gpu={scores_gpu[t, bad[0]]!r} exact={exact[bad[0]]!r} bound={bound[bad[0]]!r}"
+        assert np.all(np.isneginf(scores_gpu[t, p + 1:])), f"row {t}: entries past q_pos are not -inf"
+        worst = max(worst, float(np.max(err / np.maximum(bound, 1e-300))))
+    return worst
+
+
+def check_topk_exact(scores_gpu, q_pos, k, idx_gpu, rows=None):
+    """The oracle's selection on the GPU's own scores equals the GPU's idx."""
+    rows = range(scores_gpu.shape[0]) if rows is None else rows
+    for t in rows:
+        expect = ref.topk_select(scores_gpu[t], int(q_pos[t]), k)
+        got = idx_gpu[t]
+        if not np.array_equal(expect, got):
+            d = np.setxor1d(expect[expect >= 0], got[got >= 0])
+            raise AssertionError(f"row {t}: top-k differs from the oracle on the GPU's scores "
+                                 f"({d.size} positions differ, first {d[:8]}); got head {got[:8]} tail {got[-4:]}")
+
+
+def check_topk_band(L, B, idx_gpu, k, rows=None):
+    """The GPU's selection against the oracle's exact scores, with the tie band."""
+    n_q = idx_gpu.shape[0]
+    rows = range(n_q) if rows is None else rows
+    for t in rows:
+        p = int(B["q_pos"][t])
+        exact = ref.indexer_scores_at(L["q_idx"], L["w"], L["k_idx"], B["seq_start"], B["q_seq"], B["q_pos"], t,
+                                      np.arange(p + 1))
+        row = np.full(p + 1, -np.inf)
+        row[:] = exact
+        orc = ref.topk_select(row, p, k)
+        got = idx_gpu[t]
+        k_eff = min(k, p + 1)
+        assert np.all(got[k_eff:] == -1) and np.all(got[:k_eff] >= 0) and np.all(got[:k_eff] <= p)
+        assert np.all(np.diff(got[:k_eff]) > 0), f"row {t}: idx not strictly ascending"
+        diff = np.setxor1d(orc[orc >= 0], got[got >= 0])
+        if diff.size == 0:
+            continue
+        sel = orc[orc >= 0]
+        sigma = sel[np.lexsort((-sel, exact[sel]))[0]]      # the oracle's k-th pick
+        base = int(B["seq_start"][B["q_seq"][t]])
+        keys = L["k_idx"][base:base + p + 1]
+        eps = ref.score_error_bound(L["q_idx"][t], L["w"][t], keys[np.concatenate([[sigma], diff])])
+        tau = 1e-3 * abs(exact[sigma]) + eps[0] + eps[1:]
+        gap = np.abs(exact[diff] - exact[sigma])
+        assert np.all(gap <= tau), f"row {t}: swapped positions outside the tie band: {diff[gap > tau][:8]}"
+
+
+def check_mla(Lnp, B, idx_gpu, out_gpu, scale, rows=None, lse_gpu=None):
+    """out_gpu float64 [n_q, 64, 256] (bf16 widened); idx_gpu int64 [n_q, k]."""
+    rows = list(range(idx_gpu.shape[0])) if rows is None else list(rows)
+    sub = lambda a: a[rows]
+    out, obar, m, l, rows_l, p_l = ref.sparse_mla(sub(Lnp["q_abs"]), Lnp["kv"], B["seq_start"], sub(B["q_seq"]),
+                                                  sub(idx_gpu), Lnp["w_uv"], scale, return_parts=True)
+    got = out_gpu[rows]
+    err = np.abs(got - out)
+    ns = 2e-2 + 1e-2 * np.abs(out)
+    assert np.all(err <= ns), f"outside the 2e-2 + 1e-2|x| bar: max err {err.max()}"
+    bound = ref.mla_error_bound(out, sub(Lnp["q_abs"]), Lnp["w_uv"], rows_l, p_l, scale)
+    bad = np.argwhere(err > bound)
+    assert bad.size == 0, f"{len(bad)} outputs outside the derived bound; first {bad[0]}: " \
+                          f"gpu={got[tuple(bad[0])]} oracle={out[tuple(bad[0])]} bound={bound[tuple(bad[0])]}"
+    if lse_gpu is not None:
+        np.testing.assert_allclose(lse_gpu[rows], m + np.log(l), rtol=1e-5, atol=1e-5)
+    return float(np.max(err / np.maximum(bound, 1e-300)))
+
+
+def layer_np(L):
+    return {k: to_numpy(getattr(L, k)) for k in ("q_idx", "w", "k_idx", "q_abs", "kv", "w_uv")}

@@ -1,0 +1,107 @@
+"""The C ABI on the host: the library loads, exports every declared entry
+point, and rejects bad arguments before touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from oracle import ref
+from sparse_attention_relu_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "sparse_mla.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sa_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in _lib.SIGNATURES, f"binding has no signature for {n}"
+
+
+def test_version_and_status_strings(L):
+    assert L.sa_version() > 0
+    for code, text in [(0, b"ok"), (-1, b"invalid argument"), (-2, b"unsupported request"),
+                       (-3, b"workspace missing or too small"), (-4, b"HIP runtime error")]:
+        assert L.sa_status_string(code) == text
+    assert L.sa_status_string(-99) == b"unknown status"
+
+
+def test_layer_pattern_matches_oracle(L):
+    assert [L.sa_layer_is_full(l) == 1 for l in range(78)] == ref.layer_pattern(78)
+    assert L.sa_layer_is_full(-1) == -1
+
+
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails its host checks
+
+
+def test_indexer_rejects_bad_arguments(L):
+    assert L.sa_indexer_score(None, None, None, None, None, None, 1, 1, None, 10, None) == -1
+    assert b"null pointer" in L.sa_last_error_message()
+    assert L.sa_indexer_score(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -1, 1, FAKE, 10, None) == -1
+    assert L.sa_indexer_score(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, FAKE, 0, None) == -1
+    assert L.sa_indexer_score(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 0, FAKE, 5, None) == -1
+    assert L.sa_indexer_score(ctypes.c_void_p(0x10008), FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, FAKE, 5, None) == -1
+    assert b"aligned" in L.sa_last_error_message()
+    assert L.sa_indexer_score_algo(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, FAKE, 5, 7, None) == -1
+    # n_q = 0 is a no-op that succeeds without a device
+    assert L.sa_indexer_score(None, None, None, None, None, None, 0, 0, None, 1, None) == 0
+
+
+def test_topk_rejects_bad_arguments(L):
+    assert L.sa_topk_select(FAKE, 100, FAKE, 4, 0, FAKE, FAKE, 1 << 30, None) == -1
+    assert b"k=0" in L.sa_last_error_message()
+    assert L.sa_topk_select(FAKE, 100, FAKE, 4, 2049, FAKE, FAKE, 1 << 30, None) == -1
+    assert L.sa_topk_select(FAKE, 100, FAKE, 4, 16, FAKE, FAKE, 16, None) == -3
+    assert L.sa_topk_select(FAKE, 100, FAKE, 4, 16, FAKE, None, 1 << 30, None) == -3
+    assert L.sa_topk_select(None, 100, FAKE, 4, 16, FAKE, FAKE, 1 << 30, None) == -1
+    assert L.sa_topk_select_algo(FAKE, 100, FAKE, 4, 16, FAKE, FAKE, 1 << 30, 3, None) == -1
+    assert L.sa_topk_select(None, 100, None, 0, 16, None, None, 0, None) == 0
+
+
+def test_mla_rejects_bad_arguments(L):
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 2, 16, FAKE, 1.0 / 16, FAKE, None, FAKE, 1 << 30, None]
+    assert L.sa_mla_sparse_attn(*args[:6], 0, *args[7:]) == -1
+    assert L.sa_mla_sparse_attn(*args[:8], -1.0, *args[9:]) == -1
+    assert L.sa_mla_sparse_attn(*args[:12], 64, None) == -3
+    bad = list(args)
+    bad[1] = ctypes.c_void_p(0x10002)
+    assert L.sa_mla_sparse_attn(*bad) == -1
+
+
+def test_layer_stack_rejects_bad_arguments(L):
+    descs = (_lib.LayerDesc * 2)()
+    for d in descs:
+        d.q_idx = d.w = d.k_idx = d.idx = d.q_abs = d.kv = d.w_uv = d.out = 0x10000
+    descs[0].is_full, descs[1].is_full = 0, 1
+    batch = _lib.BatchDesc(0x10000, 0x10000, 0x10000, 4, 1, 100)
+    big = 1 << 40
+    rc = L.sa_layer_stack(descs, 2, ctypes.byref(batch), 2048, 1.0 / 16, FAKE, big, None, None)
+    assert rc == -1 and b"layer 0" in L.sa_last_error_message()
+    descs[0].is_full = 1
+    assert L.sa_layer_stack(descs, 2, ctypes.byref(batch), 2048, 1.0 / 16, FAKE, 64, None, None) == -3
+    descs[1].kv = 0x10002
+    rc = L.sa_layer_stack(descs, 2, ctypes.byref(batch), 2048, 1.0 / 16, FAKE, big, None, None)
+    assert rc == -1 and b"layer 1" in L.sa_last_error_message()
+    assert L.sa_layer_stack(descs, 2, ctypes.byref(batch), 0, 1.0 / 16, FAKE, big, None, None) == -1
+    assert L.sa_layer_stack(None, 2, ctypes.byref(batch), 16, 1.0 / 16, FAKE, big, None, None) == -1
+
+
+def test_workspace_sizes(L):
+    assert L.sa_topk_workspace_size(16, 131072, 2048) >= 16 * (4096 * 4 + 2048 * 4)
+    assert L.sa_mla_workspace_size(16, 2048) >= 16 * 64 * 512 * 4
+    s = L.sa_layer_stack_workspace_size(16, 131072, 2048)
+    assert s >= 16 * 131072 * 4 + L.sa_topk_workspace_size(16, 131072, 2048)
+    assert L.sa_topk_workspace_size(0, 10, 5) > 0 and L.sa_mla_workspace_size(0, 5) > 0

@@ -1,0 +1,210 @@
+"""HIP path against the CPU oracle, element by element, at sizes the oracle
+finishes in seconds (several tiles, ragged tails, edge cases).  Every call
+goes through the C ABI (libsparse_mla.so via the ctypes binding)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import ref
+from sparse_attention_relu_amd import api, synth
+from sparse_attention_relu_amd.synth import to_numpy
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _batch(wl, seed=0):
+    torch.manual_seed(seed)
+    return synth.make_batch(wl, DEV, seed=seed)
+
+
+def ragged_wl(n_layers=1, k=2048):
+    lens = [3000, 17, 2100, 5000, 9000]
+    queries = [(0, 2999), (1, 16), (2, 2047), (2, 2048), (3, 4999), (3, 0), (4, 8999), (4, 4500)]
+    return synth.ragged_workload(lens, queries, n_layers=n_layers, k=k, name="ragged")
+
+
+def prefill_wl():
+    # 100 consecutive queries of one sequence plus a block that mixes two sequences
+    lens = [6000, 3500]
+    queries = [(0, 5900 + i) for i in range(100)] + [(i % 2, 3000 + 37 * i) for i in range(12)]
+    return synth.ragged_workload(lens, queries, name="prefill_small")
+
+
+CASES = {"c0": lambda: synth.workload("c0"), "ragged": ragged_wl, "prefill": prefill_wl}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+@pytest.mark.parametrize("algo", [1, 2])
+def test_indexer_scores(gpu_lib, case, algo):
+    wl = CASES[case]()
+    b = _batch(wl)
+    L = b.layers[0]
+    sc = api.indexer_score(L.q_idx, L.w, L.k_idx, b.seq_start, b.q_seq, b.q_pos, wl.ld + 37, algo=algo)
+    torch.cuda.synchronize()
+    worst = parity.check_scores(parity.layer_np(L), parity.np_batch(b), to_numpy(sc))
+    print(f"{case} algo {algo}: worst |err|/bound = {worst:.3g}")
+
+
+@pytest.mark.parametrize("case", list(CASES))
+@pytest.mark.parametrize("algo", [1, 2])
+def test_topk_on_gpu_scores(gpu_lib, case, algo):
+    wl = CASES[case]()
+    b = _batch(wl)
+    L = b.layers[0]
+    sc = api.indexer_score(L.q_idx, L.w, L.k_idx, b.seq_start, b.q_seq, b.q_pos, wl.ld)
+    for k in (2048, 1000, 1):
+        idx = api.topk_select(sc, b.q_pos, k=k, algo=algo)
+        torch.cuda.synchronize()
+        parity.check_topk_exact(to_numpy(sc), to_numpy(b.q_pos), k, to_numpy(idx))
+        parity.check_topk_band(parity.layer_np(L), parity.np_batch(b), to_numpy(idx), k)
+
+
+def _synthetic_scores(kind, n_rows, ld, seed):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    if kind == "quantised":      # few distinct values: heavy ties everywhere
+        return (torch.randint(-3, 4, (n_rows, ld), generator=g, device=DEV).float() * 0.25)
+    if kind == "zeros_signed":   # +0.0 and -0.0 only: all tie
+        x = torch.zeros((n_rows, ld), device=DEV)
+        neg = torch.rand((n_rows, ld), generator=g, device=DEV) < 0.5
+        return torch.where(neg, torch.full_like(x, -0.0), x)
+    if kind == "normal":
+        return torch.randn((n_rows, ld), generator=g, device=DEV)
+    if kind == "spiky":          # a few huge values, many tiny ones, negatives
+        x = torch.randn((n_rows, ld), generator=g, device=DEV) * 1e-3
+        x[:, ::97] = 1e30
+        x[:, 5::11] = -1e30
+        return x
+    raise KeyError(kind)
+
+
+@pytest.mark.parametrize("kind", ["quantised", "zeros_signed", "normal", "spiky"])
+@pytest.mark.parametrize("algo", [1, 2])
+def test_topk_ties_and_edges(gpu_lib, kind, algo):
+    ld = 70000
+    sc = _synthetic_scores(kind, 6, ld, 7)
+    q_pos = torch.tensor([ld - 1, 0, 2047, 2048, 40000, 69998], dtype=torch.int32, device=DEV)
+    for k in (2048, 513, 1):
+        idx = api.topk_select(sc, q_pos, k=k, algo=algo)
+        torch.cuda.synchronize()
+        parity.check_topk_exact(to_numpy(sc), to_numpy(q_pos), k, to_numpy(idx))
+
+
+def test_topk_paths_agree_bitwise(gpu_lib):
+    sc = _synthetic_scores("normal", 40, 131072, 3)
+    q_pos = torch.randint(0, 131072, (40,), dtype=torch.int32, device=DEV)
+    a = api.topk_select(sc, q_pos, algo=1)
+    b = api.topk_select(sc, q_pos, algo=2)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("case", ["c0", "ragged"])
+def test_mla_on_gpu_selection(gpu_lib, case):
+    wl = CASES[case]()
+    b = _batch(wl)
+    L = b.layers[0]
+    sc = api.indexer_score(L.q_idx, L.w, L.k_idx, b.seq_start, b.q_seq, b.q_pos, wl.ld)
+    idx = api.topk_select(sc, b.q_pos, k=2048)
+    lse = torch.empty((wl.n_q, 64), dtype=torch.float32, device=DEV)
+    out = api.mla_sparse_attn(L.q_abs, L.kv, b.seq_start, b.q_seq, idx, L.w_uv, wl.scale, lse=lse)
+    torch.cuda.synchronize()
+    worst = parity.check_mla(parity.layer_np(L), parity.np_batch(b), to_numpy(idx), to_numpy(out), wl.scale,
+                             lse_gpu=to_numpy(lse))
+    print(f"{case}: worst |err|/bound = {worst:.3g}")
+
+
+@pytest.mark.parametrize("k", [1, 7, 64, 300])
+def test_mla_small_k_and_padding(gpu_lib, k):
+    wl = ragged_wl(k=k)
+    b = _batch(wl, seed=5)
+    L = b.layers[0]
+    g = torch.Generator(device="cpu").manual_seed(k)
+    idx = torch.full((wl.n_q, k), -1, dtype=torch.int32)
+    for t, p in enumerate(wl.q_pos):
+        n = min(k, p + 1)
+        pick = torch.randperm(p + 1, generator=g)[:n]
+        slots = torch.randperm(k, generator=g)[:n]        # padding anywhere in the row
+        idx[t, slots] = pick.int()
+    idx = idx.to(DEV)
+    out = api.mla_sparse_attn(L.q_abs, L.kv, b.seq_start, b.q_seq, idx, L.w_uv, wl.scale)
+    torch.cuda.synchronize()
+    parity.check_mla(parity.layer_np(L), parity.np_batch(b), to_numpy(idx), to_numpy(out), wl.scale)
+
+
+def test_mla_empty_selection_gives_zero(gpu_lib):
+    wl = ragged_wl(k=8)
+    b = _batch(wl, seed=9)
+    L = b.layers[0]
+    idx = torch.full((wl.n_q, 8), -1, dtype=torch.int32, device=DEV)
+    idx[0, 3] = 5
+    out = api.mla_sparse_attn(L.q_abs, L.kv, b.seq_start, b.q_seq, idx, L.w_uv, wl.scale)
+    torch.cuda.synchronize()
+    assert torch.all(out[1:] == 0)
+    parity.check_mla(parity.layer_np(L), parity.np_batch(b), to_numpy(idx), to_numpy(out), wl.scale, rows=[0])
+
+
+def test_layer_stack_matches_separate_calls(gpu_lib):
+    wl = ragged_wl(n_layers=4)
+    wl.full = [True, False, False, True]
+    b = _batch(wl, seed=11)
+    stack = api.LayerStack(b.layers, b.seq_start, b.q_seq, b.q_pos, wl.ld, full=wl.full)
+    outs, idxs = stack()
+    torch.cuda.synchronize()
+    cur = None
+    for l, L in enumerate(b.layers):
+        if wl.full[l]:
+            sc = api.indexer_score(L.q_idx, L.w, L.k_idx, b.seq_start, b.q_seq, b.q_pos, wl.ld)
+            cur = api.topk_select(sc, b.q_pos)
+            assert torch.equal(cur, idxs[l])
+        o = api.mla_sparse_attn(L.q_abs, L.kv, b.seq_start, b.q_seq, cur, L.w_uv, wl.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(o, outs[l]), f"layer {l}"
+    # layer 2 reuses layer 0's selection, checked against the oracle with its own inputs
+    B = parity.np_batch(b)
+    parity.check_mla(parity.layer_np(b.layers[2]), B, to_numpy(idxs[0]), to_numpy(outs[2]), wl.scale)
+    parity.check_topk_band(parity.layer_np(b.layers[3]), B, to_numpy(idxs[3]), 2048)
+
+
+def test_deterministic(gpu_lib):
+    wl = ragged_wl(n_layers=2)
+    b = _batch(wl, seed=13)
+    stack = api.LayerStack(b.layers, b.seq_start, b.q_seq, b.q_pos, wl.ld)
+    o1, i1 = stack()
+    o1 = [x.clone() for x in o1]
+    i1 = i1[0].clone()
+    o2, i2 = stack()
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2[0])
+    for a, c in zip(o1, o2):
+        assert torch.equal(a, c)
+
+
+def test_graph_replay_matches_eager(gpu_lib):
+    wl = ragged_wl(n_layers=4)
+    b = _batch(wl, seed=17)
+    stack = api.LayerStack(b.layers, b.seq_start, b.q_seq, b.q_pos, wl.ld)
+    outs, idxs = stack()
+    torch.cuda.synchronize()
+    ref_o = [o.clone() for o in outs]
+    ref_i = idxs[0].clone()
+    for o in outs:
+        o.zero_()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            stack()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in outs:
+            o.zero_()
+        idxs[0].fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idxs[0], ref_i), rep
+        for a, c in zip(outs, ref_o):
+            assert torch.equal(a, c), rep
