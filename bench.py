@@ -1,0 +1,257 @@
+"""Benchmark of the sparse MLA hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: sa_layer_stack over the
+decode workload of 16 sequences with 65,536..131,072 cached tokens each (seeded
+ragged lengths) and a 4-layer IndexShare group [full, shared, shared, shared]:
+indexer score -> exact top-2048 -> sparse MLA + W_UV on the full layer, sparse
+MLA + W_UV with the reused selection on the three shared layers.
+
+Output: one JSON line.  `value` is decode queries/s of back-to-back HIP-graph
+replays of the step with inputs resident in HBM.  `roofline` describes the
+dominant kernel (the decode indexer, ~2/3 of the step's bytes), timed with HIP
+events recorded on the library's stream around that kernel in eager steps that
+follow a 1 GiB cache flush.  `prefill_indexer` is the chunked-prefill indexer
+(4096 queries over 131,072 keys) in TFLOP/s.  `cpu_baseline` is the CPU oracle
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2", choices=["c0", "c1", "c2", "c4"])
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill indexer measurement")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-sample", type=int, default=4, help="queries in the CPU oracle sample")
+    ap.add_argument("--seed", type=int, default=0)
+    return ap.parse_args()
+
+
+def step_bytes(wl, k=2048):
+    """Algorithmic HBM bytes of one step: every input read once, every output
+    written once (intermediate scores and partial results excluded)."""
+    n_q = wl.n_q
+    keys = sum(p + 1 for p in wl.q_pos)
+    idx_bytes = keys * 256 + n_q * (32 * 128 * 2 + 32 * 4)
+    k_eff = sum(min(k, p + 1) for p in wl.q_pos)
+    per_layer = k_eff * 576 * 2 + n_q * 64 * 576 * 2 + 64 * 256 * 512 * 2 + n_q * 64 * 256 * 2
+    n_full = sum(wl.full)
+    return idx_bytes * n_full + per_layer * wl.n_layers + n_full * n_q * k * 4, idx_bytes
+
+
+def cpu_baseline(b, wl, n_sample):
+    """The CPU oracle (NumPy, float64) on the first n_sample queries: indexer
+    scores and top-k for the full layer, sparse MLA + W_UV for all layers.
+    Gathering the selected rows from device memory is done outside the timer."""
+    import numpy as np
+    import torch
+    from oracle import ref
+    from sparse_attention_relu_amd.synth import to_numpy
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    S = list(range(min(n_sample, wl.n_q)))
+    seq = [wl.q_seq[t] for t in S]
+    pos = [wl.q_pos[t] for t in S]
+    starts = wl.seq_start
+    L0 = b.layers[0]
+    kparts = [to_numpy(L0.k_idx[starts[s]:starts[s] + p + 1]) for s, p in zip(seq, pos)]
+    loc_start = np.concatenate([[0], np.cumsum([len(x) for x in kparts])[:-1]]).astype(np.int64)
+    k_cpu = np.concatenate(kparts)
+    q_cpu, w_cpu = to_numpy(L0.q_idx[S]), to_numpy(L0.w[S])
+    t0 = time.perf_counter()
+    sc = ref.indexer_scores(q_cpu, w_cpu, k_cpu, loc_start, np.arange(len(S)), np.array(pos))
+    idx = ref.topk_select_rows(sc, np.array(pos), 2048)
+    t_idx = time.perf_counter() - t0
+    t_mla = 0.0
+    for L in b.layers:
+        rows, qa = [], to_numpy(L.q_abs[S])
+        for j, t in enumerate(S):
+            sel = torch.as_tensor(idx[j][idx[j] >= 0], device=L.kv.device) + starts[seq[j]]
+            rows.append(to_numpy(L.kv[sel]))
+        k_loc = np.concatenate(rows)
+        st = np.concatenate([[0], np.cumsum([len(r) for r in rows])[:-1]]).astype(np.int64)
+        loc_idx = np.full(idx.shape, -1)
+        for j in range(len(S)):
+            n = len(rows[j])
+            loc_idx[j, :n] = np.arange(n)
+        wuv = to_numpy(L.w_uv)
+        t0 = time.perf_counter()
+        ref.sparse_mla(qa, k_loc, st, np.arange(len(S)), loc_idx, wuv, wl.scale)
+        t_mla += time.perf_counter() - t0
+    total = t_idx + t_mla
+    return {"value": len(S) / total, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {len(S)} of {wl.n_q} queries of the same workload, all {wl.n_layers} layers "
+                      f"(indexer {t_idx:.2f} s, attention {t_mla:.2f} s)",
+            "seconds": round(total, 3)}
+
+
+def prefill_indexer(seed, reps=5):
+    import torch
+    from sparse_attention_relu_amd import api, synth
+    wl = synth.workload("c3")
+    dev = torch.device("cuda:0")
+    g = synth._gen(dev, seed, 0, 4)
+    q = synth._randn((wl.n_q, 32, 128), g, dev, std=1 / 128 ** 0.5, dtype=torch.bfloat16)
+    w = synth._randn((wl.n_q, 32), synth._gen(dev, seed, 0, 5), dev, std=1 / 32 ** 0.5)
+    kI = synth.indexer_keys(wl.total_tokens, synth._gen(dev, seed, 0, 6), dev)
+    seq_start = torch.zeros(1, dtype=torch.int64, device=dev)
+    q_seq = torch.zeros(wl.n_q, dtype=torch.int32, device=dev)
+    q_pos = torch.tensor(wl.q_pos, dtype=torch.int32, device=dev)
+    scores = torch.empty((wl.n_q, wl.ld), dtype=torch.float32, device=dev)
+    for _ in range(2):
+        api.indexer_score(q, w, kI, seq_start, q_seq, q_pos, wl.ld, scores=scores)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, c in ev:
+        a.record(s)
+        api.indexer_score(q, w, kI, seq_start, q_seq, q_pos, wl.ld, scores=scores, stream=s)
+        c.record(s)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(c) for a, c in ev)[len(ev) // 2]
+    causal_flops = sum(2.0 * 32 * 128 * (p + 1) for p in wl.q_pos)
+    tflops = causal_flops / (ms * 1e-3) / 1e12
+    return {"workload": wl.name, "tflops": round(tflops, 1), "ms": round(ms, 4), "unit": "TFLOP/s",
+            "flops": causal_flops, "frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
+            "peak": BF16_PEAK_TFLOPS, "timing": "median of %d HIP-event-timed launches" % reps}
+
+
+class HipEvents:
+    """Raw hipEvents (the library records them on its stream)."""
+
+    def __init__(self, n):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(h.value)
+
+    def ms(self, a, b):
+        out = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(out), self.ev[a], self.ev[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return out.value
+
+    def close(self):
+        for h in self.ev:
+            self.hip.hipEventDestroy(h)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the sharding plan is in DESIGN.md); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from sparse_attention_relu_amd import api, synth
+
+    dev = torch.device("cuda:0")
+    wl = synth.workload(args.workload, seed=args.seed)
+    print(f"[bench] generating {wl.name}: {wl.n_q} queries, {wl.total_tokens} cached tokens, {wl.n_layers} layers",
+          file=sys.stderr, flush=True)
+    b = synth.make_batch(wl, dev, seed=args.seed)
+    stack = api.LayerStack(b.layers, b.seq_start, b.q_seq, b.q_pos, wl.ld, full=wl.full)
+    stack()
+    torch.cuda.synchronize()
+
+    # HIP graph of one step on a side stream
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            stack()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    print(f"[bench] timed {args.steps} graph replays: {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
+
+    # Per-kernel HIP-event timing in eager steps after a cache flush.
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    s = torch.cuda.current_stream()
+    names = ["indexer", "topk", "attn"]
+    acc = {n: [] for n in names}
+    steps_ms = []
+    hev = HipEvents(6)
+    for _ in range(max(5, min(args.steps, 20))):
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        stack(events=hev.ev, stream=s)
+        e1.record(s)
+        torch.cuda.synchronize()
+        for i, n in enumerate(names):
+            acc[n].append(hev.ms(2 * i, 2 * i + 1))
+        steps_ms.append(e0.elapsed_time(e1))
+    hev.close()
+    kern_ms = {n: sum(v) / len(v) for n, v in acc.items()}
+    total_bytes, idx_bytes = step_bytes(wl)
+    idx_gbs = idx_bytes / (kern_ms["indexer"] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(idx_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(idx_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "indexer_decode_kernel", "bytes_per_launch": idx_bytes,
+                "avg_launch_ms": round(kern_ms["indexer"], 5)}
+
+    out = {
+        "metric": "sparse-attn decode queries/s + HBM GB/s at 128K ctx; indexer prefill TFLOP/s",
+        "value": round(wl.n_q / (ms_step * 1e-3), 1),
+        "unit": "queries/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "n_q": wl.n_q, "layers": wl.n_layers,
+                   "full_layers": sum(wl.full), "context_tokens": wl.total_tokens,
+                   "topk": 2048, "heads": 64, "index_heads": 32, "seed": args.seed},
+        "hbm_gbs_step": round(total_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "step_bytes": total_bytes,
+        "roofline": roofline,
+        "kernel_ms_first_layer": {n: round(v, 5) for n, v in kern_ms.items()},
+        "eager_flushed_ms_per_step": round(sum(steps_ms) / len(steps_ms), 5),
+    }
+    del flush
+    if not args.no_prefill:
+        print("[bench] prefill indexer", file=sys.stderr, flush=True)
+        out["prefill_indexer"] = prefill_indexer(args.seed)
+    if not args.no_cpu:
+        print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(b, wl, args.cpu_sample)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

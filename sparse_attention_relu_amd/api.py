@@ -151,8 +151,8 @@ class LayerStack:
 
     def __call__(self, events=None, stream=None):
         ev = None
-        if events is not None:
-            ev = _lib.StageEvents(*[(e.cuda_event if e is not None else None) for e in events])
+        if events is not None:     # six raw hipEvent_t handles (ints) or None
+            ev = _lib.StageEvents(*events)
         st = _lib.lib().sa_layer_stack(self._descs, self.n_layers, ctypes_byref(self._batch), self.k, self.scale,
                                        _ptr(self.ws), self.ws.numel(), ctypes_byref(ev) if ev is not None else None,
                                        _stream(stream))
