@@ -6,7 +6,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
-#include "sa_common.h"
+#include "topk_common.h"
 
 namespace sa_host {
 
@@ -31,6 +31,14 @@ int32_t check_launch(const char* what) {
 int32_t launch_indexer(const void* q_idx, const float* w, const void* k_idx, const int64_t* seq_start,
                        const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, float* scores, int64_t ld, int algo,
                        hipStream_t stream);
+int32_t launch_indexer_ex(const void* q_idx, const float* w, const void* k_idx, const int64_t* seq_start,
+                          const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, float* scores, int64_t ld, int algo,
+                          const sa::TopkWs* hist_ws, int k, hipStream_t stream);
+sa::TopkWs topk_carve(void* ws, int32_t n_q, int64_t ld);
+int32_t topk_zero(const sa::TopkWs& w, int32_t* extra, int64_t n_extra, hipStream_t stream);
+int32_t topk_after_hist(const float* scores, int64_t ld, const int32_t* q_pos, int32_t n_q, int32_t k, int32_t* idx,
+                        const sa::TopkWs& w, hipStream_t stream);
+
 size_t topk_workspace_size(int32_t n_q, int64_t ld, int32_t k);
 int32_t launch_topk(const float* scores, int64_t ld, const int32_t* q_pos, int32_t n_q, int32_t k, int32_t* idx,
                     void* ws, int algo, hipStream_t stream);
@@ -226,18 +234,30 @@ int32_t sa_layer_stack(const sa_layer_desc* layers, int32_t n_layers, const sa_b
   const int32_t* cur_idx = nullptr;
   bool rec_idx = false, rec_topk = false, rec_attn = false;
   int32_t rc;
+  // Decode batches score one query per workgroup column and build the top-k's
+  // first-digit histogram while scoring; larger batches use the query-blocked
+  // indexer and the separate histogram pass.
+  const bool fused = n_q < 64;
+  const sa::TopkWs tw = topk_carve(topk_ws, n_q, ld);
   for (int l = 0; l < n_layers; ++l) {
     const sa_layer_desc& L = layers[l];
     if (L.is_full) {
+      if (fused) {
+        // histogram and state words of the top-k
+        rc = topk_zero(tw, nullptr, 0, st);
+        if (rc) return rc;
+      }
       const bool ev = events && !rec_idx && events->indexer_begin && events->indexer_end;
       if (ev && (rc = record(events->indexer_begin, st))) return rc;
-      rc = launch_indexer(L.q_idx, L.w, L.k_idx, batch->seq_start, batch->q_seq, batch->q_pos, n_q, scores, ld, 0, st);
+      rc = launch_indexer_ex(L.q_idx, L.w, L.k_idx, batch->seq_start, batch->q_seq, batch->q_pos, n_q, scores, ld,
+                             fused ? 1 : 2, fused ? &tw : nullptr, k, st);
       if (rc) return rc;
       if (ev && (rc = record(events->indexer_end, st))) return rc;
       rec_idx |= ev;
       const bool evt = events && !rec_topk && events->topk_begin && events->topk_end;
       if (evt && (rc = record(events->topk_begin, st))) return rc;
-      rc = launch_topk(scores, ld, batch->q_pos, n_q, k, L.idx, topk_ws, 0, st);
+      rc = fused ? topk_after_hist(scores, ld, batch->q_pos, n_q, k, L.idx, tw, st)
+                 : launch_topk(scores, ld, batch->q_pos, n_q, k, L.idx, topk_ws, 0, st);
       if (rc) return rc;
       if (evt && (rc = record(events->topk_end, st))) return rc;
       rec_topk |= evt;

@@ -20,7 +20,7 @@
 //                           sequence).  HBM-bound: 256 B of keys per 8 KFLOP.
 //   indexer_prefill_kernel  8 queries of one sequence share each key tile staged
 //                           in LDS: the dense contraction of chunked prefill.
-#include "sa_common.h"
+#include "topk_common.h"
 
 namespace sa {
 
@@ -32,68 +32,132 @@ __device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 
 __device__ __forceinline__ float relu_weighted_sum(const f32x16& acc, const float (&wr)[16]) {
   float part = 0.f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) part = fmaf(wr[i], fmaxf(acc[i], 0.f), part);
+  for (int i = 0; i < 16; ++i) part = fmaf(wr[i], __builtin_amdgcn_fmed3f(acc[i], 0.f, INFINITY), part);
   return part + __shfl_xor(part, 32, 64);
 }
 
 // ------------------------------------------------------------ decode kernel
+// Each wave streams its own contiguous 512-key range of one query's sequence
+// (128 KB): 32 keys (8 KB) per step through wave-private LDS into the MFMA,
+// with the next step's loads in flight.  With HIST the wave also counts each
+// score's top 12 key bits into a workgroup histogram, which is added to the
+// row's histogram in the top-k workspace (the first radix digit of the top-k).
 constexpr int kDecWaves = 4;
-constexpr int kDecIters = 4;
-constexpr int kDecChunk = kDecWaves * 32 * kDecIters;   // keys per workgroup
+constexpr int kWaveKeys = 512;
+constexpr int kDecChunk = kDecWaves * kWaveKeys;          // keys per workgroup
 constexpr int kKeyPitch = 272;                            // LDS bytes per key row (256 + 16 pad)
 
-__global__ __launch_bounds__(256) void indexer_decode_kernel(
-    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
-    const int64_t* __restrict__ seq_start, const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos,
-    float* __restrict__ scores, int64_t ld, int n_chunks) {
-  const int t = blockIdx.x / n_chunks;
-  const int chunk = blockIdx.x - t * n_chunks;
+struct DecArgs {
+  const uint16_t* q_idx;
+  const float* w;
+  const uint16_t* k_idx;
+  const int64_t* seq_start;
+  const int32_t* q_seq;
+  const int32_t* q_pos;
+  float* scores;
+  int64_t ld;
+  int n_chunks;
+  int k;               // with HIST: selection size (rows with q_pos < k need no histogram)
+  TopkWs ws;           // with HIST: histogram and state of the top-k workspace
+};
+
+// Orders a wave's LDS writes before its reads of other lanes' data (and the
+// reads before the next writes).  LDS-only: in-flight global loads are not
+// waited for.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <bool HIST>
+__global__ __launch_bounds__(256) void indexer_decode_kernel(DecArgs A) {
+  const int t = blockIdx.x / A.n_chunks;
+  const int chunk = blockIdx.x - t * A.n_chunks;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t pos = q_pos[t];
+  const int64_t pos = A.q_pos[t];
   const int64_t c0 = (int64_t)chunk * kDecChunk;
-  float* srow = scores + (int64_t)t * ld;
+  float* srow = A.scores + (int64_t)t * A.ld;
   if (c0 > pos) {
-    const int64_t end = min(c0 + (int64_t)kDecChunk, ld);
+    const int64_t end = min(c0 + (int64_t)kDecChunk, A.ld);
     for (int64_t s = c0 + threadIdx.x; s < end; s += 256) srow[s] = -INFINITY;
     return;
   }
   __shared__ __align__(16) uint8_t lds[kDecWaves][32 * kKeyPitch];
+  __shared__ __align__(16) uint32_t hist[HIST ? kBins1 : 1];
+  const bool do_hist = HIST && pos + 1 > A.k;
+  if (do_hist) {
+    for (int i = threadIdx.x; i < kBins1; i += 256) hist[i] = 0u;
+    __syncthreads();
+  }
 
-  const uint16_t* qt = q_idx + (int64_t)t * kIdxHeads * kIdxDim;
+  const uint16_t* qt = A.q_idx + (int64_t)t * kIdxHeads * kIdxDim;
   bf16x8 a[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) a[s] = as_bf16x8(ld16(qt + (lane & 31) * kIdxDim + 16 * s + 8 * (lane >> 5)));
   float wr[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) wr[i] = w[(int64_t)t * kIdxHeads + acc_row(i, lane)];
-  const uint16_t* kbase = k_idx + seq_start[q_seq[t]] * kIdxDim;
+  for (int i = 0; i < 16; ++i) wr[i] = A.w[(int64_t)t * kIdxHeads + acc_row(i, lane)];
+
+  const int64_t wbase = c0 + (int64_t)wave * kWaveKeys;          // first key of this wave
+  const int64_t wlast = pos - wbase;                              // last valid local key
+  const uint16_t* kb = A.k_idx + (A.seq_start[A.q_seq[t]] + wbase) * kIdxDim;
+  const int n_it = wlast < 0 ? 0 : (int)min((int64_t)(kWaveKeys / 32), wlast / 32 + 1);
   uint8_t* my = lds[wave];
 
-#pragma unroll 1
-  for (int it = 0; it < kDecIters; ++it) {
-    const int64_t key0 = c0 + (int64_t)(it * kDecWaves + wave) * 32;
-    // 8 KB of keys per wave: load j covers keys key0 + 4j .. +3, 16 B per lane.
-    u32x4 g[8];
+  // Loads past the causal bound re-read the last valid key (always in bounds);
+  // their scores are replaced by -inf, so no load needs a branch.
+  auto load = [&](u32x4 (&g)[8], int it) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int64_t key = key0 + 4 * j + (lane >> 4);
-      g[j] = key <= pos ? ld16(kbase + key * kIdxDim + (lane & 15) * 8) : u32x4{0, 0, 0, 0};
+      const int64_t key = min((int64_t)(it * 32 + 4 * j + (lane >> 4)), wlast);
+      g[j] = ld16(kb + key * kIdxDim + (lane & 15) * 8);
     }
+  };
+  auto step = [&](const u32x4 (&g)[8], int it) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       *reinterpret_cast<u32x4*>(my + (4 * j + (lane >> 4)) * kKeyPitch + (lane & 15) * 16) = g[j];
-    __syncthreads();
+    wave_lds_fence();
     f32x16 acc = {};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const u32x4 b = *reinterpret_cast<const u32x4*>(my + (lane & 31) * kKeyPitch + (2 * s + (lane >> 5)) * 16);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], as_bf16x8(b), acc, 0, 0, 0);
     }
-    __syncthreads();
+    wave_lds_fence();
     const float sc = relu_weighted_sum(acc, wr);
-    const int64_t key = key0 + (lane & 31);
-    if (lane < 32 && key < ld) srow[key] = key <= pos ? sc : -INFINITY;
+    const int64_t key = wbase + it * 32 + (lane & 31);
+    if (lane < 32 && key < A.ld) {
+      const bool valid = key <= pos;
+      srow[key] = valid ? sc : -INFINITY;
+      if (HIST && do_hist && valid) atomicAdd(&hist[score_key(sc) >> 20], 1u);
+    }
+  };
+
+  // Prefetches are unconditional (clamped to the last valid step) so the
+  // loads stay in order and each step waits only for its own data.
+  u32x4 g0[8], g1[8];
+  const int it_last = max(n_it - 1, 0);
+  load(g0, 0);
+  load(g1, min(1, it_last));
+#pragma unroll 1
+  for (int it = 0; it < n_it; it += 2) {
+    step(g0, it);
+    load(g0, min(it + 2, it_last));
+    if (it + 1 < n_it) step(g1, it + 1);
+    load(g1, min(it + 3, it_last));
+  }
+  // keys of this wave past the last valid step
+  for (int64_t s = wbase + (int64_t)n_it * 32 + lane; s < min(wbase + kWaveKeys, A.ld); s += 64) srow[s] = -INFINITY;
+
+  if (HIST && do_hist) {
+    // merge into the row's global histogram; the compaction kernel reads it
+    __syncthreads();
+    uint32_t* gh = A.ws.hist + (int64_t)t * kBins1;
+    for (int i = threadIdx.x; i < kBins1; i += 256)
+      if (hist[i]) atomicAdd(&gh[i], hist[i]);
   }
 }
 
@@ -226,9 +290,9 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
 // ------------------------------------------------------------------ launchers
 namespace sa_host {
 
-int32_t launch_indexer(const void* q_idx, const float* w, const void* k_idx, const int64_t* seq_start,
-                       const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, float* scores, int64_t ld,
-                       int algo, hipStream_t stream) {
+int32_t launch_indexer_ex(const void* q_idx, const float* w, const void* k_idx, const int64_t* seq_start,
+                          const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, float* scores, int64_t ld, int algo,
+                          const sa::TopkWs* hist_ws, int k, hipStream_t stream) {
   if (algo == 0) algo = n_q >= 64 ? 2 : 1;
   if (algo == 1) {
     const int n_chunks = (int)((ld + sa::kDecChunk - 1) / sa::kDecChunk);
@@ -237,9 +301,13 @@ int32_t launch_indexer(const void* q_idx, const float* w, const void* k_idx, con
       set_error("indexer: grid of %lld workgroups is too large", (long long)grid);
       return SA_ERR_UNSUPPORTED;
     }
-    hipLaunchKernelGGL(sa::indexer_decode_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
-                       (const uint16_t*)q_idx, w, (const uint16_t*)k_idx, seq_start, q_seq, q_pos, scores, ld,
-                       n_chunks);
+    sa::DecArgs A{(const uint16_t*)q_idx, w, (const uint16_t*)k_idx, seq_start, q_seq, q_pos, scores, ld, n_chunks, k,
+                  hist_ws ? *hist_ws : sa::TopkWs{}};
+    if (hist_ws) {
+      hipLaunchKernelGGL(sa::indexer_decode_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, A);
+    } else {
+      hipLaunchKernelGGL(sa::indexer_decode_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream, A);
+    }
     return check_launch("indexer_decode_kernel");
   }
   const int n_splits = (int)((ld + sa::kPfSplit - 1) / sa::kPfSplit);
@@ -253,6 +321,12 @@ int32_t launch_indexer(const void* q_idx, const float* w, const void* k_idx, con
                      (const uint16_t*)q_idx, w, (const uint16_t*)k_idx, seq_start, q_seq, q_pos, n_q, scores, ld,
                      n_splits);
   return check_launch("indexer_prefill_kernel");
+}
+
+int32_t launch_indexer(const void* q_idx, const float* w, const void* k_idx, const int64_t* seq_start,
+                       const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, float* scores, int64_t ld, int algo,
+                       hipStream_t stream) {
+  return launch_indexer_ex(q_idx, w, k_idx, seq_start, q_seq, q_pos, n_q, scores, ld, algo, nullptr, 0, stream);
 }
 
 }  // namespace sa_host

@@ -12,7 +12,8 @@
 // selection); its 4 waves take 16-row tiles of the slice in turn and merge
 // their running (max, sum, accumulator) in LDS at the end.  Per tile a wave
 //   - gathers 16 rows (18 KB) with 16-byte loads into wave-private LDS, the
-//     next tile's loads in flight while the current one is computed;
+//     next tile's loads in flight while the current one is computed (the
+//     slice's positions are staged in LDS first, so no load waits on another);
 //   - S^T[16 rows x 16 heads] = R . Q^T with v_mfma_f32_16x16x32_bf16 over the
 //     576 dims (R from LDS, Q^T held in registers for the whole slice);
 //   - runs the online softmax in base 2; the running maximum is only moved
@@ -23,9 +24,12 @@
 //     the S^T accumulator layout (each lane holds 4 keys of one head), and the
 //     V^T operand is assembled from the lane's own row chunks with byte
 //     permutes (dims are permuted consistently, no LDS transpose).
-// mla_combine_wuv_kernel: one workgroup per (head, 64 value rows) keeps its
-// 64 x 512 slice of W_UV in registers, merges the slices' partial softmax
-// states of each query and applies the up-projection, rounding to bf16.
+// With one slice per query the workgroup normalises and writes the latent
+// average obar (bf16) itself; with several, each writes a partial state and
+// mla_merge_kernel combines them.
+// mla_wuv_kernel: one workgroup per (head, 64 value rows) holds that 64 x 512
+// slice of W_UV in registers and multiplies it with obar^T, 16 queries per
+// v_mfma_f32_16x16x32_bf16 column block, rounding the output to bf16.
 #include <atomic>
 
 #include "sa_common.h"
@@ -38,10 +42,12 @@ constexpr int kRowPitch = 1168;           // LDS bytes per gathered row (1152 + 
 constexpr int kHg = 4;                    // head groups of 16
 constexpr float kRescaleSlack = 8.0f;     // log2 units
 
+// Orders a wave's LDS writes before its reads of other lanes' data (LDS-only:
+// in-flight global loads are not waited for).
 __device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 __device__ __forceinline__ uint32_t perm_lo(uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x05040100u); }
@@ -58,9 +64,15 @@ struct AttnArgs {
   int n_sp;
   int kps;               // selection entries per slice (multiple of 64)
   float scale_log2;      // scale * log2(e)
-  float* part_o;         // [n_q][4][n_sp][16][512]
-  float* part_ml;        // [n_q][4][n_sp][16][2]  (max in log2 units, sum)
+  float* part_o;         // [n_q][4][n_sp][16][512]   (n_sp > 1)
+  float* part_ml;        // [n_q][4][n_sp][16][2]     (max in log2 units, sum)
+  uint16_t* obar;        // [n_q][64][512] bf16 latent average
+  float* lse;            // [n_q][64] or null
 };
+
+constexpr int kMaxSlice = 2048;
+constexpr size_t kAttnTileBytes = (size_t)kAttnWaves * 2 * kTile * kRowPitch;     // 149,504
+constexpr size_t kAttnSmem = kAttnTileBytes + kMaxSlice * 4;                      // + staged positions
 
 __global__ __launch_bounds__(256, 1) void mla_attn_kernel(AttnArgs A) {
   // Workgroup -> (query t, slice sp, head group hg).  The 4 head groups of a
@@ -79,6 +91,21 @@ __global__ __launch_bounds__(256, 1) void mla_attn_kernel(AttnArgs A) {
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* buf0 = smem + wave * (2 * kTile * kRowPitch);
   uint8_t* buf1 = buf0 + kTile * kRowPitch;
+  int32_t* spos = reinterpret_cast<int32_t*>(smem + kAttnTileBytes);
+
+  const int j0 = sp * A.kps;
+  const int j1 = min(A.k, j0 + A.kps);
+  const int n_sel = max(j1 - j0, 0);
+  if (n_sel > 0) {
+    // Stage the slice's positions (all loads issued before any is used).
+    const int32_t* irow = A.idx + (int64_t)t * A.k + j0;
+    int pv[kMaxSlice / 256];
+#pragma unroll
+    for (int u = 0; u < kMaxSlice / 256; ++u) pv[u] = irow[min((int)threadIdx.x + 256 * u, n_sel - 1)];
+#pragma unroll
+    for (int u = 0; u < kMaxSlice / 256; ++u)
+      if ((int)threadIdx.x + 256 * u < n_sel) spos[threadIdx.x + 256 * u] = pv[u];
+  }
 
   // Q^T operand for this wave's 16 heads: head hg*16 + l16, dims 32s + 8g .. +8.
   bf16x8 qb[18];
@@ -88,29 +115,28 @@ __global__ __launch_bounds__(256, 1) void mla_attn_kernel(AttnArgs A) {
     for (int s = 0; s < 18; ++s) qb[s] = as_bf16x8(ld16(qp + 32 * s));
   }
   const uint16_t* rows = A.kv + A.seq_start[A.q_seq[t]] * kRow;
-  const int32_t* irow = A.idx + (int64_t)t * A.k;
-  const int j0 = sp * A.kps;
-  const int j1 = min(A.k, j0 + A.kps);
-  const int n_tiles = j1 > j0 ? (j1 - j0 + kTile - 1) / kTile : 0;
+  const int n_tiles = (n_sel + kTile - 1) / kTile;
+  __syncthreads();
 
   // Gather of one tile into registers: 16 chunks of the latent (keys 4g+i,
   // dims 8m..8m+7 with m = l16 + 16b) and 2 chunks of the rope part (key l16,
-  // dims 512 + 32u + 8g).
+  // dims 512 + 32u + 8g).  Padding entries (-1) and slots past the slice read
+  // row 0 and are masked out of the softmax.
   u32x4 gv[16], gr[2];
-  int my_pos[4];          // selection entries of keys 4g + i of the current tile (for masking)
+  const int last_sel = max(n_sel - 1, 0);
+  auto row_of = [&](int j) {      // branch-free: out-of-slice or padding entries read row 0
+    const int p = spos[min(j, last_sel)];
+    return (j < n_sel && p >= 0) ? p : 0;
+  };
   auto gather = [&](int tile) {
-    const int jt = j0 + tile * kTile;
+    const int jt = tile * kTile;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int j = jt + 4 * g + i;
-      const int p = j < j1 ? irow[j] : -1;
-      const uint16_t* r = rows + (int64_t)max(p, 0) * kRow;
+      const uint16_t* r = rows + (int64_t)row_of(jt + 4 * g + i) * kRow;
 #pragma unroll
       for (int b = 0; b < 4; ++b) gv[4 * i + b] = ld16(r + 8 * (l16 + 16 * b));
     }
-    const int jr = jt + l16;
-    const int pr = jr < j1 ? irow[jr] : -1;
-    const uint16_t* rr = rows + (int64_t)max(pr, 0) * kRow + kLatent;
+    const uint16_t* rr = rows + (int64_t)row_of(jt + l16) * kRow + kLatent;
 #pragma unroll
     for (int u = 0; u < 2; ++u) gr[u] = ld16(rr + 32 * u + 8 * g);
   };
@@ -130,26 +156,23 @@ __global__ __launch_bounds__(256, 1) void mla_attn_kernel(AttnArgs A) {
   for (int i = 0; i < 32; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Wave w takes tiles w, w+4, ...
+  // Wave w takes tiles w, w+4, ...  (the first gather is unconditional so that
+  // every path into the loop has drained the same loads)
   int tile = wave;
-  if (tile < n_tiles) {
-    gather(tile);
-    stash(buf0);
-  }
+  gather(min(tile, max(n_tiles - 1, 0)));
+  stash(buf0);
   wave_lds_sync();
   uint8_t* cur = buf0;
   uint8_t* nxt = buf1;
 #pragma unroll 1
   for (; tile < n_tiles; tile += kAttnWaves) {
-    const bool more = tile + kAttnWaves < n_tiles;
-    if (more) gather(tile + kAttnWaves);
-    // Valid keys of this tile for this lane: keys 4g + i.
-    const int jt = j0 + tile * kTile;
+    // Next tile's gather, unconditional (clamped) so the loads stay in order.
+    gather(min(tile + kAttnWaves, n_tiles - 1));
     bool valid[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int j = jt + 4 * g + i;
-      valid[i] = j < j1 && irow[j] >= 0;
+      const int j = tile * kTile + 4 * g + i;
+      valid[i] = j < n_sel && spos[min(j, last_sel)] >= 0;
     }
     // S^T = R . Q^T over 576 dims.
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
@@ -206,7 +229,7 @@ __global__ __launch_bounds__(256, 1) void mla_attn_kernel(AttnArgs A) {
         o[8 * b + e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s16x4(av), pt, o[8 * b + e], 0, 0, 0);
       }
     }
-    if (more) stash(nxt);
+    stash(nxt);
     wave_lds_sync();
     uint8_t* tmp = cur;
     cur = nxt;
@@ -220,6 +243,8 @@ __global__ __launch_bounds__(256, 1) void mla_attn_kernel(AttnArgs A) {
   __syncthreads();
   float* lo = reinterpret_cast<float*>(smem);                  // [4][16][512]
   float* lml = lo + kAttnWaves * 16 * kLatent;                 // [4][16][2]
+  float* lw = lml + kAttnWaves * 16 * 2;                       // [4][16] merge weights
+  float* lhs = lw + kAttnWaves * 16;                           // [16][2]  merged (max, sum)
 #pragma unroll
   for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -234,110 +259,136 @@ __global__ __launch_bounds__(256, 1) void mla_attn_kernel(AttnArgs A) {
     lml[(wave * 16 + l16) * 2 + 1] = l_run;
   }
   __syncthreads();
-  const int64_t pbase = (((int64_t)t * kHg + hg) * A.n_sp + sp) * 16;
-  for (int i = threadIdx.x; i < 16 * kLatent; i += 256) {
-    const int hh = i / kLatent, dim = i - hh * kLatent;
-    float mw[kAttnWaves], M = -INFINITY;
+  if (threadIdx.x < 16) {
+    const int hh = threadIdx.x;
+    float M = -INFINITY;
+    for (int w2 = 0; w2 < kAttnWaves; ++w2) M = fmaxf(M, lml[(w2 * 16 + hh) * 2]);
+    float L = 0.f;
+    for (int w2 = 0; w2 < kAttnWaves; ++w2) {
+      const float m = lml[(w2 * 16 + hh) * 2];
+      const float a = m == -INFINITY ? 0.f : fast_exp2(m - M);
+      lw[w2 * 16 + hh] = a;
+      L = fmaf(a, lml[(w2 * 16 + hh) * 2 + 1], L);
+    }
+    lhs[hh * 2] = M;
+    lhs[hh * 2 + 1] = L;
+    if (A.n_sp == 1) {
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      for (int w2 = 0; w2 < kAttnWaves; ++w2) lw[w2 * 16 + hh] *= inv;
+      if (A.lse) A.lse[(int64_t)t * kHeads + hg * 16 + hh] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f
+                                                                      : -INFINITY;
+    }
+  }
+  __syncthreads();
+  if (A.n_sp == 1) {
+    // One slice: normalise and write obar (bf16) directly.
+    uint16_t* ob = A.obar + ((int64_t)t * kHeads + hg * 16) * kLatent;
+    for (int i = threadIdx.x; i < 16 * kLatent / 2; i += 256) {
+      const int hh = (2 * i) / kLatent, dim = 2 * i - hh * kLatent;
+      float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < kAttnWaves; ++w2) {
+        const float a = lw[w2 * 16 + hh];
+        v0 = fmaf(a, lo[(w2 * 16 + hh) * kLatent + dim], v0);
+        v1 = fmaf(a, lo[(w2 * 16 + hh) * kLatent + dim + 1], v1);
+      }
+      *reinterpret_cast<uint32_t*>(ob + hh * kLatent + dim) = pack_bf16x2(v0, v1);
+    }
+    return;
+  }
+  // Several slices: write this slice's partial state ...
+  const int64_t gbase = ((int64_t)t * kHg + hg) * A.n_sp;
+  const int64_t pbase = (gbase + sp) * 16;
+  for (int i = threadIdx.x; i < 16 * kLatent / 4; i += 256) {
+    const int hh = (4 * i) / kLatent, dim = 4 * i - hh * kLatent;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w2 = 0; w2 < kAttnWaves; ++w2) {
-      mw[w2] = lml[(w2 * 16 + hh) * 2];
-      M = fmaxf(M, mw[w2]);
+      const float a = lw[w2 * 16 + hh];
+      const f32x4 x = *reinterpret_cast<const f32x4*>(lo + (w2 * 16 + hh) * kLatent + dim);
+      acc += a * x;
     }
-    float acc = 0.f, lsum = 0.f;
-#pragma unroll
-    for (int w2 = 0; w2 < kAttnWaves; ++w2) {
-      const float a = mw[w2] == -INFINITY ? 0.f : fast_exp2(mw[w2] - M);
-      acc = fmaf(a, lo[(w2 * 16 + hh) * kLatent + dim], acc);
-      lsum = fmaf(a, lml[(w2 * 16 + hh) * 2 + 1], lsum);
-    }
-    A.part_o[(pbase + hh) * kLatent + dim] = acc;
-    if (dim == 0) {
-      A.part_ml[(pbase + hh) * 2 + 0] = M;
-      A.part_ml[(pbase + hh) * 2 + 1] = lsum;
-    }
+    *reinterpret_cast<f32x4*>(A.part_o + (pbase + hh) * kLatent + dim) = acc;
+  }
+  if (threadIdx.x < 16) {
+    A.part_ml[(pbase + threadIdx.x) * 2 + 0] = lhs[threadIdx.x * 2];
+    A.part_ml[(pbase + threadIdx.x) * 2 + 1] = lhs[threadIdx.x * 2 + 1];
   }
 }
 
-// ------------------------------------------------------------ combine + W_UV
-constexpr int kQB = 16;                     // queries per batch
-constexpr int kObarPitch = 132;             // floats per 128-wide quarter (+4 pad)
+// Merge of the slices' partial softmax states: obar = sum_s a_s O_s / sum_s a_s l_s
+// with a_s = 2^(m_s - max m).  One workgroup per (query, head group, 64 dims);
+// each thread owns one head and 4 dims and issues all its loads at once.
+constexpr int kMaxSp = 8;
 
-struct CombineArgs {
-  const float* part_o;
-  const float* part_ml;
-  const uint16_t* w_uv;
+__global__ __launch_bounds__(256) void mla_merge_kernel(AttnArgs A) {
+  const int blk = blockIdx.x;
+  const int dblk = blk & 7;
+  const int hg = (blk >> 3) & 3;
+  const int t = blk >> 5;
+  const int hh = threadIdx.x >> 4;
+  const int dim = dblk * 64 + (threadIdx.x & 15) * 4;
+  const int64_t gbase = ((int64_t)t * kHg + hg) * A.n_sp;
+  float m[kMaxSp], l[kMaxSp];
+  f32x4 o[kMaxSp];
+#pragma unroll
+  for (int s2 = 0; s2 < kMaxSp; ++s2) {
+    const int sc = min(s2, A.n_sp - 1);
+    m[s2] = A.part_ml[((gbase + sc) * 16 + hh) * 2];
+    l[s2] = A.part_ml[((gbase + sc) * 16 + hh) * 2 + 1];
+    o[s2] = *reinterpret_cast<const f32x4*>(A.part_o + ((gbase + sc) * 16 + hh) * kLatent + dim);
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s2 = 0; s2 < kMaxSp; ++s2) M = fmaxf(M, m[s2]);
+  float L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s2 = 0; s2 < kMaxSp; ++s2) {
+    const float a = (s2 < A.n_sp && m[s2] != -INFINITY) ? fast_exp2(m[s2] - M) : 0.f;
+    L = fmaf(a, l[s2], L);
+    acc += a * o[s2];
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  acc *= inv;
+  const u32x2 pk = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+  *reinterpret_cast<u32x2*>(A.obar + ((int64_t)t * kHeads + hg * 16 + hh) * kLatent + dim) = pk;
+  if (A.lse && dblk == 0 && (threadIdx.x & 15) == 0)
+    A.lse[(int64_t)t * kHeads + hg * 16 + hh] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
+}
+
+// ------------------------------------------------------------------ W_UV
+struct WuvArgs {
+  const uint16_t* obar;     // [n_q][64][512] bf16
+  const uint16_t* w_uv;     // [64][256][512] bf16
+  uint16_t* out;            // [n_q][64][256] bf16
   int n_q;
-  int n_sp;
-  uint16_t* out;        // [n_q][64][256]
-  float* lse;           // [n_q][64] or null
 };
 
-__global__ __launch_bounds__(256) void mla_combine_wuv_kernel(CombineArgs C) {
+__global__ __launch_bounds__(256) void mla_wuv_kernel(WuvArgs W) {
   const int h = blockIdx.x >> 2;
-  const int vblk = blockIdx.x & 3;
-  const int tid = threadIdx.x;
-  const int v = vblk * 64 + (tid >> 2);
-  const int cq = tid & 3;
-  const int hg = h >> 4, hh = h & 15;
-
-  // W_UV[h][v][128 cq .. +128) as 64 packed bf16 pairs.
-  u32x4 wreg[16];
-  {
-    const uint16_t* wp = C.w_uv + ((int64_t)h * kVdim + v) * kLatent + 128 * cq;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int v0 = (blockIdx.x & 3) * 64 + wave * 16;          // this wave's 16 value rows
+  // A operand: W_UV[h][v0 + l16][32s + 8g .. +8], held for every query block.
+  bf16x8 wa[16];
+  const uint16_t* wp = W.w_uv + ((int64_t)h * kVdim + v0 + l16) * kLatent + 8 * g;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) wreg[i] = ld16(wp + 8 * i);
-  }
-  __shared__ float obar[kQB * 4 * kObarPitch];
-  __shared__ float wgt[kQB * 32];
-  __shared__ float lse_sh[kQB];
-
-  for (int q0 = 0; q0 < C.n_q; q0 += kQB) {
-    const int nqb = min(kQB, C.n_q - q0);
-    // Softmax-state merge weights per (query, slice).
-    if (tid < nqb) {
-      const int t = q0 + tid;
-      const float* ml = C.part_ml + (((int64_t)t * kHg + hg) * C.n_sp) * 16 * 2;
-      float M = -INFINITY;
-      for (int sp = 0; sp < C.n_sp; ++sp) M = fmaxf(M, ml[(sp * 16 + hh) * 2]);
-      float L = 0.f;
-      for (int sp = 0; sp < C.n_sp; ++sp) {
-        const float m = ml[(sp * 16 + hh) * 2];
-        const float a = m == -INFINITY ? 0.f : fast_exp2(m - M);
-        wgt[tid * 32 + sp] = a;
-        L = fmaf(a, ml[(sp * 16 + hh) * 2 + 1], L);
-      }
-      const float inv = L > 0.f ? 1.f / L : 0.f;
-      for (int sp = 0; sp < C.n_sp; ++sp) wgt[tid * 32 + sp] *= inv;
-      lse_sh[tid] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
-    }
-    __syncthreads();
-    for (int i = tid; i < nqb * kLatent; i += 256) {
-      const int tq = i / kLatent, c = i - tq * kLatent;
-      const int t = q0 + tq;
-      const float* po = C.part_o + ((((int64_t)t * kHg + hg) * C.n_sp) * 16 + hh) * kLatent + c;
-      float acc = 0.f;
-      for (int sp = 0; sp < C.n_sp; ++sp) acc = fmaf(wgt[tq * 32 + sp], po[(int64_t)sp * 16 * kLatent], acc);
-      obar[tq * 4 * kObarPitch + (c >> 7) * kObarPitch + (c & 127)] = acc;
-    }
-    __syncthreads();
-    for (int tq = 0; tq < nqb; ++tq) {
-      const float* ob = obar + tq * 4 * kObarPitch + cq * kObarPitch;
-      float acc = 0.f;
+  for (int s = 0; s < 16; ++s) wa[s] = as_bf16x8(ld16(wp + 32 * s));
+  for (int tb = 0; tb < W.n_q; tb += 16) {
+    const int t = min(tb + l16, W.n_q - 1);
+    const uint16_t* op = W.obar + ((int64_t)t * kHeads + h) * kLatent + 8 * g;
+    bf16x8 ob[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+    for (int s = 0; s < 16; ++s) ob[s] = as_bf16x8(ld16(op + 32 * s));
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const uint32_t wv = wreg[i][d];
-          acc = fmaf(__uint_as_float(wv << 16), ob[8 * i + 2 * d], acc);
-          acc = fmaf(__uint_as_float(wv & 0xffff0000u), ob[8 * i + 2 * d + 1], acc);
-        }
-      }
-      acc += __shfl_xor(acc, 1, 64);
-      acc += __shfl_xor(acc, 2, 64);
-      if (cq == 0) C.out[((int64_t)(q0 + tq) * kHeads + h) * kVdim + v] = (uint16_t)f32_to_bf16_rne(acc);
+    for (int s = 0; s < 16; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[s], ob[s], acc, 0, 0, 0);
+    // acc[j] = out[t = tb + l16][h][v0 + 4g + j]
+    if (tb + l16 < W.n_q) {
+      const u32x2 pk = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+      *reinterpret_cast<u32x2*>(W.out + ((int64_t)(tb + l16) * kHeads + h) * kVdim + v0 + 4 * g) = pk;
     }
-    if (C.lse && vblk == 0 && tid < nqb) C.lse[(int64_t)(q0 + tid) * kHeads + h] = lse_sh[tid];
-    __syncthreads();
   }
 }
 
@@ -352,14 +403,33 @@ int mla_n_splits(int32_t n_q, int32_t k) {
   int n_sp = (target + 4 * n_q - 1) / (4 * n_q);
   const int max_sp = (k + 63) / 64;
   if (n_sp > max_sp) n_sp = max_sp;
-  if (n_sp > 32) n_sp = 32;
+  if (n_sp > sa::kMaxSp) n_sp = sa::kMaxSp;
   if (n_sp < 1) n_sp = 1;
   return n_sp;
 }
 
+struct MlaWs {
+  float* part_o;
+  float* part_ml;
+  uint16_t* obar;
+};
+
+static MlaWs mla_carve(void* ws, int32_t n_q, int n_sp) {
+  MlaWs m;
+  uint8_t* p = (uint8_t*)ws;
+  m.obar = (uint16_t*)p;
+  p += align256((size_t)n_q * sa::kHeads * sa::kLatent * 2);
+  m.part_ml = (float*)p;
+  p += n_sp > 1 ? align256((size_t)n_q * 4 * n_sp * 16 * 2 * 4) : 0;
+  m.part_o = (float*)p;
+  return m;
+}
+
 size_t mla_workspace_size(int32_t n_q, int32_t k) {
   const int n_sp = mla_n_splits(n_q, k);
-  return align256((size_t)n_q * 4 * n_sp * 16 * sa::kLatent * 4) + align256((size_t)n_q * 4 * n_sp * 16 * 2 * 4);
+  size_t s = align256((size_t)n_q * sa::kHeads * sa::kLatent * 2);
+  if (n_sp > 1) s += align256((size_t)n_q * 4 * n_sp * 16 * 2 * 4) + align256((size_t)n_q * 4 * n_sp * 16 * sa::kLatent * 4);
+  return s;
 }
 
 // hipFuncSetAttribute is per device; remember which devices have been set up.
@@ -371,6 +441,7 @@ int32_t launch_mla(const void* q_abs, const void* kv, const int64_t* seq_start, 
   const int n_sp = mla_n_splits(n_q, k);
   int kps = (k + n_sp - 1) / n_sp;
   kps = (kps + 63) / 64 * 64;
+  MlaWs m = mla_carve(ws, n_q, n_sp);
   sa::AttnArgs A;
   A.q_abs = (const uint16_t*)q_abs;
   A.kv = (const uint16_t*)kv;
@@ -382,9 +453,11 @@ int32_t launch_mla(const void* q_abs, const void* kv, const int64_t* seq_start, 
   A.n_sp = n_sp;
   A.kps = kps;
   A.scale_log2 = scale * sa::kLog2e;
-  A.part_o = (float*)ws;
-  A.part_ml = (float*)((uint8_t*)ws + align256((size_t)n_q * 4 * n_sp * 16 * sa::kLatent * 4));
-  const size_t smem = (size_t)sa::kAttnWaves * 2 * sa::kTile * sa::kRowPitch;   // 149,504 B
+  A.part_o = m.part_o;
+  A.part_ml = m.part_ml;
+  A.obar = m.obar;
+  A.lse = lse;
+  const size_t smem = sa::kAttnSmem;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
     set_error("mla: hipGetDevice failed");
@@ -408,16 +481,13 @@ int32_t launch_mla(const void* q_abs, const void* kv, const int64_t* seq_start, 
   hipLaunchKernelGGL(sa::mla_attn_kernel, dim3((unsigned)grid), dim3(256), smem, stream, A);
   int32_t rc = check_launch("mla_attn_kernel");
   if (rc) return rc;
-  sa::CombineArgs C;
-  C.part_o = A.part_o;
-  C.part_ml = A.part_ml;
-  C.w_uv = (const uint16_t*)w_uv;
-  C.n_q = n_q;
-  C.n_sp = n_sp;
-  C.out = (uint16_t*)out;
-  C.lse = lse;
-  hipLaunchKernelGGL(sa::mla_combine_wuv_kernel, dim3(sa::kHeads * 4), dim3(256), 0, stream, C);
-  return check_launch("mla_combine_wuv_kernel");
+  if (n_sp > 1) {
+    hipLaunchKernelGGL(sa::mla_merge_kernel, dim3((unsigned)(n_q * 32)), dim3(256), 0, stream, A);
+    if ((rc = check_launch("mla_merge_kernel"))) return rc;
+  }
+  sa::WuvArgs W{m.obar, (const uint16_t*)w_uv, (uint16_t*)out, n_q};
+  hipLaunchKernelGGL(sa::mla_wuv_kernel, dim3(sa::kHeads * 4), dim3(256), 0, stream, W);
+  return check_launch("mla_wuv_kernel");
 }
 
 }  // namespace sa_host
