@@ -16,6 +16,9 @@ FLAGS = [
     # packed fp32 instructions stay off: ordinary fp32 code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
+    # MFMA results in ordinary VGPRs: keeps the attention loop from shuttling
+    # values through AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

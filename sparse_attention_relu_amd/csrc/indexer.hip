@@ -37,14 +37,15 @@ __device__ __forceinline__ float relu_weighted_sum(const f32x16& acc, const floa
 }
 
 // ------------------------------------------------------------ decode kernel
-// Each wave streams its own contiguous 512-key range of one query's sequence
-// (128 KB): 32 keys (8 KB) per step through wave-private LDS into the MFMA,
-// with the next step's loads in flight.  With HIST the wave also counts each
+// A workgroup covers 512 consecutive keys of one query's sequence: at each of
+// its 4 steps the 4 waves take the next 128 keys (32 each, 8 KB), staged
+// through wave-private LDS into the MFMA, with the next step's loads in
+// flight.  With HIST the wave also counts each
 // score's top 12 key bits into a workgroup histogram, which is added to the
 // row's histogram in the top-k workspace (the first radix digit of the top-k).
 constexpr int kDecWaves = 4;
-constexpr int kWaveKeys = 512;
-constexpr int kDecChunk = kDecWaves * kWaveKeys;          // keys per workgroup
+constexpr int kDecSteps = 4;
+constexpr int kDecChunk = kDecWaves * 32 * kDecSteps;     // keys per workgroup
 constexpr int kKeyPitch = 272;                            // LDS bytes per key row (256 + 16 pad)
 
 struct DecArgs {
@@ -100,18 +101,19 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(DecArgs A) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) wr[i] = A.w[(int64_t)t * kIdxHeads + acc_row(i, lane)];
 
-  const int64_t wbase = c0 + (int64_t)wave * kWaveKeys;          // first key of this wave
-  const int64_t wlast = pos - wbase;                              // last valid local key
-  const uint16_t* kb = A.k_idx + (A.seq_start[A.q_seq[t]] + wbase) * kIdxDim;
-  const int n_it = wlast < 0 ? 0 : (int)min((int64_t)(kWaveKeys / 32), wlast / 32 + 1);
+  // step it of this wave covers keys c0 + (4 it + wave) * 32 .. +31
+  const int64_t wlast = pos - c0;                                 // last valid key, relative to c0
+  const uint16_t* kb = A.k_idx + (A.seq_start[A.q_seq[t]] + c0) * kIdxDim;
+  const int n_it = kDecSteps;
   uint8_t* my = lds[wave];
+  auto key_of = [&](int it) { return (int64_t)(it * kDecWaves + wave) * 32; };
 
   // Loads past the causal bound re-read the last valid key (always in bounds);
   // their scores are replaced by -inf, so no load needs a branch.
   auto load = [&](u32x4 (&g)[8], int it) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int64_t key = min((int64_t)(it * 32 + 4 * j + (lane >> 4)), wlast);
+      const int64_t key = min(key_of(it) + 4 * j + (lane >> 4), wlast);
       g[j] = ld16(kb + key * kIdxDim + (lane & 15) * 8);
     }
   };
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(DecArgs A) {
     }
     wave_lds_fence();
     const float sc = relu_weighted_sum(acc, wr);
-    const int64_t key = wbase + it * 32 + (lane & 31);
+    const int64_t key = c0 + key_of(it) + (lane & 31);
     if (lane < 32 && key < A.ld) {
       const bool valid = key <= pos;
       srow[key] = valid ? sc : -INFINITY;
@@ -139,18 +141,14 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(DecArgs A) {
   // Prefetches are unconditional (clamped to the last valid step) so the
   // loads stay in order and each step waits only for its own data.
   u32x4 g0[8], g1[8];
-  const int it_last = max(n_it - 1, 0);
   load(g0, 0);
-  load(g1, min(1, it_last));
-#pragma unroll 1
+#pragma unroll
   for (int it = 0; it < n_it; it += 2) {
+    load(g1, it + 1);
     step(g0, it);
-    load(g0, min(it + 2, it_last));
-    if (it + 1 < n_it) step(g1, it + 1);
-    load(g1, min(it + 3, it_last));
+    if (it + 2 < n_it) load(g0, it + 2);
+    step(g1, it + 1);
   }
-  // keys of this wave past the last valid step
-  for (int64_t s = wbase + (int64_t)n_it * 32 + lane; s < min(wbase + kWaveKeys, A.ld); s += 64) srow[s] = -INFINITY;
 
   if (HIST && do_hist) {
     // merge into the row's global histogram; the compaction kernel reads it

@@ -8,24 +8,23 @@
 //     z_j = scale * q_abs[t, h] . R_j,  obar = softmax(z) @ R[:, :512],
 //     out[t, h] = bf16(W_UV[h] @ obar).
 //
-// mla_attn_kernel: one workgroup per (query, group of 16 heads, slice of the
-// selection); its 4 waves take 16-row tiles of the slice in turn and merge
-// their running (max, sum, accumulator) in LDS at the end.  Per tile a wave
-//   - gathers 16 rows (18 KB) with 16-byte loads into wave-private LDS, the
-//     next tile's loads in flight while the current one is computed (the
-//     slice's positions are staged in LDS first, so no load waits on another);
-//   - S^T[16 rows x 16 heads] = R . Q^T with v_mfma_f32_16x16x32_bf16 over the
-//     576 dims (R from LDS, Q^T held in registers for the whole slice);
-//   - runs the online softmax in base 2; the running maximum is only moved
-//     when a tile exceeds it by more than 2^8, so the accumulator is rarely
-//     rescaled;
-//   - O^T[512 dims x 16 heads] += V^T . P^T with v_mfma_f32_16x16x16_bf16:
-//     the 16 keys of the tile are the contraction, P^T comes straight out of
-//     the S^T accumulator layout (each lane holds 4 keys of one head), and the
-//     V^T operand is assembled from the lane's own row chunks with byte
-//     permutes (dims are permuted consistently, no LDS transpose).
+// mla_attn_kernel: one workgroup per (query, slice of the selection); all 64
+// heads share every gathered row.  The slice is consumed in 32-row tiles:
+//   - the workgroup gathers each tile (36 KB) with 16-byte direct-to-LDS loads
+//     into a 3-buffer ring, so two tiles are in flight without registers;
+//   - wave w computes S^T[32 rows x heads 16w..16w+15] = R . Q^T with
+//     v_mfma_f32_16x16x32_bf16 over the 576 dims (R from LDS, Q^T in registers)
+//     and runs the online softmax of its 16 heads in base 2 (the running max is
+//     only moved when a tile exceeds it by more than 2^8, so rescaling is rare);
+//     its bf16 weights and any rescale factors go to LDS;
+//   - after one workgroup barrier, wave w accumulates O^T[latent dims
+//     128w..128w+127 x all 64 heads] += V^T . P^T with v_mfma_f32_16x16x32_bf16:
+//     the 32 rows are the contraction, the V^T operand is assembled from 16-byte
+//     row chunks with byte permutes (rows and dims are permuted consistently in
+//     both operands, no transpose through LDS), P^T comes from the 4 waves'
+//     weights.
 // With one slice per query the workgroup normalises and writes the latent
-// average obar (bf16) itself; with several, each writes a partial state and
+// average obar (bf16); with several, each writes its partial state and
 // mla_merge_kernel combines them.
 // mla_wuv_kernel: one workgroup per (head, 64 value rows) holds that 64 x 512
 // slice of W_UV in registers and multiplies it with obar^T, 16 queries per
@@ -37,21 +36,31 @@
 namespace sa {
 
 constexpr int kAttnWaves = 4;
-constexpr int kTile = 16;                 // rows per wave tile
-constexpr int kRowPitch = 1168;           // LDS bytes per gathered row (1152 + 16)
-constexpr int kHg = 4;                    // head groups of 16
-constexpr float kRescaleSlack = 8.0f;     // log2 units
-
-// Orders a wave's LDS writes before its reads of other lanes' data (LDS-only:
-// in-flight global loads are not waited for).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
+constexpr int kTile = 32;                  // rows per tile
+constexpr int kRowBytes = kRow * 2;        // 1152: rows are stored unpadded in LDS ...
+constexpr int kTileBytes = kTile * kRowBytes;                     // 36,864
+constexpr int kRing = 3;                   // LDS tile buffers (two tiles in flight)
+constexpr int kLoadsPerWave = kTileBytes / 1024 / kAttnWaves;    // 9 direct-to-LDS loads of 1 KB
+constexpr float kRescaleSlack = 8.0f;      // log2 units
+constexpr int kMaxSp = 32;
 
 __device__ __forceinline__ uint32_t perm_lo(uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x05040100u); }
 __device__ __forceinline__ uint32_t perm_hi(uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x07060302u); }
+
+// ... with the 16-byte chunks of row r permuted within groups of 8
+// (chunk c sits at position c ^ (r & 7)), so that 8 lanes reading the same
+// chunk of 8 consecutive rows hit 8 different LDS bank groups.
+__device__ __forceinline__ int lds_chunk_offset(int r, int c) { return r * kRowBytes + 16 * (c ^ (r & 7)); }
+
+// Workgroup barrier that completes this wave's LDS instructions first but
+// leaves the direct-to-LDS tile loads in flight (__syncthreads, and even an
+// LDS-scoped fence, would wait for them: they are tracked as memory writes).
+// Tile loads are waited for explicitly with SA_WAIT_VMCNT.  The "memory"
+// clobber keeps the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// s_waitcnt vmcnt(n) leaving the other counters unconstrained (gfx9 encoding).
+#define SA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8))
 
 struct AttnArgs {
   const uint16_t* q_abs;
@@ -62,36 +71,37 @@ struct AttnArgs {
   int k;
   int n_q;
   int n_sp;
-  int kps;               // selection entries per slice (multiple of 64)
+  int kps;               // selection entries per slice (multiple of kTile)
   float scale_log2;      // scale * log2(e)
-  float* part_o;         // [n_q][4][n_sp][16][512]   (n_sp > 1)
-  float* part_ml;        // [n_q][4][n_sp][16][2]     (max in log2 units, sum)
+  float* part_o;         // [n_q][n_sp][64][512]   (n_sp > 1)
+  float* part_ml;        // [n_q][n_sp][64][2]     (max in log2 units, sum)
   uint16_t* obar;        // [n_q][64][512] bf16 latent average
   float* lse;            // [n_q][64] or null
 };
 
 constexpr int kMaxSlice = 2048;
-constexpr size_t kAttnTileBytes = (size_t)kAttnWaves * 2 * kTile * kRowPitch;     // 149,504
-constexpr size_t kAttnSmem = kAttnTileBytes + kMaxSlice * 4;                      // + staged positions
+constexpr size_t kRingBytes = (size_t)kRing * kTileBytes;                  // 110,592
+constexpr size_t kPBytes = 2 * 4 * 64 * 16;                               // weights, double-buffered
+constexpr size_t kAlphaBytes = 2 * 4 * 16 * 4;                            // rescale factors
+constexpr size_t kFlagBytes = 2 * 4 * 4;
+constexpr size_t kSBytes = 4 * 2 * 4 * 64 * 16;                           // partial S^T of each wave
+constexpr size_t kAttnSmem = kRingBytes + kSBytes + kPBytes + kAlphaBytes + kFlagBytes + kMaxSlice * 4;
 
 __global__ __launch_bounds__(256, 1) void mla_attn_kernel(AttnArgs A) {
-  // Workgroup -> (query t, slice sp, head group hg).  The 4 head groups of a
-  // (t, sp) pair gather the same rows; their ids differ by multiples of 8 so
-  // they land on the same XCD (round-robin dispatch) and share its L2.
-  const int bid = blockIdx.x;
-  const int pair = (bid >> 5) * 8 + (bid & 7);
-  const int hg = (bid >> 3) & 3;
-  if (pair >= A.n_q * A.n_sp) return;
-  const int t = pair / A.n_sp;
-  const int sp = pair - t * A.n_sp;
+  const int t = blockIdx.x / A.n_sp;
+  const int sp = blockIdx.x - t * A.n_sp;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int w = threadIdx.x >> 6;               // head group for QK, latent quarter for PV
   const int l16 = lane & 15, g = lane >> 4;
 
   extern __shared__ __align__(16) uint8_t smem[];
-  uint8_t* buf0 = smem + wave * (2 * kTile * kRowPitch);
-  uint8_t* buf1 = buf0 + kTile * kRowPitch;
-  int32_t* spos = reinterpret_cast<int32_t*>(smem + kAttnTileBytes);
+  uint8_t* ring = smem;
+  f32x4* slds = reinterpret_cast<f32x4*>(smem + kRingBytes);               // [4 waves][2 mt][4 h][64]
+  uint8_t* sm2 = smem + kRingBytes + kSBytes;
+  u32x4* plds = reinterpret_cast<u32x4*>(sm2);                             // [2][4][64]
+  float* alds = reinterpret_cast<float*>(sm2 + kPBytes);                   // [2][4][16]
+  int* flds = reinterpret_cast<int*>(sm2 + kPBytes + kAlphaBytes);         // [2][4]
+  int32_t* spos = reinterpret_cast<int32_t*>(sm2 + kPBytes + kAlphaBytes + kFlagBytes);
 
   const int j0 = sp * A.kps;
   const int j1 = min(A.k, j0 + A.kps);
@@ -106,255 +116,284 @@ __global__ __launch_bounds__(256, 1) void mla_attn_kernel(AttnArgs A) {
     for (int u = 0; u < kMaxSlice / 256; ++u)
       if ((int)threadIdx.x + 256 * u < n_sel) spos[threadIdx.x + 256 * u] = pv[u];
   }
-
-  // Q^T operand for this wave's 16 heads: head hg*16 + l16, dims 32s + 8g .. +8.
-  bf16x8 qb[18];
-  {
-    const uint16_t* qp = A.q_abs + ((int64_t)t * kHeads + hg * 16 + l16) * kRow + 8 * g;
+  // QK is split over the 576 dims: wave w takes contraction steps
+  // st0 .. st0 + nst - 1 (steps of 32 dims: 5, 5, 4, 4) for all 64 heads, so
+  // each row chunk read from LDS feeds 4 MFMAs.  Q^T operand: head 16h + l16,
+  // dims 32 st + 8g .. +8.
+  const int nst = w < 2 ? 5 : 4;
+  const int st0 = w < 2 ? 5 * w : 10 + 4 * (w - 2);
+  bf16x8 qb[4][5];
 #pragma unroll
-    for (int s = 0; s < 18; ++s) qb[s] = as_bf16x8(ld16(qp + 32 * s));
+  for (int h = 0; h < 4; ++h) {
+    const uint16_t* qp = A.q_abs + ((int64_t)t * kHeads + 16 * h + l16) * kRow + 8 * g;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) qb[h][i] = as_bf16x8(ld16(qp + 32 * min(st0 + i, 17)));
   }
   const uint16_t* rows = A.kv + A.seq_start[A.q_seq[t]] * kRow;
   const int n_tiles = (n_sel + kTile - 1) / kTile;
+  const int last_sel = max(n_sel - 1, 0);
   __syncthreads();
 
-  // Gather of one tile into registers: 16 chunks of the latent (keys 4g+i,
-  // dims 8m..8m+7 with m = l16 + 16b) and 2 chunks of the rope part (key l16,
-  // dims 512 + 32u + 8g).  Padding entries (-1) and slots past the slice read
-  // row 0 and are masked out of the softmax.
-  u32x4 gv[16], gr[2];
-  const int last_sel = max(n_sel - 1, 0);
-  auto row_of = [&](int j) {      // branch-free: out-of-slice or padding entries read row 0
+  // Branch-free row lookup: out-of-slice or padding entries read row 0.
+  auto row_of = [&](int j) {
     const int p = spos[min(j, last_sel)];
     return (j < n_sel && p >= 0) ? p : 0;
   };
-  auto gather = [&](int tile) {
-    const int jt = tile * kTile;
+  // Direct-to-LDS gather: load u of wave w fills bytes (9w + u) KB of the tile
+  // buffer, 16 bytes per lane; the lane fetches the row chunk whose swizzled
+  // position is that slot.  Slot geometry is the same for every tile.
+  // Per load: (row << 16) | byte column of the fetched chunk.
+  uint32_t lrc[kLoadsPerWave];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint16_t* r = rows + (int64_t)row_of(jt + 4 * g + i) * kRow;
+  for (int u = 0; u < kLoadsPerWave; ++u) {
+    const int f = (kLoadsPerWave * w + u) * 1024 + 16 * lane;
+    const int r = f / kRowBytes;
+    const int pslot = (f - r * kRowBytes) / 16;
+    lrc[u] = ((uint32_t)r << 16) | (uint32_t)(16 * (pslot ^ (r & 7)));
+  }
+  const uint8_t* rows_b = reinterpret_cast<const uint8_t*>(rows);
+  auto issue = [&](int tile) {
+    const int jt = min(tile, max(n_tiles - 1, 0)) * kTile;
+    uint8_t* b = ring + (tile % kRing) * kTileBytes + (kLoadsPerWave * w) * 1024;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) gv[4 * i + b] = ld16(r + 8 * (l16 + 16 * b));
+    for (int u = 0; u < kLoadsPerWave; ++u) {
+      // byte offset within the sequence: < 2^32 for sequences below 3.7M rows
+      const uint32_t off = (uint32_t)row_of(jt + (int)(lrc[u] >> 16)) * (uint32_t)kRowBytes + (lrc[u] & 0xffffu);
+      __builtin_amdgcn_global_load_lds((const void*)(rows_b + off),
+                                       (__attribute__((address_space(3))) void*)(b + 1024 * u), 16, 0, 0);
     }
-    const uint16_t* rr = rows + (int64_t)row_of(jt + l16) * kRow + kLatent;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) gr[u] = ld16(rr + 32 * u + 8 * g);
-  };
-  auto stash = [&](uint8_t* buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        *reinterpret_cast<u32x4*>(buf + (4 * g + i) * kRowPitch + 16 * (l16 + 16 * b)) = gv[4 * i + b];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-      *reinterpret_cast<u32x4*>(buf + l16 * kRowPitch + 2 * kLatent + 64 * u + 16 * g) = gr[u];
   };
 
-  f32x4 o[32];
+  f32x4 o[8][4];                 // O^T tiles: latent dims (8 x 16 rows) x head groups (4 x 16 cols)
 #pragma unroll
-  for (int i = 0; i < 32; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int h = 0; h < 4; ++h) o[e][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;    // softmax state of head 16w + l16 (lane-partial sum)
 
-  // Wave w takes tiles w, w+4, ...  (the first gather is unconditional so that
-  // every path into the loop has drained the same loads)
-  int tile = wave;
-  gather(min(tile, max(n_tiles - 1, 0)));
-  stash(buf0);
-  wave_lds_sync();
-  uint8_t* cur = buf0;
-  uint8_t* nxt = buf1;
+  issue(0);
+  issue(1);
+
+  // Contraction slot 8g + s' of the PV products holds row kap(g, s') of the tile.
+  auto kap = [&](int s2) { return s2 < 4 ? 4 * g + s2 : 16 + 4 * g + (s2 - 4); };
+  // Lane-constant LDS offsets.  QK reads chunk 4st + g of row mt*16 + l16; with
+  // x = l16 & 7 the swizzled position is 8 (st >> 1) + 4 ((st & 1) ^ (x >> 2)) +
+  // (g ^ (x & 3)), i.e. one of two bases plus an immediate 128 (st >> 1).
+  const int xsw = l16 & 7;
+  const int qk_base = l16 * kRowBytes + 16 * (g ^ (xsw & 3));
+  const int qk_even = qk_base + 64 * (xsw >> 2);
+  const int qk_odd = qk_base + 64 * (1 - (xsw >> 2));
+  int pv_off[8];
+#pragma unroll
+  for (int s2 = 0; s2 < 8; ++s2) pv_off[s2] = lds_chunk_offset(kap(s2), l16 + 16 * w);
+
 #pragma unroll 1
-  for (; tile < n_tiles; tile += kAttnWaves) {
-    // Next tile's gather, unconditional (clamped) so the loads stay in order.
-    gather(min(tile + kAttnWaves, n_tiles - 1));
-    bool valid[4];
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    // This wave's loads of tile `tile` are done once only the next tile's
+    // kLoadsPerWave are outstanding; the barrier makes every wave's part
+    // visible and frees the buffer of tile-1 for tile+2.
+    SA_WAIT_VMCNT(kLoadsPerWave);
+    lds_barrier();
+    issue(tile + 2);
+    const uint8_t* cur = ring + (tile % kRing) * kTileBytes;
+    const int pb_i = tile & 1;
+    const int jt = tile * kTile;
+    // ---- partial S^T = R . Q^T over this wave's dims, all 64 heads, 32 rows.
+    f32x4 sp[2][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = tile * kTile + 4 * g + i;
-      valid[i] = j < n_sel && spos[min(j, last_sel)] >= 0;
-    }
-    // S^T = R . Q^T over 576 dims.
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int st = 0; st < 18; ++st) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(cur + l16 * kRowPitch + 64 * st + 16 * g);
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), qb[st], s, 0, 0, 0);
+      for (int h = 0; h < 4; ++h) sp[mt][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      if (i < nst) {
+        const int st = st0 + i;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(cur + mt * 16 * kRowBytes + ((st & 1) ? qk_odd : qk_even) +
+                                                          128 * (st >> 1));
+#pragma unroll
+          for (int h = 0; h < 4; ++h)
+            sp[mt][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), qb[h][i], sp[mt][h], 0, 0, 0);
+        }
+      }
     }
-    // Online softmax (base 2), head = l16, keys 4g + i.
-    float x[4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) slds[((w * 2 + mt) * 4 + h) * 64 + lane] = sp[mt][h];
+    lds_barrier();
+    // full S^T for heads 16w .. 16w+15: sum of the 4 waves' partials
+    f32x4 s[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      s[mt] = slds[((0 * 2 + mt) * 4 + w) * 64 + lane];
+#pragma unroll
+      for (int w2 = 1; w2 < 4; ++w2) s[mt] += slds[((w2 * 2 + mt) * 4 + w) * 64 + lane];
+    }
+    // ---- online softmax of head 16w + l16 over rows mt*16 + 4g + j.
+    float x[2][4];
     float tmax = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = valid[i] ? s[i] * A.scale_log2 : -INFINITY;
-      tmax = fmaxf(tmax, x[i]);
+    for (int mt = 0; mt < 2; ++mt) {
+      // rows jt + mt*16 + 4g .. +3: one 16-byte read of the staged positions
+      const int jb = jt + mt * 16 + 4 * g;
+      const u32x4 pq = *reinterpret_cast<const u32x4*>(spos + jb);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool valid = (jb + j < n_sel) & ((int)pq[j] >= 0);
+        x[mt][j] = valid ? s[mt][j] * A.scale_log2 : -INFINITY;
+        tmax = fmaxf(tmax, x[mt][j]);
+      }
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const bool bump = tmax > m_run + kRescaleSlack;
-    if (__any(bump)) {
-      const float new_m = bump ? tmax : m_run;
-      const float alpha = (bump && m_run != -INFINITY) ? fast_exp2(m_run - new_m) : (bump ? 0.f : 1.f);
+    const bool any_bump = __any(bump);
+    if (any_bump) {
+      const float alpha = bump ? (m_run == -INFINITY ? 0.f : fast_exp2(m_run - tmax)) : 1.f;
+      if (bump) m_run = tmax;
       l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) o[i] *= alpha;
-      m_run = new_m;
+      if (g == 0) alds[(pb_i * 4 + w) * 16 + l16] = alpha;
     }
-    float p[4];
+    if (lane == 0) flds[pb_i * 4 + w] = any_bump ? 1 : 0;
+    float p[2][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = x[i] == -INFINITY ? 0.f : fast_exp2(x[i] - m_run);
-      l_run += p[i];
-    }
-    const u32x2 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
-    const s16x4 pt = as_s16x4(pb);
-    // O^T += V^T . P^T: tile (b, e) covers dims 8(r + 16b) + e for rows r = 0..15.
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      u32x4 v[4];
+      for (int j = 0; j < 4; ++j) {
+        p[mt][j] = x[mt][j] == -INFINITY ? 0.f : fast_exp2(x[mt][j] - m_run);
+        l_run += p[mt][j];
+      }
+    const u32x4 pown = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
+                        pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
+    plds[(pb_i * 4 + w) * 64 + lane] = pown;
+    lds_barrier();
+    // ---- O^T[dims of quarter w][64 heads] += V^T . P^T over the 32 rows.
+    u32x4 pt[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        v[i] = *reinterpret_cast<const u32x4*>(cur + (4 * g + i) * kRowPitch + 16 * (l16 + 16 * b));
+    for (int h = 0; h < 4; ++h) pt[h] = plds[(pb_i * 4 + h) * 64 + lane];
+    int any_resc = 0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = e >> 1;
-        u32x2 av;
-        if (e & 1) {
-          av[0] = perm_hi(v[0][d], v[1][d]);
-          av[1] = perm_hi(v[2][d], v[3][d]);
-        } else {
-          av[0] = perm_lo(v[0][d], v[1][d]);
-          av[1] = perm_lo(v[2][d], v[3][d]);
-        }
-        o[8 * b + e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s16x4(av), pt, o[8 * b + e], 0, 0, 0);
+    for (int h = 0; h < 4; ++h) any_resc |= flds[pb_i * 4 + h];
+    if (any_resc) {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float al = flds[pb_i * 4 + h] ? alds[(pb_i * 4 + h) * 16 + l16] : 1.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e][h] *= al;
       }
     }
-    stash(nxt);
-    wave_lds_sync();
-    uint8_t* tmp = cur;
-    cur = nxt;
-    nxt = tmp;
+    u32x4 v[8];
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2)
+      v[s2] = *reinterpret_cast<const u32x4*>(cur + pv_off[s2]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = e >> 1;
+      u32x4 av;
+      if (e & 1) {
+        av[0] = perm_hi(v[0][d], v[1][d]);
+        av[1] = perm_hi(v[2][d], v[3][d]);
+        av[2] = perm_hi(v[4][d], v[5][d]);
+        av[3] = perm_hi(v[6][d], v[7][d]);
+      } else {
+        av[0] = perm_lo(v[0][d], v[1][d]);
+        av[1] = perm_lo(v[2][d], v[3][d]);
+        av[2] = perm_lo(v[4][d], v[5][d]);
+        av[3] = perm_lo(v[6][d], v[7][d]);
+      }
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        o[e][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(pt[h]), o[e][h], 0, 0, 0);
+    }
   }
-  // Reduce the sum over the 4 lanes that share a head.
+  // Head 16w + l16: sum over the 4 lanes that share it.
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
-
-  // Merge the 4 waves in LDS (reusing the tile buffers).
   __syncthreads();
-  float* lo = reinterpret_cast<float*>(smem);                  // [4][16][512]
-  float* lml = lo + kAttnWaves * 16 * kLatent;                 // [4][16][2]
-  float* lw = lml + kAttnWaves * 16 * 2;                       // [4][16] merge weights
-  float* lhs = lw + kAttnWaves * 16;                           // [16][2]  merged (max, sum)
-#pragma unroll
-  for (int b = 0; b < 4; ++b)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int dim = 32 * g + 8 * jj + 128 * b + e;
-        lo[(wave * 16 + l16) * kLatent + dim] = o[8 * b + e][jj];
-      }
+  float* ml = reinterpret_cast<float*>(ring);     // [64][2] (reuses the ring)
   if (g == 0) {
-    lml[(wave * 16 + l16) * 2 + 0] = m_run;
-    lml[(wave * 16 + l16) * 2 + 1] = l_run;
+    ml[(16 * w + l16) * 2 + 0] = m_run;
+    ml[(16 * w + l16) * 2 + 1] = l_run;
+    if (A.n_sp == 1 && A.lse)
+      A.lse[(int64_t)t * kHeads + 16 * w + l16] = l_run > 0.f ? (m_run + __log2f(l_run)) * 0.69314718055994531f
+                                                             : -INFINITY;
   }
   __syncthreads();
-  if (threadIdx.x < 16) {
-    const int hh = threadIdx.x;
-    float M = -INFINITY;
-    for (int w2 = 0; w2 < kAttnWaves; ++w2) M = fmaxf(M, lml[(w2 * 16 + hh) * 2]);
-    float L = 0.f;
-    for (int w2 = 0; w2 < kAttnWaves; ++w2) {
-      const float m = lml[(w2 * 16 + hh) * 2];
-      const float a = m == -INFINITY ? 0.f : fast_exp2(m - M);
-      lw[w2 * 16 + hh] = a;
-      L = fmaf(a, lml[(w2 * 16 + hh) * 2 + 1], L);
-    }
-    lhs[hh * 2] = M;
-    lhs[hh * 2 + 1] = L;
-    if (A.n_sp == 1) {
-      const float inv = L > 0.f ? 1.f / L : 0.f;
-      for (int w2 = 0; w2 < kAttnWaves; ++w2) lw[w2 * 16 + hh] *= inv;
-      if (A.lse) A.lse[(int64_t)t * kHeads + hg * 16 + hh] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f
-                                                                      : -INFINITY;
-    }
-  }
-  __syncthreads();
+  // O^T tile (e, h): lane holds dims 8(4g + jj + 16w) + e (jj = 0..3) of head 16h + l16.
   if (A.n_sp == 1) {
-    // One slice: normalise and write obar (bf16) directly.
-    uint16_t* ob = A.obar + ((int64_t)t * kHeads + hg * 16) * kLatent;
-    for (int i = threadIdx.x; i < 16 * kLatent / 2; i += 256) {
-      const int hh = (2 * i) / kLatent, dim = 2 * i - hh * kLatent;
-      float v0 = 0.f, v1 = 0.f;
 #pragma unroll
-      for (int w2 = 0; w2 < kAttnWaves; ++w2) {
-        const float a = lw[w2 * 16 + hh];
-        v0 = fmaf(a, lo[(w2 * 16 + hh) * kLatent + dim], v0);
-        v1 = fmaf(a, lo[(w2 * 16 + hh) * kLatent + dim + 1], v1);
+    for (int h = 0; h < 4; ++h) {
+      const float L = ml[(16 * h + l16) * 2 + 1];
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      uint16_t* ob = A.obar + ((int64_t)t * kHeads + 16 * h + l16) * kLatent;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int dim0 = 8 * (4 * g + jj + 16 * w);
+        const u32x4 pk = {pack_bf16x2(o[0][h][jj] * inv, o[1][h][jj] * inv),
+                          pack_bf16x2(o[2][h][jj] * inv, o[3][h][jj] * inv),
+                          pack_bf16x2(o[4][h][jj] * inv, o[5][h][jj] * inv),
+                          pack_bf16x2(o[6][h][jj] * inv, o[7][h][jj] * inv)};
+        *reinterpret_cast<u32x4*>(ob + dim0) = pk;
       }
-      *reinterpret_cast<uint32_t*>(ob + hh * kLatent + dim) = pack_bf16x2(v0, v1);
     }
     return;
   }
-  // Several slices: write this slice's partial state ...
-  const int64_t gbase = ((int64_t)t * kHg + hg) * A.n_sp;
-  const int64_t pbase = (gbase + sp) * 16;
-  for (int i = threadIdx.x; i < 16 * kLatent / 4; i += 256) {
-    const int hh = (4 * i) / kLatent, dim = 4 * i - hh * kLatent;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // Partial accumulators in register-tile order: [t][sp][w][e][h][lane] x 4
+  // floats, so every store instruction writes 1 KB contiguously.
+  const int64_t pbase = ((int64_t)t * A.n_sp + sp) * kHeads;
+  f32x4* po = reinterpret_cast<f32x4*>(A.part_o) + (((int64_t)t * A.n_sp + sp) * 4 + w) * 32 * 64;
 #pragma unroll
-    for (int w2 = 0; w2 < kAttnWaves; ++w2) {
-      const float a = lw[w2 * 16 + hh];
-      const f32x4 x = *reinterpret_cast<const f32x4*>(lo + (w2 * 16 + hh) * kLatent + dim);
-      acc += a * x;
-    }
-    *reinterpret_cast<f32x4*>(A.part_o + (pbase + hh) * kLatent + dim) = acc;
-  }
-  if (threadIdx.x < 16) {
-    A.part_ml[(pbase + threadIdx.x) * 2 + 0] = lhs[threadIdx.x * 2];
-    A.part_ml[(pbase + threadIdx.x) * 2 + 1] = lhs[threadIdx.x * 2 + 1];
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int h = 0; h < 4; ++h) po[(e * 4 + h) * 64 + lane] = o[e][h];
+  if (g == 0) {
+    A.part_ml[(pbase + 16 * w + l16) * 2 + 0] = m_run;
+    A.part_ml[(pbase + 16 * w + l16) * 2 + 1] = l_run;
   }
 }
 
 // Merge of the slices' partial softmax states: obar = sum_s a_s O_s / sum_s a_s l_s
-// with a_s = 2^(m_s - max m).  One workgroup per (query, head group, 64 dims);
-// each thread owns one head and 4 dims and issues all its loads at once.
-constexpr int kMaxSp = 8;
-
+// with a_s = 2^(m_s - max m).  Partials are in the attention kernel's register
+// tile order; one workgroup per (query, latent quarter w, half of the 8 dim
+// tiles), thread = (head tile h, lane), 4 dim tiles e.
 __global__ __launch_bounds__(256) void mla_merge_kernel(AttnArgs A) {
-  const int blk = blockIdx.x;
-  const int dblk = blk & 7;
-  const int hg = (blk >> 3) & 3;
-  const int t = blk >> 5;
-  const int hh = threadIdx.x >> 4;
-  const int dim = dblk * 64 + (threadIdx.x & 15) * 4;
-  const int64_t gbase = ((int64_t)t * kHg + hg) * A.n_sp;
-  float m[kMaxSp], l[kMaxSp];
-  f32x4 o[kMaxSp];
-#pragma unroll
-  for (int s2 = 0; s2 < kMaxSp; ++s2) {
-    const int sc = min(s2, A.n_sp - 1);
-    m[s2] = A.part_ml[((gbase + sc) * 16 + hh) * 2];
-    l[s2] = A.part_ml[((gbase + sc) * 16 + hh) * 2 + 1];
-    o[s2] = *reinterpret_cast<const f32x4*>(A.part_o + ((gbase + sc) * 16 + hh) * kLatent + dim);
-  }
+  const int eh = blockIdx.x & 1;
+  const int w = (blockIdx.x >> 1) & 3;
+  const int t = blockIdx.x >> 3;
+  const int h = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int head = 16 * h + l16;
+  const int64_t mlb = (int64_t)t * A.n_sp * kHeads + head;
   float M = -INFINITY;
-#pragma unroll
-  for (int s2 = 0; s2 < kMaxSp; ++s2) M = fmaxf(M, m[s2]);
+  for (int s2 = 0; s2 < A.n_sp; ++s2) M = fmaxf(M, A.part_ml[(mlb + (int64_t)s2 * kHeads) * 2]);
   float L = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  const f32x4* pob = reinterpret_cast<const f32x4*>(A.part_o);
+  for (int s2 = 0; s2 < A.n_sp; ++s2) {
+    const float m = A.part_ml[(mlb + (int64_t)s2 * kHeads) * 2];
+    const float l = A.part_ml[(mlb + (int64_t)s2 * kHeads) * 2 + 1];
+    const f32x4* src = pob + (((int64_t)t * A.n_sp + s2) * 4 + w) * 32 * 64;
+    f32x4 v[4];
 #pragma unroll
-  for (int s2 = 0; s2 < kMaxSp; ++s2) {
-    const float a = (s2 < A.n_sp && m[s2] != -INFINITY) ? fast_exp2(m[s2] - M) : 0.f;
-    L = fmaf(a, l[s2], L);
-    acc += a * o[s2];
+    for (int k = 0; k < 4; ++k) v[k] = src[((4 * eh + k) * 4 + h) * 64 + lane];
+    const float a = m == -INFINITY ? 0.f : fast_exp2(m - M);
+    L = fmaf(a, l, L);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[k] += a * v[k];
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  acc *= inv;
-  const u32x2 pk = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-  *reinterpret_cast<u32x2*>(A.obar + ((int64_t)t * kHeads + hg * 16 + hh) * kLatent + dim) = pk;
-  if (A.lse && dblk == 0 && (threadIdx.x & 15) == 0)
-    A.lse[(int64_t)t * kHeads + hg * 16 + hh] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
+  // element jj of tile e is dim 8 (4g + jj + 16w) + e
+  uint16_t* ob = A.obar + ((int64_t)t * kHeads + head) * kLatent;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int dim0 = 8 * (4 * g + jj + 16 * w) + 4 * eh;
+    const u32x2 pk = {pack_bf16x2(acc[0][jj] * inv, acc[1][jj] * inv), pack_bf16x2(acc[2][jj] * inv, acc[3][jj] * inv)};
+    *reinterpret_cast<u32x2*>(ob + dim0) = pk;
+  }
+  if (A.lse && w == 0 && eh == 0 && g == 0)
+    A.lse[(int64_t)t * kHeads + head] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
 // ------------------------------------------------------------------ W_UV
@@ -399,8 +438,9 @@ namespace sa_host {
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int mla_n_splits(int32_t n_q, int32_t k) {
-  const int target = 256;                      // one workgroup per CU
-  int n_sp = (target + 4 * n_q - 1) / (4 * n_q);
+  // About one workgroup per CU; a slice keeps at least two 32-row tiles.
+  const int target = 256;
+  int n_sp = (target + n_q - 1) / n_q;
   const int max_sp = (k + 63) / 64;
   if (n_sp > max_sp) n_sp = max_sp;
   if (n_sp > sa::kMaxSp) n_sp = sa::kMaxSp;
@@ -420,7 +460,7 @@ static MlaWs mla_carve(void* ws, int32_t n_q, int n_sp) {
   m.obar = (uint16_t*)p;
   p += align256((size_t)n_q * sa::kHeads * sa::kLatent * 2);
   m.part_ml = (float*)p;
-  p += n_sp > 1 ? align256((size_t)n_q * 4 * n_sp * 16 * 2 * 4) : 0;
+  p += n_sp > 1 ? align256((size_t)n_q * n_sp * sa::kHeads * 2 * 4) : 0;
   m.part_o = (float*)p;
   return m;
 }
@@ -428,7 +468,7 @@ static MlaWs mla_carve(void* ws, int32_t n_q, int n_sp) {
 size_t mla_workspace_size(int32_t n_q, int32_t k) {
   const int n_sp = mla_n_splits(n_q, k);
   size_t s = align256((size_t)n_q * sa::kHeads * sa::kLatent * 2);
-  if (n_sp > 1) s += align256((size_t)n_q * 4 * n_sp * 16 * 2 * 4) + align256((size_t)n_q * 4 * n_sp * 16 * sa::kLatent * 4);
+  if (n_sp > 1) s += align256((size_t)n_q * n_sp * sa::kHeads * 2 * 4) + align256((size_t)n_q * n_sp * sa::kHeads * sa::kLatent * 4);
   return s;
 }
 
@@ -440,7 +480,7 @@ int32_t launch_mla(const void* q_abs, const void* kv, const int64_t* seq_start, 
                    void* ws, hipStream_t stream) {
   const int n_sp = mla_n_splits(n_q, k);
   int kps = (k + n_sp - 1) / n_sp;
-  kps = (kps + 63) / 64 * 64;
+  kps = (kps + sa::kTile - 1) / sa::kTile * sa::kTile;
   MlaWs m = mla_carve(ws, n_q, n_sp);
   sa::AttnArgs A;
   A.q_abs = (const uint16_t*)q_abs;
@@ -472,8 +512,7 @@ int32_t launch_mla(const void* q_abs, const void* kv, const int64_t* seq_start, 
     }
     g_attr_set.fetch_or(bit);
   }
-  const int64_t pairs = (int64_t)n_q * n_sp;
-  const int64_t grid = (pairs + 7) / 8 * 32;
+  const int64_t grid = (int64_t)n_q * n_sp;
   if (grid > 0x7fffffff) {
     set_error("mla: grid too large");
     return SA_ERR_UNSUPPORTED;
@@ -482,7 +521,7 @@ int32_t launch_mla(const void* q_abs, const void* kv, const int64_t* seq_start, 
   int32_t rc = check_launch("mla_attn_kernel");
   if (rc) return rc;
   if (n_sp > 1) {
-    hipLaunchKernelGGL(sa::mla_merge_kernel, dim3((unsigned)(n_q * 32)), dim3(256), 0, stream, A);
+    hipLaunchKernelGGL(sa::mla_merge_kernel, dim3((unsigned)(n_q * 8)), dim3(256), 0, stream, A);
     if ((rc = check_launch("mla_merge_kernel"))) return rc;
   }
   sa::WuvArgs W{m.obar, (const uint16_t*)w_uv, (uint16_t*)out, n_q};
