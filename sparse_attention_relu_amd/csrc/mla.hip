@@ -356,43 +356,58 @@ __global__ __launch_bounds__(256, 1) void mla_attn_kernel(AttnArgs A) {
 
 // Merge of the slices' partial softmax states: obar = sum_s a_s O_s / sum_s a_s l_s
 // with a_s = 2^(m_s - max m).  Partials are in the attention kernel's register
-// tile order; one workgroup per (query, latent quarter w, half of the 8 dim
-// tiles), thread = (head tile h, lane), 4 dim tiles e.
+// tile order.  One workgroup per (query, latent quarter w, pair ep of dim
+// tiles); thread = (head tile h, lane) owns tiles e = 2ep, 2ep + 1 and reads
+// them for 8 slices at a time (one rescale per batch of 8).
 __global__ __launch_bounds__(256) void mla_merge_kernel(AttnArgs A) {
-  const int eh = blockIdx.x & 1;
-  const int w = (blockIdx.x >> 1) & 3;
-  const int t = blockIdx.x >> 3;
+  const int t = blockIdx.x >> 4;
+  const int w = (blockIdx.x >> 2) & 3;
+  const int ep = blockIdx.x & 3;
   const int h = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int l16 = lane & 15, g = lane >> 4;
   const int head = 16 * h + l16;
-  const int64_t mlb = (int64_t)t * A.n_sp * kHeads + head;
-  float M = -INFINITY;
-  for (int s2 = 0; s2 < A.n_sp; ++s2) M = fmaxf(M, A.part_ml[(mlb + (int64_t)s2 * kHeads) * 2]);
-  float L = 0.f;
-  f32x4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  const f32x4* pob = reinterpret_cast<const f32x4*>(A.part_o);
-  for (int s2 = 0; s2 < A.n_sp; ++s2) {
-    const float m = A.part_ml[(mlb + (int64_t)s2 * kHeads) * 2];
-    const float l = A.part_ml[(mlb + (int64_t)s2 * kHeads) * 2 + 1];
-    const f32x4* src = pob + (((int64_t)t * A.n_sp + s2) * 4 + w) * 32 * 64;
-    f32x4 v[4];
+  const int n_sp = A.n_sp;
+  const f32x4* src = reinterpret_cast<const f32x4*>(A.part_o) + ((int64_t)t * n_sp * 4 + w) * 2048 +
+                     (2 * ep * 4 + h) * 64 + lane;          // slice s adds s * 4 * 2048; tile e + 1 adds 4 * 64
+  const float2* mlp = reinterpret_cast<const float2*>(A.part_ml) + (int64_t)t * n_sp * kHeads + head;
+  float M = -INFINITY, L = 0.f;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < n_sp; s0 += 8) {
+    f32x4 v0[8], v1[8];
+    float2 ml[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) v[k] = src[((4 * eh + k) * 4 + h) * 64 + lane];
-    const float a = m == -INFINITY ? 0.f : fast_exp2(m - M);
-    L = fmaf(a, l, L);
+    for (int u = 0; u < 8; ++u) {
+      const int s = min(s0 + u, n_sp - 1);
+      ml[u] = mlp[(int64_t)s * kHeads];
+      v0[u] = src[(int64_t)s * 8192];
+      v1[u] = src[(int64_t)s * 8192 + 256];
+    }
+    float mb = M;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) acc[k] += a * v[k];
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < n_sp) mb = fmaxf(mb, ml[u].x);
+    if (mb > M) {                       // new running maximum (never taken while every slice is empty)
+      const float c = M == -INFINITY ? 0.f : fast_exp2(M - mb);
+      acc0 *= c;
+      acc1 *= c;
+      L *= c;
+      M = mb;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float a = (s0 + u < n_sp && ml[u].x != -INFINITY) ? fast_exp2(ml[u].x - M) : 0.f;
+      L = fmaf(a, ml[u].y, L);
+      acc0 += a * v0[u];
+      acc1 += a * v1[u];
+    }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   // element jj of tile e is dim 8 (4g + jj + 16w) + e
-  uint16_t* ob = A.obar + ((int64_t)t * kHeads + head) * kLatent;
+  uint16_t* ob = A.obar + ((int64_t)t * kHeads + head) * kLatent + 2 * ep;
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    const int dim0 = 8 * (4 * g + jj + 16 * w) + 4 * eh;
-    const u32x2 pk = {pack_bf16x2(acc[0][jj] * inv, acc[1][jj] * inv), pack_bf16x2(acc[2][jj] * inv, acc[3][jj] * inv)};
-    *reinterpret_cast<u32x2*>(ob + dim0) = pk;
-  }
-  if (A.lse && w == 0 && eh == 0 && g == 0)
+  for (int jj = 0; jj < 4; ++jj)
+    *reinterpret_cast<uint32_t*>(ob + 8 * (4 * g + jj + 16 * w)) = pack_bf16x2(acc0[jj] * inv, acc1[jj] * inv);
+  if (A.lse && w == 0 && ep == 0 && g == 0)
     A.lse[(int64_t)t * kHeads + head] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
@@ -404,30 +419,70 @@ struct WuvArgs {
   int n_q;
 };
 
+constexpr int kWuvRows = 64;                    // value rows per workgroup
+constexpr int kWuvQ = 16;                       // queries per block (MFMA N)
+constexpr size_t kWuvSmem = (size_t)(kWuvRows + 2 * kWuvQ) * kLatent * 2;   // 96 KB
+
+// One workgroup per (head, 64 value rows).  Its W_UV rows and, block by block,
+// the obar rows of 16 queries are staged in LDS with 1 KB direct-to-LDS loads
+// (one 512-wide row each, chunks swizzled by row so the MFMA operand reads are
+// conflict-free).  Wave w multiplies value rows 16w..16w+15 with each block.
 __global__ __launch_bounds__(256) void mla_wuv_kernel(WuvArgs W) {
+  extern __shared__ __align__(16) uint8_t smem[];
   const int h = blockIdx.x >> 2;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int vb = (blockIdx.x & 3) * kWuvRows;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int v0 = (blockIdx.x & 3) * 64 + wave * 16;          // this wave's 16 value rows
-  // A operand: W_UV[h][v0 + l16][32s + 8g .. +8], held for every query block.
+  uint8_t* wl = smem;                                   // [64 rows][1 KB]
+  uint8_t* ol = smem + kWuvRows * 1024;                 // [2 buffers][16 rows][1 KB]
+  // Row r of a staged block: lane p fills slot p with chunk p ^ (r & 15).
+  auto stage_row = [&](uint8_t* dst_row, const uint16_t* src_row, int r) {
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(src_row) + 16 * (lane ^ (r & 15));
+    __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst_row, 16, 0, 0);
+  };
+  const uint16_t* wsrc = W.w_uv + ((int64_t)h * kVdim + vb) * kLatent;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) stage_row(wl + (16 * w + u) * 1024, wsrc + (int64_t)(16 * w + u) * kLatent, u);
+  const int n_blk = (W.n_q + kWuvQ - 1) / kWuvQ;
+  auto stage_block = [&](int b) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = 4 * w + u;
+      const int tq = min(b * kWuvQ + r, W.n_q - 1);
+      stage_row(ol + ((b & 1) * kWuvQ + r) * 1024, W.obar + ((int64_t)tq * kHeads + h) * kLatent, r);
+    }
+  };
+  stage_block(0);
+  // Operand reads: row l16 (value row 16w + l16, or query l16), chunk 4s + g.
+  // Byte offset of chunk 4s + g of row l16: 16 ((4s + g) ^ l16) = 64 s ^ rd.
+  const int rd = 16 * (g ^ l16);
   bf16x8 wa[16];
-  const uint16_t* wp = W.w_uv + ((int64_t)h * kVdim + v0 + l16) * kLatent + 8 * g;
+  for (int b = 0; b < n_blk; ++b) {
+    if (b + 1 < n_blk) {
+      stage_block(b + 1);
+      SA_WAIT_VMCNT(4);
+    } else {
+      SA_WAIT_VMCNT(0);
+    }
+    lds_barrier();
+    if (b == 0) {
 #pragma unroll
-  for (int s = 0; s < 16; ++s) wa[s] = as_bf16x8(ld16(wp + 32 * s));
-  for (int tb = 0; tb < W.n_q; tb += 16) {
-    const int t = min(tb + l16, W.n_q - 1);
-    const uint16_t* op = W.obar + ((int64_t)t * kHeads + h) * kLatent + 8 * g;
-    bf16x8 ob[16];
-#pragma unroll
-    for (int s = 0; s < 16; ++s) ob[s] = as_bf16x8(ld16(op + 32 * s));
+      for (int s = 0; s < 16; ++s)
+        wa[s] = *reinterpret_cast<const bf16x8*>(wl + (16 * w + l16) * 1024 + ((16 * (4 * s)) ^ rd));
+    }
+    const uint8_t* orow = ol + ((b & 1) * kWuvQ + l16) * 1024;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 16; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[s], ob[s], acc, 0, 0, 0);
-    // acc[j] = out[t = tb + l16][h][v0 + 4g + j]
-    if (tb + l16 < W.n_q) {
+    for (int s = 0; s < 16; ++s)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[s], *reinterpret_cast<const bf16x8*>(orow + ((16 * (4 * s)) ^ rd)),
+                                                    acc, 0, 0, 0);
+    // acc[j] = out[t = 16b + l16][h][vb + 16w + 4g + j]
+    const int tq = b * kWuvQ + l16;
+    if (tq < W.n_q) {
       const u32x2 pk = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-      *reinterpret_cast<u32x2*>(W.out + ((int64_t)(tb + l16) * kHeads + h) * kVdim + v0 + 4 * g) = pk;
+      *reinterpret_cast<u32x2*>(W.out + ((int64_t)tq * kHeads + h) * kVdim + vb + 16 * w + 4 * g) = pk;
     }
+    lds_barrier();                      // buffer b & 1 is refilled by the next iteration's staging
   }
 }
 
@@ -506,7 +561,9 @@ int32_t launch_mla(const void* q_abs, const void* kv, const int64_t* seq_start, 
   const uint64_t bit = 1ull << (dev & 63);
   if (!(g_attr_set.load() & bit)) {
     if (hipFuncSetAttribute((const void*)sa::mla_attn_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)smem) != hipSuccess) {
+                            (int)smem) != hipSuccess ||
+        hipFuncSetAttribute((const void*)sa::mla_wuv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)sa::kWuvSmem) != hipSuccess) {
       set_error("mla: cannot reserve %zu bytes of LDS", smem);
       return SA_ERR_HIP;
     }
@@ -521,11 +578,11 @@ int32_t launch_mla(const void* q_abs, const void* kv, const int64_t* seq_start, 
   int32_t rc = check_launch("mla_attn_kernel");
   if (rc) return rc;
   if (n_sp > 1) {
-    hipLaunchKernelGGL(sa::mla_merge_kernel, dim3((unsigned)(n_q * 8)), dim3(256), 0, stream, A);
+    hipLaunchKernelGGL(sa::mla_merge_kernel, dim3((unsigned)(n_q * 16)), dim3(256), 0, stream, A);
     if ((rc = check_launch("mla_merge_kernel"))) return rc;
   }
   sa::WuvArgs W{m.obar, (const uint16_t*)w_uv, (uint16_t*)out, n_q};
-  hipLaunchKernelGGL(sa::mla_wuv_kernel, dim3(sa::kHeads * 4), dim3(256), 0, stream, W);
+  hipLaunchKernelGGL(sa::mla_wuv_kernel, dim3(sa::kHeads * 4), dim3(256), sa::kWuvSmem, stream, W);
   return check_launch("mla_wuv_kernel");
 }
 
