@@ -44,7 +44,43 @@ def parse():
                     help="independent input sets the timed steps rotate through, so one step's data is not "
                          "still in the 256 MB last-level cache when the next step reads it")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (reads and writes that many bytes): the "
+                         "reference kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_decode_c2_traffic.md")
+INDEXER_SOURCES = [os.path.join(ROOT, "sparse_attention_relu_amd", "csrc", f)
+                   for f in ("indexer.hip", "topk_common.h", "sa_common.h")]
+
+
+def indexer_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in INDEXER_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the decode indexer from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, scaled by a plain copy of known size; None
+    when the summary is missing, is for another workload, or was taken on
+    different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            fields = dict(line.split(":", 1) for line in fh.read().splitlines() if line.startswith("- ") and ":" in line)
+    except OSError:
+        return None
+    fields = {k[2:].strip(): v.strip().strip("`") for k, v in fields.items()}
+    if fields.get("workload") != workload or fields.get("source_sha256") != indexer_source_hash():
+        return None
+    try:
+        return int(fields["fetch_bytes_per_launch"]) + int(fields["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def step_bytes(wl, k=2048):
@@ -57,6 +93,13 @@ def step_bytes(wl, k=2048):
     per_layer = k_eff * 576 * 2 + n_q * 64 * 576 * 2 + 64 * 256 * 512 * 2 + n_q * 64 * 256 * 2
     n_full = sum(wl.full)
     return idx_bytes * n_full + per_layer * wl.n_layers + n_full * n_q * k * 4, idx_bytes
+
+
+def layer_attn_bytes(wl, k=2048):
+    """Algorithmic bytes of one layer's sparse attention + W_UV: the selected
+    rows, the absorbed queries, W_UV and the output (indices excluded)."""
+    k_eff = sum(min(k, p + 1) for p in wl.q_pos)
+    return k_eff * 576 * 2 + wl.n_q * 64 * 576 * 2 + 64 * 256 * 512 * 2 + wl.n_q * 64 * 256 * 2
 
 
 def cpu_baseline(b, wl, n_sample, min_seconds):
@@ -216,6 +259,14 @@ def main():
     torch.cuda.synchronize()
     for i in range(args.warmup):
         graphs[i % len(graphs)].replay()
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)        # elementwise: reads and writes calib_copy_mib MiB
+        torch.cuda.synchronize()
+        del src, dst
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -243,9 +294,11 @@ def main():
     hev.close()
     kern_ms = {n: sum(v) / len(v) for n, v in acc.items()}
     total_bytes, idx_bytes = step_bytes(wl)
+    attn_bytes = layer_attn_bytes(wl)
     idx_gbs = idx_bytes / (kern_ms["indexer"] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(idx_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(idx_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(idx_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name),
+                "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "kernel": "indexer_decode_kernel", "bytes_per_launch": idx_bytes,
                 "avg_launch_ms": round(kern_ms["indexer"], 5)}
 
@@ -264,6 +317,7 @@ def main():
         "step_bytes": total_bytes,
         "roofline": roofline,
         "kernel_ms_first_layer": {n: round(v, 5) for n, v in kern_ms.items()},
+        "attn_layer_gbs": round(attn_bytes / (kern_ms["attn"] * 1e-3) / 1e9, 1),
         "eager_ms_per_step": round(sum(steps_ms) / len(steps_ms), 5),
         "input_copies": len(stacks),
     }

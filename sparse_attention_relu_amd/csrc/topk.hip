@@ -14,13 +14,14 @@
 //
 // Path 1 (many workgroups per row, used by default):
 //   hist     rows x chunks: 4096-bin histogram of the top 12 key bits (LDS,
-//            then global atomics); the last chunk of a row to finish finds the
-//            bin b1 holding the k_eff-th largest key.  (sa_layer_stack builds
-//            this histogram inside the decode indexer kernel instead.)
-//   compact  rows x chunks, one pass with the chunk in registers: positions in
-//            bins above b1 are kept outright, those in b1 become candidates
-//            (composite keys); one atomic per workgroup and counter reserves
-//            the output slots.
+//            then global atomics).  (sa_layer_stack builds this histogram
+//            inside the decode indexer kernel instead.)
+//   compact  rows x chunks, one pass with the chunk in registers: every
+//            workgroup reads the finished histogram and finds the bin b1 that
+//            holds the k_eff-th largest key (no hand-off between workgroups);
+//            positions in bins above b1 are kept outright, those in b1 become
+//            candidates (composite keys); one atomic per workgroup and counter
+//            reserves the output slots.
 //   finish   one workgroup per row: the candidates go to LDS, a radix select
 //            finds the remaining count among them, and a bitonic sort puts the
 //            kept positions in ascending order.
