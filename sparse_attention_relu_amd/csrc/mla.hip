@@ -85,13 +85,16 @@ constexpr size_t kPBytes = 2 * 4 * 64 * 16;                               // wei
 constexpr size_t kAlphaBytes = 2 * 4 * 16 * 4;                            // rescale factors
 constexpr size_t kFlagBytes = 2 * 4 * 4;
 constexpr size_t kSBytes = 4 * 2 * 4 * 64 * 16;                           // partial S^T of each wave
-constexpr size_t kAttnSmem = kRingBytes + kSBytes + kPBytes + kAlphaBytes + kFlagBytes + kMaxSlice * 4;
+constexpr size_t kMlBytes = 64 * 2 * 4;                                  // (m, l) per head at the end
+constexpr size_t kAttnSmem = kRingBytes + kSBytes + kPBytes + kAlphaBytes + kFlagBytes + kMlBytes + kMaxSlice * 4;
+constexpr int kAttnThreads = 512;          // 4 score waves + 4 output waves
 
-__global__ __launch_bounds__(256, 1) void mla_attn_kernel(AttnArgs A) {
+__global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
   const int t = blockIdx.x / A.n_sp;
   const int sp = blockIdx.x - t * A.n_sp;
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;               // head group for QK, latent quarter for PV
+  const int wave = threadIdx.x >> 6;
+  const int w = wave & 3;                       // head group (score waves) / latent quarter (output waves)
   const int l16 = lane & 15, g = lane >> 4;
 
   extern __shared__ __align__(16) uint8_t smem[];
@@ -101,7 +104,8 @@ __global__ __launch_bounds__(256, 1) void mla_attn_kernel(AttnArgs A) {
   u32x4* plds = reinterpret_cast<u32x4*>(sm2);                             // [2][4][64]
   float* alds = reinterpret_cast<float*>(sm2 + kPBytes);                   // [2][4][16]
   int* flds = reinterpret_cast<int*>(sm2 + kPBytes + kAlphaBytes);         // [2][4]
-  int32_t* spos = reinterpret_cast<int32_t*>(sm2 + kPBytes + kAlphaBytes + kFlagBytes);
+  float* mlds = reinterpret_cast<float*>(sm2 + kPBytes + kAlphaBytes + kFlagBytes);          // [64][2]
+  int32_t* spos = reinterpret_cast<int32_t*>(sm2 + kPBytes + kAlphaBytes + kFlagBytes + kMlBytes);
 
   const int j0 = sp * A.kps;
   const int j1 = min(A.k, j0 + A.kps);
@@ -109,223 +113,250 @@ __global__ __launch_bounds__(256, 1) void mla_attn_kernel(AttnArgs A) {
   if (n_sel > 0) {
     // Stage the slice's positions (all loads issued before any is used).
     const int32_t* irow = A.idx + (int64_t)t * A.k + j0;
-    int pv[kMaxSlice / 256];
+    int pv[kMaxSlice / kAttnThreads];
 #pragma unroll
-    for (int u = 0; u < kMaxSlice / 256; ++u) pv[u] = irow[min((int)threadIdx.x + 256 * u, n_sel - 1)];
+    for (int u = 0; u < kMaxSlice / kAttnThreads; ++u)
+      pv[u] = irow[min((int)threadIdx.x + kAttnThreads * u, n_sel - 1)];
 #pragma unroll
-    for (int u = 0; u < kMaxSlice / 256; ++u)
-      if ((int)threadIdx.x + 256 * u < n_sel) spos[threadIdx.x + 256 * u] = pv[u];
+    for (int u = 0; u < kMaxSlice / kAttnThreads; ++u)
+      if ((int)threadIdx.x + kAttnThreads * u < n_sel) spos[threadIdx.x + kAttnThreads * u] = pv[u];
   }
-  // QK is split over the 576 dims: wave w takes contraction steps
-  // st0 .. st0 + nst - 1 (steps of 32 dims: 5, 5, 4, 4) for all 64 heads, so
-  // each row chunk read from LDS feeds 4 MFMAs.  Q^T operand: head 16h + l16,
-  // dims 32 st + 8g .. +8.
-  const int nst = w < 2 ? 5 : 4;
-  const int st0 = w < 2 ? 5 * w : 10 + 4 * (w - 2);
-  bf16x8 qb[4][5];
-#pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    const uint16_t* qp = A.q_abs + ((int64_t)t * kHeads + 16 * h + l16) * kRow + 8 * g;
-#pragma unroll
-    for (int i = 0; i < 5; ++i) qb[h][i] = as_bf16x8(ld16(qp + 32 * min(st0 + i, 17)));
-  }
-  const uint16_t* rows = A.kv + A.seq_start[A.q_seq[t]] * kRow;
   const int n_tiles = (n_sel + kTile - 1) / kTile;
   const int last_sel = max(n_sel - 1, 0);
-  __syncthreads();
 
-  // Branch-free row lookup: out-of-slice or padding entries read row 0.
-  auto row_of = [&](int j) {
-    const int p = spos[min(j, last_sel)];
-    return (j < n_sel && p >= 0) ? p : 0;
-  };
-  // Direct-to-LDS gather: load u of wave w fills bytes (9w + u) KB of the tile
-  // buffer, 16 bytes per lane; the lane fetches the row chunk whose swizzled
-  // position is that slot.  Slot geometry is the same for every tile.
-  // Per load: (row << 16) | byte column of the fetched chunk.
-  uint32_t lrc[kLoadsPerWave];
+  // Both roles pass the same sequence of workgroup barriers: B0 (positions
+  // staged), B1 (tile 0 staged), then per step BAR_s and BAR_p, then BAR_end.
+  if (wave < 4) {
+    // =========================== score waves: QK^T and the online softmax of tile `step`
+    // QK is split over the 576 dims: wave w takes contraction steps
+    // st0 .. st0 + nst - 1 (steps of 32 dims: 5, 5, 4, 4) for all 64 heads, so
+    // each row chunk read from LDS feeds 4 MFMAs.  Q^T operand: head 16h + l16,
+    // dims 32 st + 8g .. +8.
+    const int nst = w < 2 ? 5 : 4;
+    const int st0 = w < 2 ? 5 * w : 10 + 4 * (w - 2);
+    bf16x8 qb[4][5];
 #pragma unroll
-  for (int u = 0; u < kLoadsPerWave; ++u) {
-    const int f = (kLoadsPerWave * w + u) * 1024 + 16 * lane;
-    const int r = f / kRowBytes;
-    const int pslot = (f - r * kRowBytes) / 16;
-    lrc[u] = ((uint32_t)r << 16) | (uint32_t)(16 * (pslot ^ (r & 7)));
-  }
-  const uint8_t* rows_b = reinterpret_cast<const uint8_t*>(rows);
-  auto issue = [&](int tile) {
-    const int jt = min(tile, max(n_tiles - 1, 0)) * kTile;
-    uint8_t* b = ring + (tile % kRing) * kTileBytes + (kLoadsPerWave * w) * 1024;
+    for (int h = 0; h < 4; ++h) {
+      const uint16_t* qp = A.q_abs + ((int64_t)t * kHeads + 16 * h + l16) * kRow + 8 * g;
+#pragma unroll
+      for (int i = 0; i < 5; ++i) qb[h][i] = as_bf16x8(ld16(qp + 32 * min(st0 + i, 17)));
+    }
+    const uint8_t* rows_b = reinterpret_cast<const uint8_t*>(A.kv + A.seq_start[A.q_seq[t]] * kRow);
+    // Direct-to-LDS gather: load u of wave w fills bytes (9w + u) KB of the tile
+    // buffer, 16 bytes per lane; the lane fetches the row chunk whose swizzled
+    // position is that slot.  Per load: (row << 16) | byte column of the chunk.
+    uint32_t lrc[kLoadsPerWave];
 #pragma unroll
     for (int u = 0; u < kLoadsPerWave; ++u) {
-      // byte offset within the sequence: < 2^32 for sequences below 3.7M rows
-      const uint32_t off = (uint32_t)row_of(jt + (int)(lrc[u] >> 16)) * (uint32_t)kRowBytes + (lrc[u] & 0xffffu);
-      __builtin_amdgcn_global_load_lds((const void*)(rows_b + off),
-                                       (__attribute__((address_space(3))) void*)(b + 1024 * u), 16, 0, 0);
+      const int f = (kLoadsPerWave * w + u) * 1024 + 16 * lane;
+      const int r = f / kRowBytes;
+      const int pslot = (f - r * kRowBytes) / 16;
+      lrc[u] = ((uint32_t)r << 16) | (uint32_t)(16 * (pslot ^ (r & 7)));
     }
-  };
-
+    // The staged positions must be visible; the query loads stay in flight.
+    lds_barrier();                                                     // B0
+    // Branch-free row lookup: out-of-slice or padding entries read row 0.
+    auto row_of = [&](int j) {
+      const int p = spos[min(j, last_sel)];
+      return (j < n_sel && p >= 0) ? p : 0;
+    };
+    auto issue = [&](int tile) {
+      const int jt = min(tile, max(n_tiles - 1, 0)) * kTile;
+      uint8_t* b = ring + (tile % kRing) * kTileBytes + (kLoadsPerWave * w) * 1024;
+#pragma unroll
+      for (int u = 0; u < kLoadsPerWave; ++u) {
+        // byte offset within the sequence: < 2^32 for sequences below 3.7M rows
+        const uint32_t off = (uint32_t)row_of(jt + (int)(lrc[u] >> 16)) * (uint32_t)kRowBytes + (lrc[u] & 0xffffu);
+        __builtin_amdgcn_global_load_lds((const void*)(rows_b + off),
+                                         (__attribute__((address_space(3))) void*)(b + 1024 * u), 16, 0, 0);
+      }
+    };
+    issue(0);
+    issue(1);
+    // QK reads chunk 4st + g of row mt*16 + l16; with x = l16 & 7 the swizzled
+    // position is 8 (st >> 1) + 4 ((st & 1) ^ (x >> 2)) + (g ^ (x & 3)), i.e.
+    // one of two bases plus an immediate 128 (st >> 1).
+    const int xsw = l16 & 7;
+    const int qk_base = l16 * kRowBytes + 16 * (g ^ (xsw & 3));
+    const int qk_even = qk_base + 64 * (xsw >> 2);
+    const int qk_odd = qk_base + 64 * (1 - (xsw >> 2));
+    float m_run = -INFINITY, l_run = 0.f;     // softmax state of head 16w + l16 (lane-partial sum)
+    // Tile 0 is in (tile 1 may still be in flight).
+    SA_WAIT_VMCNT(kLoadsPerWave);
+    lds_barrier();                                                     // B1
+#pragma unroll 1
+    for (int tile = 0; tile <= n_tiles; ++tile) {
+      const bool active = tile < n_tiles;
+      const uint8_t* cur = ring + (tile % kRing) * kTileBytes;
+      const int pb_i = tile & 1;
+      const int jt = tile * kTile;
+      if (active) {
+        // ---- partial S^T = R . Q^T over this wave's dims, all 64 heads, 32 rows.
+        f32x4 spt[2][4];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int h = 0; h < 4; ++h) spt[mt][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+          if (i < nst) {
+            const int st = st0 + i;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+              const u32x4 a = *reinterpret_cast<const u32x4*>(cur + mt * 16 * kRowBytes +
+                                                              ((st & 1) ? qk_odd : qk_even) + 128 * (st >> 1));
+#pragma unroll
+              for (int h = 0; h < 4; ++h)
+                spt[mt][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), qb[h][i], spt[mt][h], 0, 0, 0);
+            }
+          }
+        }
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int h = 0; h < 4; ++h) slds[((w * 2 + mt) * 4 + h) * 64 + lane] = spt[mt][h];
+      }
+      lds_barrier();                                                   // BAR_s
+      if (active) {
+        // The buffer of tile - 1 is free (its QK and PV reads completed before BAR_s).
+        issue(tile + 2);
+        // full S^T for heads 16w .. 16w+15: sum of the 4 waves' partials
+        f32x4 s[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          s[mt] = slds[((0 * 2 + mt) * 4 + w) * 64 + lane];
+#pragma unroll
+          for (int w2 = 1; w2 < 4; ++w2) s[mt] += slds[((w2 * 2 + mt) * 4 + w) * 64 + lane];
+        }
+        // ---- online softmax of head 16w + l16 over rows mt*16 + 4g + j.
+        float x[2][4];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          // rows jt + mt*16 + 4g .. +3: one 16-byte read of the staged positions
+          const int jb = jt + mt * 16 + 4 * g;
+          const u32x4 pq = *reinterpret_cast<const u32x4*>(spos + jb);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bool valid = (jb + j < n_sel) & ((int)pq[j] >= 0);
+            x[mt][j] = valid ? s[mt][j] * A.scale_log2 : -INFINITY;
+            tmax = fmaxf(tmax, x[mt][j]);
+          }
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const bool bump = tmax > m_run + kRescaleSlack;
+        const bool any_bump = __any(bump);
+        if (any_bump) {
+          const float alpha = bump ? (m_run == -INFINITY ? 0.f : fast_exp2(m_run - tmax)) : 1.f;
+          if (bump) m_run = tmax;
+          l_run *= alpha;
+          if (g == 0) alds[(pb_i * 4 + w) * 16 + l16] = alpha;
+        }
+        if (lane == 0) flds[pb_i * 4 + w] = any_bump ? 1 : 0;
+        float p[2][4];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            p[mt][j] = x[mt][j] == -INFINITY ? 0.f : fast_exp2(x[mt][j] - m_run);
+            l_run += p[mt][j];
+          }
+        const u32x4 pown = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
+                            pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
+        plds[(pb_i * 4 + w) * 64 + lane] = pown;
+        // tile + 1 must be in before the next step's QK (tile + 2 stays in flight)
+        SA_WAIT_VMCNT(kLoadsPerWave);
+      }
+      lds_barrier();                                                   // BAR_p
+    }
+    // Head 16w + l16: sum over the 4 lanes that share it.
+    l_run += __shfl_xor(l_run, 16, 64);
+    l_run += __shfl_xor(l_run, 32, 64);
+    if (g == 0) {
+      mlds[(16 * w + l16) * 2 + 0] = m_run;
+      mlds[(16 * w + l16) * 2 + 1] = l_run;
+      if (A.n_sp == 1) {
+        if (A.lse)
+          A.lse[(int64_t)t * kHeads + 16 * w + l16] =
+              l_run > 0.f ? (m_run + __log2f(l_run)) * 0.69314718055994531f : -INFINITY;
+      } else {
+        const int64_t pbase = ((int64_t)t * A.n_sp + sp) * kHeads;
+        A.part_ml[(pbase + 16 * w + l16) * 2 + 0] = m_run;
+        A.part_ml[(pbase + 16 * w + l16) * 2 + 1] = l_run;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);      // the trailing (clamped) tile loads are done before the workgroup ends
+    lds_barrier();                                                     // BAR_end
+    return;
+  }
+  // =========================== output waves: O^T += V^T . P^T of tile `step - 1`
+  // Wave w owns latent dims 128w .. 128w+127 for all 64 heads.  The 32 rows
+  // are the contraction; contraction slot 8g + s' of the products holds row
+  // kap(g, s') of the tile, in both operands.
+  auto kap = [&](int s2) { return s2 < 4 ? 4 * g + s2 : 16 + 4 * g + (s2 - 4); };
+  int pv_off[8];
+#pragma unroll
+  for (int s2 = 0; s2 < 8; ++s2) pv_off[s2] = lds_chunk_offset(kap(s2), l16 + 16 * w);
   f32x4 o[8][4];                 // O^T tiles: latent dims (8 x 16 rows) x head groups (4 x 16 cols)
 #pragma unroll
   for (int e = 0; e < 8; ++e)
 #pragma unroll
     for (int h = 0; h < 4; ++h) o[e][h] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;    // softmax state of head 16w + l16 (lane-partial sum)
-
-  issue(0);
-  issue(1);
-
-  // Contraction slot 8g + s' of the PV products holds row kap(g, s') of the tile.
-  auto kap = [&](int s2) { return s2 < 4 ? 4 * g + s2 : 16 + 4 * g + (s2 - 4); };
-  // Lane-constant LDS offsets.  QK reads chunk 4st + g of row mt*16 + l16; with
-  // x = l16 & 7 the swizzled position is 8 (st >> 1) + 4 ((st & 1) ^ (x >> 2)) +
-  // (g ^ (x & 3)), i.e. one of two bases plus an immediate 128 (st >> 1).
-  const int xsw = l16 & 7;
-  const int qk_base = l16 * kRowBytes + 16 * (g ^ (xsw & 3));
-  const int qk_even = qk_base + 64 * (xsw >> 2);
-  const int qk_odd = qk_base + 64 * (1 - (xsw >> 2));
-  int pv_off[8];
-#pragma unroll
-  for (int s2 = 0; s2 < 8; ++s2) pv_off[s2] = lds_chunk_offset(kap(s2), l16 + 16 * w);
-
+  lds_barrier();                                                       // B0
+  lds_barrier();                                                       // B1
 #pragma unroll 1
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    // This wave's loads of tile `tile` are done once only the next tile's
-    // kLoadsPerWave are outstanding; the barrier makes every wave's part
-    // visible and frees the buffer of tile-1 for tile+2.
-    SA_WAIT_VMCNT(kLoadsPerWave);
-    lds_barrier();
-    issue(tile + 2);
-    const uint8_t* cur = ring + (tile % kRing) * kTileBytes;
-    const int pb_i = tile & 1;
-    const int jt = tile * kTile;
-    // ---- partial S^T = R . Q^T over this wave's dims, all 64 heads, 32 rows.
-    f32x4 sp[2][4];
+  for (int step = 0; step <= n_tiles; ++step) {
+    if (step > 0) {
+      const int tile = step - 1;
+      const uint8_t* cur = ring + (tile % kRing) * kTileBytes;
+      const int pb_i = tile & 1;
+      u32x4 v[8];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+      for (int s2 = 0; s2 < 8; ++s2) v[s2] = *reinterpret_cast<const u32x4*>(cur + pv_off[s2]);
+      u32x4 pt[4];
 #pragma unroll
-      for (int h = 0; h < 4; ++h) sp[mt][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int h = 0; h < 4; ++h) pt[h] = plds[(pb_i * 4 + h) * 64 + lane];
+      int any_resc = 0;
 #pragma unroll
-    for (int i = 0; i < 5; ++i) {
-      if (i < nst) {
-        const int st = st0 + i;
+      for (int h = 0; h < 4; ++h) any_resc |= flds[pb_i * 4 + h];
+      if (any_resc) {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(cur + mt * 16 * kRowBytes + ((st & 1) ? qk_odd : qk_even) +
-                                                          128 * (st >> 1));
+        for (int h = 0; h < 4; ++h) {
+          const float al = flds[pb_i * 4 + h] ? alds[(pb_i * 4 + h) * 16 + l16] : 1.f;
 #pragma unroll
-          for (int h = 0; h < 4; ++h)
-            sp[mt][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), qb[h][i], sp[mt][h], 0, 0, 0);
+          for (int e = 0; e < 8; ++e) o[e][h] *= al;
         }
       }
-    }
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+      for (int e = 0; e < 8; ++e) {
+        const int d = e >> 1;
+        u32x4 av;
+        if (e & 1) {
+          av[0] = perm_hi(v[0][d], v[1][d]);
+          av[1] = perm_hi(v[2][d], v[3][d]);
+          av[2] = perm_hi(v[4][d], v[5][d]);
+          av[3] = perm_hi(v[6][d], v[7][d]);
+        } else {
+          av[0] = perm_lo(v[0][d], v[1][d]);
+          av[1] = perm_lo(v[2][d], v[3][d]);
+          av[2] = perm_lo(v[4][d], v[5][d]);
+          av[3] = perm_lo(v[6][d], v[7][d]);
+        }
 #pragma unroll
-      for (int h = 0; h < 4; ++h) slds[((w * 2 + mt) * 4 + h) * 64 + lane] = sp[mt][h];
-    lds_barrier();
-    // full S^T for heads 16w .. 16w+15: sum of the 4 waves' partials
-    f32x4 s[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      s[mt] = slds[((0 * 2 + mt) * 4 + w) * 64 + lane];
-#pragma unroll
-      for (int w2 = 1; w2 < 4; ++w2) s[mt] += slds[((w2 * 2 + mt) * 4 + w) * 64 + lane];
-    }
-    // ---- online softmax of head 16w + l16 over rows mt*16 + 4g + j.
-    float x[2][4];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      // rows jt + mt*16 + 4g .. +3: one 16-byte read of the staged positions
-      const int jb = jt + mt * 16 + 4 * g;
-      const u32x4 pq = *reinterpret_cast<const u32x4*>(spos + jb);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bool valid = (jb + j < n_sel) & ((int)pq[j] >= 0);
-        x[mt][j] = valid ? s[mt][j] * A.scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, x[mt][j]);
+        for (int h = 0; h < 4; ++h)
+          o[e][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(pt[h]), o[e][h], 0, 0, 0);
       }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const bool bump = tmax > m_run + kRescaleSlack;
-    const bool any_bump = __any(bump);
-    if (any_bump) {
-      const float alpha = bump ? (m_run == -INFINITY ? 0.f : fast_exp2(m_run - tmax)) : 1.f;
-      if (bump) m_run = tmax;
-      l_run *= alpha;
-      if (g == 0) alds[(pb_i * 4 + w) * 16 + l16] = alpha;
-    }
-    if (lane == 0) flds[pb_i * 4 + w] = any_bump ? 1 : 0;
-    float p[2][4];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        p[mt][j] = x[mt][j] == -INFINITY ? 0.f : fast_exp2(x[mt][j] - m_run);
-        l_run += p[mt][j];
-      }
-    const u32x4 pown = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
-                        pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
-    plds[(pb_i * 4 + w) * 64 + lane] = pown;
-    lds_barrier();
-    // ---- O^T[dims of quarter w][64 heads] += V^T . P^T over the 32 rows.
-    u32x4 pt[4];
-#pragma unroll
-    for (int h = 0; h < 4; ++h) pt[h] = plds[(pb_i * 4 + h) * 64 + lane];
-    int any_resc = 0;
-#pragma unroll
-    for (int h = 0; h < 4; ++h) any_resc |= flds[pb_i * 4 + h];
-    if (any_resc) {
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const float al = flds[pb_i * 4 + h] ? alds[(pb_i * 4 + h) * 16 + l16] : 1.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e][h] *= al;
-      }
-    }
-    u32x4 v[8];
-#pragma unroll
-    for (int s2 = 0; s2 < 8; ++s2)
-      v[s2] = *reinterpret_cast<const u32x4*>(cur + pv_off[s2]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = e >> 1;
-      u32x4 av;
-      if (e & 1) {
-        av[0] = perm_hi(v[0][d], v[1][d]);
-        av[1] = perm_hi(v[2][d], v[3][d]);
-        av[2] = perm_hi(v[4][d], v[5][d]);
-        av[3] = perm_hi(v[6][d], v[7][d]);
-      } else {
-        av[0] = perm_lo(v[0][d], v[1][d]);
-        av[1] = perm_lo(v[2][d], v[3][d]);
-        av[2] = perm_lo(v[4][d], v[5][d]);
-        av[3] = perm_lo(v[6][d], v[7][d]);
-      }
-#pragma unroll
-      for (int h = 0; h < 4; ++h)
-        o[e][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(pt[h]), o[e][h], 0, 0, 0);
-    }
+    lds_barrier();                                                     // BAR_s (V and P reads are done)
+    lds_barrier();                                                     // BAR_p
   }
-  // Head 16w + l16: sum over the 4 lanes that share it.
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
-  __syncthreads();
-  float* ml = reinterpret_cast<float*>(ring);     // [64][2] (reuses the ring)
-  if (g == 0) {
-    ml[(16 * w + l16) * 2 + 0] = m_run;
-    ml[(16 * w + l16) * 2 + 1] = l_run;
-    if (A.n_sp == 1 && A.lse)
-      A.lse[(int64_t)t * kHeads + 16 * w + l16] = l_run > 0.f ? (m_run + __log2f(l_run)) * 0.69314718055994531f
-                                                             : -INFINITY;
-  }
-  __syncthreads();
+  lds_barrier();                                                       // BAR_end: (m, l) of every head
   // O^T tile (e, h): lane holds dims 8(4g + jj + 16w) + e (jj = 0..3) of head 16h + l16.
   if (A.n_sp == 1) {
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      const float L = ml[(16 * h + l16) * 2 + 1];
+      const float L = mlds[(16 * h + l16) * 2 + 1];
       const float inv = L > 0.f ? 1.f / L : 0.f;
       uint16_t* ob = A.obar + ((int64_t)t * kHeads + 16 * h + l16) * kLatent;
 #pragma unroll
@@ -342,16 +373,11 @@ __global__ __launch_bounds__(256, 1) void mla_attn_kernel(AttnArgs A) {
   }
   // Partial accumulators in register-tile order: [t][sp][w][e][h][lane] x 4
   // floats, so every store instruction writes 1 KB contiguously.
-  const int64_t pbase = ((int64_t)t * A.n_sp + sp) * kHeads;
   f32x4* po = reinterpret_cast<f32x4*>(A.part_o) + (((int64_t)t * A.n_sp + sp) * 4 + w) * 32 * 64;
 #pragma unroll
   for (int e = 0; e < 8; ++e)
 #pragma unroll
     for (int h = 0; h < 4; ++h) po[(e * 4 + h) * 64 + lane] = o[e][h];
-  if (g == 0) {
-    A.part_ml[(pbase + 16 * w + l16) * 2 + 0] = m_run;
-    A.part_ml[(pbase + 16 * w + l16) * 2 + 1] = l_run;
-  }
 }
 
 // Merge of the slices' partial softmax states: obar = sum_s a_s O_s / sum_s a_s l_s
@@ -574,7 +600,7 @@ int32_t launch_mla(const void* q_abs, const void* kv, const int64_t* seq_start, 
     set_error("mla: grid too large");
     return SA_ERR_UNSUPPORTED;
   }
-  hipLaunchKernelGGL(sa::mla_attn_kernel, dim3((unsigned)grid), dim3(256), smem, stream, A);
+  hipLaunchKernelGGL(sa::mla_attn_kernel, dim3((unsigned)grid), dim3(sa::kAttnThreads), smem, stream, A);
   int32_t rc = check_launch("mla_attn_kernel");
   if (rc) return rc;
   if (n_sp > 1) {
