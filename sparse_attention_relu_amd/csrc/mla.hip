@@ -110,17 +110,22 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
   const int j0 = sp * A.kps;
   const int j1 = min(A.k, j0 + A.kps);
   const int n_sel = max(j1 - j0, 0);
+  // The slice's positions: loaded first, stored to LDS once the score waves
+  // have also issued their query loads (so the two round trips overlap).
+  int pv[kMaxSlice / kAttnThreads];
   if (n_sel > 0) {
-    // Stage the slice's positions (all loads issued before any is used).
     const int32_t* irow = A.idx + (int64_t)t * A.k + j0;
-    int pv[kMaxSlice / kAttnThreads];
 #pragma unroll
     for (int u = 0; u < kMaxSlice / kAttnThreads; ++u)
       pv[u] = irow[min((int)threadIdx.x + kAttnThreads * u, n_sel - 1)];
-#pragma unroll
-    for (int u = 0; u < kMaxSlice / kAttnThreads; ++u)
-      if ((int)threadIdx.x + kAttnThreads * u < n_sel) spos[threadIdx.x + kAttnThreads * u] = pv[u];
   }
+  auto store_positions = [&]() {
+    if (n_sel > 0) {
+#pragma unroll
+      for (int u = 0; u < kMaxSlice / kAttnThreads; ++u)
+        if ((int)threadIdx.x + kAttnThreads * u < n_sel) spos[threadIdx.x + kAttnThreads * u] = pv[u];
+    }
+  };
   const int n_tiles = (n_sel + kTile - 1) / kTile;
   const int last_sel = max(n_sel - 1, 0);
 
@@ -141,38 +146,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
 #pragma unroll
       for (int i = 0; i < 5; ++i) qb[h][i] = as_bf16x8(ld16(qp + 32 * min(st0 + i, 17)));
     }
-    const uint8_t* rows_b = reinterpret_cast<const uint8_t*>(A.kv + A.seq_start[A.q_seq[t]] * kRow);
-    // Direct-to-LDS gather: load u of wave w fills bytes (9w + u) KB of the tile
-    // buffer, 16 bytes per lane; the lane fetches the row chunk whose swizzled
-    // position is that slot.  Per load: (row << 16) | byte column of the chunk.
-    uint32_t lrc[kLoadsPerWave];
-#pragma unroll
-    for (int u = 0; u < kLoadsPerWave; ++u) {
-      const int f = (kLoadsPerWave * w + u) * 1024 + 16 * lane;
-      const int r = f / kRowBytes;
-      const int pslot = (f - r * kRowBytes) / 16;
-      lrc[u] = ((uint32_t)r << 16) | (uint32_t)(16 * (pslot ^ (r & 7)));
-    }
+    store_positions();
     // The staged positions must be visible; the query loads stay in flight.
     lds_barrier();                                                     // B0
-    // Branch-free row lookup: out-of-slice or padding entries read row 0.
-    auto row_of = [&](int j) {
-      const int p = spos[min(j, last_sel)];
-      return (j < n_sel && p >= 0) ? p : 0;
-    };
-    auto issue = [&](int tile) {
-      const int jt = min(tile, max(n_tiles - 1, 0)) * kTile;
-      uint8_t* b = ring + (tile % kRing) * kTileBytes + (kLoadsPerWave * w) * 1024;
-#pragma unroll
-      for (int u = 0; u < kLoadsPerWave; ++u) {
-        // byte offset within the sequence: < 2^32 for sequences below 3.7M rows
-        const uint32_t off = (uint32_t)row_of(jt + (int)(lrc[u] >> 16)) * (uint32_t)kRowBytes + (lrc[u] & 0xffffu);
-        __builtin_amdgcn_global_load_lds((const void*)(rows_b + off),
-                                         (__attribute__((address_space(3))) void*)(b + 1024 * u), 16, 0, 0);
-      }
-    };
-    issue(0);
-    issue(1);
     // QK reads chunk 4st + g of row mt*16 + l16; with x = l16 & 7 the swizzled
     // position is 8 (st >> 1) + 4 ((st & 1) ^ (x >> 2)) + (g ^ (x & 3)), i.e.
     // one of two bases plus an immediate 128 (st >> 1).
@@ -181,9 +157,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
     const int qk_even = qk_base + 64 * (xsw >> 2);
     const int qk_odd = qk_base + 64 * (1 - (xsw >> 2));
     float m_run = -INFINITY, l_run = 0.f;     // softmax state of head 16w + l16 (lane-partial sum)
-    // Tile 0 is in (tile 1 may still be in flight).
-    SA_WAIT_VMCNT(kLoadsPerWave);
-    lds_barrier();                                                     // B1
+    lds_barrier();                                                     // B1: tile 0 staged
 #pragma unroll 1
     for (int tile = 0; tile <= n_tiles; ++tile) {
       const bool active = tile < n_tiles;
@@ -197,18 +171,23 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int h = 0; h < 4; ++h) spt[mt][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+        u32x4 a[5][2];          // all of this wave's row chunks of the tile, read up front
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+          const int st = min(st0 + i, 17);
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+            a[i][mt] = *reinterpret_cast<const u32x4*>(cur + mt * 16 * kRowBytes + ((st & 1) ? qk_odd : qk_even) +
+                                                       128 * (st >> 1));
+        }
 #pragma unroll
         for (int i = 0; i < 5; ++i) {
           if (i < nst) {
-            const int st = st0 + i;
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-              const u32x4 a = *reinterpret_cast<const u32x4*>(cur + mt * 16 * kRowBytes +
-                                                              ((st & 1) ? qk_odd : qk_even) + 128 * (st >> 1));
+            for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
               for (int h = 0; h < 4; ++h)
-                spt[mt][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), qb[h][i], spt[mt][h], 0, 0, 0);
-            }
+                spt[mt][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[i][mt]), qb[h][i], spt[mt][h], 0, 0, 0);
           }
         }
 #pragma unroll
@@ -218,8 +197,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
       }
       lds_barrier();                                                   // BAR_s
       if (active) {
-        // The buffer of tile - 1 is free (its QK and PV reads completed before BAR_s).
-        issue(tile + 2);
         // full S^T for heads 16w .. 16w+15: sum of the 4 waves' partials
         f32x4 s[2];
 #pragma unroll
@@ -265,8 +242,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
         const u32x4 pown = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
                             pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
         plds[(pb_i * 4 + w) * 64 + lane] = pown;
-        // tile + 1 must be in before the next step's QK (tile + 2 stays in flight)
-        SA_WAIT_VMCNT(kLoadsPerWave);
       }
       lds_barrier();                                                   // BAR_p
     }
@@ -286,7 +261,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
         A.part_ml[(pbase + 16 * w + l16) * 2 + 1] = l_run;
       }
     }
-    __builtin_amdgcn_s_waitcnt(0);      // the trailing (clamped) tile loads are done before the workgroup ends
     lds_barrier();                                                     // BAR_end
     return;
   }
@@ -303,7 +277,41 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
   for (int e = 0; e < 8; ++e)
 #pragma unroll
     for (int h = 0; h < 4; ++h) o[e][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+  store_positions();
+  // Direct-to-LDS gather of the tiles, issued by these waves: load u of wave w
+  // fills bytes (9w + u) KB of the tile buffer, 16 bytes per lane; the lane
+  // fetches the row chunk whose swizzled position is that slot.
+  const uint8_t* rows_b = reinterpret_cast<const uint8_t*>(A.kv + A.seq_start[A.q_seq[t]] * kRow);
+  int lrow[kLoadsPerWave], lcol[kLoadsPerWave];
+#pragma unroll
+  for (int u = 0; u < kLoadsPerWave; ++u) {
+    const int f = (kLoadsPerWave * w + u) * 1024 + 16 * lane;
+    const int r = f / kRowBytes;
+    const int pslot = (f - r * kRowBytes) / 16;
+    lrow[u] = r;
+    lcol[u] = 16 * (pslot ^ (r & 7));
+  }
+  auto issue = [&](int tile) {
+    const int jt = min(tile, max(n_tiles - 1, 0)) * kTile;
+    // every position first (one LDS round trip), then the loads
+    int pos[kLoadsPerWave];
+#pragma unroll
+    for (int u = 0; u < kLoadsPerWave; ++u) pos[u] = spos[min(jt + lrow[u], last_sel)];
+    uint8_t* b = ring + (tile % kRing) * kTileBytes + (kLoadsPerWave * w) * 1024;
+#pragma unroll
+    for (int u = 0; u < kLoadsPerWave; ++u) {
+      // out-of-slice or padding entries read row 0; byte offsets within the
+      // sequence stay below 2^32 for sequences below 3.7M rows
+      const int p = (jt + lrow[u] < n_sel && pos[u] >= 0) ? pos[u] : 0;
+      const uint32_t off = (uint32_t)p * (uint32_t)kRowBytes + (uint32_t)lcol[u];
+      __builtin_amdgcn_global_load_lds((const void*)(rows_b + off),
+                                       (__attribute__((address_space(3))) void*)(b + 1024 * u), 16, 0, 0);
+    }
+  };
   lds_barrier();                                                       // B0
+  issue(0);
+  issue(1);
+  SA_WAIT_VMCNT(kLoadsPerWave);          // tile 0 is in (tile 1 may still be in flight)
   lds_barrier();                                                       // B1
 #pragma unroll 1
   for (int step = 0; step <= n_tiles; ++step) {
@@ -349,8 +357,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
       }
     }
     lds_barrier();                                                     // BAR_s (V and P reads are done)
+    if (step < n_tiles) {
+      // The buffer of tile step - 1 is free: its QK reads completed before the
+      // previous BAR_s and its PV reads before this one.
+      issue(step + 2);
+      // tile step + 1 must be in before the next step's QK (step + 2 stays in flight)
+      SA_WAIT_VMCNT(kLoadsPerWave);
+    }
     lds_barrier();                                                     // BAR_p
   }
+  __builtin_amdgcn_s_waitcnt(0);         // the trailing (clamped) tile loads land before the workgroup ends
   lds_barrier();                                                       // BAR_end: (m, l) of every head
   // O^T tile (e, h): lane holds dims 8(4g + jj + 16w) + e (jj = 0..3) of head 16h + l16.
   if (A.n_sp == 1) {
@@ -384,7 +400,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
 // with a_s = 2^(m_s - max m).  Partials are in the attention kernel's register
 // tile order.  One workgroup per (query, latent quarter w, pair ep of dim
 // tiles); thread = (head tile h, lane) owns tiles e = 2ep, 2ep + 1 and reads
-// them for 8 slices at a time (one rescale per batch of 8).
+// them for 8 slices at a time (one rescale per batch).
+constexpr int kMergeBatch = 8;         // slices read per round trip
+
 __global__ __launch_bounds__(256) void mla_merge_kernel(AttnArgs A) {
   const int t = blockIdx.x >> 4;
   const int w = (blockIdx.x >> 2) & 3;
@@ -398,11 +416,11 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(AttnArgs A) {
   const float2* mlp = reinterpret_cast<const float2*>(A.part_ml) + (int64_t)t * n_sp * kHeads + head;
   float M = -INFINITY, L = 0.f;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < n_sp; s0 += 8) {
-    f32x4 v0[8], v1[8];
-    float2 ml[8];
+  for (int s0 = 0; s0 < n_sp; s0 += kMergeBatch) {
+    f32x4 v0[kMergeBatch], v1[kMergeBatch];
+    float2 ml[kMergeBatch];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kMergeBatch; ++u) {
       const int s = min(s0 + u, n_sp - 1);
       ml[u] = mlp[(int64_t)s * kHeads];
       v0[u] = src[(int64_t)s * 8192];
@@ -410,7 +428,7 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(AttnArgs A) {
     }
     float mb = M;
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < kMergeBatch; ++u)
       if (s0 + u < n_sp) mb = fmaxf(mb, ml[u].x);
     if (mb > M) {                       // new running maximum (never taken while every slice is empty)
       const float c = M == -INFINITY ? 0.f : fast_exp2(M - mb);
@@ -420,7 +438,7 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(AttnArgs A) {
       M = mb;
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kMergeBatch; ++u) {
       const float a = (s0 + u < n_sp && ml[u].x != -INFINITY) ? fast_exp2(ml[u].x - M) : 0.f;
       L = fmaf(a, ml[u].y, L);
       acc0 += a * v0[u];
