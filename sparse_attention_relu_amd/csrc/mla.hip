@@ -119,15 +119,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
     for (int u = 0; u < kMaxSlice / kAttnThreads; ++u)
       pv[u] = irow[min((int)threadIdx.x + kAttnThreads * u, n_sel - 1)];
   }
+  // Entries past the slice, up to the end of its last tile (at least one
+  // tile), read as padding (-1): validity is then just position >= 0.
+  const int n_tiles = (n_sel + kTile - 1) / kTile;
+  const int n_stage = max(n_tiles, 1) * kTile;
   auto store_positions = [&]() {
-    if (n_sel > 0) {
 #pragma unroll
-      for (int u = 0; u < kMaxSlice / kAttnThreads; ++u)
-        if ((int)threadIdx.x + kAttnThreads * u < n_sel) spos[threadIdx.x + kAttnThreads * u] = pv[u];
+    for (int u = 0; u < kMaxSlice / kAttnThreads; ++u) {
+      const int j = (int)threadIdx.x + kAttnThreads * u;
+      if (j < n_stage) spos[j] = j < n_sel ? pv[u] : -1;
     }
   };
-  const int n_tiles = (n_sel + kTile - 1) / kTile;
-  const int last_sel = max(n_sel - 1, 0);
 
   // Both roles pass the same sequence of workgroup barriers: B0 (positions
   // staged), B1 (tile 0 staged), then per step BAR_s and BAR_p, then BAR_end.
@@ -215,8 +217,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
           const u32x4 pq = *reinterpret_cast<const u32x4*>(spos + jb);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const bool valid = (jb + j < n_sel) & ((int)pq[j] >= 0);
-            x[mt][j] = valid ? s[mt][j] * A.scale_log2 : -INFINITY;
+            x[mt][j] = (int)pq[j] >= 0 ? s[mt][j] * A.scale_log2 : -INFINITY;
             tmax = fmaxf(tmax, x[mt][j]);
           }
         }
@@ -228,15 +229,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
           const float alpha = bump ? (m_run == -INFINITY ? 0.f : fast_exp2(m_run - tmax)) : 1.f;
           if (bump) m_run = tmax;
           l_run *= alpha;
-          if (g == 0) alds[(pb_i * 4 + w) * 16 + l16] = alpha;
+          alds[(pb_i * 4 + w) * 16 + l16] = alpha;        // the 4 lanes of a head store the same value
         }
-        if (lane == 0) flds[pb_i * 4 + w] = any_bump ? 1 : 0;
+        flds[pb_i * 4 + w] = any_bump ? 1 : 0;
+        // masked rows have x = -inf and weight exp2(-inf) = 0; m_run is -inf
+        // only while every row so far was masked
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
         float p[2][4];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            p[mt][j] = x[mt][j] == -INFINITY ? 0.f : fast_exp2(x[mt][j] - m_run);
+            p[mt][j] = fast_exp2(x[mt][j] - m_use);
             l_run += p[mt][j];
           }
         const u32x4 pown = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
@@ -296,13 +300,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
     // every position first (one LDS round trip), then the loads
     int pos[kLoadsPerWave];
 #pragma unroll
-    for (int u = 0; u < kLoadsPerWave; ++u) pos[u] = spos[min(jt + lrow[u], last_sel)];
+    for (int u = 0; u < kLoadsPerWave; ++u) pos[u] = spos[jt + lrow[u]];
     uint8_t* b = ring + (tile % kRing) * kTileBytes + (kLoadsPerWave * w) * 1024;
 #pragma unroll
     for (int u = 0; u < kLoadsPerWave; ++u) {
-      // out-of-slice or padding entries read row 0; byte offsets within the
-      // sequence stay below 2^32 for sequences below 3.7M rows
-      const int p = (jt + lrow[u] < n_sel && pos[u] >= 0) ? pos[u] : 0;
+      // padding entries read row 0; byte offsets within the sequence stay
+      // below 2^32 for sequences below 3.7M rows
+      const int p = pos[u] >= 0 ? pos[u] : 0;
       const uint32_t off = (uint32_t)p * (uint32_t)kRowBytes + (uint32_t)lcol[u];
       __builtin_amdgcn_global_load_lds((const void*)(rows_b + off),
                                        (__attribute__((address_space(3))) void*)(b + 1024 * u), 16, 0, 0);
@@ -315,25 +319,35 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
   lds_barrier();                                                       // B1
 #pragma unroll 1
   for (int step = 0; step <= n_tiles; ++step) {
-    if (step > 0) {
-      const int tile = step - 1;
+    // Operands of tile step - 1 are read before BAR_s (which frees its buffer
+    // for the gather of tile step + 2); its products run after BAR_s, beside
+    // the score waves' softmax.
+    const bool pv_step = step > 0;
+    const int tile = step - 1;
+    const int pb_i = tile & 1;
+    u32x4 v[8], pt[4];
+    int fl[4];
+    float al[4];
+    if (pv_step) {
       const uint8_t* cur = ring + (tile % kRing) * kTileBytes;
-      const int pb_i = tile & 1;
-      u32x4 v[8];
 #pragma unroll
       for (int s2 = 0; s2 < 8; ++s2) v[s2] = *reinterpret_cast<const u32x4*>(cur + pv_off[s2]);
-      u32x4 pt[4];
 #pragma unroll
-      for (int h = 0; h < 4; ++h) pt[h] = plds[(pb_i * 4 + h) * 64 + lane];
-      int any_resc = 0;
-#pragma unroll
-      for (int h = 0; h < 4; ++h) any_resc |= flds[pb_i * 4 + h];
-      if (any_resc) {
+      for (int h = 0; h < 4; ++h) {
+        pt[h] = plds[(pb_i * 4 + h) * 64 + lane];
+        fl[h] = flds[pb_i * 4 + h];
+        al[h] = alds[(pb_i * 4 + h) * 16 + l16];        // meaningful only where fl[h] is set
+      }
+    }
+    lds_barrier();                                                     // BAR_s
+    if (step < n_tiles) issue(step + 2);
+    if (pv_step) {
+      if (fl[0] | fl[1] | fl[2] | fl[3]) {
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
-          const float al = flds[pb_i * 4 + h] ? alds[(pb_i * 4 + h) * 16 + l16] : 1.f;
+          const float sc = fl[h] ? al[h] : 1.f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[e][h] *= al;
+          for (int e = 0; e < 8; ++e) o[e][h] *= sc;
         }
       }
 #pragma unroll
@@ -356,14 +370,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
           o[e][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(pt[h]), o[e][h], 0, 0, 0);
       }
     }
-    lds_barrier();                                                     // BAR_s (V and P reads are done)
-    if (step < n_tiles) {
-      // The buffer of tile step - 1 is free: its QK reads completed before the
-      // previous BAR_s and its PV reads before this one.
-      issue(step + 2);
-      // tile step + 1 must be in before the next step's QK (step + 2 stays in flight)
-      SA_WAIT_VMCNT(kLoadsPerWave);
-    }
+    // tile step + 1 must be in before the next step's QK (step + 2 stays in flight)
+    if (step < n_tiles) SA_WAIT_VMCNT(kLoadsPerWave);
     lds_barrier();                                                     // BAR_p
   }
   __builtin_amdgcn_s_waitcnt(0);         // the trailing (clamped) tile loads land before the workgroup ends

@@ -14,6 +14,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kIdxHeads = SA_INDEX_HEADS;
 constexpr int kIdxDim = SA_INDEX_DIM;
@@ -40,8 +41,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+// Two floats to packed bf16 (lo in bits 0..15) with gfx950's
+// v_cvt_pk_bf16_f32: round to nearest even under the default rounding mode,
+// the same result as f32_to_bf16_rne for every non-NaN input.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Order-preserving map of an fp32 score to uint32: a > b (as floats) iff
