@@ -29,10 +29,15 @@ namespace sa {
 // is row 8*(i/4) + 4*(lane/32) + (i%4), column lane%32.
 __device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 
+// max(x, 0) of a finite float as one integer max of its bits: negative
+// values (and -0.0) have the sign bit set, so they compare below 0 as int32.
+// (A float max would also be preceded by a NaN-quieting max in IEEE mode.)
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 __device__ __forceinline__ float relu_weighted_sum(const f32x16& acc, const float (&wr)[16]) {
   float part = 0.f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) part = fmaf(wr[i], __builtin_amdgcn_fmed3f(acc[i], 0.f, INFINITY), part);
+  for (int i = 0; i < 16; ++i) part = fmaf(wr[i], relu(acc[i]), part);
   return part + __shfl_xor(part, 32, 64);
 }
 
@@ -162,6 +167,7 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(DecArgs A) {
 // ----------------------------------------------------------- prefill kernel
 constexpr int kPfQ = 8;            // queries per workgroup (2 per wave)
 constexpr int kPfKT = 64;          // keys per tile
+constexpr int kKeyBytes = kIdxDim * 2;
 constexpr int kPfSplit = 8192;     // keys per workgroup
 
 __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
@@ -222,36 +228,41 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
     const uint16_t* kbase = k_idx + seq_start[cur] * kIdxDim;
     const int64_t cend = min(s1, maxpos + 1);              // keys that need a product
     const int n_tiles = cend > s0 ? (int)((cend - s0 + kPfKT - 1) / kPfKT) : 0;
+    // Score rows of this wave's queries from key s0 on; positions relative to
+    // s0 (clamped into [-1, kPfSplit]), so the tile loop uses 32-bit offsets.
+    const int span = (int)(s1 - s0);
+    float* srow0 = scores + (int64_t)(t_base + 2 * wave) * ld + s0;
+    float* srow1 = srow0 + ld;
+    const int rpos0 = (int)max(min(pos[0] - s0, (int64_t)kPfSplit), (int64_t)-1);
+    const int rpos1 = (int)max(min(pos[1] - s0, (int64_t)kPfSplit), (int64_t)-1);
+    const int rmax = (int)max(min(maxpos - s0, (int64_t)kPfSplit), (int64_t)-1);
+    const uint16_t* kseg = kbase + s0 * kIdxDim;
 
-    // prologue: tile 0 into buffer 0
-    u32x4 g[4];
-    auto load_tile = [&](int tile) {
+    // Key tiles go global -> registers -> LDS (double-buffered).  Two register
+    // sets keep the loads two tiles ahead of the products: the loads of tile
+    // i + 2 are issued after the barrier that follows tile i and stored to LDS
+    // after the products of tile i + 1.
+    constexpr int kPieces = kPfKT * kKeyBytes / 16 / 256;     // 16-byte pieces per thread
+    u32x4 ga[kPieces], gb[kPieces];
+    auto load_tile = [&](u32x4 (&g)[kPieces], int tile) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int flat = j * 256 + threadIdx.x;            // 16-byte piece within the 16 KB tile
-        const int64_t key = s0 + (int64_t)tile * kPfKT + (flat >> 4);
-        g[j] = key <= maxpos ? ld16(kbase + key * kIdxDim + (flat & 15) * 8) : u32x4{0, 0, 0, 0};
+      for (int j = 0; j < kPieces; ++j) {
+        const int flat = j * 256 + threadIdx.x;            // 16-byte piece within the tile
+        const int rkey = tile * kPfKT + (flat >> 4);
+        g[j] = rkey <= rmax ? ld16(kseg + rkey * kIdxDim + (flat & 15) * 8) : u32x4{0, 0, 0, 0};
       }
     };
-    auto store_tile = [&](int buf) {
+    auto store_tile = [&](const u32x4 (&g)[kPieces], int buf) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < kPieces; ++j) {
         const int flat = j * 256 + threadIdx.x;
         *reinterpret_cast<u32x4*>(lds[buf] + (flat >> 4) * kKeyPitch + (flat & 15) * 16) = g[j];
       }
     };
-    if (n_tiles > 0) {
-      load_tile(0);
-      store_tile(0);
-    }
-    __syncthreads();
-#pragma unroll 1
-    for (int tile = 0; tile < n_tiles; ++tile) {
+    auto products = [&](int tile) {
       const int buf = tile & 1;
-      if (tile + 1 < n_tiles) load_tile(tile + 1);
-      const int64_t kt0 = s0 + (int64_t)tile * kPfKT;
 #pragma unroll
-      for (int n = 0; n < 2; ++n) {
+      for (int n = 0; n < kPfKT / 32; ++n) {
         f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
@@ -262,20 +273,38 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
         }
         const float sc0 = relu_weighted_sum(acc0, wr[0]);
         const float sc1 = relu_weighted_sum(acc1, wr[1]);
-        const int64_t key = kt0 + n * 32 + (lane & 31);
-        if (lane < 32 && key < s1) {
-          if (act0) scores[(int64_t)(t_base + 2 * wave) * ld + key] = key <= pos[0] ? sc0 : -INFINITY;
-          if (act1) scores[(int64_t)(t_base + 2 * wave + 1) * ld + key] = key <= pos[1] ? sc1 : -INFINITY;
+        const int rkey = tile * kPfKT + n * 32 + (lane & 31);
+        if (lane < 32 && rkey < span) {
+          if (act0) srow0[rkey] = rkey <= rpos0 ? sc0 : -INFINITY;
+          if (act1) srow1[rkey] = rkey <= rpos1 ? sc1 : -INFINITY;
         }
       }
-      if (tile + 1 < n_tiles) store_tile(buf ^ 1);
+    };
+    if (n_tiles > 0) {
+      load_tile(ga, 0);
+      store_tile(ga, 0);
+    }
+    if (n_tiles > 1) load_tile(ga, 1);
+    if (n_tiles > 2) load_tile(gb, 2);
+    __syncthreads();
+#pragma unroll 1
+    for (int tile = 0; tile < n_tiles; tile += 2) {
+      // buffer 0 holds tile; ga carries tile + 1, gb tile + 2
+      products(tile);
+      if (tile + 1 < n_tiles) store_tile(ga, 1);
       __syncthreads();
+      if (tile + 3 < n_tiles) load_tile(ga, tile + 3);
+      if (tile + 1 >= n_tiles) break;
+      // buffer 1 holds tile + 1; gb carries tile + 2, ga tile + 3
+      products(tile + 1);
+      if (tile + 2 < n_tiles) store_tile(gb, 0);
+      __syncthreads();
+      if (tile + 4 < n_tiles) load_tile(gb, tile + 4);
     }
     // keys of this split past the last needed tile: -inf for the active queries
-    const int64_t fill0 = s0 + (int64_t)n_tiles * kPfKT;
-    for (int64_t s = fill0 + lane; s < s1; s += 64) {
-      if (act0) scores[(int64_t)(t_base + 2 * wave) * ld + s] = -INFINITY;
-      if (act1) scores[(int64_t)(t_base + 2 * wave + 1) * ld + s] = -INFINITY;
+    for (int r = n_tiles * kPfKT + lane; r < span; r += 64) {
+      if (act0) srow0[r] = -INFINITY;
+      if (act1) srow1[r] = -INFINITY;
     }
     __syncthreads();
     if (threadIdx.x < kPfQ && sh_seq[threadIdx.x] == cur) sh_done[threadIdx.x] = 1;
