@@ -41,6 +41,20 @@ __device__ __forceinline__ float relu_weighted_sum(const f32x16& acc, const floa
   return part + __shfl_xor(part, 32, 64);
 }
 
+// The same sum with the weights of one query read from LDS: accumulator
+// element 4a + b is head 8a + 4 (lane / 32) + b, four consecutive heads per a.
+__device__ __forceinline__ float relu_weighted_sum_lds(const f32x16& acc, const float* wq, int lane) {
+  const f32x4* w4 = reinterpret_cast<const f32x4*>(wq + 4 * (lane >> 5));
+  float part = 0.f;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const f32x4 wv = w4[2 * a];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) part = fmaf(wv[b], relu(acc[4 * a + b]), part);
+  }
+  return part + __shfl_xor(part, 32, 64);
+}
+
 // ------------------------------------------------------------ decode kernel
 // A workgroup covers 512 consecutive keys of one query's sequence: at each of
 // its 4 steps the 4 waves take the next 128 keys (32 each, 8 KB), staged
@@ -174,8 +188,14 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
     const int64_t* __restrict__ seq_start, const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos,
     int n_q, float* __restrict__ scores, int64_t ld, int n_splits) {
-  const int qb = blockIdx.x / n_splits;
-  const int split = blockIdx.x - qb * n_splits;
+  // Workgroups are dealt to the 8 XCDs round-robin (bid % 8).  Give each XCD a
+  // contiguous run of the split-major work list, so the workgroups resident on
+  // one XCD share the same 2 MB key split in that XCD's L2.
+  const int n_wg = (int)gridDim.x;
+  const int item = (n_wg & 7) ? (int)blockIdx.x : (int)(blockIdx.x & 7) * (n_wg >> 3) + (int)(blockIdx.x >> 3);
+  const int n_qb = n_wg / n_splits;
+  const int split = item / n_qb;
+  const int qb = item - split * n_qb;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t s0 = (int64_t)split * kPfSplit;
@@ -186,6 +206,11 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
   __shared__ int sh_seq[kPfQ];
   __shared__ int sh_pos[kPfQ];
   __shared__ int sh_done[kPfQ];
+  __shared__ __align__(16) float sh_w[kPfQ][kIdxHeads];   // head weights (read in the ReLU sums)
+  {
+    const int t = min(t_base + (int)(threadIdx.x >> 5), n_q - 1);
+    sh_w[threadIdx.x >> 5][threadIdx.x & 31] = w[(int64_t)t * kIdxHeads + (threadIdx.x & 31)];
+  }
   if (threadIdx.x < kPfQ) {
     const int t = t_base + threadIdx.x;
     sh_seq[threadIdx.x] = t < n_q ? q_seq[t] : -1;
@@ -194,9 +219,8 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
   }
   __syncthreads();
 
-  // This wave's two queries: A operands in registers, weights per accumulator row.
+  // This wave's two queries: A operands in registers.
   bf16x8 a[2][8];
-  float wr[2][16];
   int64_t pos[2];
   int seq[2];
 #pragma unroll
@@ -208,8 +232,6 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
     const uint16_t* qt = q_idx + (int64_t)t * kIdxHeads * kIdxDim;
 #pragma unroll
     for (int s = 0; s < 8; ++s) a[qq][s] = as_bf16x8(ld16(qt + (lane & 31) * kIdxDim + 16 * s + 8 * (lane >> 5)));
-#pragma unroll
-    for (int i = 0; i < 16; ++i) wr[qq][i] = w[(int64_t)t * kIdxHeads + acc_row(i, lane)];
   }
 
   // Queries of one block may belong to several sequences: handle one sequence
@@ -248,8 +270,9 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
 #pragma unroll
       for (int j = 0; j < kPieces; ++j) {
         const int flat = j * 256 + threadIdx.x;            // 16-byte piece within the tile
-        const int rkey = tile * kPfKT + (flat >> 4);
-        g[j] = rkey <= rmax ? ld16(kseg + rkey * kIdxDim + (flat & 15) * 8) : u32x4{0, 0, 0, 0};
+        // keys past the last needed one re-read that key (their scores are -inf)
+        const int rkey = min(tile * kPfKT + (flat >> 4), rmax);
+        g[j] = ld16(kseg + rkey * kIdxDim + (flat & 15) * 8);
       }
     };
     auto store_tile = [&](const u32x4 (&g)[kPieces], int buf) {
@@ -259,26 +282,41 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
         *reinterpret_cast<u32x4*>(lds[buf] + (flat >> 4) * kKeyPitch + (flat & 15) * 16) = g[j];
       }
     };
+    // Products of key column n (32 keys) of the tile in LDS buffer buf, for
+    // both queries.
+    auto column = [&](f32x16 (&acc)[2], int buf, int n) {
+      acc[0] = f32x16{};
+      acc[1] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const u32x4 b = *reinterpret_cast<const u32x4*>(lds[buf] + (n * 32 + (lane & 31)) * kKeyPitch +
+                                                        (2 * s + (lane >> 5)) * 16);
+        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][s], as_bf16x8(b), acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][s], as_bf16x8(b), acc[1], 0, 0, 0);
+      }
+    };
+    // ReLU sums and stores of column n of a tile (skipped for tile < 0).
+    auto finish = [&](const f32x16 (&acc)[2], int tile, int n) {
+      const float sc0 = relu_weighted_sum_lds(acc[0], sh_w[2 * wave], lane);
+      const float sc1 = relu_weighted_sum_lds(acc[1], sh_w[2 * wave + 1], lane);
+      const int rkey = tile * kPfKT + n * 32 + (lane & 31);
+      if (lane < 32 && tile >= 0 && rkey < span) {
+        if (act0) srow0[rkey] = rkey <= rpos0 ? sc0 : -INFINITY;
+        if (act1) srow1[rkey] = rkey <= rpos1 ? sc1 : -INFINITY;
+      }
+    };
+    // Software pipeline over the two key columns of a tile: column 1 of a
+    // tile is finished during the next tile's column-0 products and column 0
+    // during the same tile's column-1 products, so the MFMA pipe has work
+    // while the ReLU sums run.
+    static_assert(kPfKT == 64, "two key columns per tile");
+    f32x16 acc0[2], acc1[2] = {f32x16{}, f32x16{}};
     auto products = [&](int tile) {
       const int buf = tile & 1;
-#pragma unroll
-      for (int n = 0; n < kPfKT / 32; ++n) {
-        f32x16 acc0 = {}, acc1 = {};
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const u32x4 b = *reinterpret_cast<const u32x4*>(lds[buf] + (n * 32 + (lane & 31)) * kKeyPitch +
-                                                          (2 * s + (lane >> 5)) * 16);
-          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][s], as_bf16x8(b), acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][s], as_bf16x8(b), acc1, 0, 0, 0);
-        }
-        const float sc0 = relu_weighted_sum(acc0, wr[0]);
-        const float sc1 = relu_weighted_sum(acc1, wr[1]);
-        const int rkey = tile * kPfKT + n * 32 + (lane & 31);
-        if (lane < 32 && rkey < span) {
-          if (act0) srow0[rkey] = rkey <= rpos0 ? sc0 : -INFINITY;
-          if (act1) srow1[rkey] = rkey <= rpos1 ? sc1 : -INFINITY;
-        }
-      }
+      column(acc0, buf, 0);
+      finish(acc1, tile - 1, 1);
+      column(acc1, buf, 1);
+      finish(acc0, tile, 0);
     };
     if (n_tiles > 0) {
       load_tile(ga, 0);
@@ -301,6 +339,7 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
       __syncthreads();
       if (tile + 4 < n_tiles) load_tile(gb, tile + 4);
     }
+    if (n_tiles > 0) finish(acc1, n_tiles - 1, 1);
     // keys of this split past the last needed tile: -inf for the active queries
     for (int r = n_tiles * kPfKT + lane; r < span; r += 64) {
       if (act0) srow0[r] = -INFINITY;
