@@ -38,6 +38,8 @@ constexpr int kHistThreads = 256;
 constexpr int kPer = kChunk / kHistThreads;
 constexpr int kFinThreads = 1024;
 constexpr int kLdsCand = 8192;         // candidates staged in LDS by the finish kernel
+constexpr int kFinBins = 2048;         // 11-bit digits in the finish kernel
+constexpr int kBitmapBits = 1 << 18;   // rows up to this length are emitted in order from an LDS bitmap
 
 // ----------------------------------------------------------------- path 1
 __global__ void topk_zero_kernel(uint32_t* __restrict__ a, int64_t n_a, int32_t* __restrict__ b, int64_t n_b) {
@@ -231,6 +233,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
   __shared__ __align__(16) uint32_t h[kBins1];
   __shared__ int v[2 * kFinThreads];
   __shared__ uint64_t lc[kLdsCand];
+  __shared__ uint32_t bm[kBitmapBits / 32];
   __shared__ int sh_wave[kFinThreads / 64];
   __shared__ int sh_res[2];
   __shared__ int sh_cnt;
@@ -248,22 +251,35 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
   const int n_above = st[ST_ABOVE];
   const int n_cand = st[ST_NCAND];
   const bool in_lds = n_cand <= kLdsCand;
+  const bool ordered_by_bitmap = n_t <= kBitmapBits;
   int remaining = k_eff - n_above;
   const int32_t* sel = ws.sel + (int64_t)t * kMaxTopk;
   const uint64_t* gcand = ws.cand + (int64_t)t * ws.cap;
-  for (int i = threadIdx.x; i < n_above; i += kFinThreads) v[i] = sel[i];
+  const int n_words = (int)((n_t + 31) >> 5);
+  if (ordered_by_bitmap) {
+    for (int i = threadIdx.x; i < n_words; i += kFinThreads) bm[i] = 0u;
+  } else {
+    for (int i = threadIdx.x; i < n_above; i += kFinThreads) v[i] = sel[i];
+  }
   if (in_lds)
     for (int i = threadIdx.x; i < n_cand; i += kFinThreads) lc[i] = gcand[i];
   __syncthreads();
+  if (ordered_by_bitmap)
+    for (int i = threadIdx.x; i < n_above; i += kFinThreads) {
+      const int s = sel[i];
+      atomicOr(&bm[s >> 5], 1u << (s & 31));
+    }
   const uint64_t* cand = in_lds ? lc : gcand;
-  // Radix select among candidates on the 52 bits below the shared 12-bit bin.
+  // Radix select among the candidates on the 52 composite bits below the
+  // shared 12-bit bin, 11 bits at a time (20 key bits, then position bits
+  // only while keys tie across the boundary).
   uint64_t prefix = (uint64_t)st[ST_B1] << 52;
   uint64_t mask = 0xfffull << 52;
-  const int shifts[7] = {44, 36, 28, 20, 12, 4, 0};
-  for (int p = 0; p < 7; ++p) {
+  const int shifts[5] = {41, 30, 19, 8, 0};
+  for (int p = 0; p < 5; ++p) {
     const int sh = shifts[p];
-    const uint64_t dmask = p < 6 ? 0xffull : 0xfull;
-    h[threadIdx.x] = 0u;                       // digit bins live in h[0..256); 1024 cleared for find_bin
+    const uint64_t dmask = p < 4 ? 0x7ffull : 0xffull;
+    for (int i = threadIdx.x; i < kFinBins; i += kFinThreads) h[i] = 0u;
     __syncthreads();
     for (int i = threadIdx.x; i < n_cand; i += kFinThreads) {
       const uint64_t c = cand[i];
@@ -271,26 +287,54 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
     }
     __syncthreads();
     int above;
-    const int d = find_bin<kFinThreads, 1024>(h, remaining, &above, sh_wave, sh_res);
+    const int d = find_bin<kFinThreads, kFinBins>(h, remaining, &above, sh_wave, sh_res);
     const int in_bin = (int)h[d];
     remaining -= above;
     prefix |= (uint64_t)d << sh;
     mask |= dmask << sh;
     __syncthreads();
-    if (in_bin == remaining) break;
+    if (in_bin == remaining) break;     // the whole boundary bin is kept
   }
+  // Kept: candidates at or above the resolved prefix (composites are unique,
+  // so exactly k_eff - n_above of them).
   if (threadIdx.x == 0) sh_cnt = 0;
   __syncthreads();
   for (int i = threadIdx.x; i < n_cand; i += kFinThreads) {
     const uint64_t c = cand[i];
     if ((c & mask) >= prefix) {
-      const int slot = atomicAdd(&sh_cnt, 1);
-      if (n_above + slot < k_eff) v[n_above + slot] = (int)(~(uint32_t)c);
+      const int s = (int)(~(uint32_t)c);
+      if (ordered_by_bitmap) {
+        atomicOr(&bm[s >> 5], 1u << (s & 31));
+      } else {
+        const int slot = atomicAdd(&sh_cnt, 1);
+        if (n_above + slot < k_eff) v[n_above + slot] = s;
+      }
     }
   }
   __syncthreads();
-  bitonic_sort_2048(v, k_eff);
-  for (int i = threadIdx.x; i < k; i += kFinThreads) out[i] = i < k_eff ? v[i] : -1;
+  if (!ordered_by_bitmap) {
+    bitonic_sort_2048(v, k_eff);
+    for (int i = threadIdx.x; i < k; i += kFinThreads) out[i] = i < k_eff ? v[i] : -1;
+    return;
+  }
+  // Ascending emission: thread i owns a run of bitmap words; a prefix sum of
+  // their popcounts gives each thread's first output slot.
+  const int per = (n_words + kFinThreads - 1) / kFinThreads;
+  const int w0 = min((int)threadIdx.x * per, n_words), w1 = min(w0 + per, n_words);
+  int cnt = 0;
+  for (int i = w0; i < w1; ++i) cnt += __popc(bm[i]);
+  int total;
+  int slot = block_inclusive_scan<kFinThreads>(cnt, sh_wave, &total) - cnt;
+  for (int i = w0; i < w1; ++i) {
+    uint32_t bits = bm[i];
+    while (bits) {
+      const int b = __ffs(bits) - 1;
+      bits &= bits - 1;
+      if (slot < k) out[slot] = (i << 5) + b;
+      ++slot;
+    }
+  }
+  for (int i = total + threadIdx.x; i < k; i += kFinThreads) out[i] = -1;
 }
 
 }  // namespace sa
