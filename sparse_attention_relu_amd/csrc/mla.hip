@@ -90,8 +90,13 @@ constexpr size_t kAttnSmem = kRingBytes + kSBytes + kPBytes + kAlphaBytes + kFla
 constexpr int kAttnThreads = 512;          // 4 score waves + 4 output waves
 
 __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
-  const int t = blockIdx.x / A.n_sp;
-  const int sp = blockIdx.x - t * A.n_sp;
+  // Workgroups are dealt to the 8 XCDs round-robin (bid % 8): give each XCD a
+  // contiguous run of (query, slice) items, so the slices of one query share
+  // its absorbed queries in one L2.
+  const int n_wg = (int)gridDim.x;
+  const int item = (n_wg & 7) ? (int)blockIdx.x : (int)(blockIdx.x & 7) * (n_wg >> 3) + (int)(blockIdx.x >> 3);
+  const int t = item / A.n_sp;
+  const int sp = item - t * A.n_sp;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int w = wave & 3;                       // head group (score waves) / latent quarter (output waves)
