@@ -108,7 +108,9 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(DecArgs A) {
   __shared__ __align__(16) uint32_t hist[HIST ? kBins1 : 1];
   const bool do_hist = HIST && pos + 1 > A.k;
   if (do_hist) {
-    for (int i = threadIdx.x; i < kBins1; i += 256) hist[i] = 0u;
+    u32x4* h4 = reinterpret_cast<u32x4*>(hist);
+#pragma unroll
+    for (int i = 0; i < kBins1 / 4 / 256; ++i) h4[threadIdx.x + 256 * i] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
   }
 
@@ -172,6 +174,8 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(DecArgs A) {
   if (HIST && do_hist) {
     // merge into the row's global histogram; the compaction kernel reads it
     __syncthreads();
+    // consecutive lanes take consecutive bins, so each atomic instruction
+    // stays within a few cache lines
     uint32_t* gh = A.ws.hist + (int64_t)t * kBins1;
     for (int i = threadIdx.x; i < kBins1; i += 256)
       if (hist[i]) atomicAdd(&gh[i], hist[i]);

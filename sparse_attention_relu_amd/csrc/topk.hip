@@ -130,8 +130,16 @@ __global__ __launch_bounds__(kHistThreads) void topk_compact_kernel(const float*
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const uint32_t s = (uint32_t)(b0 + threadIdx.x + kHistThreads * j);
-    if ((above_mask >> j) & 1u) sel[slot_a++] = (int32_t)s;
-    if ((cand_mask >> j) & 1u) cand[slot_c++] = ((uint64_t)score_key(v[j]) << 32) | (uint32_t)~s;
+    // (slots stay below kMaxTopk and cap whenever the histogram is complete;
+    // the checks keep inconsistent workspace contents from writing out of range)
+    if ((above_mask >> j) & 1u) {
+      if (slot_a < kMaxTopk) sel[slot_a] = (int32_t)s;
+      ++slot_a;
+    }
+    if ((cand_mask >> j) & 1u) {
+      if (slot_c < ws.cap) cand[slot_c] = ((uint64_t)score_key(v[j]) << 32) | (uint32_t)~s;
+      ++slot_c;
+    }
   }
 }
 
@@ -248,8 +256,10 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
     select_row_exact(row, n_t, k_eff, out, h, sh_wave, sh_res);
     return;
   }
-  const int n_above = st[ST_ABOVE];
-  const int n_cand = st[ST_NCAND];
+  // Counts come from the compaction; clamped so that inconsistent workspace
+  // contents cannot index out of range.
+  const int n_above = min(max(st[ST_ABOVE], 0), k_eff - 1);
+  const int n_cand = (int)min((int64_t)max(st[ST_NCAND], 0), ws.cap);
   const bool in_lds = n_cand <= kLdsCand;
   const bool ordered_by_bitmap = n_t <= kBitmapBits;
   int remaining = k_eff - n_above;
@@ -267,7 +277,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
   if (ordered_by_bitmap)
     for (int i = threadIdx.x; i < n_above; i += kFinThreads) {
       const int s = sel[i];
-      atomicOr(&bm[s >> 5], 1u << (s & 31));
+      if (s >= 0 && s < n_t) atomicOr(&bm[s >> 5], 1u << (s & 31));
     }
   const uint64_t* cand = in_lds ? lc : gcand;
   // Radix select among the candidates on the 52 composite bits below the
@@ -304,7 +314,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
     if ((c & mask) >= prefix) {
       const int s = (int)(~(uint32_t)c);
       if (ordered_by_bitmap) {
-        atomicOr(&bm[s >> 5], 1u << (s & 31));
+        if (s >= 0 && s < n_t) atomicOr(&bm[s >> 5], 1u << (s & 31));
       } else {
         const int slot = atomicAdd(&sh_cnt, 1);
         if (n_above + slot < k_eff) v[n_above + slot] = s;

@@ -50,6 +50,8 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int* sh_wave, int* to
 // Given a histogram (bins ordered by increasing key), find the bin d holding
 // the need-th largest element: count(bins > d) < need <= count(bins >= d).
 // Returns d and writes count(bins > d) to *above.  All NT threads call it.
+// need is clamped into [1, total] (total >= 1), so a bin is always found and
+// every later index stays in range even if the counts were inconsistent.
 template <int NT, int NB>
 __device__ int find_bin(const uint32_t* hist, int need, int* above_out, int* sh_wave, int* sh_res) {
   constexpr int PER = NB / NT;      // bins per thread, scanned from the top
@@ -57,7 +59,13 @@ __device__ int find_bin(const uint32_t* hist, int need, int* above_out, int* sh_
   int local = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) local += (int)hist[NB - 1 - (tid * PER + i)];
-  const int incl = block_inclusive_scan<NT>(local, sh_wave);
+  int total;
+  const int incl = block_inclusive_scan<NT>(local, sh_wave, &total);
+  if (total <= 0) {                 // empty histogram: lowest bin, nothing above
+    *above_out = 0;
+    return 0;
+  }
+  need = min(max(need, 1), total);
   const int excl = incl - local;
   if (excl < need && need <= incl) {
     int run = excl;
