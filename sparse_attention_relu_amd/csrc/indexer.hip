@@ -264,12 +264,11 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
     const int rmax = (int)max(min(maxpos - s0, (int64_t)kPfSplit), (int64_t)-1);
     const uint16_t* kseg = kbase + s0 * kIdxDim;
 
-    // Key tiles go global -> registers -> LDS (double-buffered).  Two register
-    // sets keep the loads two tiles ahead of the products: the loads of tile
-    // i + 2 are issued after the barrier that follows tile i and stored to LDS
-    // after the products of tile i + 1.
+    // Key tiles go global -> registers -> LDS (double-buffered): the loads of
+    // tile i + 1 are issued before the products of tile i and stored to LDS
+    // after them.
     constexpr int kPieces = kPfKT * kKeyBytes / 16 / 256;     // 16-byte pieces per thread
-    u32x4 ga[kPieces], gb[kPieces];
+    u32x4 ga[kPieces];
     auto load_tile = [&](u32x4 (&g)[kPieces], int tile) {
 #pragma unroll
       for (int j = 0; j < kPieces; ++j) {
@@ -289,14 +288,17 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
     // Products of key column n (32 keys) of the tile in LDS buffer buf, for
     // both queries.
     auto column = [&](f32x16 (&acc)[2], int buf, int n) {
+      u32x4 b[8];                       // the column's operands, read before its products
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        b[s] = *reinterpret_cast<const u32x4*>(lds[buf] + (n * 32 + (lane & 31)) * kKeyPitch +
+                                               (2 * s + (lane >> 5)) * 16);
       acc[0] = f32x16{};
       acc[1] = f32x16{};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const u32x4 b = *reinterpret_cast<const u32x4*>(lds[buf] + (n * 32 + (lane & 31)) * kKeyPitch +
-                                                        (2 * s + (lane >> 5)) * 16);
-        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][s], as_bf16x8(b), acc[0], 0, 0, 0);
-        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][s], as_bf16x8(b), acc[1], 0, 0, 0);
+        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][s], as_bf16x8(b[s]), acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][s], as_bf16x8(b[s]), acc[1], 0, 0, 0);
       }
     };
     // ReLU sums and stores of column n of a tile (skipped for tile < 0).
@@ -326,22 +328,13 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
       load_tile(ga, 0);
       store_tile(ga, 0);
     }
-    if (n_tiles > 1) load_tile(ga, 1);
-    if (n_tiles > 2) load_tile(gb, 2);
     __syncthreads();
 #pragma unroll 1
-    for (int tile = 0; tile < n_tiles; tile += 2) {
-      // buffer 0 holds tile; ga carries tile + 1, gb tile + 2
+    for (int tile = 0; tile < n_tiles; ++tile) {
+      if (tile + 1 < n_tiles) load_tile(ga, tile + 1);
       products(tile);
-      if (tile + 1 < n_tiles) store_tile(ga, 1);
+      if (tile + 1 < n_tiles) store_tile(ga, (tile + 1) & 1);
       __syncthreads();
-      if (tile + 3 < n_tiles) load_tile(ga, tile + 3);
-      if (tile + 1 >= n_tiles) break;
-      // buffer 1 holds tile + 1; gb carries tile + 2, ga tile + 3
-      products(tile + 1);
-      if (tile + 2 < n_tiles) store_tile(gb, 0);
-      __syncthreads();
-      if (tile + 4 < n_tiles) load_tile(gb, tile + 4);
     }
     if (n_tiles > 0) finish(acc1, n_tiles - 1, 1);
     // keys of this split past the last needed tile: -inf for the active queries
