@@ -122,19 +122,22 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(DecArgs A) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) wr[i] = A.w[(int64_t)t * kIdxHeads + acc_row(i, lane)];
 
-  // step it of this wave covers keys c0 + (4 it + wave) * 32 .. +31
-  const int64_t wlast = pos - c0;                                 // last valid key, relative to c0
+  // step it of this wave covers keys c0 + (4 it + wave) * 32 .. +31; keys
+  // and score columns are handled relative to c0 in 32 bits
+  const int wlast = (int)min(pos - c0, (int64_t)kDecChunk - 1);       // last valid key
+  const int wend = (int)min(A.ld - c0, (int64_t)kDecChunk);          // columns of this chunk in the row
   const uint16_t* kb = A.k_idx + (A.seq_start[A.q_seq[t]] + c0) * kIdxDim;
+  float* sc0 = srow + c0;
   const int n_it = kDecSteps;
   uint8_t* my = lds[wave];
-  auto key_of = [&](int it) { return (int64_t)(it * kDecWaves + wave) * 32; };
+  auto key_of = [&](int it) { return (it * kDecWaves + wave) * 32; };
 
   // Loads past the causal bound re-read the last valid key (always in bounds);
   // their scores are replaced by -inf, so no load needs a branch.
   auto load = [&](u32x4 (&g)[8], int it) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int64_t key = min(key_of(it) + 4 * j + (lane >> 4), wlast);
+      const int key = min(key_of(it) + 4 * j + (lane >> 4), wlast);
       g[j] = ld16(kb + key * kIdxDim + (lane & 15) * 8);
     }
   };
@@ -151,10 +154,10 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(DecArgs A) {
     }
     wave_lds_fence();
     const float sc = relu_weighted_sum(acc, wr);
-    const int64_t key = c0 + key_of(it) + (lane & 31);
-    if (lane < 32 && key < A.ld) {
-      const bool valid = key <= pos;
-      srow[key] = valid ? sc : -INFINITY;
+    const int key = key_of(it) + (lane & 31);
+    if (lane < 32 && key < wend) {
+      const bool valid = key <= wlast;
+      sc0[key] = valid ? sc : -INFINITY;
       if (HIST && do_hist && valid) atomicAdd(&hist[score_key(sc) >> 20], 1u);
     }
   };
