@@ -231,6 +231,64 @@ __device__ void select_row_exact(const float* __restrict__ row, int64_t n_t, int
   }
 }
 
+// Radix select among n_cand candidate composites (all in first-digit bin b1):
+// the `remaining` largest are kept.  Works on the 52 composite bits below the
+// shared 12-bit bin, 11 bits at a time (20 key bits, then position bits only
+// while keys tie across the boundary).  Returns (prefix, mask): a candidate c
+// is kept iff (c & mask) >= prefix (composites are unique, so exactly
+// `remaining` of them).  h needs kFinBins entries.
+struct Kept {
+  uint64_t prefix, mask;
+};
+__device__ Kept select_candidates(const uint64_t* cand, int n_cand, uint32_t b1, int remaining, uint32_t* h,
+                                  int* sh_wave, int* sh_res) {
+  uint64_t prefix = (uint64_t)b1 << 52;
+  uint64_t mask = 0xfffull << 52;
+  const int shifts[5] = {41, 30, 19, 8, 0};
+  for (int p = 0; p < 5; ++p) {
+    const int sh = shifts[p];
+    const uint64_t dmask = p < 4 ? 0x7ffull : 0xffull;
+    for (int i = threadIdx.x; i < kFinBins; i += kFinThreads) h[i] = 0u;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n_cand; i += kFinThreads) {
+      const uint64_t c = cand[i];
+      if ((c & mask) == prefix) atomicAdd(&h[(c >> sh) & dmask], 1u);
+    }
+    __syncthreads();
+    int above;
+    const int d = find_bin<kFinThreads, kFinBins>(h, remaining, &above, sh_wave, sh_res);
+    const int in_bin = (int)h[d];
+    remaining -= above;
+    prefix |= (uint64_t)d << sh;
+    mask |= dmask << sh;
+    __syncthreads();
+    if (in_bin == remaining) break;     // the whole boundary bin is kept
+  }
+  return Kept{prefix, mask};
+}
+
+// Ascending emission of the positions set in bm[0 .. n_words): thread i owns a
+// run of words; a prefix sum of their popcounts gives its first output slot.
+// Slots past the set bits (up to k) get -1.
+__device__ void emit_bitmap(const uint32_t* bm, int n_words, int32_t* __restrict__ out, int k, int* sh_wave) {
+  const int per = (n_words + kFinThreads - 1) / kFinThreads;
+  const int w0 = min((int)threadIdx.x * per, n_words), w1 = min(w0 + per, n_words);
+  int cnt = 0;
+  for (int i = w0; i < w1; ++i) cnt += __popc(bm[i]);
+  int total;
+  int slot = block_inclusive_scan<kFinThreads>(cnt, sh_wave, &total) - cnt;
+  for (int i = w0; i < w1; ++i) {
+    uint32_t bits = bm[i];
+    while (bits) {
+      const int b = __ffs(bits) - 1;
+      bits &= bits - 1;
+      if (slot < k) out[slot] = (i << 5) + b;
+      ++slot;
+    }
+  }
+  for (int i = total + threadIdx.x; i < k; i += kFinThreads) out[i] = -1;
+}
+
 __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* __restrict__ scores, int64_t ld,
                                                                     const int32_t* __restrict__ q_pos, int k,
                                                                     int32_t* __restrict__ idx, TopkWs ws,
@@ -262,7 +320,6 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
   const int n_cand = (int)min((int64_t)max(st[ST_NCAND], 0), ws.cap);
   const bool in_lds = n_cand <= kLdsCand;
   const bool ordered_by_bitmap = n_t <= kBitmapBits;
-  int remaining = k_eff - n_above;
   const int32_t* sel = ws.sel + (int64_t)t * kMaxTopk;
   const uint64_t* gcand = ws.cand + (int64_t)t * ws.cap;
   const int n_words = (int)((n_t + 31) >> 5);
@@ -280,38 +337,12 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
       if (s >= 0 && s < n_t) atomicOr(&bm[s >> 5], 1u << (s & 31));
     }
   const uint64_t* cand = in_lds ? lc : gcand;
-  // Radix select among the candidates on the 52 composite bits below the
-  // shared 12-bit bin, 11 bits at a time (20 key bits, then position bits
-  // only while keys tie across the boundary).
-  uint64_t prefix = (uint64_t)st[ST_B1] << 52;
-  uint64_t mask = 0xfffull << 52;
-  const int shifts[5] = {41, 30, 19, 8, 0};
-  for (int p = 0; p < 5; ++p) {
-    const int sh = shifts[p];
-    const uint64_t dmask = p < 4 ? 0x7ffull : 0xffull;
-    for (int i = threadIdx.x; i < kFinBins; i += kFinThreads) h[i] = 0u;
-    __syncthreads();
-    for (int i = threadIdx.x; i < n_cand; i += kFinThreads) {
-      const uint64_t c = cand[i];
-      if ((c & mask) == prefix) atomicAdd(&h[(c >> sh) & dmask], 1u);
-    }
-    __syncthreads();
-    int above;
-    const int d = find_bin<kFinThreads, kFinBins>(h, remaining, &above, sh_wave, sh_res);
-    const int in_bin = (int)h[d];
-    remaining -= above;
-    prefix |= (uint64_t)d << sh;
-    mask |= dmask << sh;
-    __syncthreads();
-    if (in_bin == remaining) break;     // the whole boundary bin is kept
-  }
-  // Kept: candidates at or above the resolved prefix (composites are unique,
-  // so exactly k_eff - n_above of them).
+  const Kept kept = select_candidates(cand, n_cand, (uint32_t)st[ST_B1], k_eff - n_above, h, sh_wave, sh_res);
   if (threadIdx.x == 0) sh_cnt = 0;
   __syncthreads();
   for (int i = threadIdx.x; i < n_cand; i += kFinThreads) {
     const uint64_t c = cand[i];
-    if ((c & mask) >= prefix) {
+    if ((c & kept.mask) >= kept.prefix) {
       const int s = (int)(~(uint32_t)c);
       if (ordered_by_bitmap) {
         if (s >= 0 && s < n_t) atomicOr(&bm[s >> 5], 1u << (s & 31));
@@ -327,24 +358,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
     for (int i = threadIdx.x; i < k; i += kFinThreads) out[i] = i < k_eff ? v[i] : -1;
     return;
   }
-  // Ascending emission: thread i owns a run of bitmap words; a prefix sum of
-  // their popcounts gives each thread's first output slot.
-  const int per = (n_words + kFinThreads - 1) / kFinThreads;
-  const int w0 = min((int)threadIdx.x * per, n_words), w1 = min(w0 + per, n_words);
-  int cnt = 0;
-  for (int i = w0; i < w1; ++i) cnt += __popc(bm[i]);
-  int total;
-  int slot = block_inclusive_scan<kFinThreads>(cnt, sh_wave, &total) - cnt;
-  for (int i = w0; i < w1; ++i) {
-    uint32_t bits = bm[i];
-    while (bits) {
-      const int b = __ffs(bits) - 1;
-      bits &= bits - 1;
-      if (slot < k) out[slot] = (i << 5) + b;
-      ++slot;
-    }
-  }
-  for (int i = total + threadIdx.x; i < k; i += kFinThreads) out[i] = -1;
+  emit_bitmap(bm, n_words, out, k, sh_wave);
 }
 
 }  // namespace sa
