@@ -314,18 +314,22 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
         if (act1) srow1[rkey] = rkey <= rpos1 ? sc1 : -INFINITY;
       }
     };
-    // Software pipeline over the two key columns of a tile: column 1 of a
-    // tile is finished during the next tile's column-0 products and column 0
-    // during the same tile's column-1 products, so the MFMA pipe has work
-    // while the ReLU sums run.
-    static_assert(kPfKT == 64, "two key columns per tile");
+    // Software pipeline over the key columns of a tile: each column is
+    // finished during the products of the next one (the last column of a tile
+    // during the next tile's first), so the MFMA pipe has work while the ReLU
+    // sums run.  Columns alternate between the two accumulator sets.
+    constexpr int kCols = kPfKT / 32;
+    static_assert(kCols % 2 == 0, "an even number of key columns per tile");
     f32x16 acc0[2], acc1[2] = {f32x16{}, f32x16{}};
     auto products = [&](int tile) {
       const int buf = tile & 1;
-      column(acc0, buf, 0);
-      finish(acc1, tile - 1, 1);
-      column(acc1, buf, 1);
-      finish(acc0, tile, 0);
+#pragma unroll
+      for (int c = 0; c < kCols; c += 2) {
+        column(acc0, buf, c);
+        finish(acc1, c == 0 ? tile - 1 : tile, c == 0 ? kCols - 1 : c - 1);
+        column(acc1, buf, c + 1);
+        finish(acc0, tile, c);
+      }
     };
     if (n_tiles > 0) {
       load_tile(ga, 0);
@@ -339,7 +343,7 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
       if (tile + 1 < n_tiles) store_tile(ga, (tile + 1) & 1);
       __syncthreads();
     }
-    if (n_tiles > 0) finish(acc1, n_tiles - 1, 1);
+    if (n_tiles > 0) finish(acc1, n_tiles - 1, kCols - 1);
     // keys of this split past the last needed tile: -inf for the active queries
     for (int r = n_tiles * kPfKT + lane; r < span; r += 64) {
       if (act0) srow0[r] = -INFINITY;
