@@ -9,20 +9,21 @@
 //     out[t, h] = bf16(W_UV[h] @ obar).
 //
 // mla_attn_kernel: one workgroup per (query, slice of the selection); all 64
-// heads share every gathered row.  The slice is consumed in 32-row tiles:
-//   - the workgroup gathers each tile (36 KB) with 16-byte direct-to-LDS loads
-//     into a 3-buffer ring, so two tiles are in flight without registers;
-//   - wave w computes S^T[32 rows x heads 16w..16w+15] = R . Q^T with
-//     v_mfma_f32_16x16x32_bf16 over the 576 dims (R from LDS, Q^T in registers)
-//     and runs the online softmax of its 16 heads in base 2 (the running max is
-//     only moved when a tile exceeds it by more than 2^8, so rescaling is rare);
-//     its bf16 weights and any rescale factors go to LDS;
-//   - after one workgroup barrier, wave w accumulates O^T[latent dims
-//     128w..128w+127 x all 64 heads] += V^T . P^T with v_mfma_f32_16x16x32_bf16:
-//     the 32 rows are the contraction, the V^T operand is assembled from 16-byte
-//     row chunks with byte permutes (rows and dims are permuted consistently in
-//     both operands, no transpose through LDS), P^T comes from the 4 waves'
-//     weights.
+// heads share every gathered row.  The slice is consumed in 32-row tiles by
+// 4 score waves and 4 output waves working one tile apart:
+//   - the output waves gather each tile (36 KB) with 16-byte direct-to-LDS
+//     loads into a 3-buffer ring, so two tiles are in flight without registers;
+//   - score wave w computes the partial S^T[32 rows x 64 heads] = R . Q^T over
+//     dims 144w..144w+143 with v_mfma_f32_32x32x16_bf16 (R from LDS, Q^T in
+//     registers); after an exchange through LDS it runs the online softmax of
+//     heads 16w..16w+15 in base 2 (the running max is only moved when a tile
+//     exceeds it by more than 2^8, so rescaling is rare) and puts its bf16
+//     weights and any rescale factors in LDS;
+//   - output wave w accumulates O^T[latent dims 128w..128w+127 x 64 heads] +=
+//     V^T . P^T of the previous tile with v_mfma_f32_32x32x16_bf16: the 32 rows
+//     are the contraction, the V^T operand is assembled from 8-byte row pieces
+//     with byte permutes (rows and dims are permuted consistently in both
+//     operands, no transpose through LDS), P^T comes from the score waves.
 // With one slice per query the workgroup normalises and writes the latent
 // average obar (bf16); with several, each writes its partial state and
 // mla_merge_kernel combines them.
@@ -99,12 +100,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
   const int sp = item - t * A.n_sp;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int w = wave & 3;                       // head group (score waves) / latent quarter (output waves)
-  const int l16 = lane & 15, g = lane >> 4;
+  const int w = wave & 3;                       // dim quarter of QK (score waves) / latent quarter (output waves)
+  const int l32 = lane & 31, hl = lane >> 5;    // MFMA column / row within the 32x32 tile, and lane half
 
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* ring = smem;
-  f32x4* slds = reinterpret_cast<f32x4*>(smem + kRingBytes);               // [4 waves][2 mt][4 h][64]
+  f32x4* slds = reinterpret_cast<f32x4*>(smem + kRingBytes);               // [4 waves][2 nt][4 ig][64]
   uint8_t* sm2 = smem + kRingBytes + kSBytes;
   u32x4* plds = reinterpret_cast<u32x4*>(sm2);                             // [2][4][64]
   float* alds = reinterpret_cast<float*>(sm2 + kPBytes);                   // [2][4][16]
@@ -138,32 +139,41 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
 
   // Both roles pass the same sequence of workgroup barriers: B0 (positions
   // staged), B1 (tile 0 staged), then per step BAR_s and BAR_p, then BAR_end.
+  //
+  // Products use v_mfma_f32_32x32x16_bf16 (lane l: A row / B column l % 32,
+  // contraction slots 8 (l / 32) .. +8; result element i of lane l is row
+  // 8 (i / 4) + 4 (l / 32) + i % 4, column l % 32).
   if (wave < 4) {
     // =========================== score waves: QK^T and the online softmax of tile `step`
-    // QK is split over the 576 dims: wave w takes contraction steps
-    // st0 .. st0 + nst - 1 (steps of 32 dims: 5, 5, 4, 4) for all 64 heads, so
-    // each row chunk read from LDS feeds 4 MFMAs.  Q^T operand: head 16h + l16,
-    // dims 32 st + 8g .. +8.
-    const int nst = w < 2 ? 5 : 4;
-    const int st0 = w < 2 ? 5 * w : 10 + 4 * (w - 2);
-    bf16x8 qb[4][5];
+    // S^T[32 rows x 64 heads] is split over the 576 dims: wave w takes dims
+    // 144w .. 144w + 143 (9 steps of 16) for both 32-head column tiles, so each
+    // row chunk read from LDS feeds 2 MFMAs.  Q operand: head 32nt + l32,
+    // dims 144w + 16s + 8hl .. +8.
+    bf16x8 qb[2][9];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const uint16_t* qp = A.q_abs + ((int64_t)t * kHeads + 16 * h + l16) * kRow + 8 * g;
+    for (int nt = 0; nt < 2; ++nt) {
+      const uint16_t* qp = A.q_abs + ((int64_t)t * kHeads + 32 * nt + l32) * kRow + 144 * w + 8 * hl;
 #pragma unroll
-      for (int i = 0; i < 5; ++i) qb[h][i] = as_bf16x8(ld16(qp + 32 * min(st0 + i, 17)));
+      for (int s = 0; s < 9; ++s) qb[nt][s] = as_bf16x8(ld16(qp + 16 * s));
     }
     store_positions();
     // The staged positions must be visible; the query loads stay in flight.
     lds_barrier();                                                     // B0
-    // QK reads chunk 4st + g of row mt*16 + l16; with x = l16 & 7 the swizzled
-    // position is 8 (st >> 1) + 4 ((st & 1) ^ (x >> 2)) + (g ^ (x & 3)), i.e.
-    // one of two bases plus an immediate 128 (st >> 1).
-    const int xsw = l16 & 7;
-    const int qk_base = l16 * kRowBytes + 16 * (g ^ (xsw & 3));
-    const int qk_even = qk_base + 64 * (xsw >> 2);
-    const int qk_odd = qk_base + 64 * (1 - (xsw >> 2));
-    float m_run = -INFINITY, l_run = 0.f;     // softmax state of head 16w + l16 (lane-partial sum)
+    // R operand: row l32, 16-byte chunk 18w + 2s + hl, at its swizzled slot.
+    const int rbase = l32 * kRowBytes;
+    const int rsw = l32 & 7;
+    const int c0 = 18 * w + hl;
+    // Softmax ownership: this wave finishes heads 16w .. 16w + 15; lane
+    // (hd, p) = (lane & 15, lane >> 4) takes head 16w + hd and rows
+    // 16 (p >> 1) + 8a + 4 (p & 1) + j (a = 0, 1; j = 0..3), i.e. elements
+    // 8 (p >> 1) + 4a + j of result column 16 (w & 1) + hd + 32 (p & 1) of
+    // column tile w >> 1.
+    const int hd = lane & 15, pq4 = lane >> 4;
+    const int own_nt = w >> 1;
+    const int src_lane = 16 * (w & 1) + hd + 32 * (pq4 & 1);
+    const int ig0 = 2 * (pq4 >> 1);
+    const int row0 = 16 * (pq4 >> 1) + 4 * (pq4 & 1);
+    float m_run = -INFINITY, l_run = 0.f;     // softmax state of head 16w + hd (lane-partial sum)
     lds_barrier();                                                     // B1: tile 0 staged
 #pragma unroll 1
     for (int tile = 0; tile <= n_tiles; ++tile) {
@@ -173,57 +183,44 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
       const int jt = tile * kTile;
       if (active) {
         // ---- partial S^T = R . Q^T over this wave's dims, all 64 heads, 32 rows.
-        f32x4 spt[2][4];
+        u32x4 ra[9];            // all of this wave's row chunks of the tile, read up front
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int s = 0; s < 9; ++s)
+          ra[s] = *reinterpret_cast<const u32x4*>(cur + rbase + 16 * ((c0 + 2 * s) ^ rsw));
+        f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-          for (int h = 0; h < 4; ++h) spt[mt][h] = f32x4{0.f, 0.f, 0.f, 0.f};
-        u32x4 a[5][2];          // all of this wave's row chunks of the tile, read up front
+        for (int s = 0; s < 9; ++s)
 #pragma unroll
-        for (int i = 0; i < 5; ++i) {
-          const int st = min(st0 + i, 17);
+          for (int nt = 0; nt < 2; ++nt)
+            acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ra[s]), qb[nt][s], acc[nt], 0, 0, 0);
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-            a[i][mt] = *reinterpret_cast<const u32x4*>(cur + mt * 16 * kRowBytes + ((st & 1) ? qk_odd : qk_even) +
-                                                       128 * (st >> 1));
-        }
+        for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int i = 0; i < 5; ++i) {
-          if (i < nst) {
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-              for (int h = 0; h < 4; ++h)
-                spt[mt][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[i][mt]), qb[h][i], spt[mt][h], 0, 0, 0);
-          }
-        }
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int h = 0; h < 4; ++h) slds[((w * 2 + mt) * 4 + h) * 64 + lane] = spt[mt][h];
+          for (int ig = 0; ig < 4; ++ig)
+            slds[((w * 2 + nt) * 4 + ig) * 64 + lane] =
+                f32x4{acc[nt][4 * ig], acc[nt][4 * ig + 1], acc[nt][4 * ig + 2], acc[nt][4 * ig + 3]};
       }
       lds_barrier();                                                   // BAR_s
       if (active) {
-        // full S^T for heads 16w .. 16w+15: sum of the 4 waves' partials
+        // full scores of this lane's 8 rows: sum of the 4 waves' partials
         f32x4 s[2];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          s[mt] = slds[((0 * 2 + mt) * 4 + w) * 64 + lane];
+        for (int a = 0; a < 2; ++a) {
+          s[a] = slds[((0 * 2 + own_nt) * 4 + ig0 + a) * 64 + src_lane];
 #pragma unroll
-          for (int w2 = 1; w2 < 4; ++w2) s[mt] += slds[((w2 * 2 + mt) * 4 + w) * 64 + lane];
+          for (int w2 = 1; w2 < 4; ++w2) s[a] += slds[((w2 * 2 + own_nt) * 4 + ig0 + a) * 64 + src_lane];
         }
-        // ---- online softmax of head 16w + l16 over rows mt*16 + 4g + j.
+        // ---- online softmax of head 16w + hd over rows row0 + 8a + j.
         float x[2][4];
         float tmax = -INFINITY;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          // rows jt + mt*16 + 4g .. +3: one 16-byte read of the staged positions
-          const int jb = jt + mt * 16 + 4 * g;
-          const u32x4 pq = *reinterpret_cast<const u32x4*>(spos + jb);
+        for (int a = 0; a < 2; ++a) {
+          // rows jt + row0 + 8a .. +3: one 16-byte read of the staged positions
+          const u32x4 pq = *reinterpret_cast<const u32x4*>(spos + jt + row0 + 8 * a);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            x[mt][j] = (int)pq[j] >= 0 ? s[mt][j] * A.scale_log2 : -INFINITY;
-            tmax = fmaxf(tmax, x[mt][j]);
+            x[a][j] = (int)pq[j] >= 0 ? s[a][j] * A.scale_log2 : -INFINITY;
+            tmax = fmaxf(tmax, x[a][j]);
           }
         }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
@@ -234,7 +231,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
           const float alpha = bump ? (m_run == -INFINITY ? 0.f : fast_exp2(m_run - tmax)) : 1.f;
           if (bump) m_run = tmax;
           l_run *= alpha;
-          alds[(pb_i * 4 + w) * 16 + l16] = alpha;        // the 4 lanes of a head store the same value
+          alds[(pb_i * 4 + w) * 16 + hd] = alpha;        // the 4 lanes of a head store the same value
         }
         flds[pb_i * 4 + w] = any_bump ? 1 : 0;
         // masked rows have x = -inf and weight exp2(-inf) = 0; m_run is -inf
@@ -242,51 +239,47 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
         const float m_use = m_run == -INFINITY ? 0.f : m_run;
         float p[2][4];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int a = 0; a < 2; ++a)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            p[mt][j] = fast_exp2(x[mt][j] - m_use);
-            l_run += p[mt][j];
+            p[a][j] = fast_exp2(x[a][j] - m_use);
+            l_run += p[a][j];
           }
+        // The weights of rows row0 + 8a + j are the PV contraction slots
+        // 4a + j of the lanes that read this entry.
         const u32x4 pown = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
                             pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
         plds[(pb_i * 4 + w) * 64 + lane] = pown;
       }
       lds_barrier();                                                   // BAR_p
     }
-    // Head 16w + l16: sum over the 4 lanes that share it.
+    // Head 16w + hd: sum over the 4 lanes that share it.
     l_run += __shfl_xor(l_run, 16, 64);
     l_run += __shfl_xor(l_run, 32, 64);
-    if (g == 0) {
-      mlds[(16 * w + l16) * 2 + 0] = m_run;
-      mlds[(16 * w + l16) * 2 + 1] = l_run;
+    if (pq4 == 0) {
+      mlds[(16 * w + hd) * 2 + 0] = m_run;
+      mlds[(16 * w + hd) * 2 + 1] = l_run;
       if (A.n_sp == 1) {
         if (A.lse)
-          A.lse[(int64_t)t * kHeads + 16 * w + l16] =
+          A.lse[(int64_t)t * kHeads + 16 * w + hd] =
               l_run > 0.f ? (m_run + __log2f(l_run)) * 0.69314718055994531f : -INFINITY;
       } else {
         const int64_t pbase = ((int64_t)t * A.n_sp + sp) * kHeads;
-        A.part_ml[(pbase + 16 * w + l16) * 2 + 0] = m_run;
-        A.part_ml[(pbase + 16 * w + l16) * 2 + 1] = l_run;
+        A.part_ml[(pbase + 16 * w + hd) * 2 + 0] = m_run;
+        A.part_ml[(pbase + 16 * w + hd) * 2 + 1] = l_run;
       }
     }
     lds_barrier();                                                     // BAR_end
     return;
   }
   // =========================== output waves: O^T += V^T . P^T of tile `step - 1`
-  // Wave w owns latent dims 128w .. 128w+127 for all 64 heads.  The 32 rows
-  // are the contraction; contraction slot 8g + s' of the products holds row
-  // kap(g, s') of the tile, in both operands.
-  auto kap = [&](int s2) { return s2 < 4 ? 4 * g + s2 : 16 + 4 * g + (s2 - 4); };
-  int pv_off[8];
-#pragma unroll
-  for (int s2 = 0; s2 < 8; ++s2) pv_off[s2] = lds_chunk_offset(kap(s2), l16 + 16 * w);
-  f32x4 o[8][4];                 // O^T tiles: latent dims (8 x 16 rows) x head groups (4 x 16 cols)
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-#pragma unroll
-    for (int h = 0; h < 4; ++h) o[e][h] = f32x4{0.f, 0.f, 0.f, 0.f};
-  store_positions();
+  // Wave w owns latent dims 128w .. 128w+127 for all 64 heads: result tile
+  // (mt, nt) holds dims 128w + 4m + mt (m = result row) of heads 32nt + n.
+  // The 32 rows of a tile are two contraction steps ks of 16; slot 8hl + e of
+  // step ks is row 16ks + 8 (e >> 2) + 4hl + (e & 3) in both operands (the
+  // order in which the score waves pack their weights).  The V^T operand of
+  // lane (m = l32, hl) takes 8 bytes (dims 4m .. 4m+3) of each of its 8 rows
+  // and byte permutes form the four dim tiles mt.
   // Direct-to-LDS gather of the tiles, issued by these waves: load u of wave w
   // fills bytes (9w + u) KB of the tile buffer, 16 bytes per lane; the lane
   // fetches the row chunk whose swizzled position is that slot.
@@ -317,11 +310,26 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
                                        (__attribute__((address_space(3))) void*)(b + 1024 * u), 16, 0, 0);
     }
   };
+  // V^T operand: 8-byte read of row rho = 16ks + 8(e >> 2) + 4hl + (e & 3),
+  // dims 128w + 4 l32 .. +3 (chunk 16w + l32 / 2, half l32 & 1); rho & 7 is
+  // 4hl + (e & 3) for every ks and e >> 2.
+  int voff[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    voff[e] = (4 * hl + e) * kRowBytes + 16 * ((16 * w + (l32 >> 1)) ^ (4 * hl + e)) + 8 * (l32 & 1);
+  f32x16 o[4][2];                // O^T tiles: dim tiles mt x head tiles nt
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) o[mt][nt] = f32x16{};
+  store_positions();
   lds_barrier();                                                       // B0
   issue(0);
   issue(1);
   SA_WAIT_VMCNT(kLoadsPerWave);          // tile 0 is in (tile 1 may still be in flight)
   lds_barrier();                                                       // B1
+  // weights / rescale of head 32nt + l32 come from score wave 2nt + (l32 >> 4), lane entry (l32 & 15)
+  const int pw_hi = l32 >> 4;
 #pragma unroll 1
   for (int step = 0; step <= n_tiles; ++step) {
     // Operands of tile step - 1 are read before BAR_s (which frees its buffer
@@ -330,49 +338,59 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
     const bool pv_step = step > 0;
     const int tile = step - 1;
     const int pb_i = tile & 1;
-    u32x4 v[8], pt[4];
-    int fl[4];
-    float al[4];
+    u32x2 v[2][8];
+    u32x4 pt[2][2];
+    int fl[2];
+    float al[2];
     if (pv_step) {
       const uint8_t* cur = ring + (tile % kRing) * kTileBytes;
 #pragma unroll
-      for (int s2 = 0; s2 < 8; ++s2) v[s2] = *reinterpret_cast<const u32x4*>(cur + pv_off[s2]);
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        pt[h] = plds[(pb_i * 4 + h) * 64 + lane];
-        fl[h] = flds[pb_i * 4 + h];
-        al[h] = alds[(pb_i * 4 + h) * 16 + l16];        // meaningful only where fl[h] is set
+        for (int e = 0; e < 8; ++e)
+          v[ks][e] = *reinterpret_cast<const u32x2*>(cur + (16 * ks + 8 * (e >> 2)) * kRowBytes + voff[e & 3]);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          pt[nt][ks] = plds[(pb_i * 4 + 2 * nt + pw_hi) * 64 + (l32 & 15) + 16 * (2 * ks + hl)];
+        // this lane's own flag (a lane-dependent pick among registers would go through scratch memory)
+        fl[nt] = flds[pb_i * 4 + 2 * nt + pw_hi];
+        al[nt] = alds[(pb_i * 4 + 2 * nt + pw_hi) * 16 + (l32 & 15)];   // meaningful only where its flag is set
       }
     }
     lds_barrier();                                                     // BAR_s
     if (step < n_tiles) issue(step + 2);
     if (pv_step) {
-      if (fl[0] | fl[1] | fl[2] | fl[3]) {
+      if (__any(fl[0] | fl[1])) {
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const float sc = fl[h] ? al[h] : 1.f;
+        for (int nt = 0; nt < 2; ++nt) {
+          const float sc = fl[nt] ? al[nt] : 1.f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[e][h] *= sc;
+          for (int mt = 0; mt < 4; ++mt) o[mt][nt] *= sc;
         }
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = e >> 1;
-        u32x4 av;
-        if (e & 1) {
-          av[0] = perm_hi(v[0][d], v[1][d]);
-          av[1] = perm_hi(v[2][d], v[3][d]);
-          av[2] = perm_hi(v[4][d], v[5][d]);
-          av[3] = perm_hi(v[6][d], v[7][d]);
-        } else {
-          av[0] = perm_lo(v[0][d], v[1][d]);
-          av[1] = perm_lo(v[2][d], v[3][d]);
-          av[2] = perm_lo(v[4][d], v[5][d]);
-          av[3] = perm_lo(v[6][d], v[7][d]);
-        }
+      for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-        for (int h = 0; h < 4; ++h)
-          o[e][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(pt[h]), o[e][h], 0, 0, 0);
+        for (int mt = 0; mt < 4; ++mt) {
+          const int d = mt >> 1;
+          u32x4 av;
+          if (mt & 1) {
+            av[0] = perm_hi(v[ks][0][d], v[ks][1][d]);
+            av[1] = perm_hi(v[ks][2][d], v[ks][3][d]);
+            av[2] = perm_hi(v[ks][4][d], v[ks][5][d]);
+            av[3] = perm_hi(v[ks][6][d], v[ks][7][d]);
+          } else {
+            av[0] = perm_lo(v[ks][0][d], v[ks][1][d]);
+            av[1] = perm_lo(v[ks][2][d], v[ks][3][d]);
+            av[2] = perm_lo(v[ks][4][d], v[ks][5][d]);
+            av[3] = perm_lo(v[ks][6][d], v[ks][7][d]);
+          }
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+            o[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(pt[nt][ks]), o[mt][nt], 0, 0, 0);
+        }
       }
     }
     // tile step + 1 must be in before the next step's QK (step + 2 stays in flight)
@@ -381,51 +399,61 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
   }
   __builtin_amdgcn_s_waitcnt(0);         // the trailing (clamped) tile loads land before the workgroup ends
   lds_barrier();                                                       // BAR_end: (m, l) of every head
-  // O^T tile (e, h): lane holds dims 8(4g + jj + 16w) + e (jj = 0..3) of head 16h + l16.
+  // Result element 4a + b of tile (mt, nt) is dim 128w + 32a + 16hl + 4b + mt
+  // of head 32nt + l32: for each (nt, a) a lane holds 16 consecutive dims.
   if (A.n_sp == 1) {
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const float L = mlds[(16 * h + l16) * 2 + 1];
+    for (int nt = 0; nt < 2; ++nt) {
+      const float L = mlds[(32 * nt + l32) * 2 + 1];
       const float inv = L > 0.f ? 1.f / L : 0.f;
-      uint16_t* ob = A.obar + ((int64_t)t * kHeads + 16 * h + l16) * kLatent;
+      uint16_t* ob = A.obar + ((int64_t)t * kHeads + 32 * nt + l32) * kLatent + 128 * w + 16 * hl;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int dim0 = 8 * (4 * g + jj + 16 * w);
-        const u32x4 pk = {pack_bf16x2(o[0][h][jj] * inv, o[1][h][jj] * inv),
-                          pack_bf16x2(o[2][h][jj] * inv, o[3][h][jj] * inv),
-                          pack_bf16x2(o[4][h][jj] * inv, o[5][h][jj] * inv),
-                          pack_bf16x2(o[6][h][jj] * inv, o[7][h][jj] * inv)};
-        *reinterpret_cast<u32x4*>(ob + dim0) = pk;
+      for (int a = 0; a < 4; ++a) {
+#pragma unroll
+        for (int bh = 0; bh < 2; ++bh) {          // dims 8bh .. 8bh + 7 of the 16: b = 2bh, 2bh + 1
+          const int i0 = 4 * a + 2 * bh;
+          const u32x4 pk = {pack_bf16x2(o[0][nt][i0] * inv, o[1][nt][i0] * inv),
+                            pack_bf16x2(o[2][nt][i0] * inv, o[3][nt][i0] * inv),
+                            pack_bf16x2(o[0][nt][i0 + 1] * inv, o[1][nt][i0 + 1] * inv),
+                            pack_bf16x2(o[2][nt][i0 + 1] * inv, o[3][nt][i0 + 1] * inv)};
+          *reinterpret_cast<u32x4*>(ob + 32 * a + 8 * bh) = pk;
+        }
       }
     }
     return;
   }
-  // Partial accumulators in register-tile order: [t][sp][w][e][h][lane] x 4
-  // floats, so every store instruction writes 1 KB contiguously.
+  // Partial accumulators in register-tile order: [t][sp][w][nt][mt][a][lane]
+  // x 4 values (b = 0..3), so every store instruction writes 1 KB contiguously.
   f32x4* po = reinterpret_cast<f32x4*>(A.part_o) + (((int64_t)t * A.n_sp + sp) * 4 + w) * 32 * 64;
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
+  for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-    for (int h = 0; h < 4; ++h) po[(e * 4 + h) * 64 + lane] = o[e][h];
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        po[((nt * 4 + mt) * 4 + a) * 64 + lane] =
+            f32x4{o[mt][nt][4 * a], o[mt][nt][4 * a + 1], o[mt][nt][4 * a + 2], o[mt][nt][4 * a + 3]};
 }
 
 // Merge of the slices' partial softmax states: obar = sum_s a_s O_s / sum_s a_s l_s
 // with a_s = 2^(m_s - max m).  Partials are in the attention kernel's register
-// tile order.  One workgroup per (query, latent quarter w, pair ep of dim
-// tiles); thread = (head tile h, lane) owns tiles e = 2ep, 2ep + 1 and reads
-// them for 8 slices at a time (one rescale per batch).
+// tile order.  One workgroup per (query, latent quarter w, head tile nt, dim
+// tile pair mp); thread = (a, lane) owns dim tiles mt = 2mp, 2mp + 1 of head
+// 32nt + (lane & 31), i.e. dims 128w + 32a + 16 (lane >> 5) + 4b + mt, and
+// reads them for 8 slices at a time (one rescale per batch).
 constexpr int kMergeBatch = 8;         // slices read per round trip
 
 __global__ __launch_bounds__(256) void mla_merge_kernel(AttnArgs A) {
   const int t = blockIdx.x >> 4;
   const int w = (blockIdx.x >> 2) & 3;
-  const int ep = blockIdx.x & 3;
-  const int h = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int l16 = lane & 15, g = lane >> 4;
-  const int head = 16 * h + l16;
+  const int nt = (blockIdx.x >> 1) & 1;
+  const int mp = blockIdx.x & 1;
+  const int a = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int head = 32 * nt + l32;
   const int n_sp = A.n_sp;
   const f32x4* src = reinterpret_cast<const f32x4*>(A.part_o) + ((int64_t)t * n_sp * 4 + w) * 2048 +
-                     (2 * ep * 4 + h) * 64 + lane;          // slice s adds s * 4 * 2048; tile e + 1 adds 4 * 64
+                     ((nt * 4 + 2 * mp) * 4 + a) * 64 + lane;     // slice s adds s * 4 * 2048; tile mt + 1 adds 4 * 64
   const float2* mlp = reinterpret_cast<const float2*>(A.part_ml) + (int64_t)t * n_sp * kHeads + head;
   float M = -INFINITY, L = 0.f;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
@@ -452,19 +480,19 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(AttnArgs A) {
     }
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
-      const float a = (s0 + u < n_sp && ml[u].x != -INFINITY) ? fast_exp2(ml[u].x - M) : 0.f;
-      L = fmaf(a, ml[u].y, L);
-      acc0 += a * v0[u];
-      acc1 += a * v1[u];
+      const float wt = (s0 + u < n_sp && ml[u].x != -INFINITY) ? fast_exp2(ml[u].x - M) : 0.f;
+      L = fmaf(wt, ml[u].y, L);
+      acc0 += wt * v0[u];
+      acc1 += wt * v1[u];
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  // element jj of tile e is dim 8 (4g + jj + 16w) + e
-  uint16_t* ob = A.obar + ((int64_t)t * kHeads + head) * kLatent + 2 * ep;
+  // acc0[b] is dim 128w + 32a + 16hl + 4b + 2mp, acc1[b] the next dim
+  uint16_t* ob = A.obar + ((int64_t)t * kHeads + head) * kLatent + 128 * w + 32 * a + 16 * hl + 2 * mp;
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj)
-    *reinterpret_cast<uint32_t*>(ob + 8 * (4 * g + jj + 16 * w)) = pack_bf16x2(acc0[jj] * inv, acc1[jj] * inv);
-  if (A.lse && w == 0 && ep == 0 && g == 0)
+  for (int b = 0; b < 4; ++b)
+    *reinterpret_cast<uint32_t*>(ob + 4 * b) = pack_bf16x2(acc0[b] * inv, acc1[b] * inv);
+  if (A.lse && w == 0 && mp == 0 && a == 0 && hl == 0)
     A.lse[(int64_t)t * kHeads + head] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
