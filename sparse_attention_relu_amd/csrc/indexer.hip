@@ -41,9 +41,10 @@ __device__ __forceinline__ float relu_weighted_sum(const f32x16& acc, const floa
   return part + __shfl_xor(part, 32, 64);
 }
 
-// The same sum with the weights of one query read from LDS: accumulator
-// element 4a + b is head 8a + 4 (lane / 32) + b, four consecutive heads per a.
-__device__ __forceinline__ float relu_weighted_sum_lds(const f32x16& acc, const float* wq, int lane) {
+// This lane's 16 heads of the sum, with the weights of one query read from
+// LDS: accumulator element 4a + b is head 8a + 4 (lane / 32) + b, four
+// consecutive heads per a.  The other 16 heads are in the lane 32 away.
+__device__ __forceinline__ float relu_weighted_part_lds(const f32x16& acc, const float* wq, int lane) {
   const f32x4* w4 = reinterpret_cast<const f32x4*>(wq + 4 * (lane >> 5));
   float part = 0.f;
 #pragma unroll
@@ -52,7 +53,7 @@ __device__ __forceinline__ float relu_weighted_sum_lds(const f32x16& acc, const 
 #pragma unroll
     for (int b = 0; b < 4; ++b) part = fmaf(wv[b], relu(acc[4 * a + b]), part);
   }
-  return part + __shfl_xor(part, 32, 64);
+  return part;
 }
 
 // ------------------------------------------------------------ decode kernel
@@ -106,21 +107,8 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(DecArgs A) {
   }
   __shared__ __align__(16) uint8_t lds[kDecWaves][32 * kKeyPitch];
   __shared__ __align__(16) uint32_t hist[HIST ? kBins1 : 1];
+  __shared__ float sh_w[kIdxHeads];
   const bool do_hist = HIST && pos + 1 > A.k;
-  if (do_hist) {
-    u32x4* h4 = reinterpret_cast<u32x4*>(hist);
-#pragma unroll
-    for (int i = 0; i < kBins1 / 4 / 256; ++i) h4[threadIdx.x + 256 * i] = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();
-  }
-
-  const uint16_t* qt = A.q_idx + (int64_t)t * kIdxHeads * kIdxDim;
-  bf16x8 a[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) a[s] = as_bf16x8(ld16(qt + (lane & 31) * kIdxDim + 16 * s + 8 * (lane >> 5)));
-  float wr[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) wr[i] = A.w[(int64_t)t * kIdxHeads + acc_row(i, lane)];
 
   // step it of this wave covers keys c0 + (4 it + wave) * 32 .. +31; keys
   // and score columns are handled relative to c0 in 32 bits
@@ -141,6 +129,48 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(DecArgs A) {
       g[j] = ld16(kb + key * kIdxDim + (lane & 15) * 8);
     }
   };
+
+  // The query (32 head rows, laid out like a block of 32 keys) is read from
+  // global memory once per workgroup into wave 0's staging buffer, and the
+  // head weights into sh_w; every wave takes its operands from there.  The
+  // first two key blocks of each wave are requested before that (loads
+  // complete in order, so staging the query waits only for the query).
+  const uint16_t* qt = A.q_idx + (int64_t)t * kIdxHeads * kIdxDim;
+  u32x4 qv[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int f = (int)threadIdx.x + 256 * u;           // 16-byte piece: head f / 16, chunk f % 16
+    qv[u] = ld16(qt + (f >> 4) * kIdxDim + (f & 15) * 8);
+  }
+  const float wv = A.w[(int64_t)t * kIdxHeads + (threadIdx.x & (kIdxHeads - 1))];
+  // Prefetches are unconditional (clamped to the last valid step) so the
+  // loads stay in order and each step waits only for its own data.
+  u32x4 g0[8], g1[8];
+  load(g0, 0);
+  load(g1, 1);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int f = (int)threadIdx.x + 256 * u;
+    *reinterpret_cast<u32x4*>(lds[0] + (f >> 4) * kKeyPitch + (f & 15) * 16) = qv[u];
+  }
+  sh_w[threadIdx.x & (kIdxHeads - 1)] = wv;     // every thread (equal values): no branch, no late load
+  if (do_hist) {
+    u32x4* h4 = reinterpret_cast<u32x4*>(hist);
+#pragma unroll
+    for (int i = 0; i < kBins1 / 4 / 256; ++i) h4[threadIdx.x + 256 * i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  lds_barrier();
+  // A operand: head lane % 32, dims 16 s + 8 (lane / 32) .. +8 (chunk 2 s + lane / 32)
+  bf16x8 a[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    a[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(lds[0] + (lane & 31) * kKeyPitch + (2 * s + (lane >> 5)) * 16));
+  float wr[16];         // weights of this lane's accumulator rows
+#pragma unroll
+  for (int i = 0; i < 16; ++i) wr[i] = sh_w[acc_row(i, lane)];
+  // wave 0 stages keys in lds[0] from here on
+  lds_barrier();
+
   auto step = [&](const u32x4 (&g)[8], int it) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
@@ -162,16 +192,13 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(DecArgs A) {
     }
   };
 
-  // Prefetches are unconditional (clamped to the last valid step) so the
-  // loads stay in order and each step waits only for its own data.
-  u32x4 g0[8], g1[8];
-  load(g0, 0);
+  static_assert(kDecSteps % 2 == 0, "steps alternate between two register sets");
 #pragma unroll
   for (int it = 0; it < n_it; it += 2) {
-    load(g1, it + 1);
     step(g0, it);
     if (it + 2 < n_it) load(g0, it + 2);
     step(g1, it + 1);
+    if (it + 3 < n_it) load(g1, it + 3);
   }
 
   if (HIST && do_hist) {
@@ -305,14 +332,17 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
       }
     };
     // ReLU sums and stores of column n of a tile (skipped for tile < 0).
+    // Lanes 0..31 finish the first query's scores of the column's 32 keys,
+    // lanes 32..63 the second query's: one exchange, one store.
+    const bool hi = lane >= 32;
+    const bool act_l = hi ? act1 : act0;
+    const int rpos_l = hi ? rpos1 : rpos0;
+    float* srow_l = hi ? srow1 : srow0;
     auto finish = [&](const f32x16 (&acc)[2], int tile, int n) {
-      const float sc0 = relu_weighted_sum_lds(acc[0], sh_w[2 * wave], lane);
-      const float sc1 = relu_weighted_sum_lds(acc[1], sh_w[2 * wave + 1], lane);
+      const float sc = sum_halves(relu_weighted_part_lds(acc[0], sh_w[2 * wave], lane),
+                                  relu_weighted_part_lds(acc[1], sh_w[2 * wave + 1], lane));
       const int rkey = tile * kPfKT + n * 32 + (lane & 31);
-      if (lane < 32 && tile >= 0 && rkey < span) {
-        if (act0) srow0[rkey] = rkey <= rpos0 ? sc0 : -INFINITY;
-        if (act1) srow1[rkey] = rkey <= rpos1 ? sc1 : -INFINITY;
-      }
+      if (act_l && tile >= 0 && rkey < span) srow_l[rkey] = rkey <= rpos_l ? sc : -INFINITY;
     };
     // Software pipeline over the key columns of a tile: each column is
     // finished during the products of the next one (the last column of a tile

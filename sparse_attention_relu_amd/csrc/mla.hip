@@ -53,16 +53,6 @@ __device__ __forceinline__ uint32_t perm_hi(uint32_t x, uint32_t y) { return __b
 // chunk of 8 consecutive rows hit 8 different LDS bank groups.
 __device__ __forceinline__ int lds_chunk_offset(int r, int c) { return r * kRowBytes + 16 * (c ^ (r & 7)); }
 
-// Workgroup barrier that completes this wave's LDS instructions first but
-// leaves the direct-to-LDS tile loads in flight (__syncthreads, and even an
-// LDS-scoped fence, would wait for them: they are tracked as memory writes).
-// Tile loads are waited for explicitly with SA_WAIT_VMCNT.  The "memory"
-// clobber keeps the compiler from moving memory accesses across the barrier.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// s_waitcnt vmcnt(n) leaving the other counters unconstrained (gfx9 encoding).
-#define SA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8))
-
 struct AttnArgs {
   const uint16_t* q_abs;
   const uint16_t* kv;
@@ -444,10 +434,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
 constexpr int kMergeBatch = 8;         // slices read per round trip
 
 __global__ __launch_bounds__(256) void mla_merge_kernel(AttnArgs A) {
-  const int t = blockIdx.x >> 4;
-  const int w = (blockIdx.x >> 2) & 3;
-  const int nt = (blockIdx.x >> 1) & 1;
-  const int mp = blockIdx.x & 1;
+  // The same XCD-contiguous dealing as the attention kernel: a query's merge
+  // workgroups run on the XCD whose L2 took that query's partial states.
+  const int n_wg = (int)gridDim.x;
+  const int item = (n_wg & 7) ? (int)blockIdx.x : (int)(blockIdx.x & 7) * (n_wg >> 3) + (int)(blockIdx.x >> 3);
+  const int t = item >> 4;
+  const int w = (item >> 2) & 3;
+  const int nt = (item >> 1) & 1;
+  const int mp = item & 1;
   const int a = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int l32 = lane & 31, hl = lane >> 5;
   const int head = 32 * nt + l32;

@@ -60,6 +60,25 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Workgroup barrier that completes this wave's LDS instructions first but
+// leaves the direct-to-LDS tile loads in flight (__syncthreads, and even an
+// LDS-scoped fence, would wait for them: they are tracked as memory writes).
+// Tile loads are waited for explicitly with SA_WAIT_VMCNT.  The "memory"
+// clobber keeps the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// s_waitcnt vmcnt(n) leaving the other counters unconstrained (gfx9 encoding).
+#define SA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8))
+
+// Half-wave sums with v_permlane32_swap (a VALU exchange of the wave's two
+// 32-lane halves; no LDS round trip): returns p[l] + p[l + 32] in lanes
+// l < 32 and q[l - 32] + q[l] in lanes l >= 32.  With q = p every lane gets
+// the sum of its lane pair.
+__device__ __forceinline__ float sum_halves(float p, float q) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(q), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
   return __shfl_xor(v, mask, 64);
