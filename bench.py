@@ -52,7 +52,7 @@ def parse():
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_decode_c2_traffic.md")
 INDEXER_SOURCES = [os.path.join(ROOT, "sparse_attention_relu_amd", "csrc", f)
-                   for f in ("indexer.hip", "topk_common.h", "sa_common.h")]
+                   for f in ("indexer.hip", "sa_common.h")]
 
 
 def indexer_source_hash():

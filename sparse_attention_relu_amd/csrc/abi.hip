@@ -6,7 +6,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
-#include "topk_common.h"
+#include "sa_common.h"
 
 namespace sa_host {
 
@@ -28,20 +28,15 @@ int32_t check_launch(const char* what) {
   return SA_OK;
 }
 
+int indexer_algo(int32_t n_q, int algo);
 int32_t launch_indexer(const void* q_idx, const float* w, const void* k_idx, const int64_t* seq_start,
                        const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, float* scores, int64_t ld, int algo,
-                       hipStream_t stream);
-int32_t launch_indexer_ex(const void* q_idx, const float* w, const void* k_idx, const int64_t* seq_start,
-                          const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, float* scores, int64_t ld, int algo,
-                          const sa::TopkWs* hist_ws, int k, hipStream_t stream);
-sa::TopkWs topk_carve(void* ws, int32_t n_q, int64_t ld);
-int32_t topk_zero(const sa::TopkWs& w, int32_t* extra, int64_t n_extra, hipStream_t stream);
-int32_t topk_after_hist(const float* scores, int64_t ld, const int32_t* q_pos, int32_t n_q, int32_t k, int32_t* idx,
-                        const sa::TopkWs& w, hipStream_t stream);
+                       hipStream_t stream, uint32_t* clear, int64_t n_clear);
+void topk_clear_range(void* ws, int32_t n_q, int64_t ld, uint32_t** p, int64_t* n);
 
 size_t topk_workspace_size(int32_t n_q, int64_t ld, int32_t k);
 int32_t launch_topk(const float* scores, int64_t ld, const int32_t* q_pos, int32_t n_q, int32_t k, int32_t* idx,
-                    void* ws, int algo, hipStream_t stream);
+                    void* ws, int algo, hipStream_t stream, bool cleared);
 size_t mla_workspace_size(int32_t n_q, int32_t k);
 int32_t launch_mla(const void* q_abs, const void* kv, const int64_t* seq_start, const int32_t* q_seq,
                    const int32_t* idx, int32_t n_q, int32_t k, const void* w_uv, float scale, void* out, float* lse,
@@ -136,7 +131,8 @@ int32_t sa_indexer_score_algo(const void* q_idx, const float* w, const void* k_i
   if (rc) return rc;
   SA_REQUIRE(algo >= 0 && algo <= 2, SA_ERR_INVALID_ARG, "indexer: unknown algo %d", algo);
   if (n_q == 0) return SA_OK;
-  return launch_indexer(q_idx, w, k_idx, seq_start, q_seq, q_pos, n_q, scores, ld, algo, (hipStream_t)stream);
+  return launch_indexer(q_idx, w, k_idx, seq_start, q_seq, q_pos, n_q, scores, ld, algo, (hipStream_t)stream, nullptr,
+                        0);
 }
 
 int32_t sa_indexer_score(const void* q_idx, const float* w, const void* k_idx, const int64_t* seq_start,
@@ -159,7 +155,7 @@ int32_t sa_topk_select_algo(const float* scores, int64_t ld, const int32_t* q_po
   const size_t need = topk_workspace_size(n_q, ld, k);
   SA_REQUIRE(ws && ws_bytes >= need, SA_ERR_WORKSPACE, "topk: workspace of %zu bytes, %zu needed", ws_bytes, need);
   SA_REQUIRE(((uintptr_t)ws & 255u) == 0, SA_ERR_INVALID_ARG, "topk: workspace not 256-byte aligned");
-  return launch_topk(scores, ld, q_pos, n_q, k, idx, ws, algo, (hipStream_t)stream);
+  return launch_topk(scores, ld, q_pos, n_q, k, idx, ws, algo, (hipStream_t)stream, false);
 }
 
 int32_t sa_topk_select(const float* scores, int64_t ld, const int32_t* q_pos, int32_t n_q, int32_t k, int32_t* idx,
@@ -234,30 +230,28 @@ int32_t sa_layer_stack(const sa_layer_desc* layers, int32_t n_layers, const sa_b
   const int32_t* cur_idx = nullptr;
   bool rec_idx = false, rec_topk = false, rec_attn = false;
   int32_t rc;
-  // Decode batches score one query per workgroup column and build the top-k's
-  // first-digit histogram while scoring; larger batches use the query-blocked
-  // indexer and the separate histogram pass.
-  const bool fused = n_q < 64;
-  const sa::TopkWs tw = topk_carve(topk_ws, n_q, ld);
+  // Decode batches (n_q < 64) score one query per workgroup column, larger
+  // batches use the query-blocked indexer; the top-k then runs its own
+  // first-digit histogram pass over the scores.  The decode indexer also
+  // clears the top-k's histograms and counters on the side, which saves the
+  // top-k a launch of its own for that.
+  const int ialgo = indexer_algo(n_q, 0);
+  uint32_t* clear = nullptr;
+  int64_t n_clear = 0;
+  if (ialgo == 1) topk_clear_range(topk_ws, n_q, ld, &clear, &n_clear);
   for (int l = 0; l < n_layers; ++l) {
     const sa_layer_desc& L = layers[l];
     if (L.is_full) {
-      if (fused) {
-        // histogram and state words of the top-k
-        rc = topk_zero(tw, nullptr, 0, st);
-        if (rc) return rc;
-      }
       const bool ev = events && !rec_idx && events->indexer_begin && events->indexer_end;
       if (ev && (rc = record(events->indexer_begin, st))) return rc;
-      rc = launch_indexer_ex(L.q_idx, L.w, L.k_idx, batch->seq_start, batch->q_seq, batch->q_pos, n_q, scores, ld,
-                             fused ? 1 : 2, fused ? &tw : nullptr, k, st);
+      rc = launch_indexer(L.q_idx, L.w, L.k_idx, batch->seq_start, batch->q_seq, batch->q_pos, n_q, scores, ld, ialgo,
+                          st, clear, n_clear);
       if (rc) return rc;
       if (ev && (rc = record(events->indexer_end, st))) return rc;
       rec_idx |= ev;
       const bool evt = events && !rec_topk && events->topk_begin && events->topk_end;
       if (evt && (rc = record(events->topk_begin, st))) return rc;
-      rc = fused ? topk_after_hist(scores, ld, batch->q_pos, n_q, k, L.idx, tw, st)
-                 : launch_topk(scores, ld, batch->q_pos, n_q, k, L.idx, topk_ws, 0, st);
+      rc = launch_topk(scores, ld, batch->q_pos, n_q, k, L.idx, topk_ws, 0, st, ialgo == 1);
       if (rc) return rc;
       if (evt && (rc = record(events->topk_end, st))) return rc;
       rec_topk |= evt;

@@ -20,7 +20,7 @@
 //                           sequence).  HBM-bound: 256 B of keys per 8 KFLOP.
 //   indexer_prefill_kernel  8 queries of one sequence share each key tile staged
 //                           in LDS: the dense contraction of chunked prefill.
-#include "topk_common.h"
+#include "sa_common.h"
 
 namespace sa {
 
@@ -60,9 +60,7 @@ __device__ __forceinline__ float relu_weighted_part_lds(const f32x16& acc, const
 // A workgroup covers 512 consecutive keys of one query's sequence: at each of
 // its 4 steps the 4 waves take the next 128 keys (32 each, 8 KB), staged
 // through wave-private LDS into the MFMA, with the next step's loads in
-// flight.  With HIST the wave also counts each
-// score's top 12 key bits into a workgroup histogram, which is added to the
-// row's histogram in the top-k workspace (the first radix digit of the top-k).
+// flight.
 constexpr int kDecWaves = 4;
 constexpr int kDecSteps = 4;
 constexpr int kDecChunk = kDecWaves * 32 * kDecSteps;     // keys per workgroup
@@ -78,8 +76,8 @@ struct DecArgs {
   float* scores;
   int64_t ld;
   int n_chunks;
-  int k;               // with HIST: selection size (rows with q_pos < k need no histogram)
-  TopkWs ws;           // with HIST: histogram and state of the top-k workspace
+  uint32_t* clear;     // optional: words set to zero on the side (the next kernel's counters)
+  int64_t n_clear;
 };
 
 // Orders a wave's LDS writes before its reads of other lanes' data (and the
@@ -91,8 +89,9 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <bool HIST>
 __global__ __launch_bounds__(256) void indexer_decode_kernel(DecArgs A) {
+  // side job: clear the caller's words (a grid-stride loop over all workgroups)
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < A.n_clear; i += (int64_t)gridDim.x * 256) A.clear[i] = 0u;
   const int t = blockIdx.x / A.n_chunks;
   const int chunk = blockIdx.x - t * A.n_chunks;
   const int lane = threadIdx.x & 63;
@@ -106,9 +105,7 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(DecArgs A) {
     return;
   }
   __shared__ __align__(16) uint8_t lds[kDecWaves][32 * kKeyPitch];
-  __shared__ __align__(16) uint32_t hist[HIST ? kBins1 : 1];
   __shared__ float sh_w[kIdxHeads];
-  const bool do_hist = HIST && pos + 1 > A.k;
 
   // step it of this wave covers keys c0 + (4 it + wave) * 32 .. +31; keys
   // and score columns are handled relative to c0 in 32 bits
@@ -154,11 +151,6 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(DecArgs A) {
     *reinterpret_cast<u32x4*>(lds[0] + (f >> 4) * kKeyPitch + (f & 15) * 16) = qv[u];
   }
   sh_w[threadIdx.x & (kIdxHeads - 1)] = wv;     // every thread (equal values): no branch, no late load
-  if (do_hist) {
-    u32x4* h4 = reinterpret_cast<u32x4*>(hist);
-#pragma unroll
-    for (int i = 0; i < kBins1 / 4 / 256; ++i) h4[threadIdx.x + 256 * i] = u32x4{0u, 0u, 0u, 0u};
-  }
   lds_barrier();
   // A operand: head lane % 32, dims 16 s + 8 (lane / 32) .. +8 (chunk 2 s + lane / 32)
   bf16x8 a[8];
@@ -185,11 +177,7 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(DecArgs A) {
     wave_lds_fence();
     const float sc = relu_weighted_sum(acc, wr);
     const int key = key_of(it) + (lane & 31);
-    if (lane < 32 && key < wend) {
-      const bool valid = key <= wlast;
-      sc0[key] = valid ? sc : -INFINITY;
-      if (HIST && do_hist && valid) atomicAdd(&hist[score_key(sc) >> 20], 1u);
-    }
+    if (lane < 32 && key < wend) sc0[key] = key <= wlast ? sc : -INFINITY;
   };
 
   static_assert(kDecSteps % 2 == 0, "steps alternate between two register sets");
@@ -199,16 +187,6 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(DecArgs A) {
     if (it + 2 < n_it) load(g0, it + 2);
     step(g1, it + 1);
     if (it + 3 < n_it) load(g1, it + 3);
-  }
-
-  if (HIST && do_hist) {
-    // merge into the row's global histogram; the compaction kernel reads it
-    __syncthreads();
-    // consecutive lanes take consecutive bins, so each atomic instruction
-    // stays within a few cache lines
-    uint32_t* gh = A.ws.hist + (int64_t)t * kBins1;
-    for (int i = threadIdx.x; i < kBins1; i += 256)
-      if (hist[i]) atomicAdd(&gh[i], hist[i]);
   }
 }
 
@@ -390,10 +368,18 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
 // ------------------------------------------------------------------ launchers
 namespace sa_host {
 
-int32_t launch_indexer_ex(const void* q_idx, const float* w, const void* k_idx, const int64_t* seq_start,
-                          const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, float* scores, int64_t ld, int algo,
-                          const sa::TopkWs* hist_ws, int k, hipStream_t stream) {
-  if (algo == 0) algo = n_q >= 64 ? 2 : 1;
+int indexer_algo(int32_t n_q, int algo) { return algo != 0 ? algo : (n_q >= 64 ? 2 : 1); }
+
+// clear / n_clear: words the decode kernel (algo 1) sets to zero on the side;
+// the caller passes none with algo 2.
+int32_t launch_indexer(const void* q_idx, const float* w, const void* k_idx, const int64_t* seq_start,
+                       const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, float* scores, int64_t ld, int algo,
+                       hipStream_t stream, uint32_t* clear, int64_t n_clear) {
+  algo = indexer_algo(n_q, algo);
+  if (algo != 1 && n_clear > 0) {
+    set_error("indexer: only the decode kernel clears words on the side");
+    return SA_ERR_INVALID_ARG;
+  }
   if (algo == 1) {
     const int n_chunks = (int)((ld + sa::kDecChunk - 1) / sa::kDecChunk);
     const int64_t grid = (int64_t)n_chunks * n_q;
@@ -401,13 +387,9 @@ int32_t launch_indexer_ex(const void* q_idx, const float* w, const void* k_idx, 
       set_error("indexer: grid of %lld workgroups is too large", (long long)grid);
       return SA_ERR_UNSUPPORTED;
     }
-    sa::DecArgs A{(const uint16_t*)q_idx, w, (const uint16_t*)k_idx, seq_start, q_seq, q_pos, scores, ld, n_chunks, k,
-                  hist_ws ? *hist_ws : sa::TopkWs{}};
-    if (hist_ws) {
-      hipLaunchKernelGGL(sa::indexer_decode_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, A);
-    } else {
-      hipLaunchKernelGGL(sa::indexer_decode_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream, A);
-    }
+    sa::DecArgs A{(const uint16_t*)q_idx, w, (const uint16_t*)k_idx, seq_start, q_seq, q_pos, scores, ld, n_chunks,
+                  clear, n_clear > 0 ? n_clear : 0};
+    hipLaunchKernelGGL(sa::indexer_decode_kernel, dim3((unsigned)grid), dim3(256), 0, stream, A);
     return check_launch("indexer_decode_kernel");
   }
   const int n_splits = (int)((ld + sa::kPfSplit - 1) / sa::kPfSplit);
@@ -421,12 +403,6 @@ int32_t launch_indexer_ex(const void* q_idx, const float* w, const void* k_idx, 
                      (const uint16_t*)q_idx, w, (const uint16_t*)k_idx, seq_start, q_seq, q_pos, n_q, scores, ld,
                      n_splits);
   return check_launch("indexer_prefill_kernel");
-}
-
-int32_t launch_indexer(const void* q_idx, const float* w, const void* k_idx, const int64_t* seq_start,
-                       const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, float* scores, int64_t ld, int algo,
-                       hipStream_t stream) {
-  return launch_indexer_ex(q_idx, w, k_idx, seq_start, q_seq, q_pos, n_q, scores, ld, algo, nullptr, 0, stream);
 }
 
 }  // namespace sa_host

@@ -425,8 +425,17 @@ int32_t topk_after_hist(const float* scores, int64_t ld, const int32_t* q_pos, i
   return check_launch("topk_finish_kernel");
 }
 
+// Words that path 1 needs at zero before it starts (histograms and state
+// words, adjacent in the carve).
+void topk_clear_range(void* ws, int32_t n_q, int64_t ld, uint32_t** p, int64_t* n) {
+  const sa::TopkWs w = topk_carve(ws, n_q, ld);
+  *p = w.hist;
+  *n = (int64_t)((uint8_t*)w.sel - (uint8_t*)w.hist) / 4;
+}
+
+// cleared: path 1's words (topk_clear_range) are already zero in stream order.
 int32_t launch_topk(const float* scores, int64_t ld, const int32_t* q_pos, int32_t n_q, int32_t k, int32_t* idx,
-                    void* ws, int algo, hipStream_t stream) {
+                    void* ws, int algo, hipStream_t stream, bool cleared) {
   if (algo == 0) algo = 1;
   sa::TopkWs w = topk_carve(ws, n_q, ld);
   const int n_chunks = (int)((ld + sa::kChunk - 1) / sa::kChunk);
@@ -435,7 +444,7 @@ int32_t launch_topk(const float* scores, int64_t ld, const int32_t* q_pos, int32
     return SA_ERR_UNSUPPORTED;
   }
   if (algo == 1) {
-    int32_t rc = topk_zero(w, nullptr, 0, stream);
+    int32_t rc = cleared ? SA_OK : topk_zero(w, nullptr, 0, stream);
     if (rc) return rc;
     hipLaunchKernelGGL(sa::topk_hist_kernel, dim3(n_chunks * n_q), dim3(sa::kHistThreads), 0, stream, scores, ld,
                        q_pos, k, n_chunks, w);
