@@ -8,18 +8,19 @@
 //     z_j = scale * q_abs[t, h] . R_j,  obar = softmax(z) @ R[:, :512],
 //     out[t, h] = bf16(W_UV[h] @ obar).
 //
-// mla_attn_kernel: one workgroup per (query, slice of the selection); all 64
-// heads share every gathered row.  The slice is consumed in 32-row tiles by
-// 4 score waves and 4 output waves working one tile apart:
+// mla_attn_kernel: one workgroup per (query, slice of the selection, group of
+// 32 heads); the two head groups of a slice gather the same rows at the same
+// time through one XCD's L2.  The slice is consumed in 32-row tiles by 4
+// score waves and 4 output waves working one tile apart:
 //   - the output waves gather each tile (36 KB) with 16-byte direct-to-LDS
 //     loads into a 3-buffer ring, so two tiles are in flight without registers;
-//   - score wave w computes the partial S^T[32 rows x 64 heads] = R . Q^T over
+//   - score wave w computes the partial S^T[32 rows x 32 heads] = R . Q^T over
 //     dims 144w..144w+143 with v_mfma_f32_32x32x16_bf16 (R from LDS, Q^T in
 //     registers); after an exchange through LDS it runs the online softmax of
-//     heads 16w..16w+15 in base 2 (the running max is only moved when a tile
-//     exceeds it by more than 2^8, so rescaling is rare) and puts its bf16
-//     weights and any rescale factors in LDS;
-//   - output wave w accumulates O^T[latent dims 128w..128w+127 x 64 heads] +=
+//     heads 8w..8w+7 of the group in base 2 (the running max is only moved
+//     when a tile exceeds it by more than 2^8, so rescaling is rare) and puts
+//     its bf16 weights and any rescale factors in LDS;
+//   - output wave w accumulates O^T[latent dims 128w..128w+127 x 32 heads] +=
 //     V^T . P^T of the previous tile with v_mfma_f32_32x32x16_bf16: the 32 rows
 //     are the contraction, the V^T operand is assembled from 8-byte row pieces
 //     with byte permutes (rows and dims are permuted consistently in both
@@ -71,23 +72,39 @@ struct AttnArgs {
 };
 
 constexpr int kMaxSlice = 2048;
+constexpr int kHeadGroup = 32;             // heads per workgroup (two groups per query)
 constexpr size_t kRingBytes = (size_t)kRing * kTileBytes;                  // 110,592
-constexpr size_t kPBytes = 2 * 4 * 64 * 16;                               // weights, double-buffered
-constexpr size_t kAlphaBytes = 2 * 4 * 16 * 4;                            // rescale factors
+constexpr size_t kSBytes = 4 * 4 * 64 * 16;                               // partial S^T of each score wave
+constexpr size_t kPBytes = 2 * kHeadGroup * 8 * 8;                        // bf16 weights, double-buffered
+constexpr size_t kAlphaBytes = 2 * kHeadGroup * 4;                        // rescale factors
 constexpr size_t kFlagBytes = 2 * 4 * 4;
-constexpr size_t kSBytes = 4 * 2 * 4 * 64 * 16;                           // partial S^T of each wave
-constexpr size_t kMlBytes = 64 * 2 * 4;                                  // (m, l) per head at the end
+constexpr size_t kMlBytes = kHeadGroup * 2 * 4;                           // (m, l) per head at the end
 constexpr size_t kAttnSmem = kRingBytes + kSBytes + kPBytes + kAlphaBytes + kFlagBytes + kMlBytes + kMaxSlice * 4;
 constexpr int kAttnThreads = 512;          // 4 score waves + 4 output waves
 
+// Slot of the 4-row group p (rows 4p..4p+3) in a head's weight entry: the
+// output waves read groups (4ks + hl, 4ks + 2 + hl) as one 16-byte operand.
+__device__ __forceinline__ int p_slot(int p) { return (p & 4) | ((p & 1) << 1) | ((p >> 1) & 1); }
+
+// x combined over the 8 lanes of an aligned group, every lane gets the result
+// (DPP: mirror within the 8, then swap neighbours, then swap pairs).
+template <typename Op>
+__device__ __forceinline__ float reduce8(float x, Op op) {
+  x = op(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xf, 0xf, false)));   // row_half_mirror
+  x = op(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xb1, 0xf, 0xf, false)));    // quad_perm 1,0,3,2
+  x = op(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4e, 0xf, 0xf, false)));    // quad_perm 2,3,0,1
+  return x;
+}
+
 __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
   // Workgroups are dealt to the 8 XCDs round-robin (bid % 8): give each XCD a
-  // contiguous run of (query, slice) items, so the slices of one query share
-  // its absorbed queries in one L2.
+  // contiguous run of (query, slice, head group) items, so the two head
+  // groups of a slice gather the same rows through one L2 at the same time.
   const int n_wg = (int)gridDim.x;
   const int item = (n_wg & 7) ? (int)blockIdx.x : (int)(blockIdx.x & 7) * (n_wg >> 3) + (int)(blockIdx.x >> 3);
-  const int t = item / A.n_sp;
-  const int sp = item - t * A.n_sp;
+  const int hg = item & 1;
+  const int t = (item >> 1) / A.n_sp;
+  const int sp = (item >> 1) - t * A.n_sp;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int w = wave & 3;                       // dim quarter of QK (score waves) / latent quarter (output waves)
@@ -95,12 +112,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
 
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* ring = smem;
-  f32x4* slds = reinterpret_cast<f32x4*>(smem + kRingBytes);               // [4 waves][2 nt][4 ig][64]
+  f32x4* slds = reinterpret_cast<f32x4*>(smem + kRingBytes);               // [4 waves][4 row groups][64]
   uint8_t* sm2 = smem + kRingBytes + kSBytes;
-  u32x4* plds = reinterpret_cast<u32x4*>(sm2);                             // [2][4][64]
-  float* alds = reinterpret_cast<float*>(sm2 + kPBytes);                   // [2][4][16]
-  int* flds = reinterpret_cast<int*>(sm2 + kPBytes + kAlphaBytes);         // [2][4]
-  float* mlds = reinterpret_cast<float*>(sm2 + kPBytes + kAlphaBytes + kFlagBytes);          // [64][2]
+  u32x2* plds = reinterpret_cast<u32x2*>(sm2);                             // [2][32 heads][8 slots]
+  float* alds = reinterpret_cast<float*>(sm2 + kPBytes);                   // [2][32 heads]
+  int* flds = reinterpret_cast<int*>(sm2 + kPBytes + kAlphaBytes);         // [2][4 score waves]
+  float* mlds = reinterpret_cast<float*>(sm2 + kPBytes + kAlphaBytes + kFlagBytes);          // [32][2]
   int32_t* spos = reinterpret_cast<int32_t*>(sm2 + kPBytes + kAlphaBytes + kFlagBytes + kMlBytes);
 
   const int j0 = sp * A.kps;
@@ -135,16 +152,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
   // 8 (i / 4) + 4 (l / 32) + i % 4, column l % 32).
   if (wave < 4) {
     // =========================== score waves: QK^T and the online softmax of tile `step`
-    // S^T[32 rows x 64 heads] is split over the 576 dims: wave w takes dims
-    // 144w .. 144w + 143 (9 steps of 16) for both 32-head column tiles, so each
-    // row chunk read from LDS feeds 2 MFMAs.  Q operand: head 32nt + l32,
-    // dims 144w + 16s + 8hl .. +8.
-    bf16x8 qb[2][9];
+    // S^T[32 rows x 32 heads] is split over the 576 dims: wave w takes dims
+    // 144w .. 144w + 143 (9 steps of 16).  Q operand: head 32hg + l32, dims
+    // 144w + 16s + 8hl .. +8.
+    bf16x8 qb[9];
+    {
+      const uint16_t* qp = A.q_abs + ((int64_t)t * kHeads + kHeadGroup * hg + l32) * kRow + 144 * w + 8 * hl;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const uint16_t* qp = A.q_abs + ((int64_t)t * kHeads + 32 * nt + l32) * kRow + 144 * w + 8 * hl;
-#pragma unroll
-      for (int s = 0; s < 9; ++s) qb[nt][s] = as_bf16x8(ld16(qp + 16 * s));
+      for (int s = 0; s < 9; ++s) qb[s] = as_bf16x8(ld16(qp + 16 * s));
     }
     store_positions();
     // The staged positions must be visible; the query loads stay in flight.
@@ -153,17 +168,15 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
     const int rbase = l32 * kRowBytes;
     const int rsw = l32 & 7;
     const int c0 = 18 * w + hl;
-    // Softmax ownership: this wave finishes heads 16w .. 16w + 15; lane
-    // (hd, p) = (lane & 15, lane >> 4) takes head 16w + hd and rows
-    // 16 (p >> 1) + 8a + 4 (p & 1) + j (a = 0, 1; j = 0..3), i.e. elements
-    // 8 (p >> 1) + 4a + j of result column 16 (w & 1) + hd + 32 (p & 1) of
-    // column tile w >> 1.
-    const int hd = lane & 15, pq4 = lane >> 4;
-    const int own_nt = w >> 1;
-    const int src_lane = 16 * (w & 1) + hd + 32 * (pq4 & 1);
-    const int ig0 = 2 * (pq4 >> 1);
-    const int row0 = 16 * (pq4 >> 1) + 4 * (pq4 & 1);
-    float m_run = -INFINITY, l_run = 0.f;     // softmax state of head 16w + hd (lane-partial sum)
+    // Softmax ownership: this wave finishes heads 8w .. 8w + 7 of the group;
+    // lane (hd, p) = (lane / 8, lane % 8) takes head 8w + hd and rows
+    // 4p .. 4p + 3, i.e. elements 4 (p / 2) .. +3 of result column
+    // 8w + hd + 32 (p % 2).
+    const int hd = lane >> 3, pq = lane & 7;
+    const int hloc = 8 * w + hd;
+    const int src_lane = hloc + 32 * (pq & 1);
+    const int ig = pq >> 1;
+    float m_run = -INFINITY, l_run = 0.f;     // softmax state of head hloc (lane-partial sum)
     lds_barrier();                                                     // B1: tile 0 staged
 #pragma unroll 1
     for (int tile = 0; tile <= n_tiles; ++tile) {
@@ -172,104 +185,82 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
       const int pb_i = tile & 1;
       const int jt = tile * kTile;
       if (active) {
-        // ---- partial S^T = R . Q^T over this wave's dims, all 64 heads, 32 rows.
+        // ---- partial S^T = R . Q^T over this wave's dims, 32 heads, 32 rows.
         u32x4 ra[9];            // all of this wave's row chunks of the tile, read up front
 #pragma unroll
         for (int s = 0; s < 9; ++s)
           ra[s] = *reinterpret_cast<const u32x4*>(cur + rbase + 16 * ((c0 + 2 * s) ^ rsw));
-        f32x16 acc[2] = {f32x16{}, f32x16{}};
+        f32x16 acc = {};
 #pragma unroll
-        for (int s = 0; s < 9; ++s)
+        for (int s = 0; s < 9; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ra[s]), qb[s], acc, 0, 0, 0);
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
-            acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ra[s]), qb[nt][s], acc[nt], 0, 0, 0);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-          for (int ig = 0; ig < 4; ++ig)
-            slds[((w * 2 + nt) * 4 + ig) * 64 + lane] =
-                f32x4{acc[nt][4 * ig], acc[nt][4 * ig + 1], acc[nt][4 * ig + 2], acc[nt][4 * ig + 3]};
+        for (int g = 0; g < 4; ++g)
+          slds[(w * 4 + g) * 64 + lane] = f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
       }
       lds_barrier();                                                   // BAR_s
       if (active) {
-        // full scores of this lane's 8 rows: sum of the 4 waves' partials
-        f32x4 s[2];
+        // full scores of this lane's 4 rows: sum of the 4 waves' partials
+        f32x4 s4 = slds[(0 * 4 + ig) * 64 + src_lane];
 #pragma unroll
-        for (int a = 0; a < 2; ++a) {
-          s[a] = slds[((0 * 2 + own_nt) * 4 + ig0 + a) * 64 + src_lane];
-#pragma unroll
-          for (int w2 = 1; w2 < 4; ++w2) s[a] += slds[((w2 * 2 + own_nt) * 4 + ig0 + a) * 64 + src_lane];
-        }
-        // ---- online softmax of head 16w + hd over rows row0 + 8a + j.
-        float x[2][4];
+        for (int w2 = 1; w2 < 4; ++w2) s4 += slds[(w2 * 4 + ig) * 64 + src_lane];
+        // ---- online softmax of head hloc over rows jt + 4pq .. +3
+        const u32x4 pos4 = *reinterpret_cast<const u32x4*>(spos + jt + 4 * pq);
+        float x[4];
         float tmax = -INFINITY;
 #pragma unroll
-        for (int a = 0; a < 2; ++a) {
-          // rows jt + row0 + 8a .. +3: one 16-byte read of the staged positions
-          const u32x4 pq = *reinterpret_cast<const u32x4*>(spos + jt + row0 + 8 * a);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            x[a][j] = (int)pq[j] >= 0 ? s[a][j] * A.scale_log2 : -INFINITY;
-            tmax = fmaxf(tmax, x[a][j]);
-          }
+        for (int j = 0; j < 4; ++j) {
+          x[j] = (int)pos4[j] >= 0 ? s4[j] * A.scale_log2 : -INFINITY;
+          tmax = fmaxf(tmax, x[j]);
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        tmax = reduce8(tmax, [](float a, float b) { return fmaxf(a, b); });
         const bool bump = tmax > m_run + kRescaleSlack;
         const bool any_bump = __any(bump);
         if (any_bump) {
           const float alpha = bump ? (m_run == -INFINITY ? 0.f : fast_exp2(m_run - tmax)) : 1.f;
           if (bump) m_run = tmax;
           l_run *= alpha;
-          alds[(pb_i * 4 + w) * 16 + hd] = alpha;        // the 4 lanes of a head store the same value
+          alds[pb_i * kHeadGroup + hloc] = alpha;      // the 8 lanes of a head store the same value
         }
         flds[pb_i * 4 + w] = any_bump ? 1 : 0;
         // masked rows have x = -inf and weight exp2(-inf) = 0; m_run is -inf
         // only while every row so far was masked
         const float m_use = m_run == -INFINITY ? 0.f : m_run;
-        float p[2][4];
+        float p[4];
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            p[a][j] = fast_exp2(x[a][j] - m_use);
-            l_run += p[a][j];
-          }
-        // The weights of rows row0 + 8a + j are the PV contraction slots
-        // 4a + j of the lanes that read this entry.
-        const u32x4 pown = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
-                            pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
-        plds[(pb_i * 4 + w) * 64 + lane] = pown;
+        for (int j = 0; j < 4; ++j) {
+          p[j] = fast_exp2(x[j] - m_use);
+          l_run += p[j];
+        }
+        plds[(pb_i * kHeadGroup + hloc) * 8 + p_slot(pq)] = u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
       }
       lds_barrier();                                                   // BAR_p
     }
-    // Head 16w + hd: sum over the 4 lanes that share it.
-    l_run += __shfl_xor(l_run, 16, 64);
-    l_run += __shfl_xor(l_run, 32, 64);
-    if (pq4 == 0) {
-      mlds[(16 * w + hd) * 2 + 0] = m_run;
-      mlds[(16 * w + hd) * 2 + 1] = l_run;
+    // Head hloc: sum over the 8 lanes that share it.
+    l_run = reduce8(l_run, [](float a, float b) { return a + b; });
+    if (pq == 0) {
+      const int head = kHeadGroup * hg + hloc;
+      mlds[hloc * 2 + 0] = m_run;
+      mlds[hloc * 2 + 1] = l_run;
       if (A.n_sp == 1) {
         if (A.lse)
-          A.lse[(int64_t)t * kHeads + 16 * w + hd] =
-              l_run > 0.f ? (m_run + __log2f(l_run)) * 0.69314718055994531f : -INFINITY;
+          A.lse[(int64_t)t * kHeads + head] = l_run > 0.f ? (m_run + __log2f(l_run)) * 0.69314718055994531f : -INFINITY;
       } else {
         const int64_t pbase = ((int64_t)t * A.n_sp + sp) * kHeads;
-        A.part_ml[(pbase + 16 * w + hd) * 2 + 0] = m_run;
-        A.part_ml[(pbase + 16 * w + hd) * 2 + 1] = l_run;
+        A.part_ml[(pbase + head) * 2 + 0] = m_run;
+        A.part_ml[(pbase + head) * 2 + 1] = l_run;
       }
     }
     lds_barrier();                                                     // BAR_end
     return;
   }
   // =========================== output waves: O^T += V^T . P^T of tile `step - 1`
-  // Wave w owns latent dims 128w .. 128w+127 for all 64 heads: result tile
-  // (mt, nt) holds dims 128w + 4m + mt (m = result row) of heads 32nt + n.
-  // The 32 rows of a tile are two contraction steps ks of 16; slot 8hl + e of
-  // step ks is row 16ks + 8 (e >> 2) + 4hl + (e & 3) in both operands (the
-  // order in which the score waves pack their weights).  The V^T operand of
-  // lane (m = l32, hl) takes 8 bytes (dims 4m .. 4m+3) of each of its 8 rows
-  // and byte permutes form the four dim tiles mt.
+  // Wave w owns latent dims 128w .. 128w+127 for the 32 heads: result tile mt
+  // holds dims 128w + 4m + mt (m = result row) of heads 32hg + n.  The 32
+  // rows of a tile are two contraction steps ks of 16; slot 8hl + e of step
+  // ks is row 16ks + 8 (e >> 2) + 4hl + (e & 3) in both operands (the score
+  // waves' weight slots 4ks + 2hl and +1 hold exactly these rows).  The V^T
+  // operand of lane (m = l32, hl) takes 8 bytes (dims 4m .. 4m+3) of each of
+  // its 8 rows and byte permutes form the four dim tiles mt.
   // Direct-to-LDS gather of the tiles, issued by these waves: load u of wave w
   // fills bytes (9w + u) KB of the tile buffer, 16 bytes per lane; the lane
   // fetches the row chunk whose swizzled position is that slot.
@@ -307,19 +298,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
 #pragma unroll
   for (int e = 0; e < 4; ++e)
     voff[e] = (4 * hl + e) * kRowBytes + 16 * ((16 * w + (l32 >> 1)) ^ (4 * hl + e)) + 8 * (l32 & 1);
-  f32x16 o[4][2];                // O^T tiles: dim tiles mt x head tiles nt
+  f32x16 o[4];                   // O^T tiles: dim tiles mt
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) o[mt][nt] = f32x16{};
+  for (int mt = 0; mt < 4; ++mt) o[mt] = f32x16{};
   store_positions();
   lds_barrier();                                                       // B0
   issue(0);
   issue(1);
   SA_WAIT_VMCNT(kLoadsPerWave);          // tile 0 is in (tile 1 may still be in flight)
   lds_barrier();                                                       // B1
-  // weights / rescale of head 32nt + l32 come from score wave 2nt + (l32 >> 4), lane entry (l32 & 15)
-  const int pw_hi = l32 >> 4;
+  // weights / rescale of head l32 come from score wave l32 / 8
+  const int pw = l32 >> 3;
 #pragma unroll 1
   for (int step = 0; step <= n_tiles; ++step) {
     // Operands of tile step - 1 are read before BAR_s (which frees its buffer
@@ -329,9 +318,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
     const int tile = step - 1;
     const int pb_i = tile & 1;
     u32x2 v[2][8];
-    u32x4 pt[2][2];
-    int fl[2];
-    float al[2];
+    u32x4 pt[2];
+    int fl = 0;
+    float al = 1.f;
     if (pv_step) {
       const uint8_t* cur = ring + (tile % kRing) * kTileBytes;
 #pragma unroll
@@ -340,25 +329,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
         for (int e = 0; e < 8; ++e)
           v[ks][e] = *reinterpret_cast<const u32x2*>(cur + (16 * ks + 8 * (e >> 2)) * kRowBytes + voff[e & 3]);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          pt[nt][ks] = plds[(pb_i * 4 + 2 * nt + pw_hi) * 64 + (l32 & 15) + 16 * (2 * ks + hl)];
-        // this lane's own flag (a lane-dependent pick among registers would go through scratch memory)
-        fl[nt] = flds[pb_i * 4 + 2 * nt + pw_hi];
-        al[nt] = alds[(pb_i * 4 + 2 * nt + pw_hi) * 16 + (l32 & 15)];   // meaningful only where its flag is set
-      }
+      for (int ks = 0; ks < 2; ++ks)
+        pt[ks] = *reinterpret_cast<const u32x4*>(plds + (pb_i * kHeadGroup + l32) * 8 + 4 * ks + 2 * hl);
+      fl = flds[pb_i * 4 + pw];
+      al = alds[pb_i * kHeadGroup + l32];          // meaningful only where the flag is set
     }
     lds_barrier();                                                     // BAR_s
     if (step < n_tiles) issue(step + 2);
     if (pv_step) {
-      if (__any(fl[0] | fl[1])) {
+      if (__any(fl)) {
+        const float sc = fl ? al : 1.f;
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const float sc = fl[nt] ? al[nt] : 1.f;
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) o[mt][nt] *= sc;
-        }
+        for (int mt = 0; mt < 4; ++mt) o[mt] *= sc;
       }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -377,9 +359,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
             av[2] = perm_lo(v[ks][4][d], v[ks][5][d]);
             av[3] = perm_lo(v[ks][6][d], v[ks][7][d]);
           }
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
-            o[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(pt[nt][ks]), o[mt][nt], 0, 0, 0);
+          o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(pt[ks]), o[mt], 0, 0, 0);
         }
       }
     }
@@ -389,65 +369,58 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
   }
   __builtin_amdgcn_s_waitcnt(0);         // the trailing (clamped) tile loads land before the workgroup ends
   lds_barrier();                                                       // BAR_end: (m, l) of every head
-  // Result element 4a + b of tile (mt, nt) is dim 128w + 32a + 16hl + 4b + mt
-  // of head 32nt + l32: for each (nt, a) a lane holds 16 consecutive dims.
+  // Result element 4a + b of tile mt is dim 128w + 32a + 16hl + 4b + mt of
+  // head 32hg + l32: for each a a lane holds 16 consecutive dims.
   if (A.n_sp == 1) {
+    const float L = mlds[l32 * 2 + 1];
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    uint16_t* ob = A.obar + ((int64_t)t * kHeads + kHeadGroup * hg + l32) * kLatent + 128 * w + 16 * hl;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const float L = mlds[(32 * nt + l32) * 2 + 1];
-      const float inv = L > 0.f ? 1.f / L : 0.f;
-      uint16_t* ob = A.obar + ((int64_t)t * kHeads + 32 * nt + l32) * kLatent + 128 * w + 16 * hl;
+    for (int a = 0; a < 4; ++a) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-#pragma unroll
-        for (int bh = 0; bh < 2; ++bh) {          // dims 8bh .. 8bh + 7 of the 16: b = 2bh, 2bh + 1
-          const int i0 = 4 * a + 2 * bh;
-          const u32x4 pk = {pack_bf16x2(o[0][nt][i0] * inv, o[1][nt][i0] * inv),
-                            pack_bf16x2(o[2][nt][i0] * inv, o[3][nt][i0] * inv),
-                            pack_bf16x2(o[0][nt][i0 + 1] * inv, o[1][nt][i0 + 1] * inv),
-                            pack_bf16x2(o[2][nt][i0 + 1] * inv, o[3][nt][i0 + 1] * inv)};
-          *reinterpret_cast<u32x4*>(ob + 32 * a + 8 * bh) = pk;
-        }
+      for (int bh = 0; bh < 2; ++bh) {            // dims 8bh .. 8bh + 7 of the 16: b = 2bh, 2bh + 1
+        const int i0 = 4 * a + 2 * bh;
+        const u32x4 pk = {pack_bf16x2(o[0][i0] * inv, o[1][i0] * inv), pack_bf16x2(o[2][i0] * inv, o[3][i0] * inv),
+                          pack_bf16x2(o[0][i0 + 1] * inv, o[1][i0 + 1] * inv),
+                          pack_bf16x2(o[2][i0 + 1] * inv, o[3][i0 + 1] * inv)};
+        *reinterpret_cast<u32x4*>(ob + 32 * a + 8 * bh) = pk;
       }
     }
     return;
   }
-  // Partial accumulators in register-tile order: [t][sp][w][nt][mt][a][lane]
+  // Partial accumulators in register-tile order: [t][sp][hg][w][mt][a][lane]
   // x 4 values (b = 0..3), so every store instruction writes 1 KB contiguously.
-  f32x4* po = reinterpret_cast<f32x4*>(A.part_o) + (((int64_t)t * A.n_sp + sp) * 4 + w) * 32 * 64;
+  f32x4* po = reinterpret_cast<f32x4*>(A.part_o) + ((((int64_t)t * A.n_sp + sp) * 2 + hg) * 4 + w) * 16 * 64;
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-        po[((nt * 4 + mt) * 4 + a) * 64 + lane] =
-            f32x4{o[mt][nt][4 * a], o[mt][nt][4 * a + 1], o[mt][nt][4 * a + 2], o[mt][nt][4 * a + 3]};
+    for (int a = 0; a < 4; ++a)
+      po[(mt * 4 + a) * 64 + lane] = f32x4{o[mt][4 * a], o[mt][4 * a + 1], o[mt][4 * a + 2], o[mt][4 * a + 3]};
 }
 
 // Merge of the slices' partial softmax states: obar = sum_s a_s O_s / sum_s a_s l_s
 // with a_s = 2^(m_s - max m).  Partials are in the attention kernel's register
-// tile order.  One workgroup per (query, latent quarter w, head tile nt, dim
-// tile pair mp); thread = (a, lane) owns dim tiles mt = 2mp, 2mp + 1 of head
-// 32nt + (lane & 31), i.e. dims 128w + 32a + 16 (lane >> 5) + 4b + mt, and
-// reads them for 8 slices at a time (one rescale per batch).
+// tile order.  One workgroup per (query, latent quarter w, head group hg, dim
+// tile pair mp), dealt to the XCDs like the attention kernel's items; thread
+// (a, lane) owns dim tiles mt = 2mp, 2mp + 1 of head 32hg + (lane & 31), i.e.
+// dims 128w + 32a + 16 (lane >> 5) + 4b + mt, and reads them for 8 slices at
+// a time (one rescale per batch).
 constexpr int kMergeBatch = 8;         // slices read per round trip
 
 __global__ __launch_bounds__(256) void mla_merge_kernel(AttnArgs A) {
-  // The same XCD-contiguous dealing as the attention kernel: a query's merge
-  // workgroups run on the XCD whose L2 took that query's partial states.
   const int n_wg = (int)gridDim.x;
   const int item = (n_wg & 7) ? (int)blockIdx.x : (int)(blockIdx.x & 7) * (n_wg >> 3) + (int)(blockIdx.x >> 3);
   const int t = item >> 4;
   const int w = (item >> 2) & 3;
-  const int nt = (item >> 1) & 1;
+  const int hg = (item >> 1) & 1;
   const int mp = item & 1;
   const int a = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int l32 = lane & 31, hl = lane >> 5;
-  const int head = 32 * nt + l32;
+  const int head = kHeadGroup * hg + l32;
   const int n_sp = A.n_sp;
-  const f32x4* src = reinterpret_cast<const f32x4*>(A.part_o) + ((int64_t)t * n_sp * 4 + w) * 2048 +
-                     ((nt * 4 + 2 * mp) * 4 + a) * 64 + lane;     // slice s adds s * 4 * 2048; tile mt + 1 adds 4 * 64
+  // slice s adds s * 2 * 4 * 1024; tile mt + 1 adds 4 * 64
+  const f32x4* src = reinterpret_cast<const f32x4*>(A.part_o) + (((int64_t)t * n_sp * 2 + hg) * 4 + w) * 1024 +
+                     (2 * mp * 4 + a) * 64 + lane;
   const float2* mlp = reinterpret_cast<const float2*>(A.part_ml) + (int64_t)t * n_sp * kHeads + head;
   float M = -INFINITY, L = 0.f;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
@@ -572,8 +545,9 @@ namespace sa_host {
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int mla_n_splits(int32_t n_q, int32_t k) {
-  // About one workgroup per CU; a slice keeps at least two 32-row tiles.
-  const int target = 256;
+  // About one workgroup per CU (two head groups per slice); a slice keeps at
+  // least two 32-row tiles.
+  const int target = 128;
   int n_sp = (target + n_q - 1) / n_q;
   const int max_sp = (k + 63) / 64;
   if (n_sp > max_sp) n_sp = max_sp;
@@ -648,7 +622,7 @@ int32_t launch_mla(const void* q_abs, const void* kv, const int64_t* seq_start, 
     }
     g_attr_set.fetch_or(bit);
   }
-  const int64_t grid = (int64_t)n_q * n_sp;
+  const int64_t grid = (int64_t)n_q * n_sp * 2;
   if (grid > 0x7fffffff) {
     set_error("mla: grid too large");
     return SA_ERR_UNSUPPORTED;
