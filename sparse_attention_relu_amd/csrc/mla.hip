@@ -390,12 +390,15 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
   }
   // Partial accumulators in register-tile order: [t][sp][hg][w][mt][a][lane]
   // x 4 values (b = 0..3), so every store instruction writes 1 KB contiguously.
+  // Streaming stores: the partials go out as they are written instead of
+  // being written back from L2 when the kernel ends (-1 us per launch).
   f32x4* po = reinterpret_cast<f32x4*>(A.part_o) + ((((int64_t)t * A.n_sp + sp) * 2 + hg) * 4 + w) * 16 * 64;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int a = 0; a < 4; ++a)
-      po[(mt * 4 + a) * 64 + lane] = f32x4{o[mt][4 * a], o[mt][4 * a + 1], o[mt][4 * a + 2], o[mt][4 * a + 3]};
+      __builtin_nontemporal_store(f32x4{o[mt][4 * a], o[mt][4 * a + 1], o[mt][4 * a + 2], o[mt][4 * a + 3]},
+                                  &po[(mt * 4 + a) * 64 + lane]);
 }
 
 // Merge of the slices' partial softmax states: obar = sum_s a_s O_s / sum_s a_s l_s
