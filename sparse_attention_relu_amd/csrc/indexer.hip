@@ -118,12 +118,13 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(DecArgs A) {
   auto key_of = [&](int it) { return (it * kDecWaves + wave) * 32; };
 
   // Loads past the causal bound re-read the last valid key (always in bounds);
-  // their scores are replaced by -inf, so no load needs a branch.
+  // their scores are replaced by -inf, so no load needs a branch.  Keys are
+  // read once: streaming loads keep them from displacing cached data.
   auto load = [&](u32x4 (&g)[8], int it) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int key = min(key_of(it) + 4 * j + (lane >> 4), wlast);
-      g[j] = ld16(kb + key * kIdxDim + (lane & 15) * 8);
+      g[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + key * kIdxDim + (lane & 15) * 8));
     }
   };
 
