@@ -57,12 +57,12 @@ __device__ __forceinline__ float relu_weighted_part_lds(const f32x16& acc, const
 }
 
 // ------------------------------------------------------------ decode kernel
-// A workgroup covers 512 consecutive keys of one query's sequence: at each of
-// its 4 steps the 4 waves take the next 128 keys (32 each, 8 KB), staged
+// A workgroup covers 256 consecutive keys of one query's sequence: at each of
+// its 2 steps the 4 waves take the next 128 keys (32 each, 8 KB), staged
 // through wave-private LDS into the MFMA, with the next step's loads in
 // flight.
 constexpr int kDecWaves = 4;
-constexpr int kDecSteps = 4;
+constexpr int kDecSteps = 2;
 constexpr int kDecChunk = kDecWaves * 32 * kDecSteps;     // keys per workgroup
 constexpr int kKeyPitch = 272;                            // LDS bytes per key row (256 + 16 pad)
 
