@@ -57,13 +57,14 @@ __device__ __forceinline__ float relu_weighted_part_lds(const f32x16& acc, const
 }
 
 // ------------------------------------------------------------ decode kernel
-// A workgroup covers 256 consecutive keys of one query's sequence: at each of
-// its 2 steps the 4 waves take the next 128 keys (32 each, 8 KB), staged
+// A workgroup covers 128 consecutive keys of one query's sequence: at each of
+// its 2 steps the 2 waves take the next 64 keys (32 each, 8 KB), staged
 // through wave-private LDS into the MFMA, with the next step's loads in
 // flight.
-constexpr int kDecWaves = 4;
+constexpr int kDecWaves = 2;
 constexpr int kDecSteps = 2;
 constexpr int kDecChunk = kDecWaves * 32 * kDecSteps;     // keys per workgroup
+constexpr int kDecThreads = kDecWaves * 64;
 constexpr int kKeyPitch = 272;                            // LDS bytes per key row (256 + 16 pad)
 
 struct DecArgs {
@@ -89,9 +90,10 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-__global__ __launch_bounds__(256) void indexer_decode_kernel(DecArgs A) {
+__global__ __launch_bounds__(kDecThreads) void indexer_decode_kernel(DecArgs A) {
   // side job: clear the caller's words (a grid-stride loop over all workgroups)
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < A.n_clear; i += (int64_t)gridDim.x * 256) A.clear[i] = 0u;
+  for (int64_t i = (int64_t)blockIdx.x * kDecThreads + threadIdx.x; i < A.n_clear; i += (int64_t)gridDim.x * kDecThreads)
+    A.clear[i] = 0u;
   const int t = blockIdx.x / A.n_chunks;
   const int chunk = blockIdx.x - t * A.n_chunks;
   const int lane = threadIdx.x & 63;
@@ -101,7 +103,7 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(DecArgs A) {
   float* srow = A.scores + (int64_t)t * A.ld;
   if (c0 > pos) {
     const int64_t end = min(c0 + (int64_t)kDecChunk, A.ld);
-    for (int64_t s = c0 + threadIdx.x; s < end; s += 256) srow[s] = -INFINITY;
+    for (int64_t s = c0 + threadIdx.x; s < end; s += kDecThreads) srow[s] = -INFINITY;
     return;
   }
   __shared__ __align__(16) uint8_t lds[kDecWaves][32 * kKeyPitch];
@@ -134,10 +136,12 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(DecArgs A) {
   // first two key blocks of each wave are requested before that (loads
   // complete in order, so staging the query waits only for the query).
   const uint16_t* qt = A.q_idx + (int64_t)t * kIdxHeads * kIdxDim;
-  u32x4 qv[2];
+  constexpr int kQPieces = kIdxHeads * kIdxDim * 2 / 16 / kDecThreads;    // 16-byte pieces per thread
+  static_assert(kQPieces * kDecThreads * 16 == kIdxHeads * kIdxDim * 2, "query pieces");
+  u32x4 qv[kQPieces];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int f = (int)threadIdx.x + 256 * u;           // 16-byte piece: head f / 16, chunk f % 16
+  for (int u = 0; u < kQPieces; ++u) {
+    const int f = (int)threadIdx.x + kDecThreads * u;   // 16-byte piece: head f / 16, chunk f % 16
     qv[u] = ld16(qt + (f >> 4) * kIdxDim + (f & 15) * 8);
   }
   const float wv = A.w[(int64_t)t * kIdxHeads + (threadIdx.x & (kIdxHeads - 1))];
@@ -147,8 +151,8 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(DecArgs A) {
   load(g0, 0);
   load(g1, 1);
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int f = (int)threadIdx.x + 256 * u;
+  for (int u = 0; u < kQPieces; ++u) {
+    const int f = (int)threadIdx.x + kDecThreads * u;
     *reinterpret_cast<u32x4*>(lds[0] + (f >> 4) * kKeyPitch + (f & 15) * 16) = qv[u];
   }
   sh_w[threadIdx.x & (kIdxHeads - 1)] = wv;     // every thread (equal values): no branch, no late load
@@ -390,7 +394,7 @@ int32_t launch_indexer(const void* q_idx, const float* w, const void* k_idx, con
     }
     sa::DecArgs A{(const uint16_t*)q_idx, w, (const uint16_t*)k_idx, seq_start, q_seq, q_pos, scores, ld, n_chunks,
                   clear, n_clear > 0 ? n_clear : 0};
-    hipLaunchKernelGGL(sa::indexer_decode_kernel, dim3((unsigned)grid), dim3(256), 0, stream, A);
+    hipLaunchKernelGGL(sa::indexer_decode_kernel, dim3((unsigned)grid), dim3(sa::kDecThreads), 0, stream, A);
     return check_launch("indexer_decode_kernel");
   }
   const int n_splits = (int)((ld + sa::kPfSplit - 1) / sa::kPfSplit);
