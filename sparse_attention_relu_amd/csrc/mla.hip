@@ -45,6 +45,7 @@ constexpr int kRing = 3;                   // LDS tile buffers (two tiles in fli
 constexpr int kLoadsPerWave = kTileBytes / 1024 / kAttnWaves;    // 9 direct-to-LDS loads of 1 KB
 constexpr float kRescaleSlack = 8.0f;      // log2 units
 constexpr int kMaxSp = 32;
+constexpr int kCpolNt = 2;                 // cache-policy operand of global_load_lds: non-temporal
 
 __device__ __forceinline__ uint32_t perm_lo(uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x05040100u); }
 __device__ __forceinline__ uint32_t perm_hi(uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x07060302u); }
@@ -284,11 +285,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
 #pragma unroll
     for (int u = 0; u < kLoadsPerWave; ++u) {
       // padding entries read row 0; byte offsets within the sequence stay
-      // below 2^32 for sequences below 3.7M rows
+      // below 2^32 for sequences below 3.7M rows.  Cache policy: streaming
+      // (non-temporal), the rows are dead after this step's two head groups
+      // (-1.5 us per launch against the default policy).
       const int p = pos[u] >= 0 ? pos[u] : 0;
       const uint32_t off = (uint32_t)p * (uint32_t)kRowBytes + (uint32_t)lcol[u];
       __builtin_amdgcn_global_load_lds((const void*)(rows_b + off),
-                                       (__attribute__((address_space(3))) void*)(b + 1024 * u), 16, 0, 0);
+                                       (__attribute__((address_space(3))) void*)(b + 1024 * u), 16, 0, kCpolNt);
     }
   };
   // V^T operand: 8-byte read of row rho = 16ks + 8(e >> 2) + 4hl + (e & 3),
