@@ -33,8 +33,8 @@
 
 namespace sa {
 
-constexpr int kChunk = 4096;           // elements per workgroup in path 1
-constexpr int kHistThreads = 256;
+constexpr int kChunk = 8192;           // elements per workgroup in path 1
+constexpr int kHistThreads = 1024;
 constexpr int kPer = kChunk / kHistThreads;
 constexpr int kFinThreads = 1024;
 constexpr int kLdsCand = 8192;         // candidates staged in LDS by the finish kernel
