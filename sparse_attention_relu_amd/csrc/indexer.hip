@@ -18,7 +18,7 @@
 //   indexer_decode_kernel   one query per workgroup column: streams that
 //                           query's keys once (decode: every query has its own
 //                           sequence).  HBM-bound: 256 B of keys per 8 KFLOP.
-//   indexer_prefill_kernel  8 queries of one sequence share each key tile staged
+//   indexer_prefill_kernel  16 queries of one sequence share each key tile staged
 //                           in LDS: the dense contraction of chunked prefill.
 #include "sa_common.h"
 
@@ -196,18 +196,19 @@ __global__ __launch_bounds__(kDecThreads) void indexer_decode_kernel(DecArgs A) 
 }
 
 // ----------------------------------------------------------- prefill kernel
-constexpr int kPfQ = 8;            // queries per workgroup (2 per wave)
-constexpr int kPfKT = 64;          // keys per tile
+constexpr int kPfQ = 16;           // queries per workgroup (2 per wave)
+constexpr int kPfThreads = kPfQ * 32;
+constexpr int kPfKT = 128;         // keys per tile
 constexpr int kKeyBytes = kIdxDim * 2;
-constexpr int kPfSplit = 8192;     // keys per workgroup
+constexpr int kPfSplit = 16384;    // keys per workgroup
 
-__global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
+__global__ __launch_bounds__(kPfThreads, 512 / kPfThreads) void indexer_prefill_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
     const int64_t* __restrict__ seq_start, const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos,
     int n_q, float* __restrict__ scores, int64_t ld, int n_splits) {
   // Workgroups are dealt to the 8 XCDs round-robin (bid % 8).  Give each XCD a
   // contiguous run of the split-major work list, so the workgroups resident on
-  // one XCD share the same 2 MB key split in that XCD's L2.
+  // one XCD share the same 4 MB key split in that XCD's L2.
   const int n_wg = (int)gridDim.x;
   const int item = (n_wg & 7) ? (int)blockIdx.x : (int)(blockIdx.x & 7) * (n_wg >> 3) + (int)(blockIdx.x >> 3);
   const int n_qb = n_wg / n_splits;
@@ -280,12 +281,12 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
     // Key tiles go global -> registers -> LDS (double-buffered): the loads of
     // tile i + 1 are issued before the products of tile i and stored to LDS
     // after them.
-    constexpr int kPieces = kPfKT * kKeyBytes / 16 / 256;     // 16-byte pieces per thread
+    constexpr int kPieces = kPfKT * kKeyBytes / 16 / kPfThreads;     // 16-byte pieces per thread
     u32x4 ga[kPieces];
     auto load_tile = [&](u32x4 (&g)[kPieces], int tile) {
 #pragma unroll
       for (int j = 0; j < kPieces; ++j) {
-        const int flat = j * 256 + threadIdx.x;            // 16-byte piece within the tile
+        const int flat = j * kPfThreads + threadIdx.x;     // 16-byte piece within the tile
         // keys past the last needed one re-read that key (their scores are -inf)
         const int rkey = min(tile * kPfKT + (flat >> 4), rmax);
         g[j] = ld16(kseg + rkey * kIdxDim + (flat & 15) * 8);
@@ -294,7 +295,7 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
     auto store_tile = [&](const u32x4 (&g)[kPieces], int buf) {
 #pragma unroll
       for (int j = 0; j < kPieces; ++j) {
-        const int flat = j * 256 + threadIdx.x;
+        const int flat = j * kPfThreads + threadIdx.x;
         *reinterpret_cast<u32x4*>(lds[buf] + (flat >> 4) * kKeyPitch + (flat & 15) * 16) = g[j];
       }
     };
@@ -404,7 +405,7 @@ int32_t launch_indexer(const void* q_idx, const float* w, const void* k_idx, con
     set_error("indexer: grid of %lld workgroups is too large", (long long)grid);
     return SA_ERR_UNSUPPORTED;
   }
-  hipLaunchKernelGGL(sa::indexer_prefill_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+  hipLaunchKernelGGL(sa::indexer_prefill_kernel, dim3((unsigned)grid), dim3(sa::kPfThreads), 0, stream,
                      (const uint16_t*)q_idx, w, (const uint16_t*)k_idx, seq_start, q_seq, q_pos, n_q, scores, ld,
                      n_splits);
   return check_launch("indexer_prefill_kernel");
