@@ -33,8 +33,8 @@ BF16_PEAK_TFLOPS = 2500.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="c2", choices=["c0", "c1", "c2", "c4"])
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill indexer measurement")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
