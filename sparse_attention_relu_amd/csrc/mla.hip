@@ -13,7 +13,11 @@
 // time through one XCD's L2.  The slice is consumed in 32-row tiles by 4
 // score waves and 4 output waves working one tile apart:
 //   - the output waves gather each tile (36 KB) with 16-byte direct-to-LDS
-//     loads into a 3-buffer ring, so two tiles are in flight without registers;
+//     loads into a 3-buffer ring, so two tiles are in flight without registers.
+//     A tile buffer is latent-quarter-major, [4 quarters][32 rows][256 B] and
+//     then [32 rows][128 B] of rope, so output wave w refills exactly the
+//     quarter it reads and can issue the next gather as soon as its own reads
+//     of the old tile are done, while the score waves are still in QK^T;
 //   - score wave w computes the partial S^T[32 rows x 32 heads] = R . Q^T over
 //     dims 144w..144w+143 with v_mfma_f32_32x32x16_bf16 (R from LDS, Q^T in
 //     registers); after an exchange through LDS it runs the online softmax of
@@ -25,6 +29,9 @@
 //     are the contraction, the V^T operand is assembled from 8-byte row pieces
 //     with byte permutes (rows and dims are permuted consistently in both
 //     operands, no transpose through LDS), P^T comes from the score waves.
+// Within a quarter row (16 chunks of 16 bytes) chunk c of row r sits at slot
+// c ^ (r & 15), within a rope row (8 chunks) at slot c ^ ((r >> 1) & 7): the
+// 16 lanes of one operand read hit 16 different bank groups.
 // With one slice per query the workgroup normalises and writes the latent
 // average obar (bf16); with several, each writes its partial state and
 // mla_merge_kernel combines them.
@@ -39,8 +46,10 @@ namespace sa {
 
 constexpr int kAttnWaves = 4;
 constexpr int kTile = 32;                  // rows per tile
-constexpr int kRowBytes = kRow * 2;        // 1152: rows are stored unpadded in LDS ...
+constexpr int kRowBytes = kRow * 2;        // 1152
 constexpr int kTileBytes = kTile * kRowBytes;                     // 36,864
+constexpr int kQuarterBytes = kTile * 256;                        // one latent quarter (128 dims) of a tile
+constexpr int kRopeOff = 4 * kQuarterBytes;                       // the tile's rope block
 constexpr int kRing = 3;                   // LDS tile buffers (two tiles in flight)
 constexpr int kLoadsPerWave = kTileBytes / 1024 / kAttnWaves;    // 9 direct-to-LDS loads of 1 KB
 constexpr float kRescaleSlack = 8.0f;      // log2 units
@@ -50,10 +59,11 @@ constexpr int kCpolNt = 2;                 // cache-policy operand of global_loa
 __device__ __forceinline__ uint32_t perm_lo(uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x05040100u); }
 __device__ __forceinline__ uint32_t perm_hi(uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x07060302u); }
 
-// ... with the 16-byte chunks of row r permuted within groups of 8
-// (chunk c sits at position c ^ (r & 7)), so that 8 lanes reading the same
-// chunk of 8 consecutive rows hit 8 different LDS bank groups.
-__device__ __forceinline__ int lds_chunk_offset(int r, int c) { return r * kRowBytes + 16 * (c ^ (r & 7)); }
+// Byte offset in a tile buffer of 16-byte chunk c (0..71) of row r.
+__device__ __forceinline__ int tile_chunk_offset(int r, int c) {
+  return c < 64 ? (c >> 4) * kQuarterBytes + r * 256 + 16 * ((c & 15) ^ (r & 15))
+                : kRopeOff + r * 128 + 16 * ((c - 64) ^ ((r >> 1) & 7));
+}
 
 struct AttnArgs {
   const uint16_t* q_abs;
@@ -76,7 +86,7 @@ constexpr int kMaxSlice = 2048;
 constexpr int kHeadGroup = 32;             // heads per workgroup (two groups per query)
 constexpr size_t kRingBytes = (size_t)kRing * kTileBytes;                  // 110,592
 constexpr size_t kSBytes = 4 * 4 * 64 * 16;                               // partial S^T of each score wave
-constexpr size_t kPBytes = 2 * kHeadGroup * 8 * 8;                        // bf16 weights, double-buffered
+constexpr size_t kPBytes = 2 * kHeadGroup * 80;                           // bf16 weights, double-buffered, 80 B per head
 constexpr size_t kAlphaBytes = 2 * kHeadGroup * 4;                        // rescale factors
 constexpr size_t kFlagBytes = 2 * 4 * 4;
 constexpr size_t kMlBytes = kHeadGroup * 2 * 4;                           // (m, l) per head at the end
@@ -113,9 +123,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
 
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* ring = smem;
-  f32x4* slds = reinterpret_cast<f32x4*>(smem + kRingBytes);               // [4 waves][4 row groups][64]
+  // [4 waves][4 row groups][64 lanes, lane l at slot l ^ 2 (2 group + l / 32)]
+  f32x4* slds = reinterpret_cast<f32x4*>(smem + kRingBytes);
   uint8_t* sm2 = smem + kRingBytes + kSBytes;
-  u32x2* plds = reinterpret_cast<u32x2*>(sm2);                             // [2][32 heads][8 slots]
+  u32x2* plds = reinterpret_cast<u32x2*>(sm2);                             // [2][32 heads][10 slots, 8 used]
   float* alds = reinterpret_cast<float*>(sm2 + kPBytes);                   // [2][32 heads]
   int* flds = reinterpret_cast<int*>(sm2 + kPBytes + kAlphaBytes);         // [2][4 score waves]
   float* mlds = reinterpret_cast<float*>(sm2 + kPBytes + kAlphaBytes + kFlagBytes);          // [32][2]
@@ -165,10 +176,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
     store_positions();
     // The staged positions must be visible; the query loads stay in flight.
     lds_barrier();                                                     // B0
-    // R operand: row l32, 16-byte chunk 18w + 2s + hl, at its swizzled slot.
-    const int rbase = l32 * kRowBytes;
-    const int rsw = l32 & 7;
-    const int c0 = 18 * w + hl;
+    // R operand: row l32, 16-byte chunk 18w + 2s + hl.
+    int roff[9];
+#pragma unroll
+    for (int s = 0; s < 9; ++s) roff[s] = tile_chunk_offset(l32, 18 * w + 2 * s + hl);
     // Softmax ownership: this wave finishes heads 8w .. 8w + 7 of the group;
     // lane (hd, p) = (lane / 8, lane % 8) takes head 8w + hd and rows
     // 4p .. 4p + 3, i.e. elements 4 (p / 2) .. +3 of result column
@@ -190,20 +201,22 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
         u32x4 ra[9];            // all of this wave's row chunks of the tile, read up front
 #pragma unroll
         for (int s = 0; s < 9; ++s)
-          ra[s] = *reinterpret_cast<const u32x4*>(cur + rbase + 16 * ((c0 + 2 * s) ^ rsw));
+          ra[s] = *reinterpret_cast<const u32x4*>(cur + roff[s]);
         f32x16 acc = {};
 #pragma unroll
         for (int s = 0; s < 9; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ra[s]), qb[s], acc, 0, 0, 0);
 #pragma unroll
         for (int g = 0; g < 4; ++g)
-          slds[(w * 4 + g) * 64 + lane] = f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+          slds[(w * 4 + g) * 64 + (lane ^ (2 * (2 * g + hl)))] = f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
       }
       lds_barrier();                                                   // BAR_s
       if (active) {
         // full scores of this lane's 4 rows: sum of the 4 waves' partials
-        f32x4 s4 = slds[(0 * 4 + ig) * 64 + src_lane];
+        // (the swizzle puts the 16 lanes of a read on 16 bank groups)
+        const int src_sw = src_lane ^ (2 * pq);
+        f32x4 s4 = slds[(0 * 4 + ig) * 64 + src_sw];
 #pragma unroll
-        for (int w2 = 1; w2 < 4; ++w2) s4 += slds[(w2 * 4 + ig) * 64 + src_lane];
+        for (int w2 = 1; w2 < 4; ++w2) s4 += slds[(w2 * 4 + ig) * 64 + src_sw];
         // ---- online softmax of head hloc over rows jt + 4pq .. +3
         const u32x4 pos4 = *reinterpret_cast<const u32x4*>(spos + jt + 4 * pq);
         float x[4];
@@ -232,7 +245,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
           p[j] = fast_exp2(x[j] - m_use);
           l_run += p[j];
         }
-        plds[(pb_i * kHeadGroup + hloc) * 8 + p_slot(pq)] = u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+        plds[(pb_i * kHeadGroup + hloc) * 10 + p_slot(pq)] = u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
       }
       lds_barrier();                                                   // BAR_p
     }
@@ -262,18 +275,22 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
   // waves' weight slots 4ks + 2hl and +1 hold exactly these rows).  The V^T
   // operand of lane (m = l32, hl) takes 8 bytes (dims 4m .. 4m+3) of each of
   // its 8 rows and byte permutes form the four dim tiles mt.
-  // Direct-to-LDS gather of the tiles, issued by these waves: load u of wave w
-  // fills bytes (9w + u) KB of the tile buffer, 16 bytes per lane; the lane
-  // fetches the row chunk whose swizzled position is that slot.
+  // Direct-to-LDS gather of the tiles, issued by these waves, 16 bytes per
+  // lane: loads u < 8 of wave w fill quarter w of rows 4u .. 4u + 3 (1 KB),
+  // load 8 the rope of rows 8w .. 8w + 7; each lane fetches the row chunk
+  // whose swizzled slot it fills.
   const uint8_t* rows_b = reinterpret_cast<const uint8_t*>(A.kv + A.seq_start[A.q_seq[t]] * kRow);
   int lrow[kLoadsPerWave], lcol[kLoadsPerWave];
 #pragma unroll
-  for (int u = 0; u < kLoadsPerWave; ++u) {
-    const int f = (kLoadsPerWave * w + u) * 1024 + 16 * lane;
-    const int r = f / kRowBytes;
-    const int pslot = (f - r * kRowBytes) / 16;
+  for (int u = 0; u < 8; ++u) {
+    const int r = 4 * u + (lane >> 4);
     lrow[u] = r;
-    lcol[u] = 16 * (pslot ^ (r & 7));
+    lcol[u] = 16 * (16 * w + ((lane & 15) ^ (r & 15)));
+  }
+  {
+    const int r = 8 * w + (lane >> 3);
+    lrow[8] = r;
+    lcol[8] = 16 * (64 + ((lane & 7) ^ ((r >> 1) & 7)));
   }
   auto issue = [&](int tile) {
     const int jt = min(tile, max(n_tiles - 1, 0)) * kTile;
@@ -281,7 +298,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
     int pos[kLoadsPerWave];
 #pragma unroll
     for (int u = 0; u < kLoadsPerWave; ++u) pos[u] = spos[jt + lrow[u]];
-    uint8_t* b = ring + (tile % kRing) * kTileBytes + (kLoadsPerWave * w) * 1024;
+    uint8_t* b = ring + (tile % kRing) * kTileBytes;
 #pragma unroll
     for (int u = 0; u < kLoadsPerWave; ++u) {
       // padding entries read row 0; byte offsets within the sequence stay
@@ -290,17 +307,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
       // (-1.5 us per launch against the default policy).
       const int p = pos[u] >= 0 ? pos[u] : 0;
       const uint32_t off = (uint32_t)p * (uint32_t)kRowBytes + (uint32_t)lcol[u];
-      __builtin_amdgcn_global_load_lds((const void*)(rows_b + off),
-                                       (__attribute__((address_space(3))) void*)(b + 1024 * u), 16, 0, kCpolNt);
+      uint8_t* dst = b + (u < 8 ? w * kQuarterBytes + 1024 * u : kRopeOff + 1024 * w);
+      __builtin_amdgcn_global_load_lds((const void*)(rows_b + off), (__attribute__((address_space(3))) void*)dst, 16,
+                                       0, kCpolNt);
     }
   };
   // V^T operand: 8-byte read of row rho = 16ks + 8(e >> 2) + 4hl + (e & 3),
-  // dims 128w + 4 l32 .. +3 (chunk 16w + l32 / 2, half l32 & 1); rho & 7 is
-  // 4hl + (e & 3) for every ks and e >> 2.
-  int voff[4];
+  // dims 128w + 4 l32 .. +3 (chunk 16w + l32 / 2, half l32 & 1); rho & 15 is
+  // 8(e >> 2) + 4hl + (e & 3) for every ks.
+  int voff[8];
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-    voff[e] = (4 * hl + e) * kRowBytes + 16 * ((16 * w + (l32 >> 1)) ^ (4 * hl + e)) + 8 * (l32 & 1);
+  for (int e = 0; e < 8; ++e) voff[e] = tile_chunk_offset(8 * (e >> 2) + 4 * hl + (e & 3), 16 * w + (l32 >> 1)) + 8 * (l32 & 1);
   f32x16 o[4];                   // O^T tiles: dim tiles mt
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) o[mt] = f32x16{};
@@ -314,9 +331,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
   const int pw = l32 >> 3;
 #pragma unroll 1
   for (int step = 0; step <= n_tiles; ++step) {
-    // Operands of tile step - 1 are read before BAR_s (which frees its buffer
-    // for the gather of tile step + 2); its products run after BAR_s, beside
-    // the score waves' softmax.
+    // Operands of tile step - 1 are read before BAR_s; its products run after
+    // BAR_s, beside the score waves' softmax.  Once this wave's reads have
+    // returned, its quarter (and its rope rows) of that buffer are dead: the
+    // score waves finished tile step - 1 before the previous BAR_s and no other
+    // output wave reads this quarter.  So the gather of tile step + 2 into it
+    // is issued here, while the score waves are still in QK^T of tile step.
     const bool pv_step = step > 0;
     const int tile = step - 1;
     const int pb_i = tile & 1;
@@ -330,15 +350,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          v[ks][e] = *reinterpret_cast<const u32x2*>(cur + (16 * ks + 8 * (e >> 2)) * kRowBytes + voff[e & 3]);
+          v[ks][e] = *reinterpret_cast<const u32x2*>(cur + 16 * ks * 256 + voff[e]);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
-        pt[ks] = *reinterpret_cast<const u32x4*>(plds + (pb_i * kHeadGroup + l32) * 8 + 4 * ks + 2 * hl);
+        pt[ks] = *reinterpret_cast<const u32x4*>(plds + (pb_i * kHeadGroup + l32) * 10 + 4 * ks + 2 * hl);
       fl = flds[pb_i * 4 + pw];
       al = alds[pb_i * kHeadGroup + l32];          // meaningful only where the flag is set
     }
+    if (step < n_tiles) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue(step + 2);
+    }
     lds_barrier();                                                     // BAR_s
-    if (step < n_tiles) issue(step + 2);
     if (pv_step) {
       if (__any(fl)) {
         const float sc = fl ? al : 1.f;
