@@ -40,6 +40,7 @@ constexpr int kFinThreads = 1024;
 constexpr int kLdsCand = 8192;         // candidates staged in LDS by the finish kernel
 constexpr int kFinBins = 2048;         // 11-bit digits in the finish kernel
 constexpr int kBitmapBits = 1 << 18;   // rows up to this length are emitted in order from an LDS bitmap
+static_assert(kMaxTopk % kFinThreads == 0, "the finish kernel loads the kept positions in whole rounds");
 
 // ----------------------------------------------------------------- path 1
 __global__ void topk_zero_kernel(uint32_t* __restrict__ a, int64_t n_a, int32_t* __restrict__ b, int64_t n_b) {
@@ -282,7 +283,7 @@ __device__ void emit_bitmap(const uint32_t* bm, int n_words, int32_t* __restrict
     while (bits) {
       const int b = __ffs(bits) - 1;
       bits &= bits - 1;
-      if (slot < k) out[slot] = (i << 5) + b;
+      if (slot >= 0 && slot < k) out[slot] = (i << 5) + b;
       ++slot;
     }
   }
@@ -323,17 +324,30 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
   const int32_t* sel = ws.sel + (int64_t)t * kMaxTopk;
   const uint64_t* gcand = ws.cand + (int64_t)t * ws.cap;
   const int n_words = (int)((n_t + 31) >> 5);
+  // The kept positions (n_above < kMaxTopk = 2 x kFinThreads) are loaded
+  // beside the candidates, in one round trip.
+  int sv[kMaxTopk / kFinThreads];
+#pragma unroll
+  for (int u = 0; u < kMaxTopk / kFinThreads; ++u) {
+    const int i = (int)threadIdx.x + kFinThreads * u;
+    sv[u] = i < n_above ? sel[i] : -1;
+  }
   if (ordered_by_bitmap) {
     for (int i = threadIdx.x; i < n_words; i += kFinThreads) bm[i] = 0u;
   } else {
-    for (int i = threadIdx.x; i < n_above; i += kFinThreads) v[i] = sel[i];
+#pragma unroll
+    for (int u = 0; u < kMaxTopk / kFinThreads; ++u) {
+      const int i = (int)threadIdx.x + kFinThreads * u;
+      if (i < n_above) v[i] = sv[u];
+    }
   }
   if (in_lds)
     for (int i = threadIdx.x; i < n_cand; i += kFinThreads) lc[i] = gcand[i];
   __syncthreads();
   if (ordered_by_bitmap)
-    for (int i = threadIdx.x; i < n_above; i += kFinThreads) {
-      const int s = sel[i];
+#pragma unroll
+    for (int u = 0; u < kMaxTopk / kFinThreads; ++u) {
+      const int s = sv[u];
       if (s >= 0 && s < n_t) atomicOr(&bm[s >> 5], 1u << (s & 31));
     }
   const uint64_t* cand = in_lds ? lc : gcand;

@@ -19,25 +19,31 @@ struct TopkWs {
   int64_t cap;
 };
 
+// Inclusive scan over the 64 lanes of a wave in registers (DPP, no LDS round
+// trip): prefix sums within each row of 16 lanes (row_shr 1, 2, 4, 8; lanes
+// without a source add 0), then lane 15 of rows 0 and 2 is added to rows 1 and
+// 3 (row_bcast:15), then lane 31 to rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);
+  return v;
+}
+
 // Inclusive scan over a workgroup of NT threads (NT a multiple of 64).
 // *total receives the workgroup sum.  sh_wave needs NT/64 ints.
 template <int NT>
 __device__ __forceinline__ int block_inclusive_scan(int v, int* sh_wave, int* total = nullptr) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(v, o, 64);
-    if (lane >= o) v += u;
-  }
+  v = wave_inclusive_scan(v);
   if (lane == 63) sh_wave[wave] = v;
   __syncthreads();
   if (wave == 0) {
     int x = lane < NT / 64 ? sh_wave[lane] : 0;
-#pragma unroll
-    for (int o = 1; o < NT / 64; o <<= 1) {
-      const int u = __shfl_up(x, o, 64);
-      if (lane >= o) x += u;
-    }
+    x = wave_inclusive_scan(x);
     if (lane < NT / 64) sh_wave[lane] = x;
   }
   __syncthreads();
