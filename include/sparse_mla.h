@@ -227,7 +227,9 @@ int32_t sa_layer_is_full(int32_t layer);
  * Variants that pin an internal algorithm, for tests and measurements.
  * algo 0 = automatic (what the entry points above use).
  *   indexer: 1 = one query per workgroup (streams keys once per query),
- *            2 = query blocks sharing key tiles (MFMA over queries x heads).
+ *            2 = query blocks sharing key tiles (MFMA over queries x heads);
+ *            automatic picks 2 when n_q >= 64 and n_q >= 16 * n_seq (at least
+ *            16 queries per sequence on average), else 1.
  *   topk:    1 = rows split over many workgroups with candidate compaction,
  *            2 = one workgroup per row, full radix passes (the exact fallback).
  * Returns SA_ERR_INVALID_ARG for an unknown algo.

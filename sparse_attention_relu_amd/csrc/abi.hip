@@ -28,10 +28,10 @@ int32_t check_launch(const char* what) {
   return SA_OK;
 }
 
-int indexer_algo(int32_t n_q, int algo);
+int indexer_algo(int32_t n_q, int32_t n_seq, int algo);
 int32_t launch_indexer(const void* q_idx, const float* w, const void* k_idx, const int64_t* seq_start,
-                       const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, float* scores, int64_t ld, int algo,
-                       hipStream_t stream, uint32_t* clear, int64_t n_clear);
+                       const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, int32_t n_seq, float* scores,
+                       int64_t ld, int algo, hipStream_t stream, uint32_t* clear, int64_t n_clear);
 void topk_clear_range(void* ws, int32_t n_q, int64_t ld, uint32_t** p, int64_t* n);
 
 size_t topk_workspace_size(int32_t n_q, int64_t ld, int32_t k);
@@ -131,8 +131,8 @@ int32_t sa_indexer_score_algo(const void* q_idx, const float* w, const void* k_i
   if (rc) return rc;
   SA_REQUIRE(algo >= 0 && algo <= 2, SA_ERR_INVALID_ARG, "indexer: unknown algo %d", algo);
   if (n_q == 0) return SA_OK;
-  return launch_indexer(q_idx, w, k_idx, seq_start, q_seq, q_pos, n_q, scores, ld, algo, (hipStream_t)stream, nullptr,
-                        0);
+  return launch_indexer(q_idx, w, k_idx, seq_start, q_seq, q_pos, n_q, n_seq, scores, ld, algo, (hipStream_t)stream,
+                        nullptr, 0);
 }
 
 int32_t sa_indexer_score(const void* q_idx, const float* w, const void* k_idx, const int64_t* seq_start,
@@ -230,12 +230,12 @@ int32_t sa_layer_stack(const sa_layer_desc* layers, int32_t n_layers, const sa_b
   const int32_t* cur_idx = nullptr;
   bool rec_idx = false, rec_topk = false, rec_attn = false;
   int32_t rc;
-  // Decode batches (n_q < 64) score one query per workgroup column, larger
-  // batches use the query-blocked indexer; the top-k then runs its own
-  // first-digit histogram pass over the scores.  The decode indexer also
-  // clears the top-k's histograms and counters on the side, which saves the
-  // top-k a launch of its own for that.
-  const int ialgo = indexer_algo(n_q, 0);
+  // Decode batches score one query per workgroup column; batches with at
+  // least 16 queries per sequence (chunked prefill) use the query-blocked
+  // indexer.  The top-k then runs its own first-digit histogram pass over the
+  // scores.  The decode indexer also clears the top-k's histograms and
+  // counters on the side, which saves the top-k a launch of its own for that.
+  const int ialgo = indexer_algo(n_q, batch->n_seq, 0);
   uint32_t* clear = nullptr;
   int64_t n_clear = 0;
   if (ialgo == 1) topk_clear_range(topk_ws, n_q, ld, &clear, &n_clear);
@@ -244,8 +244,8 @@ int32_t sa_layer_stack(const sa_layer_desc* layers, int32_t n_layers, const sa_b
     if (L.is_full) {
       const bool ev = events && !rec_idx && events->indexer_begin && events->indexer_end;
       if (ev && (rc = record(events->indexer_begin, st))) return rc;
-      rc = launch_indexer(L.q_idx, L.w, L.k_idx, batch->seq_start, batch->q_seq, batch->q_pos, n_q, scores, ld, ialgo,
-                          st, clear, n_clear);
+      rc = launch_indexer(L.q_idx, L.w, L.k_idx, batch->seq_start, batch->q_seq, batch->q_pos, n_q, batch->n_seq, scores,
+                          ld, ialgo, st, clear, n_clear);
       if (rc) return rc;
       if (ev && (rc = record(events->indexer_end, st))) return rc;
       rec_idx |= ev;

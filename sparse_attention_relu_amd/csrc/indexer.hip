@@ -374,14 +374,22 @@ __global__ __launch_bounds__(kPfThreads, 512 / kPfThreads) void indexer_prefill_
 // ------------------------------------------------------------------ launchers
 namespace sa_host {
 
-int indexer_algo(int32_t n_q, int algo) { return algo != 0 ? algo : (n_q >= 64 ? 2 : 1); }
+// Automatic choice: the query-blocked kernel pays off only when its 16-query
+// blocks share a sequence, i.e. when the batch holds at least 16 queries per
+// sequence on average (chunked prefill); batches of decode queries, one or a
+// few per sequence, stream each query's keys (64 queries of 64 sequences run
+// 80x faster that way than as 16-sequence blocks).
+int indexer_algo(int32_t n_q, int32_t n_seq, int algo) {
+  if (algo != 0) return algo;
+  return (n_q >= 64 && (int64_t)n_q >= 16 * (int64_t)(n_seq > 0 ? n_seq : 1)) ? 2 : 1;
+}
 
 // clear / n_clear: words the decode kernel (algo 1) sets to zero on the side;
 // the caller passes none with algo 2.
 int32_t launch_indexer(const void* q_idx, const float* w, const void* k_idx, const int64_t* seq_start,
-                       const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, float* scores, int64_t ld, int algo,
-                       hipStream_t stream, uint32_t* clear, int64_t n_clear) {
-  algo = indexer_algo(n_q, algo);
+                       const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, int32_t n_seq, float* scores,
+                       int64_t ld, int algo, hipStream_t stream, uint32_t* clear, int64_t n_clear) {
+  algo = indexer_algo(n_q, n_seq, algo);
   if (algo != 1 && n_clear > 0) {
     set_error("indexer: only the decode kernel clears words on the side");
     return SA_ERR_INVALID_ARG;
