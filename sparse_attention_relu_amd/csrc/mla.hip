@@ -34,7 +34,8 @@
 // 16 lanes of one operand read hit 16 different bank groups.
 // With one slice per query the workgroup normalises and writes the latent
 // average obar (bf16); with several, each writes its partial state and
-// mla_merge_kernel combines them.
+// mla_merge_kernel (up to 8 slices) or mla_merge_wide_kernel (more slices,
+// i.e. few queries) combines them.
 // mla_wuv_kernel: one workgroup per (head, 64 value rows) holds that 64 x 512
 // slice of W_UV in registers and multiplies it with obar^T, 16 queries per
 // v_mfma_f32_16x16x32_bf16 column block, rounding the output to bf16.
@@ -492,6 +493,98 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(AttnArgs A) {
     A.lse[(int64_t)t * kHeads + head] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
+// The same merge for more than 8 slices (few queries): work item
+// qb = ((hg * 4 + w) * 2 + mp) * 4 + a of a query, the same dims per lane as
+// above; G = 2 or 4 waves split an item's slices, at most 8 each (one round
+// trip), and their partial merges are combined through LDS, so one query's 32
+// slices take one round trip over 64 workgroups instead of four over 16.
+constexpr int kMergeWaves = 4;
+static_assert(kMergeBatch * kMergeWaves >= kMaxSp, "a workgroup's waves cover every slice");
+
+__host__ __device__ inline int merge_groups(int n_sp) { return n_sp <= 2 * kMergeBatch ? 2 : 4; }
+
+__global__ __launch_bounds__(kMergeWaves * 64) void mla_merge_wide_kernel(AttnArgs A) {
+  const int n_sp = A.n_sp;
+  const int G = merge_groups(n_sp);
+  const int n_wg = (int)gridDim.x;
+  const int item = (n_wg & 7) ? (int)blockIdx.x : (int)(blockIdx.x & 7) * (n_wg >> 3) + (int)(blockIdx.x >> 3);
+  const int t = item / (16 * G);
+  const int j = item - t * 16 * G;
+  const int g = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int qb = j * (kMergeWaves / G) + g / G;   // this wave's item
+  const int sg = g % G;                           // and its share of the slices
+  const int hg = qb >> 5, w = (qb >> 3) & 3, mp = (qb >> 2) & 1, a = qb & 3;
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int head = kHeadGroup * hg + l32;
+  const int per = (n_sp + G - 1) / G;
+  const int s_lo = sg * per, s_hi = min(n_sp, s_lo + per);
+  // slice s adds s * 2 * 4 * 1024; tile mt + 1 adds 4 * 64
+  const f32x4* src = reinterpret_cast<const f32x4*>(A.part_o) + (((int64_t)t * n_sp * 2 + hg) * 4 + w) * 1024 +
+                     (2 * mp * 4 + a) * 64 + lane;
+  const float2* mlp = reinterpret_cast<const float2*>(A.part_ml) + (int64_t)t * n_sp * kHeads + head;
+  f32x4 v0[kMergeBatch], v1[kMergeBatch];
+  float2 ml[kMergeBatch];
+#pragma unroll
+  for (int u = 0; u < kMergeBatch; ++u) {
+    const int s = min(s_lo + u, n_sp - 1);
+    ml[u] = mlp[(int64_t)s * kHeads];
+    v0[u] = src[(int64_t)s * 8192];
+    v1[u] = src[(int64_t)s * 8192 + 256];
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kMergeBatch; ++u)
+    if (s_lo + u < s_hi) M = fmaxf(M, ml[u].x);
+  float L = 0.f;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < kMergeBatch; ++u) {
+    const float wt = (s_lo + u < s_hi && ml[u].x != -INFINITY) ? fast_exp2(ml[u].x - M) : 0.f;
+    L = fmaf(wt, ml[u].y, L);
+    acc0 += wt * v0[u];
+    acc1 += wt * v1[u];
+  }
+  {
+    // combine the G waves of an item: [wave][field][lane]
+    __shared__ float part[kMergeWaves][10][64];
+    part[g][0][lane] = M;
+    part[g][1][lane] = L;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      part[g][2 + b][lane] = acc0[b];
+      part[g][6 + b][lane] = acc1[b];
+    }
+    __syncthreads();
+    if (sg != 0) return;
+    float Mt = -INFINITY;
+    for (int q = g; q < g + G; ++q) Mt = fmaxf(Mt, part[q][0][lane]);
+    float Lt = 0.f;
+    f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+    for (int q = g; q < g + G; ++q) {
+      const float mq = part[q][0][lane];
+      const float c = mq != -INFINITY ? fast_exp2(mq - Mt) : 0.f;   // waves without slices have M = -inf
+      Lt = fmaf(c, part[q][1][lane], Lt);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        o0[b] = fmaf(c, part[q][2 + b][lane], o0[b]);
+        o1[b] = fmaf(c, part[q][6 + b][lane], o1[b]);
+      }
+    }
+    M = Mt;
+    L = Lt;
+    acc0 = o0;
+    acc1 = o1;
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  // acc0[b] is dim 128w + 32a + 16hl + 4b + 2mp, acc1[b] the next dim
+  uint16_t* ob = A.obar + ((int64_t)t * kHeads + head) * kLatent + 128 * w + 32 * a + 16 * hl + 2 * mp;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+    *reinterpret_cast<uint32_t*>(ob + 4 * b) = pack_bf16x2(acc0[b] * inv, acc1[b] * inv);
+  if (A.lse && w == 0 && mp == 0 && a == 0 && hl == 0)
+    A.lse[(int64_t)t * kHeads + head] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
+}
+
 // ------------------------------------------------------------------ W_UV
 struct WuvArgs {
   const uint16_t* obar;     // [n_q][64][512] bf16
@@ -652,7 +745,9 @@ int32_t launch_mla(const void* q_abs, const void* kv, const int64_t* seq_start, 
     g_attr_set.fetch_or(bit);
   }
   const int64_t grid = (int64_t)n_q * n_sp * 2;
-  if (grid > 0x7fffffff) {
+  const bool wide = n_sp > sa::kMergeBatch;
+  const int64_t merge_grid = (int64_t)n_q * 16 * (wide ? sa::merge_groups(n_sp) : 1);
+  if (grid > 0x7fffffff || merge_grid > 0x7fffffff) {
     set_error("mla: grid too large");
     return SA_ERR_UNSUPPORTED;
   }
@@ -660,8 +755,11 @@ int32_t launch_mla(const void* q_abs, const void* kv, const int64_t* seq_start, 
   int32_t rc = check_launch("mla_attn_kernel");
   if (rc) return rc;
   if (n_sp > 1) {
-    hipLaunchKernelGGL(sa::mla_merge_kernel, dim3((unsigned)(n_q * 16)), dim3(256), 0, stream, A);
-    if ((rc = check_launch("mla_merge_kernel"))) return rc;
+    if (wide)
+      hipLaunchKernelGGL(sa::mla_merge_wide_kernel, dim3((unsigned)merge_grid), dim3(sa::kMergeWaves * 64), 0, stream, A);
+    else
+      hipLaunchKernelGGL(sa::mla_merge_kernel, dim3((unsigned)merge_grid), dim3(256), 0, stream, A);
+    if ((rc = check_launch(wide ? "mla_merge_wide_kernel" : "mla_merge_kernel"))) return rc;
   }
   sa::WuvArgs W{m.obar, (const uint16_t*)w_uv, (uint16_t*)out, n_q};
   hipLaunchKernelGGL(sa::mla_wuv_kernel, dim3(sa::kHeads * 4), dim3(256), sa::kWuvSmem, stream, W);
