@@ -115,6 +115,24 @@ def test_mla_on_gpu_selection(gpu_lib, case):
     print(f"{case}: worst |err|/bound = {worst:.3g}")
 
 
+@pytest.mark.parametrize("n_q", [3, 5, 10])
+def test_mla_slice_counts(gpu_lib, n_q):
+    # about 128 / n_q slices per query: 32, 26 and 13, i.e. the merge with 4
+    # waves per item (even and uneven slice shares) and with 2 waves (uneven)
+    lens = [4096, 3000, 2500]
+    queries = [(i % 3, lens[i % 3] - 1 - 7 * i) for i in range(n_q)]
+    wl = synth.ragged_workload(lens, queries, name=f"slices{n_q}")
+    b = _batch(wl, seed=11 + n_q)
+    L = b.layers[0]
+    sc = api.indexer_score(L.q_idx, L.w, L.k_idx, b.seq_start, b.q_seq, b.q_pos, wl.ld)
+    idx = api.topk_select(sc, b.q_pos, k=2048)
+    lse = torch.empty((wl.n_q, 64), dtype=torch.float32, device=DEV)
+    out = api.mla_sparse_attn(L.q_abs, L.kv, b.seq_start, b.q_seq, idx, L.w_uv, wl.scale, lse=lse)
+    torch.cuda.synchronize()
+    parity.check_mla(parity.layer_np(L), parity.np_batch(b), to_numpy(idx), to_numpy(out), wl.scale,
+                     lse_gpu=to_numpy(lse))
+
+
 @pytest.mark.parametrize("k", [1, 7, 64, 300])
 def test_mla_small_k_and_padding(gpu_lib, k):
     wl = ragged_wl(k=k)
