@@ -457,12 +457,19 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(AttnArgs A) {
   for (int s0 = 0; s0 < n_sp; s0 += kMergeBatch) {
     f32x4 v0[kMergeBatch], v1[kMergeBatch];
     float2 ml[kMergeBatch];
+    // slices past n_sp are not loaded (a uniform branch): clamped re-reads
+    // would pass 4x the bytes through the load path at 2 slices
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
-      const int s = min(s0 + u, n_sp - 1);
-      ml[u] = mlp[(int64_t)s * kHeads];
-      v0[u] = src[(int64_t)s * 8192];
-      v1[u] = src[(int64_t)s * 8192 + 256];
+      ml[u] = float2{-INFINITY, 0.f};
+      v0[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      v1[u] = v0[u];
+      if (s0 + u < n_sp) {
+        const int s = s0 + u;
+        ml[u] = mlp[(int64_t)s * kHeads];
+        v0[u] = src[(int64_t)s * 8192];
+        v1[u] = src[(int64_t)s * 8192 + 256];
+      }
     }
     float mb = M;
 #pragma unroll
