@@ -77,7 +77,7 @@ struct AttnArgs {
   int n_sp;
   int kps;               // selection entries per slice (multiple of kTile)
   float scale_log2;      // scale * log2(e)
-  float* part_o;         // [n_q][n_sp][64][512]   (n_sp > 1)
+  float* part_o;         // [n_q][n_sp] blocks of 64 x 512 fp32 in register-tile order (n_sp > 1)
   float* part_ml;        // [n_q][n_sp][64][2]     (max in log2 units, sum)
   uint16_t* obar;        // [n_q][64][512] bf16 latent average
   float* lse;            // [n_q][64] or null
