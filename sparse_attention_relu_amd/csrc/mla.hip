@@ -394,6 +394,21 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
     if (step < n_tiles) SA_WAIT_VMCNT(kLoadsPerWave);
     lds_barrier();                                                     // BAR_p
   }
+  // Partial accumulators in register-tile order: [t][sp][hg][w][mt][a][lane]
+  // x 4 values (b = 0..3), so every store instruction writes 1 KB contiguously.
+  // Streaming stores: the partials go out as they are written instead of
+  // being written back from L2 when the kernel ends (-1 us per launch).  They
+  // need no (m, l), so they are issued before BAR_end, beside the score waves'
+  // last softmax.
+  if (A.n_sp > 1) {
+    f32x4* po = reinterpret_cast<f32x4*>(A.part_o) + ((((int64_t)t * A.n_sp + sp) * 2 + hg) * 4 + w) * 16 * 64;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        __builtin_nontemporal_store(f32x4{o[mt][4 * a], o[mt][4 * a + 1], o[mt][4 * a + 2], o[mt][4 * a + 3]},
+                                    &po[(mt * 4 + a) * 64 + lane]);
+  }
   __builtin_amdgcn_s_waitcnt(0);         // the trailing (clamped) tile loads land before the workgroup ends
   lds_barrier();                                                       // BAR_end: (m, l) of every head
   // Result element 4a + b of tile mt is dim 128w + 32a + 16hl + 4b + mt of
@@ -413,19 +428,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
         *reinterpret_cast<u32x4*>(ob + 32 * a + 8 * bh) = pk;
       }
     }
-    return;
   }
-  // Partial accumulators in register-tile order: [t][sp][hg][w][mt][a][lane]
-  // x 4 values (b = 0..3), so every store instruction writes 1 KB contiguously.
-  // Streaming stores: the partials go out as they are written instead of
-  // being written back from L2 when the kernel ends (-1 us per launch).
-  f32x4* po = reinterpret_cast<f32x4*>(A.part_o) + ((((int64_t)t * A.n_sp + sp) * 2 + hg) * 4 + w) * 16 * 64;
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-      __builtin_nontemporal_store(f32x4{o[mt][4 * a], o[mt][4 * a + 1], o[mt][4 * a + 2], o[mt][4 * a + 3]},
-                                  &po[(mt * 4 + a) * 64 + lane]);
 }
 
 // Merge of the slices' partial softmax states: obar = sum_s a_s O_s / sum_s a_s l_s
