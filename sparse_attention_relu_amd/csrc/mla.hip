@@ -8,10 +8,13 @@
 //     z_j = scale * q_abs[t, h] . R_j,  obar = softmax(z) @ R[:, :512],
 //     out[t, h] = bf16(W_UV[h] @ obar).
 //
-// mla_attn_kernel: one workgroup per (query, slice of the selection, group of
-// 32 heads); the two head groups of a slice gather the same rows at the same
-// time through one XCD's L2.  The slice is consumed in 32-row tiles by 4
-// score waves and 4 output waves working one tile apart:
+// mla_attn_kernel: for decode batches below 64 queries one workgroup per
+// (query, slice of the selection, group of 32 heads), the two head groups of a
+// slice gathering the same rows at the same time through one XCD's L2; from
+// 64 queries on one workgroup per (query, slice) for both groups, which share
+// every gathered tile (the same code with two head blocks).  The slice is
+// consumed in 32-row tiles by 4 score waves and 4 output waves working one tile
+// apart:
 //   - the output waves gather each tile (36 KB) with 16-byte direct-to-LDS
 //     loads into a 3-buffer ring, so two tiles are in flight without registers.
 //     A tile buffer is latent-quarter-major, [4 quarters][32 rows][256 B] and
@@ -84,14 +87,20 @@ struct AttnArgs {
 };
 
 constexpr int kMaxSlice = 2048;
-constexpr int kHeadGroup = 32;             // heads per workgroup (two groups per query)
+constexpr int kHeadGroup = 32;             // heads per block (two blocks per query)
 constexpr size_t kRingBytes = (size_t)kRing * kTileBytes;                  // 110,592
+// per block of 32 heads:
 constexpr size_t kSBytes = 4 * 4 * 64 * 16;                               // partial S^T of each score wave
 constexpr size_t kPBytes = 2 * kHeadGroup * 80;                           // bf16 weights, double-buffered, 80 B per head
 constexpr size_t kAlphaBytes = 2 * kHeadGroup * 4;                        // rescale factors
-constexpr size_t kFlagBytes = 2 * 4 * 4;
 constexpr size_t kMlBytes = kHeadGroup * 2 * 4;                           // (m, l) per head at the end
-constexpr size_t kAttnSmem = kRingBytes + kSBytes + kPBytes + kAlphaBytes + kFlagBytes + kMlBytes + kMaxSlice * 4;
+constexpr size_t kFlagBytes = 2 * 4 * 4;
+// LDS of a workgroup with NB blocks of 32 heads (NB = 2: 162,848 bytes)
+template <int NB>
+constexpr size_t attn_smem() {
+  return kRingBytes + NB * (kSBytes + kPBytes + kAlphaBytes + kMlBytes) + kFlagBytes + kMaxSlice * 4;
+}
+static_assert(attn_smem<2>() <= 160 * 1024, "two head blocks fit the LDS of a CU");
 constexpr int kAttnThreads = 512;          // 4 score waves + 4 output waves
 
 // Slot of the 4-row group p (rows 4p..4p+3) in a head's weight entry: the
@@ -108,15 +117,21 @@ __device__ __forceinline__ float reduce8(float x, Op op) {
   return x;
 }
 
+// NB = 1: one workgroup per (query, slice, group of 32 heads); NB = 2: one per
+// (query, slice) for all 64 heads, the two blocks of 32 heads sharing every
+// gathered tile (half the gathers and steps per head, twice the products per
+// step).  Head block blk of a workgroup is head group hg + blk.
+template <int NB>
 __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
   // Workgroups are dealt to the 8 XCDs round-robin (bid % 8): give each XCD a
   // contiguous run of (query, slice, head group) items, so the two head
   // groups of a slice gather the same rows through one L2 at the same time.
   const int n_wg = (int)gridDim.x;
   const int item = (n_wg & 7) ? (int)blockIdx.x : (int)(blockIdx.x & 7) * (n_wg >> 3) + (int)(blockIdx.x >> 3);
-  const int hg = item & 1;
-  const int t = (item >> 1) / A.n_sp;
-  const int sp = (item >> 1) - t * A.n_sp;
+  const int hg = NB == 1 ? (item & 1) : 0;
+  const int ts = NB == 1 ? (item >> 1) : item;
+  const int t = ts / A.n_sp;
+  const int sp = ts - t * A.n_sp;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int w = wave & 3;                       // dim quarter of QK (score waves) / latent quarter (output waves)
@@ -124,14 +139,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
 
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* ring = smem;
-  // [4 waves][4 row groups][64 lanes, lane l at slot l ^ 2 (2 group + l / 32)]
+  // [NB][4 waves][4 row groups][64 lanes, lane l at slot l ^ 2 (2 group + l / 32)]
   f32x4* slds = reinterpret_cast<f32x4*>(smem + kRingBytes);
-  uint8_t* sm2 = smem + kRingBytes + kSBytes;
-  u32x2* plds = reinterpret_cast<u32x2*>(sm2);                             // [2][32 heads][10 slots, 8 used]
-  float* alds = reinterpret_cast<float*>(sm2 + kPBytes);                   // [2][32 heads]
-  int* flds = reinterpret_cast<int*>(sm2 + kPBytes + kAlphaBytes);         // [2][4 score waves]
-  float* mlds = reinterpret_cast<float*>(sm2 + kPBytes + kAlphaBytes + kFlagBytes);          // [32][2]
-  int32_t* spos = reinterpret_cast<int32_t*>(sm2 + kPBytes + kAlphaBytes + kFlagBytes + kMlBytes);
+  uint8_t* sm2 = smem + kRingBytes + NB * kSBytes;
+  u32x2* plds = reinterpret_cast<u32x2*>(sm2);                             // [2][NB * 32 heads][10 slots, 8 used]
+  float* alds = reinterpret_cast<float*>(sm2 + NB * kPBytes);              // [2][NB * 32 heads]
+  int* flds = reinterpret_cast<int*>(sm2 + NB * (kPBytes + kAlphaBytes));  // [2][4 score waves]
+  float* mlds = reinterpret_cast<float*>(sm2 + NB * (kPBytes + kAlphaBytes) + kFlagBytes);   // [NB * 32][2]
+  int32_t* spos = reinterpret_cast<int32_t*>(sm2 + NB * (kPBytes + kAlphaBytes + kMlBytes) + kFlagBytes);
 
   const int j0 = sp * A.kps;
   const int j1 = min(A.k, j0 + A.kps);
@@ -168,11 +183,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
     // S^T[32 rows x 32 heads] is split over the 576 dims: wave w takes dims
     // 144w .. 144w + 143 (9 steps of 16).  Q operand: head 32hg + l32, dims
     // 144w + 16s + 8hl .. +8.
-    bf16x8 qb[9];
-    {
-      const uint16_t* qp = A.q_abs + ((int64_t)t * kHeads + kHeadGroup * hg + l32) * kRow + 144 * w + 8 * hl;
+    bf16x8 qb[NB][9];
 #pragma unroll
-      for (int s = 0; s < 9; ++s) qb[s] = as_bf16x8(ld16(qp + 16 * s));
+    for (int blk = 0; blk < NB; ++blk) {
+      const uint16_t* qp = A.q_abs + ((int64_t)t * kHeads + kHeadGroup * (hg + blk) + l32) * kRow + 144 * w + 8 * hl;
+#pragma unroll
+      for (int s = 0; s < 9; ++s) qb[blk][s] = as_bf16x8(ld16(qp + 16 * s));
     }
     store_positions();
     // The staged positions must be visible; the query loads stay in flight.
@@ -189,7 +205,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
     const int hloc = 8 * w + hd;
     const int src_lane = hloc + 32 * (pq & 1);
     const int ig = pq >> 1;
-    float m_run = -INFINITY, l_run = 0.f;     // softmax state of head hloc (lane-partial sum)
+    float m_run[NB], l_run[NB];               // softmax state of head hloc of each block (lane-partial sum)
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      m_run[blk] = -INFINITY;
+      l_run[blk] = 0.f;
+    }
     lds_barrier();                                                     // B1: tile 0 staged
 #pragma unroll 1
     for (int tile = 0; tile <= n_tiles; ++tile) {
@@ -203,66 +224,90 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
 #pragma unroll
         for (int s = 0; s < 9; ++s)
           ra[s] = *reinterpret_cast<const u32x4*>(cur + roff[s]);
-        f32x16 acc = {};
 #pragma unroll
-        for (int s = 0; s < 9; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ra[s]), qb[s], acc, 0, 0, 0);
+        for (int blk = 0; blk < NB; ++blk) {
+          f32x16 acc = {};
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          slds[(w * 4 + g) * 64 + (lane ^ (2 * (2 * g + hl)))] = f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+          for (int s = 0; s < 9; ++s)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ra[s]), qb[blk][s], acc, 0, 0, 0);
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            slds[((blk * 4 + w) * 4 + g) * 64 + (lane ^ (2 * (2 * g + hl)))] =
+                f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+        }
       }
       lds_barrier();                                                   // BAR_s
       if (active) {
         // full scores of this lane's 4 rows: sum of the 4 waves' partials
         // (the swizzle puts the 16 lanes of a read on 16 bank groups)
         const int src_sw = src_lane ^ (2 * pq);
-        f32x4 s4 = slds[(0 * 4 + ig) * 64 + src_sw];
-#pragma unroll
-        for (int w2 = 1; w2 < 4; ++w2) s4 += slds[(w2 * 4 + ig) * 64 + src_sw];
-        // ---- online softmax of head hloc over rows jt + 4pq .. +3
         const u32x4 pos4 = *reinterpret_cast<const u32x4*>(spos + jt + 4 * pq);
-        float x[4];
-        float tmax = -INFINITY;
+        float x[NB][4];
+        float tmax[NB];
+        bool bump[NB];
+        bool bump_any = false;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          x[j] = (int)pos4[j] >= 0 ? s4[j] * A.scale_log2 : -INFINITY;
-          tmax = fmaxf(tmax, x[j]);
+        for (int blk = 0; blk < NB; ++blk) {
+          f32x4 s4 = slds[((blk * 4 + 0) * 4 + ig) * 64 + src_sw];
+#pragma unroll
+          for (int w2 = 1; w2 < 4; ++w2) s4 += slds[((blk * 4 + w2) * 4 + ig) * 64 + src_sw];
+          // ---- online softmax of head hloc of the block over rows jt + 4pq .. +3
+          tmax[blk] = -INFINITY;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            x[blk][j] = (int)pos4[j] >= 0 ? s4[j] * A.scale_log2 : -INFINITY;
+            tmax[blk] = fmaxf(tmax[blk], x[blk][j]);
+          }
+          tmax[blk] = reduce8(tmax[blk], [](float a, float b) { return fmaxf(a, b); });
+          bump[blk] = tmax[blk] > m_run[blk] + kRescaleSlack;
+          bump_any |= bump[blk];
         }
-        tmax = reduce8(tmax, [](float a, float b) { return fmaxf(a, b); });
-        const bool bump = tmax > m_run + kRescaleSlack;
-        const bool any_bump = __any(bump);
+        // One flag per wave and step covers its heads in every block, so when
+        // it is set every block's factor is written (1 where nothing moved).
+        const bool any_bump = __any(bump_any);
         if (any_bump) {
-          const float alpha = bump ? (m_run == -INFINITY ? 0.f : fast_exp2(m_run - tmax)) : 1.f;
-          if (bump) m_run = tmax;
-          l_run *= alpha;
-          alds[pb_i * kHeadGroup + hloc] = alpha;      // the 8 lanes of a head store the same value
+#pragma unroll
+          for (int blk = 0; blk < NB; ++blk) {
+            const float alpha = bump[blk] ? (m_run[blk] == -INFINITY ? 0.f : fast_exp2(m_run[blk] - tmax[blk])) : 1.f;
+            if (bump[blk]) m_run[blk] = tmax[blk];
+            l_run[blk] *= alpha;
+            alds[pb_i * NB * kHeadGroup + blk * kHeadGroup + hloc] = alpha;   // the 8 lanes of a head store the same value
+          }
         }
         flds[pb_i * 4 + w] = any_bump ? 1 : 0;
-        // masked rows have x = -inf and weight exp2(-inf) = 0; m_run is -inf
-        // only while every row so far was masked
-        const float m_use = m_run == -INFINITY ? 0.f : m_run;
-        float p[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          p[j] = fast_exp2(x[j] - m_use);
-          l_run += p[j];
+        for (int blk = 0; blk < NB; ++blk) {
+          // masked rows have x = -inf and weight exp2(-inf) = 0; m_run is -inf
+          // only while every row so far was masked
+          const float m_use = m_run[blk] == -INFINITY ? 0.f : m_run[blk];
+          float p[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            p[j] = fast_exp2(x[blk][j] - m_use);
+            l_run[blk] += p[j];
+          }
+          plds[((pb_i * NB + blk) * kHeadGroup + hloc) * 10 + p_slot(pq)] =
+              u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
         }
-        plds[(pb_i * kHeadGroup + hloc) * 10 + p_slot(pq)] = u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
       }
       lds_barrier();                                                   // BAR_p
     }
-    // Head hloc: sum over the 8 lanes that share it.
-    l_run = reduce8(l_run, [](float a, float b) { return a + b; });
-    if (pq == 0) {
-      const int head = kHeadGroup * hg + hloc;
-      mlds[hloc * 2 + 0] = m_run;
-      mlds[hloc * 2 + 1] = l_run;
-      if (A.n_sp == 1) {
-        if (A.lse)
-          A.lse[(int64_t)t * kHeads + head] = l_run > 0.f ? (m_run + __log2f(l_run)) * 0.69314718055994531f : -INFINITY;
-      } else {
-        const int64_t pbase = ((int64_t)t * A.n_sp + sp) * kHeads;
-        A.part_ml[(pbase + head) * 2 + 0] = m_run;
-        A.part_ml[(pbase + head) * 2 + 1] = l_run;
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      // Head hloc of the block: sum over the 8 lanes that share it.
+      const float lsum = reduce8(l_run[blk], [](float a, float b) { return a + b; });
+      if (pq == 0) {
+        const int head = kHeadGroup * (hg + blk) + hloc;
+        mlds[(blk * kHeadGroup + hloc) * 2 + 0] = m_run[blk];
+        mlds[(blk * kHeadGroup + hloc) * 2 + 1] = lsum;
+        if (A.n_sp == 1) {
+          if (A.lse)
+            A.lse[(int64_t)t * kHeads + head] = lsum > 0.f ? (m_run[blk] + __log2f(lsum)) * 0.69314718055994531f : -INFINITY;
+        } else {
+          const int64_t pbase = ((int64_t)t * A.n_sp + sp) * kHeads;
+          A.part_ml[(pbase + head) * 2 + 0] = m_run[blk];
+          A.part_ml[(pbase + head) * 2 + 1] = lsum;
+        }
       }
     }
     lds_barrier();                                                     // BAR_end
@@ -319,9 +364,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
   int voff[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) voff[e] = tile_chunk_offset(8 * (e >> 2) + 4 * hl + (e & 3), 16 * w + (l32 >> 1)) + 8 * (l32 & 1);
-  f32x16 o[4];                   // O^T tiles: dim tiles mt
+  f32x16 o[NB][4];               // O^T tiles of each head block: dim tiles mt
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) o[mt] = f32x16{};
+  for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) o[blk][mt] = f32x16{};
   store_positions();
   lds_barrier();                                                       // B0
   issue(0);
@@ -342,9 +389,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
     const int tile = step - 1;
     const int pb_i = tile & 1;
     u32x2 v[2][8];
-    u32x4 pt[2];
+    u32x4 pt[NB][2];
     int fl = 0;
-    float al = 1.f;
+    float al[NB];
     if (pv_step) {
       const uint8_t* cur = ring + (tile % kRing) * kTileBytes;
 #pragma unroll
@@ -353,10 +400,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
         for (int e = 0; e < 8; ++e)
           v[ks][e] = *reinterpret_cast<const u32x2*>(cur + 16 * ks * 256 + voff[e]);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        pt[ks] = *reinterpret_cast<const u32x4*>(plds + (pb_i * kHeadGroup + l32) * 10 + 4 * ks + 2 * hl);
+      for (int blk = 0; blk < NB; ++blk) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          pt[blk][ks] = *reinterpret_cast<const u32x4*>(plds + ((pb_i * NB + blk) * kHeadGroup + l32) * 10 + 4 * ks + 2 * hl);
+        al[blk] = alds[pb_i * NB * kHeadGroup + blk * kHeadGroup + l32];   // meaningful only where the flag is set
+      }
       fl = flds[pb_i * 4 + pw];
-      al = alds[pb_i * kHeadGroup + l32];          // meaningful only where the flag is set
     }
     if (step < n_tiles) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -365,9 +415,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
     lds_barrier();                                                     // BAR_s
     if (pv_step) {
       if (__any(fl)) {
-        const float sc = fl ? al : 1.f;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) o[mt] *= sc;
+        for (int blk = 0; blk < NB; ++blk) {
+          const float sc = fl ? al[blk] : 1.f;
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) o[blk][mt] *= sc;
+        }
       }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -386,7 +439,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
             av[2] = perm_lo(v[ks][4][d], v[ks][5][d]);
             av[3] = perm_lo(v[ks][6][d], v[ks][7][d]);
           }
-          o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(pt[ks]), o[mt], 0, 0, 0);
+#pragma unroll
+          for (int blk = 0; blk < NB; ++blk)
+            o[blk][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(pt[blk][ks]), o[blk][mt], 0, 0, 0);
         }
       }
     }
@@ -401,31 +456,39 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
   // need no (m, l), so they are issued before BAR_end, beside the score waves'
   // last softmax.
   if (A.n_sp > 1) {
-    f32x4* po = reinterpret_cast<f32x4*>(A.part_o) + ((((int64_t)t * A.n_sp + sp) * 2 + hg) * 4 + w) * 16 * 64;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int blk = 0; blk < NB; ++blk) {
+      f32x4* po = reinterpret_cast<f32x4*>(A.part_o) + ((((int64_t)t * A.n_sp + sp) * 2 + hg + blk) * 4 + w) * 16 * 64;
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-        __builtin_nontemporal_store(f32x4{o[mt][4 * a], o[mt][4 * a + 1], o[mt][4 * a + 2], o[mt][4 * a + 3]},
-                                    &po[(mt * 4 + a) * 64 + lane]);
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          __builtin_nontemporal_store(
+              f32x4{o[blk][mt][4 * a], o[blk][mt][4 * a + 1], o[blk][mt][4 * a + 2], o[blk][mt][4 * a + 3]},
+              &po[(mt * 4 + a) * 64 + lane]);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);         // the trailing (clamped) tile loads land before the workgroup ends
   lds_barrier();                                                       // BAR_end: (m, l) of every head
   // Result element 4a + b of tile mt is dim 128w + 32a + 16hl + 4b + mt of
   // head 32hg + l32: for each a a lane holds 16 consecutive dims.
   if (A.n_sp == 1) {
-    const float L = mlds[l32 * 2 + 1];
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    uint16_t* ob = A.obar + ((int64_t)t * kHeads + kHeadGroup * hg + l32) * kLatent + 128 * w + 16 * hl;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
+    for (int blk = 0; blk < NB; ++blk) {
+      const float L = mlds[(blk * kHeadGroup + l32) * 2 + 1];
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      uint16_t* ob = A.obar + ((int64_t)t * kHeads + kHeadGroup * (hg + blk) + l32) * kLatent + 128 * w + 16 * hl;
+      const f32x16* ot = o[blk];
 #pragma unroll
-      for (int bh = 0; bh < 2; ++bh) {            // dims 8bh .. 8bh + 7 of the 16: b = 2bh, 2bh + 1
-        const int i0 = 4 * a + 2 * bh;
-        const u32x4 pk = {pack_bf16x2(o[0][i0] * inv, o[1][i0] * inv), pack_bf16x2(o[2][i0] * inv, o[3][i0] * inv),
-                          pack_bf16x2(o[0][i0 + 1] * inv, o[1][i0 + 1] * inv),
-                          pack_bf16x2(o[2][i0 + 1] * inv, o[3][i0 + 1] * inv)};
-        *reinterpret_cast<u32x4*>(ob + 32 * a + 8 * bh) = pk;
+      for (int a = 0; a < 4; ++a) {
+#pragma unroll
+        for (int bh = 0; bh < 2; ++bh) {            // dims 8bh .. 8bh + 7 of the 16: b = 2bh, 2bh + 1
+          const int i0 = 4 * a + 2 * bh;
+          const u32x4 pk = {pack_bf16x2(ot[0][i0] * inv, ot[1][i0] * inv), pack_bf16x2(ot[2][i0] * inv, ot[3][i0] * inv),
+                            pack_bf16x2(ot[0][i0 + 1] * inv, ot[1][i0 + 1] * inv),
+                            pack_bf16x2(ot[2][i0 + 1] * inv, ot[3][i0 + 1] * inv)};
+          *reinterpret_cast<u32x4*>(ob + 32 * a + 8 * bh) = pk;
+        }
       }
     }
   }
@@ -676,10 +739,18 @@ namespace sa_host {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Head blocks per attention workgroup: 2 (all 64 heads share every gathered
+// tile, half the tile steps per head) from 64 queries on; 1 (a workgroup per
+// 32 heads, so twice the workgroups per slice) for smaller decode batches,
+// where two head blocks would need twice the slices, and so twice the partial
+// states, for the same parallelism (16 queries: 0.209 against 0.189 ms per
+// 4-layer step; 64 queries: 0.320 against 0.338 ms).
+constexpr int kTwoBlockMinQ = 64;
+int mla_head_blocks(int32_t n_q) { return n_q >= kTwoBlockMinQ ? 2 : 1; }
+
 int mla_n_splits(int32_t n_q, int32_t k) {
-  // About one workgroup per CU (two head groups per slice); a slice keeps at
-  // least two 32-row tiles.
-  const int target = 128;
+  // About one workgroup per CU; a slice keeps at least two 32-row tiles.
+  const int target = mla_head_blocks(n_q) == 2 ? 256 : 128;
   int n_sp = (target + n_q - 1) / n_q;
   const int max_sp = (k + 63) / 64;
   if (n_sp > max_sp) n_sp = max_sp;
@@ -737,7 +808,8 @@ int32_t launch_mla(const void* q_abs, const void* kv, const int64_t* seq_start, 
   A.part_ml = m.part_ml;
   A.obar = m.obar;
   A.lse = lse;
-  const size_t smem = sa::kAttnSmem;
+  const int nb = mla_head_blocks(n_q);
+  const size_t smem = nb == 2 ? sa::attn_smem<2>() : sa::attn_smem<1>();
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
     set_error("mla: hipGetDevice failed");
@@ -745,8 +817,10 @@ int32_t launch_mla(const void* q_abs, const void* kv, const int64_t* seq_start, 
   }
   const uint64_t bit = 1ull << (dev & 63);
   if (!(g_attr_set.load() & bit)) {
-    if (hipFuncSetAttribute((const void*)sa::mla_attn_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)smem) != hipSuccess ||
+    if (hipFuncSetAttribute((const void*)sa::mla_attn_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)sa::attn_smem<1>()) != hipSuccess ||
+        hipFuncSetAttribute((const void*)sa::mla_attn_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)sa::attn_smem<2>()) != hipSuccess ||
         hipFuncSetAttribute((const void*)sa::mla_wuv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)sa::kWuvSmem) != hipSuccess) {
       set_error("mla: cannot reserve %zu bytes of LDS", smem);
@@ -754,14 +828,17 @@ int32_t launch_mla(const void* q_abs, const void* kv, const int64_t* seq_start, 
     }
     g_attr_set.fetch_or(bit);
   }
-  const int64_t grid = (int64_t)n_q * n_sp * 2;
+  const int64_t grid = (int64_t)n_q * n_sp * (nb == 2 ? 1 : 2);
   const bool wide = n_sp > sa::kMergeBatch;
   const int64_t merge_grid = (int64_t)n_q * 16 * (wide ? sa::merge_groups(n_sp) : 1);
   if (grid > 0x7fffffff || merge_grid > 0x7fffffff) {
     set_error("mla: grid too large");
     return SA_ERR_UNSUPPORTED;
   }
-  hipLaunchKernelGGL(sa::mla_attn_kernel, dim3((unsigned)grid), dim3(sa::kAttnThreads), smem, stream, A);
+  if (nb == 2)
+    hipLaunchKernelGGL(sa::mla_attn_kernel<2>, dim3((unsigned)grid), dim3(sa::kAttnThreads), smem, stream, A);
+  else
+    hipLaunchKernelGGL(sa::mla_attn_kernel<1>, dim3((unsigned)grid), dim3(sa::kAttnThreads), smem, stream, A);
   int32_t rc = check_launch("mla_attn_kernel");
   if (rc) return rc;
   if (n_sp > 1) {

@@ -133,6 +133,27 @@ def test_mla_slice_counts(gpu_lib, n_q):
                      lse_gpu=to_numpy(lse))
 
 
+@pytest.mark.parametrize("n_q", [130, 300])
+def test_mla_all_heads_per_workgroup(gpu_lib, n_q):
+    # from 64 queries on, one attention workgroup takes all 64 heads of a
+    # (query, slice): 2 slices per query at 130 queries (partial states and
+    # merge), 1 at 300; positions from 1700 up, so some rows select fewer than
+    # 2048 positions
+    lens = [3000, 2600]
+    queries = [(i % 2, lens[i % 2] - 1 - (i // 2) % 900) for i in range(n_q)]
+    wl = synth.ragged_workload(lens, queries, name=f"heads64_{n_q}")
+    b = _batch(wl, seed=21 + n_q)
+    L = b.layers[0]
+    sc = api.indexer_score(L.q_idx, L.w, L.k_idx, b.seq_start, b.q_seq, b.q_pos, wl.ld)
+    idx = api.topk_select(sc, b.q_pos, k=2048)
+    lse = torch.empty((wl.n_q, 64), dtype=torch.float32, device=DEV)
+    out = api.mla_sparse_attn(L.q_abs, L.kv, b.seq_start, b.q_seq, idx, L.w_uv, wl.scale, lse=lse)
+    torch.cuda.synchronize()
+    rows = sorted({0, 1, 2, n_q // 3, n_q // 2, n_q - 3, n_q - 2, n_q - 1})
+    parity.check_mla(parity.layer_np(L), parity.np_batch(b), to_numpy(idx), to_numpy(out), wl.scale, rows=rows,
+                     lse_gpu=to_numpy(lse))
+
+
 @pytest.mark.parametrize("k", [1, 7, 64, 300])
 def test_mla_small_k_and_padding(gpu_lib, k):
     wl = ragged_wl(k=k)
