@@ -115,10 +115,10 @@ def test_mla_on_gpu_selection(gpu_lib, case):
     print(f"{case}: worst |err|/bound = {worst:.3g}")
 
 
-@pytest.mark.parametrize("n_q", [3, 5, 10])
+@pytest.mark.parametrize("n_q", [1, 3, 5, 10])
 def test_mla_slice_counts(gpu_lib, n_q):
-    # about 128 / n_q slices per query: 32, 26 and 13, i.e. the merge with 4
-    # waves per item (even and uneven slice shares) and with 2 waves (uneven)
+    # about 128 / n_q slices per query: 32, 32, 26 and 13, i.e. the merge with
+    # 4 waves per item (even and uneven slice shares) and with 2 waves (uneven)
     lens = [4096, 3000, 2500]
     queries = [(i % 3, lens[i % 3] - 1 - 7 * i) for i in range(n_q)]
     wl = synth.ragged_workload(lens, queries, name=f"slices{n_q}")
