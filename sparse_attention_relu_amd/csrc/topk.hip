@@ -14,8 +14,8 @@
 //
 // Path 1 (many workgroups per row, used by default):
 //   hist     rows x chunks: 4096-bin histogram of the top 12 key bits (LDS,
-//            then global atomics).  (sa_layer_stack builds this histogram
-//            inside the decode indexer kernel instead.)
+//            then global atomics).  Inside sa_layer_stack the decode
+//            indexer zeroes the histograms and counters on the side.
 //   compact  rows x chunks, one pass with the chunk in registers: every
 //            workgroup reads the finished histogram and finds the bin b1 that
 //            holds the k_eff-th largest key (no hand-off between workgroups);

@@ -1,5 +1,5 @@
-// Pieces of the radix top-k shared by the top-k kernels and the indexer
-// kernel that builds the first-digit histogram while it scores.
+// Pieces of the radix top-k: workspace layout, score keys, workgroup scans
+// and the bin search.
 #pragma once
 
 #include "sa_common.h"
