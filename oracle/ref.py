@@ -369,3 +369,79 @@ def layer_stack(layers, seq_start, q_seq, q_pos, k=INDEX_TOPK, scale=1.0 / 16, f
             scores_all.append(None)
         outs.append(sparse_mla(L["q_abs"], L["kv"], seq_start, q_seq, cur, L["w_uv"], scale))
     return outs, idxs, scores_all
+
+
+# --------------------------------------------------------------------------
+# Cache write: the step before the path.  Each new token's kv_a_proj output
+# (512 latent + 64 rope-key values) becomes its 576-wide cache row, and its
+# indexer-key projection becomes its 128-wide indexer key.
+#
+# [GLM-5.2 techniques map] row "Multi-head latent attention": the latent goes
+# through kv_a_layernorm, an RMSNorm over kv_lora_rank = 512 values, and the
+# decoupled 64-dim key is rotated.  Row "QK normalization": the indexer key
+# is the LayerNorm (k_norm) of the wk output.  Rows "Partial RoPE" and "YaRN
+# RoPE scaling": rotary embedding of the 64-dim part, rope_type "default"
+# (no scaling), rope_theta 8,000,000.  [GLM-5.2 llm-atlas] config fields:
+# rms_norm_eps 1e-5, rope_interleave true, indexer_rope_interleave true.
+#
+# Readings where the pages are silent (each stated again in the design notes):
+#   * RMSNorm is x / sqrt(mean(x^2) + eps) * gamma; LayerNorm is
+#     (x - mean) / sqrt(var + eps) * weight + bias with the population
+#     variance; both with eps = rms_norm_eps (the pages give none for k_norm).
+#   * "Interleaved" RoPE rotates the adjacent pairs (2i, 2i + 1) in place by
+#     the angle p * theta^(-2i / 64); the output keeps that layout.
+#   * The indexer key is rotated on its last 64 dims (64..127) with the same
+#     frequencies, the order the main attention uses for its nope/rope split.
+#   * Everything is exact here (float64); the stored row is rounded once to
+#     bfloat16.
+
+ROPE_THETA = 8.0e6        # rope_parameters.rope_theta
+RMS_NORM_EPS = 1e-5       # rms_norm_eps
+
+
+def rms_norm(x, gamma, eps=RMS_NORM_EPS):
+    """RMSNorm of each row of x (last axis), scaled by gamma."""
+    x = _f64(x)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * _f64(gamma)
+
+
+def layer_norm(x, weight, bias, eps=RMS_NORM_EPS):
+    """LayerNorm of each row of x (last axis) with an affine weight and bias."""
+    x = _f64(x)
+    mean = np.mean(x, axis=-1, keepdims=True)
+    var = np.mean((x - mean) ** 2, axis=-1, keepdims=True)
+    return (x - mean) / np.sqrt(var + eps) * _f64(weight) + _f64(bias)
+
+
+def rope_interleaved(x, pos, theta=ROPE_THETA):
+    """Rotate the adjacent pairs (2i, 2i + 1) of each row of x (shape [n, d])
+    by pos[n] * theta^(-2i / d)."""
+    x = _f64(x)
+    d = x.shape[-1]
+    inv_freq = np.power(float(theta), -np.arange(0, d, 2, dtype=np.float64) / d)
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * inv_freq[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    x0, x1 = x[:, 0::2], x[:, 1::2]
+    out = np.empty_like(x)
+    out[:, 0::2] = x0 * c - x1 * s
+    out[:, 1::2] = x0 * s + x1 * c
+    return out
+
+
+def cache_rows_from_projection(kv_a, gamma, pos):
+    """The 576-wide cache rows of n new tokens: RMSNorm(latent) * gamma, then
+    the rotated 64-dim key; rounded to bfloat16.  kv_a: [n, 576]."""
+    kv_a = _f64(kv_a)
+    lat = rms_norm(kv_a[:, :KV_LORA_RANK], gamma)
+    rot = rope_interleaved(kv_a[:, KV_LORA_RANK:], pos)
+    return round_to_bf16(np.concatenate([lat, rot], axis=1))
+
+
+def indexer_keys_from_projection(k_raw, ln_weight, ln_bias, pos):
+    """The 128-wide indexer keys of n new tokens: LayerNorm, then the last 64
+    dims rotated; rounded to bfloat16.  k_raw: [n, 128]."""
+    k = layer_norm(k_raw, ln_weight, ln_bias)
+    half = INDEX_HEAD_DIM - QK_ROPE_DIM
+    k[:, half:] = rope_interleaved(k[:, half:], pos)
+    return round_to_bf16(k)

@@ -448,4 +448,108 @@ def check_layer_stack_shares_selection(ref):
         raise AssertionError("stack starting with a shared layer accepted")
 
 
+# ---------------------------------------------------------------- cache write
+# [GLM-5.2 techniques map] rows "Multi-head latent attention", "QK
+# normalization", "Partial RoPE", "YaRN RoPE scaling"; [GLM-5.2 llm-atlas]
+# rope_theta 8e6, rms_norm_eps 1e-5, rope_interleave true.
+
+def check_rope_position_zero_is_identity(ref):
+    x = _rng(40).standard_normal((3, 64))
+    assert np.array_equal(ref.rope_interleaved(x, [0, 0, 0]), x)
+
+
+def check_rope_frequencies_from_theta(ref):
+    # One-hot input on the first slot of pair i at position 1: the pair turns
+    # by exactly that pair's frequency into its second slot (the interleaved
+    # layout), pair 0 turns by 1 radian, and consecutive frequencies fall by
+    # the factor theta^(-2/64), theta = 8e6.
+    d = 64
+    freqs = []
+    for i in range(d // 2):
+        x = np.zeros((1, d))
+        x[0, 2 * i] = 1.0
+        y = ref.rope_interleaved(x, [1])[0]
+        others = np.delete(y, [2 * i, 2 * i + 1])
+        assert np.all(others == 0.0), "rotation leaves its pair"
+        freqs.append(math.atan2(y[2 * i + 1], y[2 * i]))
+    freqs = np.array(freqs)
+    assert abs(freqs[0] - 1.0) < 1e-15
+    assert np.allclose(freqs[1:] / freqs[:-1], 8.0e6 ** (-2.0 / 64), rtol=1e-12, atol=0)
+
+
+def check_rope_is_a_rotation_by_relative_position(ref):
+    # Pair norms are kept, turning by a then b equals turning by a + b, and the
+    # product of two rotated vectors depends only on their distance.
+    r = _rng(41)
+    q, k = r.standard_normal((1, 64)), r.standard_normal((1, 64))
+    for a, b in [(3, 11), (1000, 17), (1 << 20, 5)]:
+        qa = ref.rope_interleaved(q, [a])
+        assert np.allclose(qa[0, 0::2] ** 2 + qa[0, 1::2] ** 2, q[0, 0::2] ** 2 + q[0, 1::2] ** 2, rtol=1e-12)
+        assert np.allclose(ref.rope_interleaved(qa, [b]), ref.rope_interleaved(q, [a + b]), atol=1e-9)
+        lhs = float(ref.rope_interleaved(q, [a + b])[0] @ ref.rope_interleaved(k, [b])[0])
+        rhs = float(ref.rope_interleaved(q, [a])[0] @ k[0])
+        assert abs(lhs - rhs) < 1e-9 * (1 + abs(rhs))
+
+
+def check_rms_norm_closed_forms(ref):
+    n = 512
+    for c in [1e-3, 0.5, 7.0]:
+        y = ref.rms_norm(np.full((1, n), c), np.ones(n))
+        assert np.allclose(y, c / math.sqrt(c * c + 1e-5), rtol=1e-14)
+    x = _rng(42).standard_normal((4, n))
+    ms = np.mean(x ** 2, axis=1)
+    y = ref.rms_norm(x, np.ones(n))
+    assert np.allclose(np.mean(y ** 2, axis=1), ms / (ms + 1e-5), rtol=1e-12)
+    g = _rng(43).standard_normal(n)
+    assert np.allclose(ref.rms_norm(x, g), ref.rms_norm(x, np.ones(n)) * g, rtol=1e-14)
+    assert np.allclose(ref.rms_norm(1e3 * x, np.ones(n)), ref.rms_norm(x, np.ones(n)), rtol=1e-5)
+
+
+def check_layer_norm_closed_forms(ref):
+    n = 128
+    r = _rng(44)
+    x = 3.0 + 2.0 * r.standard_normal((5, n))
+    y = ref.layer_norm(x, np.ones(n), np.zeros(n))
+    var = np.var(x, axis=1)           # population variance
+    assert np.allclose(np.mean(y, axis=1), 0.0, atol=1e-12)
+    assert np.allclose(np.mean(y ** 2, axis=1), var / (var + 1e-5), rtol=1e-12)
+    w, b = r.standard_normal(n), r.standard_normal(n)
+    assert np.allclose(ref.layer_norm(x, w, b), y * w + b, rtol=1e-13, atol=1e-13)
+    assert np.allclose(ref.layer_norm(np.full((1, n), 4.25), w, b), b, atol=1e-12)
+
+
+def check_cache_rows_structure(ref):
+    r = _rng(45)
+    n = 6
+    kv_a = _bf16_grid(r.standard_normal((n, 576)))
+    gamma = np.ones(512)
+    pos = [0, 1, 7, 4096, 131071, 1048575]
+    rows = ref.cache_rows_from_projection(kv_a, gamma, pos)
+    assert rows.shape == (n, 576)
+    assert np.array_equal(ref.round_to_bf16(rows), rows)
+    lat = kv_a[:, :512]
+    ms = np.mean(lat ** 2, axis=1, keepdims=True)
+    assert np.allclose(rows[:, :512], lat / np.sqrt(ms + 1e-5), rtol=2 ** -8)
+    rot, k = rows[:, 512:], kv_a[:, 512:]
+    assert np.allclose(rot[:, 0::2] ** 2 + rot[:, 1::2] ** 2, k[:, 0::2] ** 2 + k[:, 1::2] ** 2, rtol=2 ** -6, atol=1e-4)
+    assert np.array_equal(rot[0], k[0])           # position 0: no turn (k is bf16 already)
+
+
+def check_indexer_keys_structure(ref):
+    r = _rng(46)
+    n = 4
+    k_raw = _bf16_grid(r.standard_normal((n, 128)))
+    w, b = r.standard_normal(128), r.standard_normal(128)
+    pos = [0, 3, 65536, 1048575]
+    keys = ref.indexer_keys_from_projection(k_raw, w, b, pos)
+    mean = np.mean(k_raw, axis=1, keepdims=True)
+    var = np.mean((k_raw - mean) ** 2, axis=1, keepdims=True)
+    ln = (k_raw - mean) / np.sqrt(var + 1e-5) * w + b
+    assert np.allclose(keys[:, :64], ln[:, :64], rtol=2 ** -8, atol=1e-6)    # first half: not turned
+    assert np.allclose(keys[0], ln[0], rtol=2 ** -8, atol=1e-6)              # position 0: not turned
+    rot = keys[:, 64:]
+    assert np.allclose(rot[:, 0::2] ** 2 + rot[:, 1::2] ** 2, ln[:, 64::2] ** 2 + ln[:, 65::2] ** 2, rtol=2 ** -6, atol=1e-4)
+    assert not np.allclose(rot[1:], ln[1:, 64:], rtol=1e-3)                  # later positions: turned
+
+
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

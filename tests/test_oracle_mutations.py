@@ -41,6 +41,17 @@ MUTATIONS = [
     ("bf16_truncates", "rounded = (bits + 0x7FFF + lsb) >> 16", "rounded = bits >> 16"),
     ("bf16_ties_away", "rounded = (bits + 0x7FFF + lsb) >> 16", "rounded = (bits + 0x8000) >> 16"),
     ("bound_drops_dot_term", "return err_dot + err_sum", "return err_sum"),
+    ("rope_turns_backwards", "out[:, 1::2] = x0 * s + x1 * c", "out[:, 1::2] = -x0 * s + x1 * c"),
+    ("rope_half_split_layout", "x0, x1 = x[:, 0::2], x[:, 1::2]", "x0, x1 = x[:, : d // 2], x[:, d // 2:]"),
+    ("rope_wrong_theta", "ROPE_THETA = 8.0e6", "ROPE_THETA = 1.0e4"),
+    ("rope_exponent_over_half_dim", "-np.arange(0, d, 2, dtype=np.float64) / d)", "-np.arange(0, d, 2, dtype=np.float64) / (d // 2))"),
+    ("rms_without_eps", "return x / np.sqrt(ms + eps) * _f64(gamma)", "return x / np.sqrt(ms) * _f64(gamma)"),
+    ("rms_sum_not_mean", "ms = np.mean(x * x, axis=-1, keepdims=True)", "ms = np.sum(x * x, axis=-1, keepdims=True)"),
+    ("ln_sample_variance", "var = np.mean((x - mean) ** 2, axis=-1, keepdims=True)",
+     "var = np.sum((x - mean) ** 2, axis=-1, keepdims=True) / (x.shape[-1] - 1)"),
+    ("ln_drops_bias", "* _f64(weight) + _f64(bias)", "* _f64(weight)"),
+    ("indexer_key_turns_first_half", "k[:, half:] = rope_interleaved(k[:, half:], pos)", "k[:, :half] = rope_interleaved(k[:, :half], pos)"),
+    ("cache_row_latent_not_normalised", "lat = rms_norm(kv_a[:, :KV_LORA_RANK], gamma)", "lat = kv_a[:, :KV_LORA_RANK] * _f64(gamma)"),
 ]
 
 
