@@ -224,6 +224,43 @@ int32_t sa_layer_stack(const sa_layer_desc* layers, int32_t n_layers, const sa_b
 int32_t sa_layer_is_full(int32_t layer);
 
 /*
+ * sa_cache_write -- the step before the path: turn n new tokens' projections
+ * into their cache rows (and, optionally, their indexer keys).
+ *
+ * Defines ("Multi-head latent attention" row: kv_a_layernorm, an RMSNorm over
+ * the 512-wide latent, and a decoupled 64-wide rope key; "QK normalization"
+ * row: k_norm, a LayerNorm of the indexer key projection; "Partial RoPE" and
+ * "YaRN RoPE scaling" rows: 64 rotated dims, default rope type, theta 8e6;
+ * llm-atlas config: rms_norm_eps 1e-5, rope_interleave, indexer_rope_interleave):
+ *     kv_cache[dst[i], 0:512]   = latent / sqrt(mean(latent^2) + 1e-5) * gamma
+ *     kv_cache[dst[i], 512:576] = rope(kv_a[i, 512:576], pos[i])
+ *     k_cache[dst[i], :]        = LN(k_raw[i]) * ln_w + ln_b, then
+ *                                 dims 64..127 <- rope(dims 64..127, pos[i])
+ * where rope turns each adjacent pair (2j, 2j + 1) by pos * 8e6^(-2j / 64)
+ * and LN uses the population variance and eps 1e-5.  The pages give no eps
+ * for k_norm and do not say which half of the indexer key turns: this takes
+ * rms_norm_eps and the last 64 dims (the main attention's nope/rope order).
+ * Computed in fp64; each stored value is rounded once to bf16 (through fp32,
+ * both steps to nearest even).
+ *
+ *   kv_a      bf16  [n, 576]  kv_a_proj output (512 latent, then 64 rope key), 16-byte aligned
+ *   gamma     bf16  [512]     kv_a_layernorm weight, 16-byte aligned
+ *   k_raw     bf16  [n, 128]  indexer key projection, or NULL to skip the indexer key
+ *   ln_w      bf16  [128]     k_norm weight (ignored when k_raw is NULL)
+ *   ln_b      bf16  [128]     k_norm bias   (ignored when k_raw is NULL)
+ *   pos       int32 [n]       position of each token within its sequence (>= 0)
+ *   dst       int64 [n]       row of each token in kv_cache / k_cache (distinct rows)
+ *   kv_cache  bf16  [*, 576]  written at rows dst[i] only, 16-byte aligned
+ *   k_cache   bf16  [*, 128]  written at rows dst[i] only (ignored when k_raw is NULL)
+ * Everything is device memory owned by the caller; nothing is kept after the
+ * call.  n = 0 launches nothing.  Rows in range and distinct are preconditions
+ * the call does not check (checking would need the data on the host).
+ */
+int32_t sa_cache_write(const void* kv_a, const void* gamma, const void* k_raw, const void* ln_w,
+                       const void* ln_b, const int32_t* pos, const int64_t* dst, int32_t n,
+                       void* kv_cache, void* k_cache, sa_stream_t stream);
+
+/*
  * Variants that pin an internal algorithm, for tests and measurements.
  * algo 0 = automatic (what the entry points above use).
  *   indexer: 1 = one query per workgroup (streams keys once per query),

@@ -110,6 +110,27 @@ def mla_sparse_attn(q_abs, kv, seq_start, q_seq, idx, w_uv, scale: float = 1.0 /
     return out
 
 
+def cache_write(kv_a, gamma, pos, dst, kv_cache, k_raw=None, ln_w=None, ln_b=None, k_cache=None, stream=None):
+    """sa_cache_write: the cache rows (and optionally the indexer keys) of n
+    new tokens, written at rows dst of kv_cache (and k_cache)."""
+    n = kv_a.shape[0]
+    _need(kv_a, "kv_a", torch.bfloat16, (n, ROW))
+    _need(gamma, "gamma", torch.bfloat16, (LATENT,))
+    _need(pos, "pos", torch.int32, (n,))
+    _need(dst, "dst", torch.int64, (n,))
+    _need(kv_cache, "kv_cache", torch.bfloat16, (None, ROW))
+    if k_raw is not None:
+        _need(k_raw, "k_raw", torch.bfloat16, (n, IDX_DIM))
+        _need(ln_w, "ln_w", torch.bfloat16, (IDX_DIM,))
+        _need(ln_b, "ln_b", torch.bfloat16, (IDX_DIM,))
+        _need(k_cache, "k_cache", torch.bfloat16, (None, IDX_DIM))
+    L = _lib.lib()
+    st = L.sa_cache_write(_ptr(kv_a), _ptr(gamma), _ptr(k_raw), _ptr(ln_w), _ptr(ln_b), _ptr(pos), _ptr(dst), n,
+                          _ptr(kv_cache), _ptr(k_cache), _stream(stream))
+    _lib.check("sa_cache_write", st)
+    return kv_cache, k_cache
+
+
 class LayerStack:
     """Pre-marshalled arguments of sa_layer_stack for a fixed set of tensors,
     so a step costs one foreign call (and can be captured in a HIP graph)."""

@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsparse_mla.so")
-SOURCES = ["abi.hip", "indexer.hip", "topk.hip", "mla.hip"]
+SOURCES = ["abi.hip", "indexer.hip", "topk.hip", "mla.hip", "cache.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

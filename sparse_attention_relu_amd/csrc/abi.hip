@@ -42,6 +42,10 @@ int32_t launch_mla(const void* q_abs, const void* kv, const int64_t* seq_start, 
                    const int32_t* idx, int32_t n_q, int32_t k, const void* w_uv, float scale, void* out, float* lse,
                    void* ws, hipStream_t stream);
 
+int32_t launch_cache_write(const void* kv_a, const void* gamma, const void* k_raw, const void* ln_w, const void* ln_b,
+                           const int32_t* pos, const int64_t* dst, int32_t n, void* kv_cache, void* k_cache,
+                           hipStream_t stream);
+
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -266,6 +270,22 @@ int32_t sa_layer_stack(const sa_layer_desc* layers, int32_t n_layers, const sa_b
     rec_attn |= eva;
   }
   return SA_OK;
+}
+
+int32_t sa_cache_write(const void* kv_a, const void* gamma, const void* k_raw, const void* ln_w, const void* ln_b,
+                       const int32_t* pos, const int64_t* dst, int32_t n, void* kv_cache, void* k_cache,
+                       sa_stream_t stream) {
+  SA_REQUIRE(n >= 0, SA_ERR_INVALID_ARG, "cache_write: negative n");
+  if (n == 0) return SA_OK;
+  SA_REQUIRE(kv_a && gamma && pos && dst && kv_cache, SA_ERR_INVALID_ARG, "cache_write: null pointer argument");
+  SA_REQUIRE(aligned16(kv_a) && aligned16(gamma) && aligned16(kv_cache), SA_ERR_INVALID_ARG,
+             "cache_write: kv_a/gamma/kv_cache not 16-byte aligned");
+  if (k_raw) {
+    SA_REQUIRE(ln_w && ln_b && k_cache, SA_ERR_INVALID_ARG, "cache_write: indexer key without ln_w/ln_b/k_cache");
+    SA_REQUIRE((((uintptr_t)k_raw | (uintptr_t)ln_w | (uintptr_t)ln_b | (uintptr_t)k_cache) & 3u) == 0,
+               SA_ERR_INVALID_ARG, "cache_write: indexer key pointers not 4-byte aligned");
+  }
+  return launch_cache_write(kv_a, gamma, k_raw, ln_w, ln_b, pos, dst, n, kv_cache, k_cache, (hipStream_t)stream);
 }
 
 }  // extern "C"
