@@ -12,7 +12,9 @@ independent input sets, so no step finds the previous step's data in the 256 MB
 last-level cache.  `roofline` describes the dominant kernel (the decode
 indexer, ~2/3 of the step's bytes), timed with HIP events recorded on the
 library's stream around that kernel in eager steps over the same input sets.  `prefill_indexer` is the chunked-prefill indexer
-(4096 queries over 131,072 keys) in TFLOP/s.  `cpu_baseline` is the CPU oracle
+(4096 queries over 131,072 keys) in TFLOP/s.  `cache_write` is the cache-write step
+(`sa_cache_write`) for one 4096-token prefill chunk of one layer, in GB/s of
+algorithmic bytes against the HBM peak.  `cpu_baseline` is the CPU oracle
 on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -37,7 +39,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="c2", choices=["c0", "c1", "c2", "c3", "c4"],
                     help="c3 times the whole chunked-prefill stack; its dominant kernel is the MFMA-bound indexer")
-    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill indexer measurement")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill indexer and cache-write measurements")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-sample", type=int, default=16, help="queries in the CPU oracle sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="repeat the CPU sample for at least this long")
@@ -164,6 +166,42 @@ def cpu_baseline(b, wl, n_sample, min_seconds):
                       f"repeated {reps}x (indexer + top-k {t_idx:.2f} s, attention {t_mla:.2f} s); "
                       f"gathering rows from device memory untimed",
             "seconds": round(total, 3)}
+
+
+def cache_write_leg(seed, reps=15, warmup=5, n=4096, rows=131072):
+    """sa_cache_write on one 4096-token prefill chunk (positions 126,976..
+    131,071 of a 131,072-row cache, with indexer keys), HIP-event median."""
+    import torch
+    from sparse_attention_relu_amd import api, synth
+    dev = torch.device("cuda:0")
+    g = synth._gen(dev, seed, 0, 7)
+    kv_a = synth._randn((n, 576), g, dev, std=1.0, dtype=torch.bfloat16)
+    k_raw = synth._randn((n, 128), g, dev, std=1.0, dtype=torch.bfloat16)
+    gamma = torch.ones(512, dtype=torch.bfloat16, device=dev)
+    ln_w = torch.ones(128, dtype=torch.bfloat16, device=dev)
+    ln_b = torch.zeros(128, dtype=torch.bfloat16, device=dev)
+    pos = torch.arange(rows - n, rows, dtype=torch.int32, device=dev)
+    dst = pos.to(torch.int64)
+    kv_cache = torch.empty((rows, 576), dtype=torch.bfloat16, device=dev)
+    k_cache = torch.empty((rows, 128), dtype=torch.bfloat16, device=dev)
+    call = lambda st=None: api.cache_write(kv_a, gamma, pos, dst, kv_cache, k_raw, ln_w, ln_b, k_cache, stream=st)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, c in ev:
+        a.record(s)
+        call(s)
+        c.record(s)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(c) for a, c in ev)[len(ev) // 2]
+    # inputs read and rows written (bf16), positions and row indices, weights
+    nbytes = n * (576 + 128) * 2 * 2 + n * (4 + 8) + (512 + 2 * 128) * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "cache_write_4096_tokens_at_126976", "ms": round(ms, 5), "bytes": nbytes,
+            "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm",
+            "timing": "median of %d HIP-event-timed launches" % reps}
 
 
 def prefill_indexer(seed, reps=9, warmup=8):
@@ -342,6 +380,8 @@ def main():
     if not args.no_prefill:
         print("[bench] prefill indexer", file=sys.stderr, flush=True)
         out["prefill_indexer"] = prefill_indexer(args.seed)
+        print("[bench] cache write", file=sys.stderr, flush=True)
+        out["cache_write"] = cache_write_leg(args.seed)
     if not args.no_cpu:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(b, wl, args.cpu_sample, args.cpu_seconds)

@@ -19,12 +19,18 @@
 // nope/rope split).
 //
 // The arithmetic is done in fp64 (the kernel moves 2.8 KB per token and
-// spends a few hundred flops on it, so the rate is set by HBM either way):
-// the RoPE angles reach 10^6 rad at million-token positions, where fp32 would
-// keep no correct digit of the angle.  Each stored value is rounded once,
+// spends a few hundred flops on it): the RoPE angles reach 10^6 rad at
+// million-token positions, where fp32 would keep no correct digit of the
+// angle.  The angle is reduced to [-pi, pi] first (Cody-Waite, 2 pi in three
+// parts, the first two short enough that their products with the turn count
+// are exact), so sin and cos take their short path.  The 32 frequencies are
+// computed once on the host in fp64.  Each stored value is rounded once,
 // fp64 -> fp32 -> bf16, both steps to nearest even.  Expressions are not
-// contracted into fused multiply-adds, so every step rounds as written.
+// contracted into fused multiply-adds; the norms multiply by one reciprocal
+// square root (within an fp64 ulp of dividing by the root).
 #include <math.h>
+
+#include <cmath>
 
 #include "sa_common.h"
 
@@ -45,24 +51,57 @@ struct CacheWriteArgs {
   uint16_t* kv_cache;      // [*][576] bf16
   uint16_t* k_cache;       // [*][128] bf16
   int n;
+  double inv_freq[kRope / 2];   // theta^(-2i / 64)
 };
 
 __device__ __forceinline__ double bf16_to_f64(uint32_t h) { return (double)__uint_as_float(h << 16); }
 
-// Sum over the 64 lanes; every lane gets the same value (each butterfly step
-// adds the same two operands on both sides).
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+// One DPP move of a double (its two halves).
+template <int kCtrl>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)b, kCtrl, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), kCtrl, 0xf, 0xf, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
 }
 
-// Pair i of a 64-dim rotary block at position p: (x0, x1) -> (x0 c - x1 s, x0 s + x1 c).
-__device__ __forceinline__ void rope_pair(double& x0, double& x1, int i, int p) {
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)b, l);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+// Sum over the 64 lanes, the same value on every lane: within each row of 16
+// by DPP exchanges (lane ^ 1, lane ^ 2, then the mirror images within 8 and
+// within 16 lanes; both partners add the same two operands), then the four
+// row sums in one fixed order.
+__device__ __forceinline__ double wave_sum(double v) {
+  v += dpp_f64<0xB1>(v);      // quad_perm [1, 0, 3, 2]
+  v += dpp_f64<0x4E>(v);      // quad_perm [2, 3, 0, 1]
+  v += dpp_f64<0x141>(v);     // row_half_mirror
+  v += dpp_f64<0x140>(v);     // row_mirror
+  return ((readlane_f64(v, 0) + readlane_f64(v, 16)) + readlane_f64(v, 32)) + readlane_f64(v, 48);
+}
+
+// sin and cos of p * f: the angle (|p f| < 2^31) less k whole turns,
+// k = rint(angle / 2 pi) < 2^29, with 2 pi = C1 + C2 + C3 where C1 and C2
+// have 24 significant bits, so k C1 and k C2 are exact.
+__device__ __forceinline__ void turn_sincos(int p, double f, double& s, double& c) {
 #pragma clang fp contract(off)
-  const double inv_freq = pow(kRopeTheta, -(double)(2 * i) / (double)kRope);
-  double s, c;
-  sincos((double)p * inv_freq, &s, &c);
+  constexpr double kC1 = 6.2831854820251465;        // float(2 pi)
+  constexpr double kC2 = -1.7484555314695172e-07;   // float(2 pi - C1)
+  constexpr double kC3 = -6.8604979977715316e-15;   // 2 pi - C1 - C2
+  constexpr double kInv2Pi = 0.15915494309189535;
+  const double a = (double)p * f;
+  const double k = rint(a * kInv2Pi);
+  const double r = ((a - k * kC1) - k * kC2) - k * kC3;
+  sincos(r, &s, &c);
+}
+
+// Pair (x0, x1) turned by the angle with sine s and cosine c.
+__device__ __forceinline__ void rope_pair(double& x0, double& x1, double s, double c) {
+#pragma clang fp contract(off)
   const double y0 = x0 * c - x1 * s;
   const double y1 = x0 * s + x1 * c;
   x0 = y0;
@@ -80,6 +119,10 @@ __global__ __launch_bounds__(kCwWaves * 64) void cache_write_kernel(CacheWriteAr
   const int64_t row = A.dst[t];
   const uint16_t* src = A.kv_a + (int64_t)t * kRow;
   uint16_t* out = A.kv_cache + row * kRow;
+  // Lane l turns pair l % 32: lanes 0..31 for the rope key, 32..63 for the
+  // indexer key's last 64 dims; one sine and cosine per lane.
+  double sn, cs;
+  turn_sincos(p, A.inv_freq[lane & 31], sn, cs);
 
   // Latent: lane l holds values 8l .. 8l + 7.
   const u32x4 xv = ld16(src + 8 * lane);
@@ -95,17 +138,17 @@ __global__ __launch_bounds__(kCwWaves * 64) void cache_write_kernel(CacheWriteAr
   double ss = 0.0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) ss += x[j] * x[j];
-  const double rms = sqrt(wave_sum(ss) / (double)kLatent + kNormEps);
+  const double inv_rms = 1.0 / sqrt(wave_sum(ss) / (double)kLatent + kNormEps);
   u32x4 yv;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) yv[j] = pack2(x[2 * j] / rms * g[2 * j], x[2 * j + 1] / rms * g[2 * j + 1]);
+  for (int j = 0; j < 4; ++j) yv[j] = pack2(x[2 * j] * inv_rms * g[2 * j], x[2 * j + 1] * inv_rms * g[2 * j + 1]);
   *reinterpret_cast<u32x4*>(out + 8 * lane) = yv;
 
   // Rope key: lane i < 32 turns pair i.
   if (lane < kRope / 2) {
     const uint32_t kv = *reinterpret_cast<const uint32_t*>(src + kLatent + 2 * lane);
     double k0 = bf16_to_f64(kv & 0xffffu), k1 = bf16_to_f64(kv >> 16);
-    rope_pair(k0, k1, lane, p);
+    rope_pair(k0, k1, sn, cs);
     *reinterpret_cast<uint32_t*>(out + kLatent + 2 * lane) = pack2(k0, k1);
   }
 
@@ -118,10 +161,10 @@ __global__ __launch_bounds__(kCwWaves * 64) void cache_write_kernel(CacheWriteAr
     const double a0 = bf16_to_f64(kr & 0xffffu), a1 = bf16_to_f64(kr >> 16);
     const double mean = wave_sum(a0 + a1) / (double)kIdxDim;
     const double d0 = a0 - mean, d1 = a1 - mean;
-    const double sd = sqrt(wave_sum(d0 * d0 + d1 * d1) / (double)kIdxDim + kNormEps);
-    double y0 = d0 / sd * bf16_to_f64(wv & 0xffffu) + bf16_to_f64(bv & 0xffffu);
-    double y1 = d1 / sd * bf16_to_f64(wv >> 16) + bf16_to_f64(bv >> 16);
-    if (lane >= kIdxDim / 4) rope_pair(y0, y1, lane - kIdxDim / 4, p);
+    const double inv_sd = 1.0 / sqrt(wave_sum(d0 * d0 + d1 * d1) / (double)kIdxDim + kNormEps);
+    double y0 = d0 * inv_sd * bf16_to_f64(wv & 0xffffu) + bf16_to_f64(bv & 0xffffu);
+    double y1 = d1 * inv_sd * bf16_to_f64(wv >> 16) + bf16_to_f64(bv >> 16);
+    if (lane >= kIdxDim / 4) rope_pair(y0, y1, sn, cs);
     *reinterpret_cast<uint32_t*>(A.k_cache + row * kIdxDim + 2 * lane) = pack2(y0, y1);
   }
 }
@@ -135,7 +178,8 @@ int32_t launch_cache_write(const void* kv_a, const void* gamma, const void* k_ra
                            hipStream_t stream) {
   sa::CacheWriteArgs A{(const uint16_t*)kv_a, (const uint16_t*)gamma, (const uint16_t*)k_raw,
                        (const uint16_t*)ln_w, (const uint16_t*)ln_b, pos, dst,
-                       (uint16_t*)kv_cache, (uint16_t*)k_cache, n};
+                       (uint16_t*)kv_cache, (uint16_t*)k_cache, n, {}};
+  for (int i = 0; i < sa::kRope / 2; ++i) A.inv_freq[i] = std::pow(sa::kRopeTheta, -(double)(2 * i) / (double)sa::kRope);
   const int grid = (n + sa::kCwWaves - 1) / sa::kCwWaves;
   hipLaunchKernelGGL(sa::cache_write_kernel, dim3(grid), dim3(sa::kCwWaves * 64), 0, stream, A);
   return check_launch("cache_write_kernel");
