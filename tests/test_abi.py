@@ -81,6 +81,24 @@ def test_mla_rejects_bad_arguments(L):
     assert L.sa_mla_sparse_attn(*bad) == -1
 
 
+def test_cache_write_rejects_bad_arguments(L):
+    # kv_a, gamma, k_raw, ln_w, ln_b, pos, dst, n, kv_cache, k_cache, stream
+    ok = [FAKE, FAKE, None, None, None, FAKE, FAKE, 4, FAKE, None, None]
+    assert L.sa_cache_write(*ok[:7], -1, *ok[8:]) == -1
+    assert b"negative" in L.sa_last_error_message()
+    assert L.sa_cache_write(None, *ok[1:]) == -1
+    assert b"null pointer" in L.sa_last_error_message()
+    assert L.sa_cache_write(*ok[:8], None, *ok[9:]) == -1
+    assert L.sa_cache_write(ctypes.c_void_p(0x10008), *ok[1:]) == -1
+    assert b"aligned" in L.sa_last_error_message()
+    # an indexer key needs its norm weights and its cache
+    assert L.sa_cache_write(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 4, FAKE, FAKE, None) == -1
+    assert L.sa_cache_write(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, None, None) == -1
+    assert L.sa_cache_write(FAKE, FAKE, ctypes.c_void_p(0x10002), FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, None) == -1
+    # no tokens is a no-op that succeeds without a device
+    assert L.sa_cache_write(None, None, None, None, None, None, None, 0, None, None, None) == 0
+
+
 def test_layer_stack_rejects_bad_arguments(L):
     descs = (_lib.LayerDesc * 2)()
     for d in descs:
