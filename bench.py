@@ -204,7 +204,7 @@ def cache_write_leg(seed, reps=15, warmup=5, n=4096, rows=131072):
             "timing": "median of %d HIP-event-timed launches" % reps}
 
 
-def prefill_indexer(seed, reps=9, warmup=8):
+def prefill_indexer(seed, reps=9, warmup=20):
     import torch
     from sparse_attention_relu_amd import api, synth
     wl = synth.workload("c3")
@@ -217,7 +217,7 @@ def prefill_indexer(seed, reps=9, warmup=8):
     q_seq = torch.zeros(wl.n_q, dtype=torch.int32, device=dev)
     q_pos = torch.tensor(wl.q_pos, dtype=torch.int32, device=dev)
     scores = torch.empty((wl.n_q, wl.ld), dtype=torch.float32, device=dev)
-    # the clocks settle after a few launches of this 4 ms kernel
+    # the clocks settle over the first 10-15 launches of this 4 ms kernel
     for _ in range(warmup):
         api.indexer_score(q, w, kI, seq_start, q_seq, q_pos, wl.ld, scores=scores)
     torch.cuda.synchronize()
