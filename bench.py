@@ -214,18 +214,19 @@ def prefill_indexer(seed, reps=9, warmup=20):
     w = synth._randn((wl.n_q, 32), synth._gen(dev, seed, 0, 5), dev, std=1 / 32 ** 0.5)
     kI = synth.indexer_keys(wl.total_tokens, synth._gen(dev, seed, 0, 6), dev)
     seq_start = torch.zeros(1, dtype=torch.int64, device=dev)
+    seq_len = torch.tensor(wl.seq_lens, dtype=torch.int32, device=dev)
     q_seq = torch.zeros(wl.n_q, dtype=torch.int32, device=dev)
     q_pos = torch.tensor(wl.q_pos, dtype=torch.int32, device=dev)
     scores = torch.empty((wl.n_q, wl.ld), dtype=torch.float32, device=dev)
     # the clocks settle over the first 10-15 launches of this 4 ms kernel
     for _ in range(warmup):
-        api.indexer_score(q, w, kI, seq_start, q_seq, q_pos, wl.ld, scores=scores)
+        api.indexer_score(q, w, kI, seq_start, seq_len, q_seq, q_pos, wl.ld, scores=scores)
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for a, c in ev:
         a.record(s)
-        api.indexer_score(q, w, kI, seq_start, q_seq, q_pos, wl.ld, scores=scores, stream=s)
+        api.indexer_score(q, w, kI, seq_start, seq_len, q_seq, q_pos, wl.ld, scores=scores, stream=s)
         c.record(s)
     torch.cuda.synchronize()
     ms = sorted(a.elapsed_time(c) for a, c in ev)[len(ev) // 2]
@@ -281,7 +282,7 @@ def main():
     for c in range(max(1, args.copies)):
         b = synth.make_batch(wl, dev, seed=args.seed + c)
         batches.append(b)
-        stacks.append(api.LayerStack(b.layers, b.seq_start, b.q_seq, b.q_pos, wl.ld, full=wl.full))
+        stacks.append(api.LayerStack(b.layers, b.seq_start, b.seq_len, b.q_seq, b.q_pos, wl.ld, full=wl.full))
         stacks[-1]()
     b = batches[0]
     torch.cuda.synchronize()

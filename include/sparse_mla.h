@@ -39,9 +39,17 @@
  * Errors: every call returns SA_OK (0) or a negative sa_status.  Argument
  * checks happen on the host before anything is enqueued; a rejected call
  * enqueues nothing.  sa_last_error_message() gives a thread-local description
- * of the last failure.  Preconditions that depend on device data (q_pos below
- * the sequence length, q_pos < ld, finite inputs, idx entries in the causal
- * set) are documented per call and are not checked.
+ * of the last failure.  The shapes themselves are compile-time constants (the
+ * enum below), so the host checks cover counts, pointers, alignment, k, ld,
+ * the workspace size and grid limits.  Preconditions that depend on device
+ * data (q_seq < n_seq, q_pos below its sequence's length and below ld, idx
+ * entries in the causal set, sequences shorter than SA_MAX_SEQ_LEN, no NaN
+ * scores) are documented per call.  Release builds do not check them (that
+ * would need the data on the host, i.e. a synchronisation); the SA_DEBUG
+ * build (libsparse_mla_debug.so) checks them on the device inside every call
+ * and reports the first violation through sa_debug_check().  The indexer
+ * never reads past its sequence's keys even when q_pos violates them: it
+ * clamps the causal set at seq_len - 1.
  */
 #ifndef SPARSE_MLA_H
 #define SPARSE_MLA_H
@@ -62,7 +70,8 @@ enum sa_status {
   SA_ERR_INVALID_ARG = -1,   /* null pointer, negative size, k out of range, ... */
   SA_ERR_UNSUPPORTED = -2,   /* a request outside the fixed configuration */
   SA_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required */
-  SA_ERR_HIP = -4            /* a HIP launch or runtime call failed */
+  SA_ERR_HIP = -4,           /* a HIP launch or runtime call failed */
+  SA_ERR_DEBUG = -5          /* SA_DEBUG build: a device-side precondition check failed */
 };
 
 enum {
@@ -75,6 +84,12 @@ enum {
   SA_ROW = 576,              /* SA_LATENT + SA_ROPE: one cache row */
   SA_VDIM = 256              /* v_head_dim */
 };
+
+/* Longest sequence (rows of one layer's cache) the attention gather
+ * addresses: row offsets within a sequence are 32-bit byte offsets of
+ * 1152-byte rows, so position * 1152 + 1151 < 2^32.  The model's 1,048,576
+ * tokens are well inside. */
+#define SA_MAX_SEQ_LEN 3728270
 
 /* Library version, (major << 16) | (minor << 8) | patch. */
 int32_t sa_version(void);
@@ -99,16 +114,19 @@ const char* sa_last_error_message(void);
  *   w         fp32  [n_q, 32]        per-query head weights
  *   k_idx     bf16  [total_rows, 128] packed indexer keys
  *   seq_start int64 [n_seq]          first row of each sequence
+ *   seq_len   int32 [n_seq]          cached keys of each sequence (0 .. SA_MAX_SEQ_LEN)
  *   q_seq     int32 [n_q]            sequence of each query (0 <= q_seq < n_seq)
  *   q_pos     int32 [n_q]            position of each query (0 <= q_pos < ld,
- *                                    and below its sequence's length)
+ *                                    and q_pos < seq_len[q_seq])
  *   scores    fp32  [n_q, ld]        output; every entry is written
  *   ld        row length of scores (>= 1, < 2^31)
- * n_q = 0 is a no-op.
+ * n_q = 0 is a no-op.  Keys are read only at positions below seq_len: a query
+ * whose q_pos breaks q_pos < seq_len gets -inf from seq_len on (and the
+ * SA_DEBUG build reports it).
  */
 int32_t sa_indexer_score(const void* q_idx, const float* w, const void* k_idx,
-                         const int64_t* seq_start, const int32_t* q_seq, const int32_t* q_pos,
-                         int32_t n_q, int32_t n_seq, float* scores, int64_t ld,
+                         const int64_t* seq_start, const int32_t* seq_len, const int32_t* q_seq,
+                         const int32_t* q_pos, int32_t n_q, int32_t n_seq, float* scores, int64_t ld,
                          sa_stream_t stream);
 
 /*
@@ -151,7 +169,9 @@ int32_t sa_topk_select(const float* scores, int64_t ld, const int32_t* q_pos, in
  *
  *   q_abs   bf16  [n_q, 64, 576]
  *   kv      bf16  [total_rows, 576] packed cache rows of this layer
- *   idx     int32 [n_q, k]    positions in 0 .. q_pos[t], or -1
+ *   idx     int32 [n_q, k]    positions in 0 .. q_pos[t], or -1 (positions
+ *                             below SA_MAX_SEQ_LEN: the gather's row offsets
+ *                             within a sequence are 32-bit)
  *   k       1 .. 2048
  *   w_uv    bf16  [64, 256, 512]
  *   scale   softmax scale (1/sqrt(256) = 1/16 for this model)
@@ -181,8 +201,9 @@ int32_t sa_mla_sparse_attn(const void* q_abs, const void* kv, const int64_t* seq
  *                     idx int32 [n_q, k] (output: this layer's selection)
  *   every layer:      q_abs bf16 [n_q,64,576], kv bf16 [rows,576], w_uv bf16 [64,256,512],
  *                     out bf16 [n_q,64,256] (output)
- * sa_batch_desc: seq_start int64 [n_seq], q_seq int32 [n_q], q_pos int32 [n_q], the
- * counts, and ld (score row length, > max q_pos).
+ * sa_batch_desc: seq_start int64 [n_seq], seq_len int32 [n_seq], q_seq int32 [n_q],
+ * q_pos int32 [n_q], the counts, and ld (score row length, > max q_pos; at most
+ * SA_MAX_SEQ_LEN, so every selected position is one the gather can address).
  * events: optional (NULL or any NULL member = not recorded); hipEvents recorded on
  * `stream` just before and after the named stage of the FIRST layer where it runs.
  *   ws  workspace of at least sa_layer_stack_workspace_size(n_q, ld, k) bytes
@@ -201,6 +222,7 @@ typedef struct sa_layer_desc {
 
 typedef struct sa_batch_desc {
   const int64_t* seq_start;
+  const int32_t* seq_len;
   const int32_t* q_seq;
   const int32_t* q_pos;
   int32_t n_q;
@@ -272,9 +294,43 @@ int32_t sa_cache_write(const void* kv_a, const void* gamma, const void* k_raw, c
  * Returns SA_ERR_INVALID_ARG for an unknown algo.
  */
 int32_t sa_indexer_score_algo(const void* q_idx, const float* w, const void* k_idx,
-                              const int64_t* seq_start, const int32_t* q_seq, const int32_t* q_pos,
-                              int32_t n_q, int32_t n_seq, float* scores, int64_t ld,
-                              int32_t algo, sa_stream_t stream);
+                              const int64_t* seq_start, const int32_t* seq_len, const int32_t* q_seq,
+                              const int32_t* q_pos, int32_t n_q, int32_t n_seq, float* scores,
+                              int64_t ld, int32_t algo, sa_stream_t stream);
+
+/*
+ * Device-side precondition checks (the SA_DEBUG build).
+ *
+ * In libsparse_mla_debug.so (built with -DSA_DEBUG) every entry point above
+ * also enqueues, on its stream and before its own kernels, a check of the
+ * preconditions that depend on device data:
+ *   batch:   0 <= q_seq[t] < n_seq; 0 <= q_pos[t] < seq_len[q_seq[t]];
+ *            q_pos[t] < ld; 0 <= seq_len[b] <= SA_MAX_SEQ_LEN; seq_start[b] >= 0
+ *   top-k:   0 <= q_pos[t] < ld; no NaN in scores[t, 0 .. q_pos[t]]
+ *   attention: -1 <= idx[t, j] < SA_MAX_SEQ_LEN (and, inside sa_layer_stack,
+ *            idx[t, j] <= q_pos[t]); q_seq[t] >= 0
+ *   cache write: pos[i] >= 0, dst[i] >= 0
+ * The first violation (and a count of all of them) is kept in a device-side
+ * record.  The check kernels only read; the call's own kernels still run.
+ *
+ * sa_debug_check(stream) waits for `stream`, reads the record and clears it.
+ * It returns SA_OK when nothing was violated since the last check, and
+ * SA_ERR_DEBUG otherwise, with sa_last_error_message() naming the check, the
+ * query or sequence, and the offending value.  In the release library it does
+ * nothing and returns SA_ERR_UNSUPPORTED.  sa_debug_enabled() is 1 in the
+ * SA_DEBUG build, 0 otherwise.
+ *
+ * sa_debug_check_host runs the batch and attention-index checks above on
+ * HOST arrays (same rules, same messages), in both builds: for callers that
+ * keep the batch description on the host, and to exercise the checks without
+ * a GPU.  idx may be NULL (k is then ignored).  Returns SA_OK or SA_ERR_DEBUG;
+ * SA_ERR_INVALID_ARG for null arrays with a non-zero count.
+ */
+int32_t sa_debug_enabled(void);
+int32_t sa_debug_check(sa_stream_t stream);
+int32_t sa_debug_check_host(const int64_t* seq_start, const int32_t* seq_len, const int32_t* q_seq,
+                            const int32_t* q_pos, int32_t n_q, int32_t n_seq, int64_t ld,
+                            const int32_t* idx, int32_t k);
 int32_t sa_topk_select_algo(const float* scores, int64_t ld, const int32_t* q_pos, int32_t n_q,
                             int32_t k, int32_t* idx, void* ws, size_t ws_bytes, int32_t algo,
                             sa_stream_t stream);

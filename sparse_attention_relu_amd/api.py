@@ -51,21 +51,23 @@ def layer_is_full(layer: int) -> bool:
     return _lib.lib().sa_layer_is_full(int(layer)) == 1
 
 
-def indexer_score(q_idx, w, k_idx, seq_start, q_seq, q_pos, ld: int, scores=None, algo: int = 0, stream=None):
+def indexer_score(q_idx, w, k_idx, seq_start, seq_len, q_seq, q_pos, ld: int, scores=None, algo: int = 0,
+                  stream=None, library=None):
     n_q = q_idx.shape[0]
     _need(q_idx, "q_idx", torch.bfloat16, (n_q, IDX_HEADS, IDX_DIM))
     _need(w, "w", torch.float32, (n_q, IDX_HEADS))
     _need(k_idx, "k_idx", torch.bfloat16, (None, IDX_DIM))
     _need(seq_start, "seq_start", torch.int64, (None,))
+    _need(seq_len, "seq_len", torch.int32, (seq_start.shape[0],))
     _need(q_seq, "q_seq", torch.int32, (n_q,))
     _need(q_pos, "q_pos", torch.int32, (n_q,))
     if scores is None:
         scores = torch.empty((n_q, ld), dtype=torch.float32, device=q_idx.device)
     _need(scores, "scores", torch.float32, (n_q, ld))
-    st = _lib.lib().sa_indexer_score_algo(_ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(seq_start), _ptr(q_seq),
-                                          _ptr(q_pos), n_q, seq_start.shape[0], _ptr(scores), ld, algo,
-                                          _stream(stream))
-    _lib.check("sa_indexer_score", st)
+    L = library if library is not None else _lib.lib()
+    st = L.sa_indexer_score_algo(_ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(seq_start), _ptr(seq_len), _ptr(q_seq),
+                                 _ptr(q_pos), n_q, seq_start.shape[0], _ptr(scores), ld, algo, _stream(stream))
+    _lib.check("sa_indexer_score", st, L)
     return scores
 
 
@@ -135,13 +137,15 @@ class LayerStack:
     """Pre-marshalled arguments of sa_layer_stack for a fixed set of tensors,
     so a step costs one foreign call (and can be captured in a HIP graph)."""
 
-    def __init__(self, layers: Sequence, seq_start, q_seq, q_pos, ld: int, k: int = MAX_TOPK,
-                 scale: float = 1.0 / 16, full: Optional[List[bool]] = None, outs=None, idxs=None, ws=None):
+    def __init__(self, layers: Sequence, seq_start, seq_len, q_seq, q_pos, ld: int, k: int = MAX_TOPK,
+                 scale: float = 1.0 / 16, full: Optional[List[bool]] = None, outs=None, idxs=None, ws=None,
+                 library=None):
         n_q = q_pos.shape[0]
         dev = q_pos.device
         if full is None:
             full = [layer_is_full(l) for l in range(len(layers))]
         _need(seq_start, "seq_start", torch.int64, (None,))
+        _need(seq_len, "seq_len", torch.int32, (seq_start.shape[0],))
         _need(q_seq, "q_seq", torch.int32, (n_q,))
         _need(q_pos, "q_pos", torch.int32, (n_q,))
         self.outs = outs if outs is not None else [
@@ -162,9 +166,10 @@ class LayerStack:
             _need(L.w_uv, "w_uv", torch.bfloat16, (HEADS, VDIM, LATENT))
             d.q_abs, d.kv, d.w_uv, d.out = _ptr(L.q_abs), _ptr(L.kv), _ptr(L.w_uv), _ptr(self.outs[l])
         self._descs = descs
-        self._batch = _lib.BatchDesc(_ptr(seq_start), _ptr(q_seq), _ptr(q_pos), n_q, seq_start.shape[0], int(ld))
-        self._keep = (layers, seq_start, q_seq, q_pos)
-        lib = _lib.lib()
+        self._batch = _lib.BatchDesc(_ptr(seq_start), _ptr(seq_len), _ptr(q_seq), _ptr(q_pos), n_q,
+                                     seq_start.shape[0], int(ld))
+        self._keep = (layers, seq_start, seq_len, q_seq, q_pos)
+        self.lib = lib = library if library is not None else _lib.lib()
         nbytes = lib.sa_layer_stack_workspace_size(n_q, int(ld), k)
         self.ws = ws if ws is not None else workspace(nbytes, dev)
         self.n_layers, self.k, self.scale = len(layers), k, float(scale)
@@ -174,10 +179,10 @@ class LayerStack:
         ev = None
         if events is not None:     # six raw hipEvent_t handles (ints) or None
             ev = _lib.StageEvents(*events)
-        st = _lib.lib().sa_layer_stack(self._descs, self.n_layers, ctypes_byref(self._batch), self.k, self.scale,
-                                       _ptr(self.ws), self.ws.numel(), ctypes_byref(ev) if ev is not None else None,
-                                       _stream(stream))
-        _lib.check("sa_layer_stack", st)
+        st = self.lib.sa_layer_stack(self._descs, self.n_layers, ctypes_byref(self._batch), self.k, self.scale,
+                                     _ptr(self.ws), self.ws.numel(), ctypes_byref(ev) if ev is not None else None,
+                                     _stream(stream))
+        _lib.check("sa_layer_stack", st, self.lib)
         return self.outs, self.idxs
 
 
@@ -186,6 +191,13 @@ def ctypes_byref(x):
     return ctypes.byref(x)
 
 
-def layer_stack(layers, seq_start, q_seq, q_pos, ld: int, k: int = MAX_TOPK, scale: float = 1.0 / 16, full=None,
-                stream=None):
-    return LayerStack(layers, seq_start, q_seq, q_pos, ld, k, scale, full)(stream=stream)
+def layer_stack(layers, seq_start, seq_len, q_seq, q_pos, ld: int, k: int = MAX_TOPK, scale: float = 1.0 / 16,
+                full=None, stream=None):
+    return LayerStack(layers, seq_start, seq_len, q_seq, q_pos, ld, k, scale, full)(stream=stream)
+
+
+def debug_check(stream=None, library=None):
+    """sa_debug_check of the SA_DEBUG library (default): waits for the stream
+    and raises SparseMLAError if a device-side precondition check failed."""
+    L = library if library is not None else _lib.debug_lib()
+    _lib.check("sa_debug_check", L.sa_debug_check(_stream(stream)), L)

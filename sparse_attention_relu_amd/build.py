@@ -1,4 +1,5 @@
-"""Build libsparse_mla.so for gfx950 with hipcc (no GPU needed to build)."""
+"""Build libsparse_mla.so (release) and libsparse_mla_debug.so (SA_DEBUG:
+device-side precondition checks) for gfx950 with hipcc (no GPU needed)."""
 from __future__ import annotations
 
 import os
@@ -8,7 +9,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsparse_mla.so")
-SOURCES = ["abi.hip", "indexer.hip", "topk.hip", "mla.hip", "cache.hip"]
+DEBUG_LIB = os.path.join(HERE, "libsparse_mla_debug.so")
+SOURCES = ["abi.hip", "indexer.hip", "topk.hip", "mla.hip", "cache.hip", "debug.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -22,21 +24,33 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra=()) -> str:
+def _command(out: str, extra=()):
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *FLAGS, *extra, "-o", tmp, *srcs]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
-                    if "packed-fp32-ops" not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
-    if verbose and out.strip():
-        print(out)
-    os.replace(tmp, LIB)
+    return [hipcc, *FLAGS, *extra, "-o", out, *srcs]
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    """Compile both libraries (in parallel) and move them into place."""
+    jobs = [(LIB, list(extra)), (DEBUG_LIB, ["-DSA_DEBUG", *extra])]
+    procs = []
+    for lib, ex in jobs:
+        cmd = _command(lib + ".tmp", ex)
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((lib, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+    failed = []
+    for lib, p in procs:
+        text, _ = p.communicate()
+        out = "\n".join(l for l in text.splitlines() if "packed-fp32-ops" not in l)
+        if p.returncode != 0:
+            failed.append(f"{os.path.basename(lib)}: hipcc failed ({p.returncode}):\n{out}")
+        elif verbose and out.strip():
+            print(out)
+    if failed:
+        raise RuntimeError("\n".join(failed))
+    for lib, _ in procs:
+        os.replace(lib + ".tmp", lib)
     return LIB
 
 

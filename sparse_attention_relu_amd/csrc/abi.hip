@@ -30,8 +30,8 @@ int32_t check_launch(const char* what) {
 
 int indexer_algo(int32_t n_q, int32_t n_seq, int algo);
 int32_t launch_indexer(const void* q_idx, const float* w, const void* k_idx, const int64_t* seq_start,
-                       const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, int32_t n_seq, float* scores,
-                       int64_t ld, int algo, hipStream_t stream, uint32_t* clear, int64_t n_clear);
+                       const int32_t* seq_len, const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, int32_t n_seq,
+                       float* scores, int64_t ld, int algo, hipStream_t stream, uint32_t* clear, int64_t n_clear);
 void topk_clear_range(void* ws, int32_t n_q, int64_t ld, uint32_t** p, int64_t* n);
 
 size_t topk_workspace_size(int32_t n_q, int64_t ld, int32_t k);
@@ -46,6 +46,13 @@ int32_t launch_cache_write(const void* kv_a, const void* gamma, const void* k_ra
                            const int32_t* pos, const int64_t* dst, int32_t n, void* kv_cache, void* k_cache,
                            hipStream_t stream);
 
+int32_t debug_batch(const int64_t* seq_start, const int32_t* seq_len, const int32_t* q_seq, const int32_t* q_pos,
+                    int32_t n_q, int32_t n_seq, int64_t ld, hipStream_t stream);
+int32_t debug_idx(const int32_t* idx, int32_t n_q, int32_t k, const int32_t* q_pos, const int32_t* q_seq,
+                  hipStream_t stream);
+int32_t debug_scores(const float* scores, int64_t ld, const int32_t* q_pos, int32_t n_q, hipStream_t stream);
+int32_t debug_cache(const int32_t* pos, const int64_t* dst, int32_t n, hipStream_t stream);
+
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -58,12 +65,12 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
   } while (0)
 
 static int32_t check_indexer_args(const void* q_idx, const float* w, const void* k_idx, const int64_t* seq_start,
-                                  const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, int32_t n_seq,
-                                  const float* scores, int64_t ld) {
+                                  const int32_t* seq_len, const int32_t* q_seq, const int32_t* q_pos, int32_t n_q,
+                                  int32_t n_seq, const float* scores, int64_t ld) {
   SA_REQUIRE(n_q >= 0 && n_seq >= 0, SA_ERR_INVALID_ARG, "indexer: negative count (n_q=%d, n_seq=%d)", n_q, n_seq);
   if (n_q == 0) return SA_OK;
   SA_REQUIRE(n_seq >= 1, SA_ERR_INVALID_ARG, "indexer: queries without sequences");
-  SA_REQUIRE(q_idx && w && k_idx && seq_start && q_seq && q_pos && scores, SA_ERR_INVALID_ARG,
+  SA_REQUIRE(q_idx && w && k_idx && seq_start && seq_len && q_seq && q_pos && scores, SA_ERR_INVALID_ARG,
              "indexer: null pointer argument");
   SA_REQUIRE(aligned16(q_idx) && aligned16(k_idx), SA_ERR_INVALID_ARG, "indexer: q_idx/k_idx not 16-byte aligned");
   SA_REQUIRE(ld >= 1 && ld < ((int64_t)1 << 31), SA_ERR_INVALID_ARG, "indexer: ld=%lld out of range", (long long)ld);
@@ -108,7 +115,7 @@ using namespace sa_host;
 
 extern "C" {
 
-int32_t sa_version(void) { return (0 << 16) | (1 << 8) | 0; }
+int32_t sa_version(void) { return (0 << 16) | (2 << 8) | 0; }
 
 const char* sa_status_string(int32_t status) {
   switch (status) {
@@ -117,6 +124,7 @@ const char* sa_status_string(int32_t status) {
     case SA_ERR_UNSUPPORTED: return "unsupported request";
     case SA_ERR_WORKSPACE: return "workspace missing or too small";
     case SA_ERR_HIP: return "HIP runtime error";
+    case SA_ERR_DEBUG: return "debug check failed";
     default: return "unknown status";
   }
 }
@@ -129,20 +137,21 @@ int32_t sa_layer_is_full(int32_t layer) {
 }
 
 int32_t sa_indexer_score_algo(const void* q_idx, const float* w, const void* k_idx, const int64_t* seq_start,
-                              const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, int32_t n_seq, float* scores,
-                              int64_t ld, int32_t algo, sa_stream_t stream) {
-  int32_t rc = check_indexer_args(q_idx, w, k_idx, seq_start, q_seq, q_pos, n_q, n_seq, scores, ld);
+                              const int32_t* seq_len, const int32_t* q_seq, const int32_t* q_pos, int32_t n_q,
+                              int32_t n_seq, float* scores, int64_t ld, int32_t algo, sa_stream_t stream) {
+  int32_t rc = check_indexer_args(q_idx, w, k_idx, seq_start, seq_len, q_seq, q_pos, n_q, n_seq, scores, ld);
   if (rc) return rc;
   SA_REQUIRE(algo >= 0 && algo <= 2, SA_ERR_INVALID_ARG, "indexer: unknown algo %d", algo);
   if (n_q == 0) return SA_OK;
-  return launch_indexer(q_idx, w, k_idx, seq_start, q_seq, q_pos, n_q, n_seq, scores, ld, algo, (hipStream_t)stream,
-                        nullptr, 0);
+  if ((rc = debug_batch(seq_start, seq_len, q_seq, q_pos, n_q, n_seq, ld, (hipStream_t)stream))) return rc;
+  return launch_indexer(q_idx, w, k_idx, seq_start, seq_len, q_seq, q_pos, n_q, n_seq, scores, ld, algo,
+                        (hipStream_t)stream, nullptr, 0);
 }
 
 int32_t sa_indexer_score(const void* q_idx, const float* w, const void* k_idx, const int64_t* seq_start,
-                         const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, int32_t n_seq, float* scores,
-                         int64_t ld, sa_stream_t stream) {
-  return sa_indexer_score_algo(q_idx, w, k_idx, seq_start, q_seq, q_pos, n_q, n_seq, scores, ld, 0, stream);
+                         const int32_t* seq_len, const int32_t* q_seq, const int32_t* q_pos, int32_t n_q,
+                         int32_t n_seq, float* scores, int64_t ld, sa_stream_t stream) {
+  return sa_indexer_score_algo(q_idx, w, k_idx, seq_start, seq_len, q_seq, q_pos, n_q, n_seq, scores, ld, 0, stream);
 }
 
 size_t sa_topk_workspace_size(int32_t n_q, int64_t ld, int32_t k) {
@@ -159,6 +168,7 @@ int32_t sa_topk_select_algo(const float* scores, int64_t ld, const int32_t* q_po
   const size_t need = topk_workspace_size(n_q, ld, k);
   SA_REQUIRE(ws && ws_bytes >= need, SA_ERR_WORKSPACE, "topk: workspace of %zu bytes, %zu needed", ws_bytes, need);
   SA_REQUIRE(((uintptr_t)ws & 255u) == 0, SA_ERR_INVALID_ARG, "topk: workspace not 256-byte aligned");
+  if ((rc = debug_scores(scores, ld, q_pos, n_q, (hipStream_t)stream))) return rc;
   return launch_topk(scores, ld, q_pos, n_q, k, idx, ws, algo, (hipStream_t)stream, false);
 }
 
@@ -181,6 +191,7 @@ int32_t sa_mla_sparse_attn(const void* q_abs, const void* kv, const int64_t* seq
   const size_t need = mla_workspace_size(n_q, k);
   SA_REQUIRE(ws && ws_bytes >= need, SA_ERR_WORKSPACE, "mla: workspace of %zu bytes, %zu needed", ws_bytes, need);
   SA_REQUIRE(((uintptr_t)ws & 255u) == 0, SA_ERR_INVALID_ARG, "mla: workspace not 256-byte aligned");
+  if ((rc = debug_idx(idx, n_q, k, nullptr, q_seq, (hipStream_t)stream))) return rc;
   return launch_mla(q_abs, kv, seq_start, q_seq, idx, n_q, k, w_uv, scale, out, lse, ws, (hipStream_t)stream);
 }
 
@@ -199,6 +210,11 @@ int32_t sa_layer_stack(const sa_layer_desc* layers, int32_t n_layers, const sa_b
   const int64_t ld = batch->ld;
   SA_REQUIRE(n_q >= 0 && batch->n_seq >= 0, SA_ERR_INVALID_ARG, "layer_stack: negative count");
   if (n_layers == 0 || n_q == 0) return SA_OK;
+  // Every selected position is below ld; the attention gather addresses
+  // positions below SA_MAX_SEQ_LEN (32-bit row offsets within a sequence).
+  SA_REQUIRE(ld >= 1 && ld <= SA_MAX_SEQ_LEN, SA_ERR_UNSUPPORTED,
+             "layer_stack: ld=%lld outside 1..%d (the longest sequence the attention gather addresses)",
+             (long long)ld, SA_MAX_SEQ_LEN);
   SA_REQUIRE(layers[0].is_full, SA_ERR_INVALID_ARG, "layer_stack: layer 0 must run its own indexer");
   const size_t need = sa_layer_stack_workspace_size(n_q, ld, k);
   SA_REQUIRE(ws && ws_bytes >= need, SA_ERR_WORKSPACE, "layer_stack: workspace of %zu bytes, %zu needed", ws_bytes,
@@ -209,8 +225,8 @@ int32_t sa_layer_stack(const sa_layer_desc* layers, int32_t n_layers, const sa_b
     const sa_layer_desc& L = layers[l];
     int32_t rc;
     if (L.is_full) {
-      rc = check_indexer_args(L.q_idx, L.w, L.k_idx, batch->seq_start, batch->q_seq, batch->q_pos, n_q,
-                              batch->n_seq, (const float*)ws, ld);
+      rc = check_indexer_args(L.q_idx, L.w, L.k_idx, batch->seq_start, batch->seq_len, batch->q_seq, batch->q_pos,
+                              n_q, batch->n_seq, (const float*)ws, ld);
       if (rc) return rc;
       SA_REQUIRE(L.idx, SA_ERR_INVALID_ARG, "layer_stack: full layer %d has no idx buffer", l);
     }
@@ -243,13 +259,15 @@ int32_t sa_layer_stack(const sa_layer_desc* layers, int32_t n_layers, const sa_b
   uint32_t* clear = nullptr;
   int64_t n_clear = 0;
   if (ialgo == 1) topk_clear_range(topk_ws, n_q, ld, &clear, &n_clear);
+  if ((rc = debug_batch(batch->seq_start, batch->seq_len, batch->q_seq, batch->q_pos, n_q, batch->n_seq, ld, st)))
+    return rc;
   for (int l = 0; l < n_layers; ++l) {
     const sa_layer_desc& L = layers[l];
     if (L.is_full) {
       const bool ev = events && !rec_idx && events->indexer_begin && events->indexer_end;
       if (ev && (rc = record(events->indexer_begin, st))) return rc;
-      rc = launch_indexer(L.q_idx, L.w, L.k_idx, batch->seq_start, batch->q_seq, batch->q_pos, n_q, batch->n_seq, scores,
-                          ld, ialgo, st, clear, n_clear);
+      rc = launch_indexer(L.q_idx, L.w, L.k_idx, batch->seq_start, batch->seq_len, batch->q_seq, batch->q_pos, n_q,
+                          batch->n_seq, scores, ld, ialgo, st, clear, n_clear);
       if (rc) return rc;
       if (ev && (rc = record(events->indexer_end, st))) return rc;
       rec_idx |= ev;
@@ -257,6 +275,7 @@ int32_t sa_layer_stack(const sa_layer_desc* layers, int32_t n_layers, const sa_b
       if (evt && (rc = record(events->topk_begin, st))) return rc;
       rc = launch_topk(scores, ld, batch->q_pos, n_q, k, L.idx, topk_ws, 0, st, ialgo == 1);
       if (rc) return rc;
+      if ((rc = debug_idx(L.idx, n_q, k, batch->q_pos, nullptr, st))) return rc;
       if (evt && (rc = record(events->topk_end, st))) return rc;
       rec_topk |= evt;
       cur_idx = L.idx;
@@ -285,6 +304,8 @@ int32_t sa_cache_write(const void* kv_a, const void* gamma, const void* k_raw, c
     SA_REQUIRE((((uintptr_t)k_raw | (uintptr_t)ln_w | (uintptr_t)ln_b | (uintptr_t)k_cache) & 3u) == 0,
                SA_ERR_INVALID_ARG, "cache_write: indexer key pointers not 4-byte aligned");
   }
+  int32_t rc = debug_cache(pos, dst, n, (hipStream_t)stream);
+  if (rc) return rc;
   return launch_cache_write(kv_a, gamma, k_raw, ln_w, ln_b, pos, dst, n, kv_cache, k_cache, (hipStream_t)stream);
 }
 

@@ -66,6 +66,7 @@ struct DecArgs {
   const float* w;
   const uint16_t* k_idx;
   const int64_t* seq_start;
+  const int32_t* seq_len;
   const int32_t* q_seq;
   const int32_t* q_pos;
   float* scores;
@@ -92,7 +93,10 @@ __global__ __launch_bounds__(kDecThreads) void indexer_decode_kernel(DecArgs A) 
   const int chunk = blockIdx.x - t * A.n_chunks;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t pos = A.q_pos[t];
+  const int seq = A.q_seq[t];
+  // the causal set, clamped to the sequence's keys (q_pos < seq_len is a
+  // precondition; the clamp keeps a violation from reading other rows)
+  const int64_t pos = min((int64_t)A.q_pos[t], (int64_t)A.seq_len[seq] - 1);
   const int64_t c0 = (int64_t)chunk * kDecChunk;
   float* srow = A.scores + (int64_t)t * A.ld;
   if (c0 > pos) {
@@ -107,7 +111,7 @@ __global__ __launch_bounds__(kDecThreads) void indexer_decode_kernel(DecArgs A) 
   // and score columns are handled relative to c0 in 32 bits
   const int wlast = (int)min(pos - c0, (int64_t)kDecChunk - 1);       // last valid key
   const int wend = (int)min(A.ld - c0, (int64_t)kDecChunk);          // columns of this chunk in the row
-  const uint16_t* kb = A.k_idx + (A.seq_start[A.q_seq[t]] + c0) * kIdxDim;
+  const uint16_t* kb = A.k_idx + (A.seq_start[seq] + c0) * kIdxDim;
   float* sc0 = srow + c0;
   const int n_it = kDecSteps;
   uint8_t* my = lds[wave];
@@ -198,8 +202,8 @@ constexpr int kPfSplit = 16384;    // keys per workgroup
 
 __global__ __launch_bounds__(kPfThreads, 512 / kPfThreads) void indexer_prefill_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
-    const int64_t* __restrict__ seq_start, const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos,
-    int n_q, float* __restrict__ scores, int64_t ld, int n_splits) {
+    const int64_t* __restrict__ seq_start, const int32_t* __restrict__ seq_len, const int32_t* __restrict__ q_seq,
+    const int32_t* __restrict__ q_pos, int n_q, float* __restrict__ scores, int64_t ld, int n_splits) {
   // Workgroups are dealt to the 8 XCDs round-robin (bid % 8).  Give each XCD a
   // contiguous run of the split-major work list, so the workgroups resident on
   // one XCD share the same 4 MB key split in that XCD's L2.
@@ -225,8 +229,10 @@ __global__ __launch_bounds__(kPfThreads, 512 / kPfThreads) void indexer_prefill_
   }
   if (threadIdx.x < kPfQ) {
     const int t = t_base + threadIdx.x;
-    sh_seq[threadIdx.x] = t < n_q ? q_seq[t] : -1;
-    sh_pos[threadIdx.x] = t < n_q ? q_pos[t] : -1;
+    const int sq = t < n_q ? q_seq[t] : -1;
+    sh_seq[threadIdx.x] = sq;
+    // causal set clamped to the sequence's keys (-1: no key; the row is all -inf)
+    sh_pos[threadIdx.x] = t < n_q ? min(q_pos[t], seq_len[sq] - 1) : -1;
     sh_done[threadIdx.x] = t < n_q ? 0 : 1;
   }
   __syncthreads();
@@ -264,8 +270,10 @@ __global__ __launch_bounds__(kPfThreads, 512 / kPfThreads) void indexer_prefill_
     if (cur < 0) break;
     for (int i = 0; i < kPfQ; ++i)
       if (!sh_done[i] && sh_seq[i] == cur) maxpos = max(maxpos, (int64_t)sh_pos[i]);
-    const bool act0 = seq[0] == cur && pos[0] >= 0;
-    const bool act1 = seq[1] == cur && pos[1] >= 0;
+    // (queries past n_q have seq -1; a query with no key has pos -1 and
+    // gets -inf everywhere)
+    const bool act0 = seq[0] == cur;
+    const bool act1 = seq[1] == cur;
     const uint16_t* kbase = k_idx + seq_start[cur] * kIdxDim;
     const int64_t cend = min(s1, maxpos + 1);              // keys that need a product
     const int n_tiles = cend > s0 ? (int)((cend - s0 + kPfKT - 1) / kPfKT) : 0;
@@ -387,8 +395,8 @@ int indexer_algo(int32_t n_q, int32_t n_seq, int algo) {
 // clear / n_clear: words the decode kernel (algo 1) sets to zero on the side;
 // the caller passes none with algo 2.
 int32_t launch_indexer(const void* q_idx, const float* w, const void* k_idx, const int64_t* seq_start,
-                       const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, int32_t n_seq, float* scores,
-                       int64_t ld, int algo, hipStream_t stream, uint32_t* clear, int64_t n_clear) {
+                       const int32_t* seq_len, const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, int32_t n_seq,
+                       float* scores, int64_t ld, int algo, hipStream_t stream, uint32_t* clear, int64_t n_clear) {
   algo = indexer_algo(n_q, n_seq, algo);
   if (algo != 1 && n_clear > 0) {
     set_error("indexer: only the decode kernel clears words on the side");
@@ -401,8 +409,8 @@ int32_t launch_indexer(const void* q_idx, const float* w, const void* k_idx, con
       set_error("indexer: grid of %lld workgroups is too large", (long long)grid);
       return SA_ERR_UNSUPPORTED;
     }
-    sa::DecArgs A{(const uint16_t*)q_idx, w, (const uint16_t*)k_idx, seq_start, q_seq, q_pos, scores, ld, n_chunks,
-                  clear, n_clear > 0 ? n_clear : 0};
+    sa::DecArgs A{(const uint16_t*)q_idx, w, (const uint16_t*)k_idx, seq_start, seq_len, q_seq, q_pos, scores, ld,
+                  n_chunks, clear, n_clear > 0 ? n_clear : 0};
     hipLaunchKernelGGL(sa::indexer_decode_kernel, dim3((unsigned)grid), dim3(sa::kDecThreads), 0, stream, A);
     return check_launch("indexer_decode_kernel");
   }
@@ -414,8 +422,8 @@ int32_t launch_indexer(const void* q_idx, const float* w, const void* k_idx, con
     return SA_ERR_UNSUPPORTED;
   }
   hipLaunchKernelGGL(sa::indexer_prefill_kernel, dim3((unsigned)grid), dim3(sa::kPfThreads), 0, stream,
-                     (const uint16_t*)q_idx, w, (const uint16_t*)k_idx, seq_start, q_seq, q_pos, n_q, scores, ld,
-                     n_splits);
+                     (const uint16_t*)q_idx, w, (const uint16_t*)k_idx, seq_start, seq_len, q_seq, q_pos, n_q, scores,
+                     ld, n_splits);
   return check_launch("indexer_prefill_kernel");
 }
 

@@ -178,6 +178,7 @@ class LayerInputs:
 class Batch:
     wl: Workload
     seq_start: torch.Tensor     # int64 [n_seq]
+    seq_len: torch.Tensor       # int32 [n_seq]
     q_seq: torch.Tensor         # int32 [n_q]
     q_pos: torch.Tensor         # int32 [n_q]
     layers: List[LayerInputs]
@@ -207,6 +208,7 @@ def make_batch(wl: Workload, device, seed: int = 0, layers=None) -> Batch:
     return Batch(
         wl=wl,
         seq_start=torch.tensor(wl.seq_start, dtype=torch.int64, device=dev),
+        seq_len=torch.tensor(wl.seq_lens, dtype=torch.int32, device=dev),
         q_seq=torch.tensor(wl.q_seq, dtype=torch.int32, device=dev),
         q_pos=torch.tensor(wl.q_pos, dtype=torch.int32, device=dev),
         layers=[make_layer(wl, l, dev, seed) for l in layer_ids],

@@ -34,7 +34,8 @@ def test_every_declared_symbol_is_exported(L):
 def test_version_and_status_strings(L):
     assert L.sa_version() > 0
     for code, text in [(0, b"ok"), (-1, b"invalid argument"), (-2, b"unsupported request"),
-                       (-3, b"workspace missing or too small"), (-4, b"HIP runtime error")]:
+                       (-3, b"workspace missing or too small"), (-4, b"HIP runtime error"),
+                       (-5, b"debug check failed")]:
         assert L.sa_status_string(code) == text
     assert L.sa_status_string(-99) == b"unknown status"
 
@@ -48,16 +49,20 @@ FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails i
 
 
 def test_indexer_rejects_bad_arguments(L):
-    assert L.sa_indexer_score(None, None, None, None, None, None, 1, 1, None, 10, None) == -1
+    F6 = [FAKE] * 7
+    assert L.sa_indexer_score(*[None] * 7, 1, 1, None, 10, None) == -1
     assert b"null pointer" in L.sa_last_error_message()
-    assert L.sa_indexer_score(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -1, 1, FAKE, 10, None) == -1
-    assert L.sa_indexer_score(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, FAKE, 0, None) == -1
-    assert L.sa_indexer_score(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 0, FAKE, 5, None) == -1
-    assert L.sa_indexer_score(ctypes.c_void_p(0x10008), FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, FAKE, 5, None) == -1
+    assert L.sa_indexer_score(*F6, -1, 1, FAKE, 10, None) == -1
+    assert L.sa_indexer_score(*F6, 1, 1, FAKE, 0, None) == -1
+    assert L.sa_indexer_score(*F6, 1, 0, FAKE, 5, None) == -1
+    assert L.sa_indexer_score(ctypes.c_void_p(0x10008), *F6[1:], 1, 1, FAKE, 5, None) == -1
     assert b"aligned" in L.sa_last_error_message()
-    assert L.sa_indexer_score_algo(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, FAKE, 5, 7, None) == -1
+    # seq_len is required
+    assert L.sa_indexer_score(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1, 1, FAKE, 5, None) == -1
+    assert b"null pointer" in L.sa_last_error_message()
+    assert L.sa_indexer_score_algo(*F6, 1, 1, FAKE, 5, 7, None) == -1
     # n_q = 0 is a no-op that succeeds without a device
-    assert L.sa_indexer_score(None, None, None, None, None, None, 0, 0, None, 1, None) == 0
+    assert L.sa_indexer_score(*[None] * 7, 0, 0, None, 1, None) == 0
 
 
 def test_topk_rejects_bad_arguments(L):
@@ -104,7 +109,7 @@ def test_layer_stack_rejects_bad_arguments(L):
     for d in descs:
         d.q_idx = d.w = d.k_idx = d.idx = d.q_abs = d.kv = d.w_uv = d.out = 0x10000
     descs[0].is_full, descs[1].is_full = 0, 1
-    batch = _lib.BatchDesc(0x10000, 0x10000, 0x10000, 4, 1, 100)
+    batch = _lib.BatchDesc(0x10000, 0x10000, 0x10000, 0x10000, 4, 1, 100)
     big = 1 << 40
     rc = L.sa_layer_stack(descs, 2, ctypes.byref(batch), 2048, 1.0 / 16, FAKE, big, None, None)
     assert rc == -1 and b"layer 0" in L.sa_last_error_message()
@@ -115,6 +120,12 @@ def test_layer_stack_rejects_bad_arguments(L):
     assert rc == -1 and b"layer 1" in L.sa_last_error_message()
     assert L.sa_layer_stack(descs, 2, ctypes.byref(batch), 0, 1.0 / 16, FAKE, big, None, None) == -1
     assert L.sa_layer_stack(None, 2, ctypes.byref(batch), 16, 1.0 / 16, FAKE, big, None, None) == -1
+    descs[1].kv = 0x10000
+    # ld beyond the longest sequence the attention gather addresses
+    for bad_ld in (0, 3728271, 1 << 31):
+        batch.ld = bad_ld
+        rc = L.sa_layer_stack(descs, 2, ctypes.byref(batch), 2048, 1.0 / 16, FAKE, big, None, None)
+        assert rc == -2 and b"ld=" in L.sa_last_error_message(), bad_ld
 
 
 def test_workspace_sizes(L):

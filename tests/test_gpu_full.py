@@ -40,7 +40,7 @@ def _check_mla_compact(L, wl, idx, out, queries):
 
 def _run_stack(wl, seed=0):
     b = synth.make_batch(wl, DEV, seed=seed)
-    stack = api.LayerStack(b.layers, b.seq_start, b.q_seq, b.q_pos, wl.ld, full=wl.full)
+    stack = api.LayerStack(b.layers, b.seq_start, b.seq_len, b.q_seq, b.q_pos, wl.ld, full=wl.full)
     outs, idxs = stack()
     torch.cuda.synchronize()
     return b, stack, outs, idxs
@@ -51,7 +51,7 @@ def test_decode_config_full(gpu_lib, name):
     wl = synth.workload(name)
     b, stack, outs, idxs = _run_stack(wl)
     L0 = b.layers[0]
-    sc = api.indexer_score(L0.q_idx, L0.w, L0.k_idx, b.seq_start, b.q_seq, b.q_pos, wl.ld)
+    sc = api.indexer_score(L0.q_idx, L0.w, L0.k_idx, b.seq_start, b.seq_len, b.q_seq, b.q_pos, wl.ld)
     idx_sep = api.topk_select(sc, b.q_pos)
     torch.cuda.synchronize()
     assert torch.equal(idx_sep, idxs[0]), "layer_stack selection differs from the separate calls"
@@ -72,7 +72,7 @@ def test_prefill_config_sampled(gpu_lib):
     wl = synth.workload("c3")
     b, stack, outs, idxs = _run_stack(wl)
     L0 = b.layers[0]
-    sc = api.indexer_score(L0.q_idx, L0.w, L0.k_idx, b.seq_start, b.q_seq, b.q_pos, wl.ld)
+    sc = api.indexer_score(L0.q_idx, L0.w, L0.k_idx, b.seq_start, b.seq_len, b.q_seq, b.q_pos, wl.ld)
     torch.cuda.synchronize()
     rng = np.random.Generator(np.random.PCG64(3))
     rows = sorted(set([0, 1, 2047, 4095] + list(rng.choice(wl.n_q, 12, replace=False))))
@@ -106,7 +106,7 @@ def test_decode_1m_78_layers(gpu_lib):
     B = parity.np_batch(b)
     for l in (full_layers[0], full_layers[-1]):
         L = b.layers[l]
-        sc = api.indexer_score(L.q_idx, L.w, L.k_idx, b.seq_start, b.q_seq, b.q_pos, wl.ld)
+        sc = api.indexer_score(L.q_idx, L.w, L.k_idx, b.seq_start, b.seq_len, b.q_seq, b.q_pos, wl.ld)
         torch.cuda.synchronize()
         sc_np = to_numpy(sc)
         Lnp = {"q_idx": to_numpy(L.q_idx), "w": to_numpy(L.w), "k_idx": to_numpy(L.k_idx)}

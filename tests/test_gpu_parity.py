@@ -41,7 +41,7 @@ def test_indexer_scores(gpu_lib, case, algo):
     wl = CASES[case]()
     b = _batch(wl)
     L = b.layers[0]
-    sc = api.indexer_score(L.q_idx, L.w, L.k_idx, b.seq_start, b.q_seq, b.q_pos, wl.ld + 37, algo=algo)
+    sc = api.indexer_score(L.q_idx, L.w, L.k_idx, b.seq_start, b.seq_len, b.q_seq, b.q_pos, wl.ld + 37, algo=algo)
     torch.cuda.synchronize()
     worst = parity.check_scores(parity.layer_np(L), parity.np_batch(b), to_numpy(sc))
     print(f"{case} algo {algo}: worst |err|/bound = {worst:.3g}")
@@ -53,7 +53,7 @@ def test_topk_on_gpu_scores(gpu_lib, case, algo):
     wl = CASES[case]()
     b = _batch(wl)
     L = b.layers[0]
-    sc = api.indexer_score(L.q_idx, L.w, L.k_idx, b.seq_start, b.q_seq, b.q_pos, wl.ld)
+    sc = api.indexer_score(L.q_idx, L.w, L.k_idx, b.seq_start, b.seq_len, b.q_seq, b.q_pos, wl.ld)
     for k in (2048, 1000, 1):
         idx = api.topk_select(sc, b.q_pos, k=k, algo=algo)
         torch.cuda.synchronize()
@@ -105,7 +105,7 @@ def test_mla_on_gpu_selection(gpu_lib, case):
     wl = CASES[case]()
     b = _batch(wl)
     L = b.layers[0]
-    sc = api.indexer_score(L.q_idx, L.w, L.k_idx, b.seq_start, b.q_seq, b.q_pos, wl.ld)
+    sc = api.indexer_score(L.q_idx, L.w, L.k_idx, b.seq_start, b.seq_len, b.q_seq, b.q_pos, wl.ld)
     idx = api.topk_select(sc, b.q_pos, k=2048)
     lse = torch.empty((wl.n_q, 64), dtype=torch.float32, device=DEV)
     out = api.mla_sparse_attn(L.q_abs, L.kv, b.seq_start, b.q_seq, idx, L.w_uv, wl.scale, lse=lse)
@@ -124,7 +124,7 @@ def test_mla_slice_counts(gpu_lib, n_q):
     wl = synth.ragged_workload(lens, queries, name=f"slices{n_q}")
     b = _batch(wl, seed=11 + n_q)
     L = b.layers[0]
-    sc = api.indexer_score(L.q_idx, L.w, L.k_idx, b.seq_start, b.q_seq, b.q_pos, wl.ld)
+    sc = api.indexer_score(L.q_idx, L.w, L.k_idx, b.seq_start, b.seq_len, b.q_seq, b.q_pos, wl.ld)
     idx = api.topk_select(sc, b.q_pos, k=2048)
     lse = torch.empty((wl.n_q, 64), dtype=torch.float32, device=DEV)
     out = api.mla_sparse_attn(L.q_abs, L.kv, b.seq_start, b.q_seq, idx, L.w_uv, wl.scale, lse=lse)
@@ -144,7 +144,7 @@ def test_mla_all_heads_per_workgroup(gpu_lib, n_q):
     wl = synth.ragged_workload(lens, queries, name=f"heads64_{n_q}")
     b = _batch(wl, seed=21 + n_q)
     L = b.layers[0]
-    sc = api.indexer_score(L.q_idx, L.w, L.k_idx, b.seq_start, b.q_seq, b.q_pos, wl.ld)
+    sc = api.indexer_score(L.q_idx, L.w, L.k_idx, b.seq_start, b.seq_len, b.q_seq, b.q_pos, wl.ld)
     idx = api.topk_select(sc, b.q_pos, k=2048)
     lse = torch.empty((wl.n_q, 64), dtype=torch.float32, device=DEV)
     out = api.mla_sparse_attn(L.q_abs, L.kv, b.seq_start, b.q_seq, idx, L.w_uv, wl.scale, lse=lse)
@@ -188,13 +188,13 @@ def test_layer_stack_matches_separate_calls(gpu_lib):
     wl = ragged_wl(n_layers=4)
     wl.full = [True, False, False, True]
     b = _batch(wl, seed=11)
-    stack = api.LayerStack(b.layers, b.seq_start, b.q_seq, b.q_pos, wl.ld, full=wl.full)
+    stack = api.LayerStack(b.layers, b.seq_start, b.seq_len, b.q_seq, b.q_pos, wl.ld, full=wl.full)
     outs, idxs = stack()
     torch.cuda.synchronize()
     cur = None
     for l, L in enumerate(b.layers):
         if wl.full[l]:
-            sc = api.indexer_score(L.q_idx, L.w, L.k_idx, b.seq_start, b.q_seq, b.q_pos, wl.ld)
+            sc = api.indexer_score(L.q_idx, L.w, L.k_idx, b.seq_start, b.seq_len, b.q_seq, b.q_pos, wl.ld)
             cur = api.topk_select(sc, b.q_pos)
             assert torch.equal(cur, idxs[l])
         o = api.mla_sparse_attn(L.q_abs, L.kv, b.seq_start, b.q_seq, cur, L.w_uv, wl.scale)
@@ -209,7 +209,7 @@ def test_layer_stack_matches_separate_calls(gpu_lib):
 def test_deterministic(gpu_lib):
     wl = ragged_wl(n_layers=2)
     b = _batch(wl, seed=13)
-    stack = api.LayerStack(b.layers, b.seq_start, b.q_seq, b.q_pos, wl.ld)
+    stack = api.LayerStack(b.layers, b.seq_start, b.seq_len, b.q_seq, b.q_pos, wl.ld)
     o1, i1 = stack()
     o1 = [x.clone() for x in o1]
     i1 = i1[0].clone()
@@ -223,7 +223,7 @@ def test_deterministic(gpu_lib):
 def test_graph_replay_matches_eager(gpu_lib):
     wl = ragged_wl(n_layers=4)
     b = _batch(wl, seed=17)
-    stack = api.LayerStack(b.layers, b.seq_start, b.q_seq, b.q_pos, wl.ld)
+    stack = api.LayerStack(b.layers, b.seq_start, b.seq_len, b.q_seq, b.q_pos, wl.ld)
     outs, idxs = stack()
     torch.cuda.synchronize()
     ref_o = [o.clone() for o in outs]
