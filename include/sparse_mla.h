@@ -241,6 +241,27 @@ int32_t sa_layer_stack(const sa_layer_desc* layers, int32_t n_layers, const sa_b
                        int32_t k, float scale, void* ws, size_t ws_bytes,
                        const sa_stage_events* events, sa_stream_t stream);
 
+/*
+ * sa_layer_stack_noalloc -- sa_layer_stack for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same call without a workspace argument.  Its
+ * workspace is a static device array of SA_NOALLOC_SCRATCH_BYTES (64 MiB) per
+ * GPU, part of the library's code object, held until the process ends; the
+ * call allocates and frees nothing.  A batch whose
+ * sa_layer_stack_workspace_size(n_q, ld, k) exceeds that size is rejected with
+ * SA_ERR_WORKSPACE before anything is enqueued (64 MiB holds, e.g., 16
+ * queries over 131,072-position rows, or 64 over 32,768).  Every call on one
+ * GPU shares that GPU's array and leaves its contents behind (the call clears
+ * what it needs at zero itself): two calls that overlap on one GPU (on
+ * different streams, or from different threads) race and must not be issued.
+ * The first call on a device looks up the array's address on that device.
+ * Results equal sa_layer_stack's bit for bit.
+ */
+#define SA_NOALLOC_SCRATCH_BYTES (64u << 20)
+size_t sa_layer_stack_noalloc_max_bytes(void);
+int32_t sa_layer_stack_noalloc(const sa_layer_desc* layers, int32_t n_layers, const sa_batch_desc* batch,
+                               int32_t k, float scale, const sa_stage_events* events, sa_stream_t stream);
+
 /* IndexShare pattern of the 78-layer model: 1 if layer runs its own indexer
  * (layers 0-2, then every layer l with l mod 4 == 2), else 0; -1 if layer < 0. */
 int32_t sa_layer_is_full(int32_t layer);

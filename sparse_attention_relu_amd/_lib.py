@@ -45,6 +45,9 @@ SIGNATURES = {
     "sa_layer_stack_workspace_size": (c_sz, [c_i32, c_i64, c_i32]),
     "sa_layer_stack": (c_i32, [ctypes.POINTER(LayerDesc), c_i32, ctypes.POINTER(BatchDesc), c_i32, c_f32, c_p,
                                c_sz, ctypes.POINTER(StageEvents), c_p]),
+    "sa_layer_stack_noalloc_max_bytes": (c_sz, []),
+    "sa_layer_stack_noalloc": (c_i32, [ctypes.POINTER(LayerDesc), c_i32, ctypes.POINTER(BatchDesc), c_i32, c_f32,
+                                       ctypes.POINTER(StageEvents), c_p]),
     "sa_debug_enabled": (c_i32, []),
     "sa_debug_check": (c_i32, [c_p]),
     "sa_debug_check_host": (c_i32, [c_p, c_p, c_p, c_p, c_i32, c_i32, c_i64, c_p, c_i32]),

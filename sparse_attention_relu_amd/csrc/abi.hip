@@ -6,7 +6,15 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "sa_common.h"
+
+// Workspace of sa_layer_stack_noalloc: one array per GPU, held until the
+// process ends.  Host code never uses this name as an address (on the host it
+// is only a stand-in); it uses the per-device pointer from
+// hipGetSymbolAddress instead.
+static __device__ __align__(256) uint8_t scratch[SA_NOALLOC_SCRATCH_BYTES];
 
 namespace sa_host {
 
@@ -289,6 +297,52 @@ int32_t sa_layer_stack(const sa_layer_desc* layers, int32_t n_layers, const sa_b
     rec_attn |= eva;
   }
   return SA_OK;
+}
+
+// Per-device address of `scratch`, looked up once per device with that
+// device current (the first sa_layer_stack_noalloc call on it).
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64];
+
+static int32_t scratch_for_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    set_error("layer_stack_noalloc: no usable current device");
+    return SA_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      set_error("layer_stack_noalloc: hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                hipGetErrorString(e));
+      return SA_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SA_OK;
+}
+
+size_t sa_layer_stack_noalloc_max_bytes(void) { return SA_NOALLOC_SCRATCH_BYTES; }
+
+int32_t sa_layer_stack_noalloc(const sa_layer_desc* layers, int32_t n_layers, const sa_batch_desc* batch, int32_t k,
+                               float scale, const sa_stage_events* events, sa_stream_t stream) {
+  SA_REQUIRE(layers && batch, SA_ERR_INVALID_ARG, "layer_stack_noalloc: null descriptor");
+  SA_REQUIRE(k >= 1 && k <= SA_MAX_TOPK, SA_ERR_INVALID_ARG, "layer_stack_noalloc: k=%d outside 1..%d", k,
+             SA_MAX_TOPK);
+  if (n_layers <= 0 || batch->n_q <= 0) return sa_layer_stack(layers, n_layers, batch, k, scale, nullptr, 0, events,
+                                                              stream);
+  const size_t need = sa_layer_stack_workspace_size(batch->n_q, batch->ld, k);
+  SA_REQUIRE(need <= (size_t)SA_NOALLOC_SCRATCH_BYTES, SA_ERR_WORKSPACE,
+             "layer_stack_noalloc: %d queries with score rows of %lld need %zu bytes of workspace, more than the "
+             "%zu-byte static scratch (use sa_layer_stack with a workspace)",
+             batch->n_q, (long long)batch->ld, need, (size_t)SA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  int32_t rc = scratch_for_current_device(&ws);
+  if (rc) return rc;
+  return sa_layer_stack(layers, n_layers, batch, k, scale, ws, SA_NOALLOC_SCRATCH_BYTES, events, stream);
 }
 
 int32_t sa_cache_write(const void* kv_a, const void* gamma, const void* k_raw, const void* ln_w, const void* ln_b,
