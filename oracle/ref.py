@@ -39,6 +39,10 @@ under ``tests/`` marked ``not gpu``):
                      when k >= n, explicit (non-absorbed) kv_b_proj form,
                      k_eff = 1, zero query, hand-computed two-row example.
   layer_pattern      the pages' printed 78-layer layout and the 21/57 counts.
+  share_selection,   hand example, dense additive-mask attention over the
+  layer_stack_mtp    shared selection cut at each token's position, and the
+                     take-all case (sharing changes nothing when every causal
+                     set fits in k).
   score_error_bound  pinned against exhaustive fp32 re-summation orders on
                      small cases (the bound must cover every order).
 No function is "parity unpinned".
@@ -369,6 +373,66 @@ def layer_stack(layers, seq_start, q_seq, q_pos, k=INDEX_TOPK, scale=1.0 / 16, f
             scores_all.append(None)
         outs.append(sparse_mla(L["q_abs"], L["kv"], seq_start, q_seq, cur, L["w_uv"], scale))
     return outs, idxs, scores_all
+
+
+# --------------------------------------------------------------------------
+# MTP / speculative decode: one selection shared by several query tokens.
+#
+# [GLM-5.2 llm-atlas] config field index_share_for_mtp_iteration = true;
+# [GLM 5.2 hermosaai] "78 layers, IndexShare pattern": one Multi-Token
+# Prediction layer, tuned for a longer speculative accept length;
+# [GLM-5.2 techniques map] "decoding strategy": speculative decoding and
+# multi-token prediction.  The pages name the flag only.  Reading taken: in a
+# speculative decode step a sequence brings several consecutive query tokens
+# (the drafts being verified); the indexer and the top-k run once, for one
+# selecting query of the group (normally the group's last token, whose causal
+# set holds every other token's), and each token of the group attends over
+# that selection restricted to its own causal set: selected positions past
+# the token's own position are dropped, the rest keep their order.
+
+def share_selection(sel_idx, sel_of, q_pos):
+    """Per-token selection rows built from shared ones.
+
+    sel_idx [n_sel, k]: the selecting queries' rows (positions, -1 padding).
+    Token t uses row sel_of[t] and keeps its positions p with 0 <= p <=
+    q_pos[t], in the row's order, followed by -1 padding.  Returns int64
+    [n_q, k]."""
+    sel_idx = np.asarray(sel_idx, dtype=np.int64)
+    n_q, k = len(sel_of), sel_idx.shape[1]
+    out = np.full((n_q, k), -1, dtype=np.int64)
+    for t in range(n_q):
+        row = sel_idx[int(sel_of[t])]
+        keep = row[(row >= 0) & (row <= int(q_pos[t]))]
+        out[t, :len(keep)] = keep
+    return out
+
+
+def layer_stack_mtp(layers, seq_start, q_seq, q_pos, sel_seq, sel_pos, sel_of, k=INDEX_TOPK, scale=1.0 / 16,
+                    full=None):
+    """:func:`layer_stack` with a selection shared inside groups of tokens.
+
+    Full layers score and select for the selecting queries only (sequence
+    sel_seq[s], position sel_pos[s]; their layer inputs q_idx and w have
+    n_sel rows); token t then uses the selection of selecting query
+    sel_of[t], restricted to its own causal set (:func:`share_selection`).
+    Attention runs for every token with its own q_abs.  Returns (outs, idxs)
+    with idxs holding the per-token rows of every full layer (None for shared
+    layers)."""
+    if full is None:
+        full = layer_pattern(len(layers))
+    if len(layers) and not full[0]:
+        raise ValueError("the first layer of a stack must run its own indexer")
+    outs, idxs = [], []
+    cur = None
+    for l, L in enumerate(layers):
+        if full[l]:
+            sc = indexer_scores(L["q_idx"], L["w"], L["k_idx"], seq_start, sel_seq, sel_pos)
+            cur = share_selection(topk_select_rows(sc, sel_pos, k), sel_of, q_pos)
+            idxs.append(cur)
+        else:
+            idxs.append(None)
+        outs.append(sparse_mla(L["q_abs"], L["kv"], seq_start, q_seq, cur, L["w_uv"], scale))
+    return outs, idxs
 
 
 # --------------------------------------------------------------------------

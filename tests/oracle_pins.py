@@ -448,6 +448,98 @@ def check_layer_stack_shares_selection(ref):
         raise AssertionError("stack starting with a shared layer accepted")
 
 
+# ------------------------------------------------------ MTP shared selection
+# [GLM-5.2 llm-atlas] index_share_for_mtp_iteration; the reading: one
+# selection per group of draft tokens, cut at each token's own position.
+
+def check_mtp_share_hand_example(ref):
+    sel = np.array([[2, 5, 9, 12, -1, -1],
+                    [0, 1, 3, -1, -1, -1]])
+    sel_of = [0, 0, 0, 0, 1, 1]
+    q_pos = [9, 5, 4, 12, 3, 0]
+    expect = np.array([[2, 5, 9, -1, -1, -1],
+                       [2, 5, -1, -1, -1, -1],
+                       [2, -1, -1, -1, -1, -1],
+                       [2, 5, 9, 12, -1, -1],
+                       [0, 1, 3, -1, -1, -1],
+                       [0, -1, -1, -1, -1, -1]])
+    assert np.array_equal(ref.share_selection(sel, sel_of, q_pos), expect)
+
+
+def _mtp_layers(rng, n_sel, n_q, T, n_layers=2):
+    layers = []
+    for l in range(n_layers):
+        L = dict(q_abs=_bf16_grid(rng.standard_normal((n_q, 64, 576)) / 24),
+                 kv=_bf16_grid(rng.standard_normal((T, 576))),
+                 w_uv=_bf16_grid(rng.standard_normal((64, 256, 512)) / 22.6))
+        if l == 0:
+            L.update(q_idx=_bf16_grid(rng.standard_normal((n_sel, 32, 128)) / 11),
+                     w=rng.standard_normal((n_sel, 32)), k_idx=_bf16_grid(rng.standard_normal((T, 128))))
+        layers.append(L)
+    return layers
+
+
+def check_mtp_share_equals_dense_masked(ref):
+    """Two sequences, each verifying 4 draft tokens at its last positions; the
+    group's last token selects 12 positions.  Each token's output equals
+    dense additive-mask attention whose 0 entries are the selected positions
+    at or before the token's own position (built here from sets)."""
+    rng = _rng(71)
+    lens = [40, 33]
+    starts = [0, 40]
+    q_seq = [0, 0, 0, 0, 1, 1, 1, 1]
+    q_pos = [36, 37, 38, 39, 29, 30, 31, 32]
+    sel_seq, sel_pos, sel_of = [0, 1], [39, 32], [0, 0, 0, 0, 1, 1, 1, 1]
+    layers = _mtp_layers(rng, 2, 8, sum(lens))
+    outs, idxs = ref.layer_stack_mtp(layers, starts, q_seq, q_pos, sel_seq, sel_pos, sel_of, k=12,
+                                     full=[True, False])
+    L0 = layers[0]
+    sc = ref.indexer_scores(L0["q_idx"], L0["w"], L0["k_idx"], starts, sel_seq, sel_pos)
+    chosen = [set(sorted(range(sel_pos[s] + 1), key=lambda p: (-sc[s, p], p))[:12]) for s in range(2)]
+    for t in range(8):
+        allowed = sorted(p for p in chosen[sel_of[t]] if p <= q_pos[t])
+        assert sorted(idxs[0][t][idxs[0][t] >= 0].tolist()) == allowed
+        mask_idx = np.array([allowed])
+        for l in range(2):
+            exp = _dense_masked_reference(layers[l]["q_abs"][t:t + 1], layers[l]["kv"], starts, [q_seq[t]],
+                                          [q_pos[t]], mask_idx, layers[l]["w_uv"], 1.0 / 16)
+            np.testing.assert_allclose(outs[l][t], exp[0], rtol=1e-10, atol=1e-12)
+
+
+def check_mtp_take_all_equals_unshared(ref):
+    """When every causal set fits in k, the shared selection cut at a token's
+    position is that token's whole causal set: the same as each token
+    selecting for itself."""
+    rng = _rng(73)
+    lens = [20, 15]
+    q_seq, q_pos = [0, 0, 0, 1, 1], [16, 17, 19, 13, 14]
+    sel_seq, sel_pos, sel_of = [0, 1], [19, 14], [0, 0, 0, 1, 1]
+    layers = _mtp_layers(rng, 2, 5, sum(lens))
+    outs, idxs = ref.layer_stack_mtp(layers, [0, 20], q_seq, q_pos, sel_seq, sel_pos, sel_of, k=32,
+                                     full=[True, False])
+    own = [dict(L) for L in layers]
+    own[0]["q_idx"] = layers[0]["q_idx"][sel_of]
+    own[0]["w"] = layers[0]["w"][sel_of]
+    outs2, idxs2, _ = ref.layer_stack(own, [0, 20], q_seq, q_pos, k=32, full=[True, False])
+    assert np.array_equal(idxs[0], idxs2[0])
+    for a, b in zip(outs, outs2):
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
+
+
+def check_mtp_identity_sharing_is_plain_stack(ref):
+    """Each token its own selecting query: the plain layer stack."""
+    rng = _rng(79)
+    lens = [50, 30]
+    q_seq, q_pos = [0, 1, 1], [49, 29, 12]
+    layers = _mtp_layers(rng, 3, 3, sum(lens))
+    outs, idxs = ref.layer_stack_mtp(layers, [0, 50], q_seq, q_pos, q_seq, q_pos, [0, 1, 2], k=8,
+                                     full=[True, False])
+    outs2, idxs2, _ = ref.layer_stack(layers, [0, 50], q_seq, q_pos, k=8, full=[True, False])
+    assert np.array_equal(idxs[0], idxs2[0])
+    for a, b in zip(outs, outs2):
+        np.testing.assert_allclose(a, b, rtol=0, atol=0)
+
+
 # ---------------------------------------------------------------- cache write
 # [GLM-5.2 techniques map] rows "Multi-head latent attention", "QK
 # normalization", "Partial RoPE", "YaRN RoPE scaling"; [GLM-5.2 llm-atlas]

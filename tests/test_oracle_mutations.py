@@ -51,6 +51,12 @@ MUTATIONS = [
      "var = np.sum((x - mean) ** 2, axis=-1, keepdims=True) / (x.shape[-1] - 1)"),
     ("ln_drops_bias", "* _f64(weight) + _f64(bias)", "* _f64(weight)"),
     ("indexer_key_turns_first_half", "k[:, half:] = rope_interleaved(k[:, half:], pos)", "k[:, :half] = rope_interleaved(k[:, :half], pos)"),
+    ("mtp_cut_excludes_own_position", "keep = row[(row >= 0) & (row <= int(q_pos[t]))]",
+     "keep = row[(row >= 0) & (row < int(q_pos[t]))]"),
+    ("mtp_no_causal_cut", "keep = row[(row >= 0) & (row <= int(q_pos[t]))]", "keep = row[row >= 0]"),
+    ("mtp_first_row_for_all", "row = sel_idx[int(sel_of[t])]", "row = sel_idx[0]"),
+    ("mtp_selects_at_token_positions", "cur = share_selection(topk_select_rows(sc, sel_pos, k), sel_of, q_pos)",
+     "cur = share_selection(topk_select_rows(sc, np.minimum(sel_pos, min(q_pos)), k), sel_of, q_pos)"),
     ("cache_row_latent_not_normalised", "lat = rms_norm(kv_a[:, :KV_LORA_RANK], gamma)", "lat = kv_a[:, :KV_LORA_RANK] * _f64(gamma)"),
 ]
 
