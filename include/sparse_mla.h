@@ -204,6 +204,20 @@ int32_t sa_mla_sparse_attn(const void* q_abs, const void* kv, const int64_t* seq
  * sa_batch_desc: seq_start int64 [n_seq], seq_len int32 [n_seq], q_seq int32 [n_q],
  * q_pos int32 [n_q], the counts, and ld (score row length, > max q_pos; at most
  * SA_MAX_SEQ_LEN, so every selected position is one the gather can address).
+ *
+ * Shared selection for speculative / multi-token-prediction decode (llm-atlas
+ * "GLM-5.2", config field index_share_for_mtp_iteration; hermosaai "GLM 5.2",
+ * "78 layers, IndexShare pattern": the Multi-Token Prediction layer serves
+ * speculative decoding).  With n_sel = 0 every query selects for itself.  With
+ * 1 <= n_sel <= n_q, full layers run the indexer and top-k only for n_sel
+ * selecting queries (sequence sel_seq[s], position sel_pos[s]; the full
+ * layers' q_idx and w then hold n_sel rows), and query t uses the selection of
+ * selecting query sel_of[t] cut at its own position (sa_share_selection): the
+ * draft tokens of a sequence verified in one step share one indexer pass,
+ * normally the one of their last token, whose causal set holds the others'.
+ * Preconditions: 0 <= sel_of[t] < n_sel, sel_seq[sel_of[t]] == q_seq[t], the
+ * selecting queries obey the batch rules; the idx outputs of full layers hold
+ * the per-query rows.
  * events: optional (NULL or any NULL member = not recorded); hipEvents recorded on
  * `stream` just before and after the named stage of the FIRST layer where it runs.
  *   ws  workspace of at least sa_layer_stack_workspace_size(n_q, ld, k) bytes
@@ -228,6 +242,10 @@ typedef struct sa_batch_desc {
   int32_t n_q;
   int32_t n_seq;
   int64_t ld;
+  int32_t n_sel;            /* 0: no shared selection */
+  const int32_t* sel_seq;   /* [n_sel] */
+  const int32_t* sel_pos;   /* [n_sel] */
+  const int32_t* sel_of;    /* [n_q] */
 } sa_batch_desc;
 
 typedef struct sa_stage_events {
@@ -261,6 +279,25 @@ int32_t sa_layer_stack(const sa_layer_desc* layers, int32_t n_layers, const sa_b
 size_t sa_layer_stack_noalloc_max_bytes(void);
 int32_t sa_layer_stack_noalloc(const sa_layer_desc* layers, int32_t n_layers, const sa_batch_desc* batch,
                                int32_t k, float scale, const sa_stage_events* events, sa_stream_t stream);
+
+/*
+ * sa_share_selection -- per-token selection rows from shared ones (the step
+ * sa_layer_stack takes for a shared selection, see sa_batch_desc).
+ *
+ * Defines (the reading of index_share_for_mtp_iteration above): token t takes
+ * row sel_of[t] of sel_idx and keeps its entries p with 0 <= p <= q_pos[t],
+ * in the row's order, then -1 padding:
+ *   idx[t, :] = [p in sel_idx[sel_of[t], :] if 0 <= p <= q_pos[t]] + [-1, ...]
+ *
+ *   sel_idx int32 [n_sel, k]   shared rows (positions, -1 padding; any order)
+ *   sel_of  int32 [n_q]        0 <= sel_of[t] < n_sel
+ *   q_pos   int32 [n_q]
+ *   k       1 .. 2048
+ *   idx     int32 [n_q, k]     output (must not overlap sel_idx)
+ * Exact integer work; deterministic.
+ */
+int32_t sa_share_selection(const int32_t* sel_idx, int32_t n_sel, int32_t k, const int32_t* sel_of,
+                           const int32_t* q_pos, int32_t n_q, int32_t* idx, sa_stream_t stream);
 
 /* IndexShare pattern of the 78-layer model: 1 if layer runs its own indexer
  * (layers 0-2, then every layer l with l mod 4 == 2), else 0; -1 if layer < 0. */
@@ -330,6 +367,8 @@ int32_t sa_indexer_score_algo(const void* q_idx, const float* w, const void* k_i
  *   top-k:   0 <= q_pos[t] < ld; no NaN in scores[t, 0 .. q_pos[t]]
  *   attention: -1 <= idx[t, j] < SA_MAX_SEQ_LEN (and, inside sa_layer_stack,
  *            idx[t, j] <= q_pos[t]); q_seq[t] >= 0
+ *   shared selection: 0 <= sel_of[t] < n_sel; sel_seq[sel_of[t]] == q_seq[t]
+ *            (and the selecting queries obey the batch rules)
  *   cache write: pos[i] >= 0, dst[i] >= 0
  * The first violation (and a count of all of them) is kept in a device-side
  * record.  The check kernels only read; the call's own kernels still run.

@@ -21,7 +21,7 @@ class LayerDesc(ctypes.Structure):
 
 class BatchDesc(ctypes.Structure):
     _fields_ = [("seq_start", c_p), ("seq_len", c_p), ("q_seq", c_p), ("q_pos", c_p), ("n_q", c_i32), ("n_seq", c_i32),
-                ("ld", c_i64)]
+                ("ld", c_i64), ("n_sel", c_i32), ("sel_seq", c_p), ("sel_pos", c_p), ("sel_of", c_p)]
 
 
 class StageEvents(ctypes.Structure):
@@ -45,6 +45,7 @@ SIGNATURES = {
     "sa_layer_stack_workspace_size": (c_sz, [c_i32, c_i64, c_i32]),
     "sa_layer_stack": (c_i32, [ctypes.POINTER(LayerDesc), c_i32, ctypes.POINTER(BatchDesc), c_i32, c_f32, c_p,
                                c_sz, ctypes.POINTER(StageEvents), c_p]),
+    "sa_share_selection": (c_i32, [c_p, c_i32, c_i32, c_p, c_p, c_i32, c_p, c_p]),
     "sa_layer_stack_noalloc_max_bytes": (c_sz, []),
     "sa_layer_stack_noalloc": (c_i32, [ctypes.POINTER(LayerDesc), c_i32, ctypes.POINTER(BatchDesc), c_i32, c_f32,
                                        ctypes.POINTER(StageEvents), c_p]),

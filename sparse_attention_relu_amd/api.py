@@ -112,6 +112,22 @@ def mla_sparse_attn(q_abs, kv, seq_start, q_seq, idx, w_uv, scale: float = 1.0 /
     return out
 
 
+def share_selection(sel_idx, sel_of, q_pos, idx=None, stream=None):
+    """sa_share_selection: row sel_of[t] of sel_idx cut at q_pos[t]."""
+    n_sel, k = sel_idx.shape
+    n_q = sel_of.shape[0]
+    _need(sel_idx, "sel_idx", torch.int32, (n_sel, k))
+    _need(sel_of, "sel_of", torch.int32, (n_q,))
+    _need(q_pos, "q_pos", torch.int32, (n_q,))
+    if idx is None:
+        idx = torch.empty((n_q, k), dtype=torch.int32, device=sel_idx.device)
+    _need(idx, "idx", torch.int32, (n_q, k))
+    L = _lib.lib()
+    st = L.sa_share_selection(_ptr(sel_idx), n_sel, k, _ptr(sel_of), _ptr(q_pos), n_q, _ptr(idx), _stream(stream))
+    _lib.check("sa_share_selection", st)
+    return idx
+
+
 def cache_write(kv_a, gamma, pos, dst, kv_cache, k_raw=None, ln_w=None, ln_b=None, k_cache=None, stream=None):
     """sa_cache_write: the cache rows (and optionally the indexer keys) of n
     new tokens, written at rows dst of kv_cache (and k_cache)."""
@@ -139,8 +155,18 @@ class LayerStack:
 
     def __init__(self, layers: Sequence, seq_start, seq_len, q_seq, q_pos, ld: int, k: int = MAX_TOPK,
                  scale: float = 1.0 / 16, full: Optional[List[bool]] = None, outs=None, idxs=None, ws=None,
-                 library=None):
+                 library=None, sel=None):
+        """sel: None, or (sel_seq, sel_pos, sel_of) int32 tensors of a shared
+        selection (the full layers' q_idx and w then hold len(sel_seq) rows)."""
         n_q = q_pos.shape[0]
+        n_sel = 0
+        if sel is not None:
+            sel_seq, sel_pos, sel_of = sel
+            n_sel = sel_seq.shape[0]
+            _need(sel_seq, "sel_seq", torch.int32, (n_sel,))
+            _need(sel_pos, "sel_pos", torch.int32, (n_sel,))
+            _need(sel_of, "sel_of", torch.int32, (n_q,))
+        n_rows = n_sel if n_sel else n_q
         dev = q_pos.device
         if full is None:
             full = [layer_is_full(l) for l in range(len(layers))]
@@ -157,8 +183,8 @@ class LayerStack:
             d = descs[l]
             d.is_full = 1 if f else 0
             if f:
-                _need(L.q_idx, "q_idx", torch.bfloat16, (n_q, IDX_HEADS, IDX_DIM))
-                _need(L.w, "w", torch.float32, (n_q, IDX_HEADS))
+                _need(L.q_idx, "q_idx", torch.bfloat16, (n_rows, IDX_HEADS, IDX_DIM))
+                _need(L.w, "w", torch.float32, (n_rows, IDX_HEADS))
                 _need(L.k_idx, "k_idx", torch.bfloat16, (None, IDX_DIM))
                 d.q_idx, d.w, d.k_idx, d.idx = _ptr(L.q_idx), _ptr(L.w), _ptr(L.k_idx), _ptr(self.idxs[l])
             _need(L.q_abs, "q_abs", torch.bfloat16, (n_q, HEADS, ROW))
@@ -167,8 +193,9 @@ class LayerStack:
             d.q_abs, d.kv, d.w_uv, d.out = _ptr(L.q_abs), _ptr(L.kv), _ptr(L.w_uv), _ptr(self.outs[l])
         self._descs = descs
         self._batch = _lib.BatchDesc(_ptr(seq_start), _ptr(seq_len), _ptr(q_seq), _ptr(q_pos), n_q,
-                                     seq_start.shape[0], int(ld))
-        self._keep = (layers, seq_start, seq_len, q_seq, q_pos)
+                                     seq_start.shape[0], int(ld), n_sel,
+                                     *((_ptr(x) for x in sel) if sel is not None else (None, None, None)))
+        self._keep = (layers, seq_start, seq_len, q_seq, q_pos, sel)
         self.lib = lib = library if library is not None else _lib.lib()
         nbytes = lib.sa_layer_stack_workspace_size(n_q, int(ld), k)
         self.ws = ws if ws is not None else workspace(nbytes, dev)

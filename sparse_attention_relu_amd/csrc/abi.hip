@@ -60,6 +60,10 @@ int32_t debug_idx(const int32_t* idx, int32_t n_q, int32_t k, const int32_t* q_p
                   hipStream_t stream);
 int32_t debug_scores(const float* scores, int64_t ld, const int32_t* q_pos, int32_t n_q, hipStream_t stream);
 int32_t debug_cache(const int32_t* pos, const int64_t* dst, int32_t n, hipStream_t stream);
+int32_t debug_share(const int32_t* sel_of, int32_t n_sel, const int32_t* q_seq, const int32_t* sel_seq, int32_t n_q,
+                    hipStream_t stream);
+int32_t launch_share(const int32_t* sel_idx, int32_t n_sel, int32_t k, const int32_t* sel_of, const int32_t* q_pos,
+                     int32_t n_q, int32_t* idx, hipStream_t stream);
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -203,10 +207,14 @@ int32_t sa_mla_sparse_attn(const void* q_abs, const void* kv, const int64_t* seq
   return launch_mla(q_abs, kv, seq_start, q_seq, idx, n_q, k, w_uv, scale, out, lse, ws, (hipStream_t)stream);
 }
 
+// Layout: scores [n_q, ld] fp32, the top-k workspace, the attention
+// workspace, and the selecting queries' rows [n_q, k] int32 of a shared
+// selection (used only when the batch has one; sized for n_sel <= n_q).
 size_t sa_layer_stack_workspace_size(int32_t n_q, int64_t ld, int32_t k) {
   if (n_q <= 0 || ld <= 0 || k <= 0) return 256;
+  const int32_t kk = k > SA_MAX_TOPK ? SA_MAX_TOPK : k;
   return align256((size_t)n_q * (size_t)ld * 4) + align256(topk_workspace_size(n_q, ld, k)) +
-         align256(mla_workspace_size(n_q, k > SA_MAX_TOPK ? SA_MAX_TOPK : k));
+         align256(mla_workspace_size(n_q, kk)) + align256((size_t)n_q * kk * 4);
 }
 
 int32_t sa_layer_stack(const sa_layer_desc* layers, int32_t n_layers, const sa_batch_desc* batch, int32_t k,
@@ -224,6 +232,16 @@ int32_t sa_layer_stack(const sa_layer_desc* layers, int32_t n_layers, const sa_b
              "layer_stack: ld=%lld outside 1..%d (the longest sequence the attention gather addresses)",
              (long long)ld, SA_MAX_SEQ_LEN);
   SA_REQUIRE(layers[0].is_full, SA_ERR_INVALID_ARG, "layer_stack: layer 0 must run its own indexer");
+  // With a shared selection the indexer and the top-k run for the n_sel
+  // selecting queries; otherwise every query selects for itself.
+  const int32_t n_sel = batch->n_sel;
+  SA_REQUIRE(n_sel >= 0 && n_sel <= n_q, SA_ERR_INVALID_ARG, "layer_stack: n_sel=%d outside 0..n_q=%d", n_sel, n_q);
+  SA_REQUIRE(n_sel == 0 || (batch->sel_seq && batch->sel_pos && batch->sel_of), SA_ERR_INVALID_ARG,
+             "layer_stack: shared selection without sel_seq/sel_pos/sel_of");
+  const bool shared_sel = n_sel > 0;
+  const int32_t n_rows = shared_sel ? n_sel : n_q;            // rows of scores and top-k
+  const int32_t* r_seq = shared_sel ? batch->sel_seq : batch->q_seq;
+  const int32_t* r_pos = shared_sel ? batch->sel_pos : batch->q_pos;
   const size_t need = sa_layer_stack_workspace_size(n_q, ld, k);
   SA_REQUIRE(ws && ws_bytes >= need, SA_ERR_WORKSPACE, "layer_stack: workspace of %zu bytes, %zu needed", ws_bytes,
              need);
@@ -233,8 +251,8 @@ int32_t sa_layer_stack(const sa_layer_desc* layers, int32_t n_layers, const sa_b
     const sa_layer_desc& L = layers[l];
     int32_t rc;
     if (L.is_full) {
-      rc = check_indexer_args(L.q_idx, L.w, L.k_idx, batch->seq_start, batch->seq_len, batch->q_seq, batch->q_pos,
-                              n_q, batch->n_seq, (const float*)ws, ld);
+      rc = check_indexer_args(L.q_idx, L.w, L.k_idx, batch->seq_start, batch->seq_len, r_seq, r_pos, n_rows,
+                              batch->n_seq, (const float*)ws, ld);
       if (rc) return rc;
       SA_REQUIRE(L.idx, SA_ERR_INVALID_ARG, "layer_stack: full layer %d has no idx buffer", l);
     }
@@ -253,6 +271,8 @@ int32_t sa_layer_stack(const sa_layer_desc* layers, int32_t n_layers, const sa_b
   void* topk_ws = p;
   p += align256(topk_workspace_size(n_q, ld, k));
   void* mla_ws = p;
+  p += align256(mla_workspace_size(n_q, k));
+  int32_t* sel_idx = (int32_t*)p;
 
   hipStream_t st = (hipStream_t)stream;
   const int32_t* cur_idx = nullptr;
@@ -263,26 +283,32 @@ int32_t sa_layer_stack(const sa_layer_desc* layers, int32_t n_layers, const sa_b
   // indexer.  The top-k then runs its own first-digit histogram pass over the
   // scores.  The decode indexer also clears the top-k's histograms and
   // counters on the side, which saves the top-k a launch of its own for that.
-  const int ialgo = indexer_algo(n_q, batch->n_seq, 0);
+  const int ialgo = indexer_algo(n_rows, batch->n_seq, 0);
   uint32_t* clear = nullptr;
   int64_t n_clear = 0;
-  if (ialgo == 1) topk_clear_range(topk_ws, n_q, ld, &clear, &n_clear);
+  if (ialgo == 1) topk_clear_range(topk_ws, n_rows, ld, &clear, &n_clear);
   if ((rc = debug_batch(batch->seq_start, batch->seq_len, batch->q_seq, batch->q_pos, n_q, batch->n_seq, ld, st)))
     return rc;
+  if (shared_sel) {
+    if ((rc = debug_batch(batch->seq_start, batch->seq_len, r_seq, r_pos, n_rows, batch->n_seq, ld, st))) return rc;
+    if ((rc = debug_share(batch->sel_of, n_sel, batch->q_seq, batch->sel_seq, n_q, st))) return rc;
+  }
   for (int l = 0; l < n_layers; ++l) {
     const sa_layer_desc& L = layers[l];
     if (L.is_full) {
       const bool ev = events && !rec_idx && events->indexer_begin && events->indexer_end;
       if (ev && (rc = record(events->indexer_begin, st))) return rc;
-      rc = launch_indexer(L.q_idx, L.w, L.k_idx, batch->seq_start, batch->seq_len, batch->q_seq, batch->q_pos, n_q,
+      rc = launch_indexer(L.q_idx, L.w, L.k_idx, batch->seq_start, batch->seq_len, r_seq, r_pos, n_rows,
                           batch->n_seq, scores, ld, ialgo, st, clear, n_clear);
       if (rc) return rc;
       if (ev && (rc = record(events->indexer_end, st))) return rc;
       rec_idx |= ev;
       const bool evt = events && !rec_topk && events->topk_begin && events->topk_end;
       if (evt && (rc = record(events->topk_begin, st))) return rc;
-      rc = launch_topk(scores, ld, batch->q_pos, n_q, k, L.idx, topk_ws, 0, st, ialgo == 1);
+      rc = launch_topk(scores, ld, r_pos, n_rows, k, shared_sel ? sel_idx : L.idx, topk_ws, 0, st, ialgo == 1);
       if (rc) return rc;
+      // each query's rows: the selecting query's, cut at the query's position
+      if (shared_sel && (rc = launch_share(sel_idx, n_sel, k, batch->sel_of, batch->q_pos, n_q, L.idx, st))) return rc;
       if ((rc = debug_idx(L.idx, n_q, k, batch->q_pos, nullptr, st))) return rc;
       if (evt && (rc = record(events->topk_end, st))) return rc;
       rec_topk |= evt;
@@ -297,6 +323,20 @@ int32_t sa_layer_stack(const sa_layer_desc* layers, int32_t n_layers, const sa_b
     rec_attn |= eva;
   }
   return SA_OK;
+}
+
+int32_t sa_share_selection(const int32_t* sel_idx, int32_t n_sel, int32_t k, const int32_t* sel_of,
+                           const int32_t* q_pos, int32_t n_q, int32_t* idx, sa_stream_t stream) {
+  SA_REQUIRE(n_q >= 0 && n_sel >= 0, SA_ERR_INVALID_ARG, "share_selection: negative count");
+  SA_REQUIRE(k >= 1 && k <= SA_MAX_TOPK, SA_ERR_INVALID_ARG, "share_selection: k=%d outside 1..%d", k, SA_MAX_TOPK);
+  if (n_q == 0) return SA_OK;
+  SA_REQUIRE(n_sel >= 1, SA_ERR_INVALID_ARG, "share_selection: queries without selecting rows");
+  SA_REQUIRE(sel_idx && sel_of && q_pos && idx, SA_ERR_INVALID_ARG, "share_selection: null pointer argument");
+  SA_REQUIRE(n_q <= 0x7fffffff, SA_ERR_UNSUPPORTED, "share_selection: grid too large");
+  hipStream_t st = (hipStream_t)stream;
+  int32_t rc = debug_share(sel_of, n_sel, nullptr, nullptr, n_q, st);
+  if (rc) return rc;
+  return launch_share(sel_idx, n_sel, k, sel_of, q_pos, n_q, idx, st);
 }
 
 // Per-device address of `scratch`, looked up once per device with that

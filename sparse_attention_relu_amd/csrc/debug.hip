@@ -74,6 +74,15 @@ __global__ void scores_kernel(const float* scores, int64_t ld, const int32_t* q_
   }
 }
 
+__global__ void share_kernel(const int32_t* sel_of, int32_t n_sel, const int32_t* q_seq, const int32_t* sel_seq,
+                             int32_t n_q) {
+  for (int32_t t = blockIdx.x * blockDim.x + threadIdx.x; t < n_q; t += gridDim.x * blockDim.x) {
+    int64_t val = 0;
+    const uint32_t c = check_share(sel_of[t], n_sel, q_seq ? q_seq[t] : 0, q_seq ? sel_seq : nullptr, &val);
+    if (c) report(c, (uint32_t)t, 0, val);
+  }
+}
+
 __global__ void cache_kernel(const int32_t* pos, const int64_t* dst, int32_t n) {
   for (int32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
     if (pos[i] < 0) report(CACHE_POS_NEG, (uint32_t)i, 0, pos[i]);
@@ -127,6 +136,21 @@ int32_t debug_scores(const float* scores, int64_t ld, const int32_t* q_pos, int3
   return check_launch("debug score check");
 #else
   (void)scores, (void)ld, (void)q_pos, (void)n_q, (void)stream;
+  return SA_OK;
+#endif
+}
+
+// q_seq / sel_seq may be null (the standalone sharing call has no
+// sequences): then only the range of sel_of is checked.
+int32_t debug_share(const int32_t* sel_of, int32_t n_sel, const int32_t* q_seq, const int32_t* sel_seq, int32_t n_q,
+                    hipStream_t stream) {
+#ifdef SA_DEBUG
+  if (n_q <= 0) return SA_OK;
+  hipLaunchKernelGGL(sa_dbg::share_kernel, dim3(dbg_grid(n_q, 256)), dim3(256), 0, stream, sel_of, n_sel, q_seq,
+                     sel_seq, n_q);
+  return check_launch("debug shared-selection check");
+#else
+  (void)sel_of, (void)n_sel, (void)q_seq, (void)sel_seq, (void)n_q, (void)stream;
   return SA_OK;
 #endif
 }

@@ -23,7 +23,9 @@ enum Code : uint32_t {
   SCORE_NAN = 8,          // a NaN among scores[t, 0 .. q_pos[t]]
   CACHE_POS_NEG = 9,      // cache write: pos[i] < 0
   CACHE_DST_NEG = 10,     // cache write: dst[i] < 0
-  N_CODES = 11
+  SEL_OF_RANGE = 11,      // shared selection: sel_of[t] outside [0, n_sel)
+  SEL_SEQ_MISMATCH = 12,  // shared selection: sel_seq[sel_of[t]] != q_seq[t]
+  N_CODES = 13
 };
 
 // Record layout (device word array and host report alike):
@@ -44,6 +46,8 @@ __host__ __device__ inline const char* code_name(uint32_t c) {
     case SCORE_NAN: return "NaN score in a row the top-k reads";
     case CACHE_POS_NEG: return "cache-write position negative";
     case CACHE_DST_NEG: return "cache-write row negative";
+    case SEL_OF_RANGE: return "sel_of outside [0, n_sel)";
+    case SEL_SEQ_MISMATCH: return "selecting query of another sequence";
     default: return "unknown check";
   }
 }
@@ -89,6 +93,21 @@ __host__ __device__ inline uint32_t check_idx(int32_t idx, int32_t q_pos, int64_
   if (idx < -1 || idx >= SA_MAX_SEQ_LEN || (q_pos >= 0 && idx > q_pos)) {
     *val = idx;
     return IDX_RANGE;
+  }
+  return OK;
+}
+
+// Query t of a batch with a shared selection; sel_seq may be null (the
+// sequences are unknown: only the range of sel_of is checked).
+__host__ __device__ inline uint32_t check_share(int32_t sel_of, int32_t n_sel, int32_t q_seq, const int32_t* sel_seq,
+                                                int64_t* val) {
+  if (sel_of < 0 || sel_of >= n_sel) {
+    *val = sel_of;
+    return SEL_OF_RANGE;
+  }
+  if (sel_seq && sel_seq[sel_of] != q_seq) {
+    *val = sel_seq[sel_of];
+    return SEL_SEQ_MISMATCH;
   }
   return OK;
 }

@@ -134,3 +134,31 @@ def test_workspace_sizes(L):
     s = L.sa_layer_stack_workspace_size(16, 131072, 2048)
     assert s >= 16 * 131072 * 4 + L.sa_topk_workspace_size(16, 131072, 2048)
     assert L.sa_topk_workspace_size(0, 10, 5) > 0 and L.sa_mla_workspace_size(0, 5) > 0
+
+
+def test_share_selection_rejects_bad_arguments(L):
+    # sel_idx, n_sel, k, sel_of, q_pos, n_q, idx, stream
+    assert L.sa_share_selection(FAKE, 1, 0, FAKE, FAKE, 4, FAKE, None) == -1
+    assert L.sa_share_selection(FAKE, 1, 2049, FAKE, FAKE, 4, FAKE, None) == -1
+    assert L.sa_share_selection(FAKE, 0, 16, FAKE, FAKE, 4, FAKE, None) == -1
+    assert b"selecting rows" in L.sa_last_error_message()
+    assert L.sa_share_selection(None, 1, 16, FAKE, FAKE, 4, FAKE, None) == -1
+    assert L.sa_share_selection(FAKE, 1, 16, FAKE, FAKE, -1, FAKE, None) == -1
+    assert L.sa_share_selection(None, 0, 16, None, None, 0, None, None) == 0
+
+
+def test_layer_stack_rejects_bad_shared_selection(L):
+    descs = (_lib.LayerDesc * 1)()
+    d = descs[0]
+    d.is_full = 1
+    d.q_idx = d.w = d.k_idx = d.idx = d.q_abs = d.kv = d.w_uv = d.out = 0x10000
+    big = 1 << 40
+    batch = _lib.BatchDesc(0x10000, 0x10000, 0x10000, 0x10000, 4, 1, 100, 5, 0x10000, 0x10000, 0x10000)
+    rc = L.sa_layer_stack(descs, 1, ctypes.byref(batch), 2048, 1.0 / 16, FAKE, big, None, None)
+    assert rc == -1 and b"n_sel=5" in L.sa_last_error_message()
+    batch.n_sel = 2
+    batch.sel_of = None
+    rc = L.sa_layer_stack(descs, 1, ctypes.byref(batch), 2048, 1.0 / 16, FAKE, big, None, None)
+    assert rc == -1 and b"sel_of" in L.sa_last_error_message()
+    batch.n_sel = -1
+    assert L.sa_layer_stack(descs, 1, ctypes.byref(batch), 2048, 1.0 / 16, FAKE, big, None, None) == -1
