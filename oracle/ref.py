@@ -39,6 +39,11 @@ under ``tests/`` marked ``not gpu``):
                      when k >= n, explicit (non-absorbed) kv_b_proj form,
                      k_eff = 1, zero query, hand-computed two-row example.
   layer_pattern      the pages' printed 78-layer layout and the 21/57 counts.
+  q_project,         one- and two-hot closed forms (the nope/rope split, the
+  q_absorb           bf16 rounding), integer-exact absorbed = explicit logits,
+                     the relative-position property of the turned query
+                     against keys turned by the cache write, the indexer
+                     query's unturned first half.
   share_selection,   hand example, dense additive-mask attention over the
   layer_stack_mtp    shared selection cut at each token's position, and the
                      take-all case (sharing changes nothing when every causal
@@ -509,3 +514,92 @@ def indexer_keys_from_projection(k_raw, ln_weight, ln_bias, pos):
     half = INDEX_HEAD_DIM - QK_ROPE_DIM
     k[:, half:] = rope_interleaved(k[:, half:], pos)
     return round_to_bf16(k)
+
+
+# --------------------------------------------------------------------------
+# Query side: the projections that produce the path's query inputs.
+#
+# [GLM-5.2 techniques map] row "Multi-head latent attention": the query goes
+# through a q_lora_rank bottleneck; kv_b_proj maps the 512-wide latent to, per
+# head, qk_nope_head_dim key rows and v_head_dim value rows.  Row "Partial
+# RoPE": each head's query splits into a 192-dim part without rotation and a
+# 64-dim rotated part, in that order.  [GLM-5.2 architectures] "Every
+# architecture field": q_lora_rank 2,048, qk_nope 192, qk_rope 64; [GLM-5.2
+# llm-atlas] qk_head_dim 256, rope_interleave, indexer_rope_interleave, and
+# rope_theta 8e6 ([GLM-5.2 techniques map] row "YaRN RoPE scaling": default
+# rope type).  Row "Indexer-selected sparse attention": 32 indexer heads of
+# 128 against one shared key.
+#
+# Readings where the pages are silent (each stated again in the design notes):
+#   * The input c_q is the q_lora activation as the attention receives it
+#     (after its normalisation, which the pages do not print).
+#   * q = q_b_proj(c_q) holds, per head, [192 nope ; 64 rope]; the rope part
+#     turns with the cache key's convention (interleaved pairs, position p).
+#   * Absorption: the key half of kv_b_proj for head h, W_UK[h] ([192, 512],
+#     nope rows of the head), folds into the query: q_abs[h] =
+#     [W_UK[h]^T q_nope[h] ; q_rope[h]], so q_abs[h] . row =
+#     q_nope[h] . (W_UK[h] latent) + q_rope[h] . k_rope.
+#   * The indexer query and the head weights are projections of the same
+#     q_lora activation (the pages print the key's source only); the indexer
+#     query turns dims 64..127 of each head, as the indexer key does.  No
+#     extra scale on the weights (a positive factor leaves every selection
+#     unchanged).
+#   * Rounding as a bf16 model stores activations: each projection's output
+#     is rounded to bf16 once, the rope part is turned from those bf16 values
+#     and rounded again, the absorbed query is rounded once; the head weights
+#     stay fp32.
+
+Q_LORA_RANK = 2048        # q_lora_rank
+QK_HEAD_DIM = QK_NOPE_DIM + QK_ROPE_DIM   # 256 = qk_head_dim
+
+
+def _rope_heads(x, pos, first):
+    """Turn dims first.. of every head of x [n, H, d] at the token positions."""
+    x = _f64(x).copy()
+    n, H, d = x.shape
+    part = x[:, :, first:].reshape(n * H, d - first)
+    x[:, :, first:] = rope_interleaved(part, np.repeat(np.asarray(pos), H)).reshape(n, H, d - first)
+    return x
+
+
+def q_project(c_q, w_qb, w_iq, w_iw, pos):
+    """The query projections of n tokens.
+
+    c_q  [n, 2048] q_lora activation; w_qb [64 * 256, 2048] (q_b_proj);
+    w_iq [32 * 128, 2048] (indexer query); w_iw [32, 2048] (head weights);
+    pos  [n] token positions.
+    Returns q [n, 64, 256] (per head [192 nope ; 64 turned rope], bf16
+    values), q_idx [n, 32, 128] (dims 64..127 turned, bf16 values) and
+    w [n, 32] (float32 values)."""
+    c_q = _f64(c_q)
+    n = c_q.shape[0]
+    q = round_to_bf16(c_q @ _f64(w_qb).T).reshape(n, N_HEADS, QK_HEAD_DIM)
+    q = round_to_bf16(_rope_heads(q, pos, QK_NOPE_DIM))
+    qi = round_to_bf16(c_q @ _f64(w_iq).T).reshape(n, INDEX_N_HEADS, INDEX_HEAD_DIM)
+    qi = round_to_bf16(_rope_heads(qi, pos, INDEX_HEAD_DIM - QK_ROPE_DIM))
+    w = (c_q @ _f64(w_iw).T).astype(np.float32).astype(np.float64)
+    return q, qi, w
+
+
+def q_absorb(q, w_uk):
+    """Fold the key half of kv_b_proj into the query.
+
+    q [n, 64, 256] from :func:`q_project`; w_uk [64, 192, 512], the nope rows
+    of kv_b_proj for each head.  Returns q_abs [n, 64, 576] (bf16 values):
+    [W_UK[h]^T q_nope[h] ; q_rope[h]] per head."""
+    q, w_uk = _f64(q), _f64(w_uk)
+    n = q.shape[0]
+    out = np.empty((n, N_HEADS, ROW_DIM))
+    for h in range(N_HEADS):
+        out[:, h, :KV_LORA_RANK] = round_to_bf16(q[:, h, :QK_NOPE_DIM] @ w_uk[h])
+        out[:, h, KV_LORA_RANK:] = q[:, h, QK_NOPE_DIM:]
+    return out
+
+
+def projection_error_bound(a, b):
+    """|fp32 sum - exact| bound for each entry of a @ b.T summed in fp32 in
+    any order: gamma_K * sum_k |a_k b_k| (Higham, ch. 3), K = a.shape[-1]."""
+    K = a.shape[-1]
+    u = 2.0 ** -24
+    g = (K + 1) * u / (1 - (K + 1) * u)
+    return g * (np.abs(_f64(a)) @ np.abs(_f64(b)).T)

@@ -644,4 +644,132 @@ def check_indexer_keys_structure(ref):
     assert not np.allclose(rot[1:], ln[1:, 64:], rtol=1e-3)                  # later positions: turned
 
 
+# ----------------------------------------------------------------- query side
+# [GLM-5.2 techniques map] rows "Multi-head latent attention" (q_lora
+# bottleneck, kv_b_proj key/value rows per head) and "Partial RoPE" (192
+# unturned + 64 turned query dims per head); [GLM-5.2 architectures]
+# q_lora_rank 2,048; [GLM-5.2 llm-atlas] qk_head_dim 256, rope_theta 8e6.
+
+def _q_weights(rng, scale=1.0):
+    w_qb = _bf16_grid(rng.standard_normal((64 * 256, 2048)) * scale)
+    w_iq = _bf16_grid(rng.standard_normal((32 * 128, 2048)) * scale)
+    w_iw = rng.standard_normal((32, 2048)).astype(np.float32).astype(np.float64)
+    return w_qb, w_iq, w_iw
+
+
+def check_qproj_one_hot_columns(ref):
+    """c_q = e_j: every projection returns column j; at position 0 nothing
+    turns; at position p > 0 only the rope part of each head turns (pairs
+    keep their length, pair 0 turns by p radians)."""
+    rng = _rng(81)
+    w_qb, w_iq, w_iw = _q_weights(rng)
+    j = 1234
+    c = np.zeros((2, 2048))
+    c[:, j] = 1.0
+    q, qi, w = ref.q_project(c, w_qb, w_iq, w_iw, [0, 5])
+    assert np.array_equal(q[0].reshape(-1), w_qb[:, j])
+    assert np.array_equal(qi[0].reshape(-1), w_iq[:, j])
+    assert np.array_equal(w[0], w_iw[:, j]) and np.array_equal(w[1], w_iw[:, j])
+    col = w_qb[:, j].reshape(64, 256)
+    assert np.array_equal(q[1, :, :192], col[:, :192])                    # nope part: not turned
+    a, b = col[:, 192], col[:, 193]
+    np.testing.assert_allclose(q[1, :, 192], a * np.cos(5.0) - b * np.sin(5.0), rtol=2 ** -7, atol=1e-30)
+    np.testing.assert_allclose(q[1, :, 193], a * np.sin(5.0) + b * np.cos(5.0), rtol=2 ** -7, atol=1e-30)
+    r = q[1, :, 192:]
+    np.testing.assert_allclose(r[:, 0::2] ** 2 + r[:, 1::2] ** 2, col[:, 192::2] ** 2 + col[:, 193::2] ** 2,
+                               rtol=2 ** -6)
+    icol = w_iq[:, j].reshape(32, 128)
+    assert np.array_equal(qi[1, :, :64], icol[:, :64])                    # indexer: first half not turned
+    assert not np.allclose(qi[1, :, 64:], icol[:, 64:], rtol=1e-3)
+
+
+def check_qproj_rounds_to_nearest_even(ref):
+    """Two-hot c_q whose exact sums fall between bf16 values: 1 + 2^-8 + 2^-10
+    rounds up to 1 + 2^-7, 1 + 2^-9 down to 1, the tie 1 + 2^-8 to even (1)."""
+    w_qb = np.zeros((64 * 256, 2048))
+    w_iq = np.zeros((32 * 128, 2048))
+    w_iw = np.zeros((32, 2048))
+    w_qb[:, 0] = 1.0
+    w_iq[:, 0] = 1.0
+    c = np.zeros((3, 2048))
+    c[:, 0] = 1.0
+    c[:, 1] = [2.0 ** -8 + 2.0 ** -10, 2.0 ** -9, 2.0 ** -8]
+    w_qb[:, 1] = 1.0
+    w_iq[:, 1] = 1.0
+    q, qi, _ = ref.q_project(c, w_qb, w_iq, w_iw, [0, 0, 0])
+    for t, v in enumerate([1 + 2.0 ** -7, 1.0, 1.0]):
+        assert np.all(q[t] == v) and np.all(qi[t] == v), t
+    # The rope pair is rounded before it turns: at position 2 the pair
+    # (1.0078125, 1.0078125) (the bf16 value of 1 + 2^-8 + 2^-10) turns to
+    # (cos 2 - sin 2, sin 2 + cos 2) * 1.0078125 = (-1.33573..., 0.49621...),
+    # stored as (-1.3359375, 0.49609375); turning the unrounded sum would give
+    # -1.328125 for the first.
+    q2, _, _ = ref.q_project(c[:1], w_qb, w_iq, w_iw, [2])
+    assert np.all(q2[0, :, 192] == -1.3359375) and np.all(q2[0, :, 193] == 0.49609375)
+
+
+def check_qabsorb_integer_exact_explicit_logits(ref):
+    """With small-integer inputs every step is exact: the absorbed query's
+    logit against [latent ; k_rope] equals the explicit form
+    q_nope . (W_UK latent) + q_rope . k_rope, head by head."""
+    rng = _rng(83)
+    n = 3
+    q = rng.integers(-1, 2, size=(n, 64, 256)).astype(np.float64)
+    w_uk = rng.integers(-1, 2, size=(64, 192, 512)).astype(np.float64)
+    rows = rng.integers(-2, 3, size=(5, 576)).astype(np.float64)
+    qa = ref.q_absorb(q, w_uk)
+    assert qa.shape == (n, 64, 576)
+    for t in range(n):
+        for h in range(64):
+            k_nope = w_uk[h] @ rows[:, :512].T                  # [192, 5]: explicit keys
+            explicit = q[t, h, :192] @ k_nope + q[t, h, 192:] @ rows[:, 512:].T
+            assert np.array_equal(qa[t, h] @ rows.T, explicit), (t, h)
+
+
+def check_qproj_turned_query_scores_by_relative_position(ref):
+    """The turned query against keys turned by the cache write scores by
+    relative position: (p, s) and (p + d, s + d) give the same rope logit."""
+    rng = _rng(87)
+    w_qb, w_iq, w_iw = _q_weights(rng, scale=0.05)
+    c = _bf16_grid(rng.standard_normal((1, 2048)))
+    kv_a = _bf16_grid(rng.standard_normal((1, 576)))
+    gamma = np.ones(512)
+    for p, s, d in [(1000, 900, 5000), (70000, 3, 400000)]:
+        q1, _, _ = ref.q_project(c, w_qb, w_iq, w_iw, [p])
+        q2, _, _ = ref.q_project(c, w_qb, w_iq, w_iw, [p + d])
+        k1 = ref.cache_rows_from_projection(kv_a, gamma, [s])[0, 512:]
+        k2 = ref.cache_rows_from_projection(kv_a, gamma, [s + d])[0, 512:]
+        l1 = q1[0, :, 192:] @ k1
+        l2 = q2[0, :, 192:] @ k2
+        scale = np.abs(q1[0, :, 192:]) @ np.abs(k1)
+        assert np.all(np.abs(l1 - l2) <= 2 ** -6 * scale), (p, s, d)
+
+
+def check_projection_error_bound_covers_fp32(ref):
+    rng = _rng(89)
+    a = _bf16_grid(rng.standard_normal((4, 2048)))
+    b = _bf16_grid(rng.standard_normal((6, 2048)))
+    exact = a @ b.T
+    bound = ref.projection_error_bound(a, b)
+    prods = (a[:, None, :] * b[None, :, :]).astype(np.float32)          # exact: bf16 x bf16 fits fp32
+    for order in (slice(None), slice(None, None, -1)):
+        acc = np.zeros((4, 6), dtype=np.float32)
+        for k in range(2048)[order]:
+            acc = acc + prods[:, :, k]
+        assert np.all(np.abs(acc.astype(np.float64) - exact) <= bound)
+    pair = prods.copy()
+    while pair.shape[-1] > 1:
+        pair = (pair[..., 0::2] + pair[..., 1::2]).astype(np.float32)
+    assert np.all(np.abs(pair[..., 0].astype(np.float64) - exact) <= bound)
+    # near the worst case: 1 followed by 2047 products of 2^-24, each lost
+    # against the running fp32 sum (a tie to even at 1.0): error 2047 u
+    a1 = np.full((1, 2048), 2.0 ** -12)
+    a1[0, 0] = 1.0
+    acc = np.float32(0.0)
+    for k in range(2048):
+        acc = np.float32(acc + np.float32(a1[0, k] * a1[0, k]))
+    err = abs(float(acc) - float(a1[0] @ a1[0]))
+    assert err > 2000 * 2.0 ** -24 and err <= ref.projection_error_bound(a1, a1)[0, 0]
+
+
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

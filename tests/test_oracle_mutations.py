@@ -57,6 +57,20 @@ MUTATIONS = [
     ("mtp_first_row_for_all", "row = sel_idx[int(sel_of[t])]", "row = sel_idx[0]"),
     ("mtp_selects_at_token_positions", "cur = share_selection(topk_select_rows(sc, sel_pos, k), sel_of, q_pos)",
      "cur = share_selection(topk_select_rows(sc, np.minimum(sel_pos, min(q_pos)), k), sel_of, q_pos)"),
+    ("q_rope_on_first_dims", "q = round_to_bf16(_rope_heads(q, pos, QK_NOPE_DIM))",
+     "q = round_to_bf16(_rope_heads(q[:, :, ::-1], pos, QK_NOPE_DIM)[:, :, ::-1])"),
+    ("q_not_rounded_before_rope", "q = round_to_bf16(c_q @ _f64(w_qb).T).reshape(n, N_HEADS, QK_HEAD_DIM)",
+     "q = (c_q @ _f64(w_qb).T).reshape(n, N_HEADS, QK_HEAD_DIM)"),
+    ("q_turned_backwards", "x[:, :, first:] = rope_interleaved(part, np.repeat(np.asarray(pos), H))",
+     "x[:, :, first:] = rope_interleaved(part, -np.repeat(np.asarray(pos), H))"),
+    ("indexer_q_turns_first_half", "qi = round_to_bf16(_rope_heads(qi, pos, INDEX_HEAD_DIM - QK_ROPE_DIM))",
+     "qi = round_to_bf16(_rope_heads(qi, pos, 0))"),
+    ("absorb_one_head_for_all", "out[:, h, :KV_LORA_RANK] = round_to_bf16(q[:, h, :QK_NOPE_DIM] @ w_uk[h])",
+     "out[:, h, :KV_LORA_RANK] = round_to_bf16(q[:, h, :QK_NOPE_DIM] @ w_uk[0])"),
+    ("absorb_drops_rope", "out[:, h, KV_LORA_RANK:] = q[:, h, QK_NOPE_DIM:]", "out[:, h, KV_LORA_RANK:] = 0.0"),
+    ("head_weights_wrong_matrix", "w = (c_q @ _f64(w_iw).T).astype(np.float32).astype(np.float64)",
+     "w = (c_q @ _f64(w_iw).T)[:, ::-1].astype(np.float32).astype(np.float64)"),
+    ("projection_bound_too_small", "g = (K + 1) * u / (1 - (K + 1) * u)", "g = 8 * u"),
     ("cache_row_latent_not_normalised", "lat = rms_norm(kv_a[:, :KV_LORA_RANK], gamma)", "lat = kv_a[:, :KV_LORA_RANK] * _f64(gamma)"),
 ]
 
