@@ -41,6 +41,7 @@ def parse():
                     help="c3 times the whole chunked-prefill stack; its dominant kernel is the MFMA-bound indexer")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill indexer and cache-write measurements")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-query", action="store_true", help="skip the query-side (projection and absorption) legs")
     ap.add_argument("--cpu-sample", type=int, default=16, help="queries in the CPU oracle sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="repeat the CPU sample for at least this long")
     ap.add_argument("--copies", type=int, default=2,
@@ -237,6 +238,59 @@ def prefill_indexer(seed, reps=9, warmup=20):
             "peak": BF16_PEAK_TFLOPS, "timing": "median of %d HIP-event-timed launches" % reps}
 
 
+def query_side_leg(seed, n, reps=15, warmup=10):
+    """sa_q_project + sa_q_absorb for n tokens (random-init weights of the
+    model's shapes), HIP-event medians per call.  Algorithmic bytes: every
+    weight and activation read once, every output written once; FLOPs: the
+    two contractions."""
+    import math
+    import torch
+    from sparse_attention_relu_amd import api
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(seed + 17)
+    bf = lambda x: x.to(torch.bfloat16).contiguous()
+    w_qb = bf(torch.randn((64 * 256, 2048), generator=g, device=dev) / math.sqrt(2048))
+    w_uk_t = bf(torch.randn((64, 512, 192), generator=g, device=dev) / math.sqrt(192 * 576))
+    w_iq = bf(torch.randn((32 * 128, 2048), generator=g, device=dev) / math.sqrt(2048 * 128))
+    w_iw = bf(torch.randn((32, 2048), generator=g, device=dev) / math.sqrt(2048 * 32))
+    c = bf(torch.randn((n, 2048), generator=g, device=dev))
+    pos = torch.arange(131072 - n, 131072, dtype=torch.int32, device=dev)
+    q = torch.empty((n, 64, 256), dtype=torch.bfloat16, device=dev)
+    qi = torch.empty((n, 32, 128), dtype=torch.bfloat16, device=dev)
+    w = torch.empty((n, 32), dtype=torch.float32, device=dev)
+    qa = torch.empty((n, 64, 576), dtype=torch.bfloat16, device=dev)
+    proj = lambda st=None: api.q_project(c, w_qb, pos, w_iq=w_iq, w_iw=w_iw, q=q, q_idx=qi, w=w, stream=st)
+    absorb = lambda st=None: api.q_absorb(q, w_uk_t, q_abs=qa, stream=st)
+    for _ in range(warmup):
+        proj()
+        absorb()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    times = {}
+    for name, fn in (("q_project", proj), ("q_absorb", absorb)):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, e in ev:
+            a.record(s)
+            fn(s)
+            e.record(s)
+        torch.cuda.synchronize()
+        times[name] = sorted(a.elapsed_time(e) for a, e in ev)[reps // 2]
+    rows = 64 * 256 + 32 * 128 + 32
+    b_proj = rows * 2048 * 2 + n * 2048 * 2 + n * (64 * 256 * 2 + 32 * 128 * 2 + 32 * 4) + n * 4
+    b_abs = 64 * 512 * 192 * 2 + n * 64 * 256 * 2 + n * 64 * 576 * 2
+    f_proj = 2.0 * n * rows * 2048
+    f_abs = 2.0 * n * 64 * 192 * 512
+    out = {"tokens": n, "unit_time": "ms", "timing": "median of %d HIP-event-timed calls" % reps}
+    for name, ms, nb, fl in (("q_project", times["q_project"], b_proj, f_proj),
+                             ("q_absorb", times["q_absorb"], b_abs, f_abs)):
+        gbs = nb / (ms * 1e-3) / 1e9
+        tfl = fl / (ms * 1e-3) / 1e12
+        out[name] = {"ms": round(ms, 5), "bytes": nb, "flops": fl, "gbs": round(gbs, 1),
+                     "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "tflops": round(tfl, 1),
+                     "frac_of_bf16_peak": round(tfl / BF16_PEAK_TFLOPS, 4)}
+    return out
+
+
 class HipEvents:
     """Raw hipEvents (the library records them on its stream)."""
 
@@ -383,6 +437,10 @@ def main():
         out["prefill_indexer"] = prefill_indexer(args.seed)
         print("[bench] cache write", file=sys.stderr, flush=True)
         out["cache_write"] = cache_write_leg(args.seed)
+    if not args.no_query:
+        print("[bench] query side", file=sys.stderr, flush=True)
+        out["query_side"] = {"decode_16_tokens": query_side_leg(args.seed, 16),
+                             "prefill_4096_tokens": query_side_leg(args.seed, 4096)}
     if not args.no_cpu:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(b, wl, args.cpu_sample, args.cpu_seconds)

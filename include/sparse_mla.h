@@ -299,6 +299,61 @@ int32_t sa_layer_stack_noalloc(const sa_layer_desc* layers, int32_t n_layers, co
 int32_t sa_share_selection(const int32_t* sel_idx, int32_t n_sel, int32_t k, const int32_t* sel_of,
                            const int32_t* q_pos, int32_t n_q, int32_t* idx, sa_stream_t stream);
 
+/*
+ * sa_q_project -- the query projections of n new tokens from their q_lora
+ * activation (the step before sa_indexer_score and sa_mla_sparse_attn on the
+ * query side).
+ *
+ * Defines ("Multi-head latent attention" row: a q_lora_rank = 2048
+ * bottleneck; "Partial RoPE" row: each head's query is [192 nope ; 64 rope]
+ * and only the rope part turns; "Indexer-selected sparse attention" row: 32
+ * indexer heads of 128; llm-atlas config: qk_head_dim 256, rope_interleave,
+ * indexer_rope_interleave, rope_theta 8e6):
+ *     q[t]     = bf16(W_QB c_q[t]) as [64][256]; dims 192..255 of each head
+ *                turned in pairs (2j, 2j+1) by pos[t] * 8e6^(-2j/64)
+ *     q_idx[t] = bf16(W_IQ c_q[t]) as [32][128]; dims 64..127 turned the same way
+ *     w[t]     = W_IW c_q[t] (fp32)
+ * The pages print neither the indexer query's nor the head weights' source;
+ * both are taken from q_lora, and the indexer query turns its last 64 dims like
+ * the indexer key (sa_cache_write).  Sums in fp32; each stored bf16 value is
+ * rounded to nearest even; the pairs turn in fp64 from the rounded values and
+ * are rounded again.
+ *
+ *   c_q    bf16 [n, 2048]          q_lora activation
+ *   w_qb   bf16 [64 * 256, 2048]   q_b_proj weight (rows: head-major, [192 nope ; 64 rope])
+ *   w_iq   bf16 [32 * 128, 2048]   indexer query weight, or NULL
+ *   w_iw   bf16 [32, 2048]         head-weight projection, or NULL
+ *   pos    int32 [n]               token positions (>= 0)
+ *   q      bf16 [n, 64, 256]       output
+ *   q_idx  bf16 [n, 32, 128]       output, or NULL
+ *   w      fp32 [n, 32]            output, or NULL
+ * w_iq, w_iw, q_idx and w are all given or all NULL (NULL: only q, e.g. for a
+ * layer that reuses another layer's selection).  Every pointer 16-byte aligned.
+ */
+int32_t sa_q_project(const void* c_q, const void* w_qb, const void* w_iq, const void* w_iw,
+                     const int32_t* pos, int32_t n, void* q, void* q_idx, float* w,
+                     sa_stream_t stream);
+
+/*
+ * sa_q_absorb -- fold the key half of kv_b_proj into the query.
+ *
+ * Defines ("Multi-head latent attention" row: kv_b_proj maps the 512-wide
+ * latent to, per head, 192 key rows W_UK[h] and 256 value rows): with
+ * q_nope = q[t, h, 0:192] and q_rope = q[t, h, 192:256],
+ *     q_abs[t, h, 0:512]   = bf16(W_UK[h]^T q_nope)      (fp32 sums)
+ *     q_abs[t, h, 512:576] = q_rope
+ * so that q_abs[t, h] . [latent ; k_rope] = q_nope . (W_UK[h] latent) +
+ * q_rope . k_rope: the explicit logit over the cache row.
+ *
+ *   q       bf16 [n, 64, 256]   (sa_q_project's output)
+ *   w_uk_t  bf16 [64, 512, 192] W_UK[h]^T per head: element [h][c][d] =
+ *                               kv_b_proj.weight[h * 448 + d][c] (the transpose
+ *                               of each head's 192 key rows, arranged once when
+ *                               the weights are loaded)
+ *   q_abs   bf16 [n, 64, 576]   output (sa_mla_sparse_attn's q_abs)
+ */
+int32_t sa_q_absorb(const void* q, const void* w_uk_t, int32_t n, void* q_abs, sa_stream_t stream);
+
 /* IndexShare pattern of the 78-layer model: 1 if layer runs its own indexer
  * (layers 0-2, then every layer l with l mod 4 == 2), else 0; -1 if layer < 0. */
 int32_t sa_layer_is_full(int32_t layer);
@@ -369,7 +424,7 @@ int32_t sa_indexer_score_algo(const void* q_idx, const float* w, const void* k_i
  *            idx[t, j] <= q_pos[t]); q_seq[t] >= 0
  *   shared selection: 0 <= sel_of[t] < n_sel; sel_seq[sel_of[t]] == q_seq[t]
  *            (and the selecting queries obey the batch rules)
- *   cache write: pos[i] >= 0, dst[i] >= 0
+ *   cache write: pos[i] >= 0, dst[i] >= 0;  query projection: pos[t] >= 0
  * The first violation (and a count of all of them) is kept in a device-side
  * record.  The check kernels only read; the call's own kernels still run.
  *

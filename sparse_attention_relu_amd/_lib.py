@@ -46,6 +46,8 @@ SIGNATURES = {
     "sa_layer_stack": (c_i32, [ctypes.POINTER(LayerDesc), c_i32, ctypes.POINTER(BatchDesc), c_i32, c_f32, c_p,
                                c_sz, ctypes.POINTER(StageEvents), c_p]),
     "sa_share_selection": (c_i32, [c_p, c_i32, c_i32, c_p, c_p, c_i32, c_p, c_p]),
+    "sa_q_project": (c_i32, [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_p, c_p, c_p]),
+    "sa_q_absorb": (c_i32, [c_p, c_p, c_i32, c_p, c_p]),
     "sa_layer_stack_noalloc_max_bytes": (c_sz, []),
     "sa_layer_stack_noalloc": (c_i32, [ctypes.POINTER(LayerDesc), c_i32, ctypes.POINTER(BatchDesc), c_i32, c_f32,
                                        ctypes.POINTER(StageEvents), c_p]),

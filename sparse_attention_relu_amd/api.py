@@ -128,6 +128,51 @@ def share_selection(sel_idx, sel_of, q_pos, idx=None, stream=None):
     return idx
 
 
+QLORA = 2048
+
+
+def q_project(c_q, w_qb, pos, w_iq=None, w_iw=None, q=None, q_idx=None, w=None, stream=None):
+    """sa_q_project: q [n,64,256] (rope part turned), and with w_iq / w_iw the
+    indexer query [n,32,128] and head weights [n,32] (fp32)."""
+    n = c_q.shape[0]
+    _need(c_q, "c_q", torch.bfloat16, (n, QLORA))
+    _need(w_qb, "w_qb", torch.bfloat16, (HEADS * 256, QLORA))
+    _need(pos, "pos", torch.int32, (n,))
+    dev = c_q.device
+    if q is None:
+        q = torch.empty((n, HEADS, 256), dtype=torch.bfloat16, device=dev)
+    _need(q, "q", torch.bfloat16, (n, HEADS, 256))
+    if w_iq is not None:
+        _need(w_iq, "w_iq", torch.bfloat16, (IDX_HEADS * IDX_DIM, QLORA))
+        _need(w_iw, "w_iw", torch.bfloat16, (IDX_HEADS, QLORA))
+        if q_idx is None:
+            q_idx = torch.empty((n, IDX_HEADS, IDX_DIM), dtype=torch.bfloat16, device=dev)
+        if w is None:
+            w = torch.empty((n, IDX_HEADS), dtype=torch.float32, device=dev)
+        _need(q_idx, "q_idx", torch.bfloat16, (n, IDX_HEADS, IDX_DIM))
+        _need(w, "w", torch.float32, (n, IDX_HEADS))
+    L = _lib.lib()
+    st = L.sa_q_project(_ptr(c_q), _ptr(w_qb), _ptr(w_iq), _ptr(w_iw), _ptr(pos), n, _ptr(q), _ptr(q_idx), _ptr(w),
+                        _stream(stream))
+    _lib.check("sa_q_project", st)
+    return q, q_idx, w
+
+
+def q_absorb(q, w_uk_t, q_abs=None, stream=None):
+    """sa_q_absorb: q_abs [n,64,576] = [W_UK^T q_nope ; q_rope] per head;
+    w_uk_t is [64, 512, 192] (each head's key rows of kv_b_proj, transposed)."""
+    n = q.shape[0]
+    _need(q, "q", torch.bfloat16, (n, HEADS, 256))
+    _need(w_uk_t, "w_uk_t", torch.bfloat16, (HEADS, LATENT, 192))
+    if q_abs is None:
+        q_abs = torch.empty((n, HEADS, ROW), dtype=torch.bfloat16, device=q.device)
+    _need(q_abs, "q_abs", torch.bfloat16, (n, HEADS, ROW))
+    L = _lib.lib()
+    st = L.sa_q_absorb(_ptr(q), _ptr(w_uk_t), n, _ptr(q_abs), _stream(stream))
+    _lib.check("sa_q_absorb", st)
+    return q_abs
+
+
 def cache_write(kv_a, gamma, pos, dst, kv_cache, k_raw=None, ln_w=None, ln_b=None, k_cache=None, stream=None):
     """sa_cache_write: the cache rows (and optionally the indexer keys) of n
     new tokens, written at rows dst of kv_cache (and k_cache)."""

@@ -60,6 +60,9 @@ int32_t debug_idx(const int32_t* idx, int32_t n_q, int32_t k, const int32_t* q_p
                   hipStream_t stream);
 int32_t debug_scores(const float* scores, int64_t ld, const int32_t* q_pos, int32_t n_q, hipStream_t stream);
 int32_t debug_cache(const int32_t* pos, const int64_t* dst, int32_t n, hipStream_t stream);
+int32_t launch_q_project(const void* c_q, const void* w_qb, const void* w_iq, const void* w_iw, const int32_t* pos,
+                         int32_t n, void* q, void* q_idx, float* w, hipStream_t stream);
+int32_t launch_q_absorb(const void* q, const void* w_uk_t, int32_t n, void* q_abs, hipStream_t stream);
 int32_t debug_share(const int32_t* sel_of, int32_t n_sel, const int32_t* q_seq, const int32_t* sel_seq, int32_t n_q,
                     hipStream_t stream);
 int32_t launch_share(const int32_t* sel_idx, int32_t n_sel, int32_t k, const int32_t* sel_of, const int32_t* q_pos,
@@ -337,6 +340,32 @@ int32_t sa_share_selection(const int32_t* sel_idx, int32_t n_sel, int32_t k, con
   int32_t rc = debug_share(sel_of, n_sel, nullptr, nullptr, n_q, st);
   if (rc) return rc;
   return launch_share(sel_idx, n_sel, k, sel_of, q_pos, n_q, idx, st);
+}
+
+int32_t sa_q_project(const void* c_q, const void* w_qb, const void* w_iq, const void* w_iw, const int32_t* pos,
+                     int32_t n, void* q, void* q_idx, float* w, sa_stream_t stream) {
+  SA_REQUIRE(n >= 0, SA_ERR_INVALID_ARG, "q_project: negative n");
+  if (n == 0) return SA_OK;
+  SA_REQUIRE(c_q && w_qb && pos && q, SA_ERR_INVALID_ARG, "q_project: null pointer argument");
+  const bool idx_part = w_iq || w_iw || q_idx || w;
+  SA_REQUIRE(!idx_part || (w_iq && w_iw && q_idx && w), SA_ERR_INVALID_ARG,
+             "q_project: the indexer part needs all of w_iq, w_iw, q_idx and w (or none)");
+  SA_REQUIRE(aligned16(c_q) && aligned16(w_qb) && aligned16(q) &&
+                 (!idx_part || (aligned16(w_iq) && aligned16(w_iw) && aligned16(q_idx) && aligned16(w))),
+             SA_ERR_INVALID_ARG, "q_project: tensors not 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  int32_t rc = debug_cache(pos, nullptr, n, st);
+  if (rc) return rc;
+  return launch_q_project(c_q, w_qb, w_iq, w_iw, pos, n, q, q_idx, w, st);
+}
+
+int32_t sa_q_absorb(const void* q, const void* w_uk_t, int32_t n, void* q_abs, sa_stream_t stream) {
+  SA_REQUIRE(n >= 0, SA_ERR_INVALID_ARG, "q_absorb: negative n");
+  if (n == 0) return SA_OK;
+  SA_REQUIRE(q && w_uk_t && q_abs, SA_ERR_INVALID_ARG, "q_absorb: null pointer argument");
+  SA_REQUIRE(aligned16(q) && aligned16(w_uk_t) && aligned16(q_abs), SA_ERR_INVALID_ARG,
+             "q_absorb: tensors not 16-byte aligned");
+  return launch_q_absorb(q, w_uk_t, n, q_abs, (hipStream_t)stream);
 }
 
 // Per-device address of `scratch`, looked up once per device with that

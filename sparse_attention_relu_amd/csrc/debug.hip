@@ -86,7 +86,7 @@ __global__ void share_kernel(const int32_t* sel_of, int32_t n_sel, const int32_t
 __global__ void cache_kernel(const int32_t* pos, const int64_t* dst, int32_t n) {
   for (int32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
     if (pos[i] < 0) report(CACHE_POS_NEG, (uint32_t)i, 0, pos[i]);
-    if (dst[i] < 0) report(CACHE_DST_NEG, (uint32_t)i, 0, dst[i]);
+    if (dst && dst[i] < 0) report(CACHE_DST_NEG, (uint32_t)i, 0, dst[i]);
   }
 }
 

@@ -1,0 +1,404 @@
+// Query side for gfx950: the projections that produce the hot path's query
+// inputs from the q_lora activation.
+//
+//   q      = bf16(W_QB c_q)             per head [192 nope ; 64 rope], the rope
+//                                       part turned at the token's position
+//   q_idx  = bf16(W_IQ c_q)             32 heads x 128, dims 64..127 turned
+//   w      = W_IW c_q                   32 head weights, fp32
+//   q_abs  = [bf16(W_UK[h]^T q_nope[h]) ; q_rope[h]]   per head (absorption)
+//
+// models.inteligile.com "GLM-5.2 / Model techniques map", "Checked in its
+// code", rows "Multi-head latent attention" (q_lora_rank bottleneck; kv_b_proj
+// holds, per head, qk_nope_head_dim key rows and v_head_dim value rows),
+// "Partial RoPE" (the per-head split [192 nope ; 64 rope]) and
+// "Indexer-selected sparse attention" (32 indexer heads of 128);
+// llm-architectures-explained "GLM-5.2", "Every architecture field"
+// (q_lora_rank 2,048); llm-atlas "GLM-5.2", config fields qk_head_dim,
+// rope_interleave, indexer_rope_interleave.  The pages print neither the
+// indexer query's nor the head weights' source; both are taken from the same
+// q_lora activation, and the indexer query turns its last 64 dims like the
+// indexer key.  Each projection's output is rounded to bf16 once (the head
+// weights stay fp32); the rope pairs turn from those bf16 values in fp64 and
+// are rounded again.
+//
+// Every product is a "weights x tokens" contraction with both operands K-
+// contiguous (nn.Linear weights [rows][K]; W_UK is taken pre-arranged as
+// W_UK^T [64][512][192], its transpose per head, so the absorption is the same
+// kind of product).  Weights sit on the M side of v_mfma_f32_16x16x32_bf16
+// and tokens on the N side, so each lane of the 16x16 result holds 4
+// consecutive weight rows of one token: a rope pair (2j, 2j + 1) is in one
+// lane.
+//
+//   qgemm_skinny_kernel  decode batches (16 or 32 tokens per token block):
+//                        each wave streams its share of K (64-wide blocks w,
+//                        w + 4, ...) for 64 weight rows straight into MFMA
+//                        operand registers, 3 blocks in flight, no LDS and no
+//                        barrier in the loop; the 4 waves' partial tiles are
+//                        summed through LDS at the end.  HBM-bound on the
+//                        weights.
+//   qgemm_tiled_kernel   prefill batches: 128 weight rows x 128 tokens per
+//                        workgroup, 64-wide K chunks staged in LDS (two
+//                        buffers, global -> registers -> LDS one chunk ahead),
+//                        2 x 2 waves of 64 x 64.  MFMA-bound.
+#include <atomic>
+#include <cmath>
+
+#include "rope.h"
+#include "sa_common.h"
+
+namespace sa {
+
+constexpr int kQThreads = 256;
+constexpr int kQModeBf16 = 0;        // bf16 (RNE)
+constexpr int kQModeRope = 1;        // bf16, rows r % period >= rope_start turned in pairs
+constexpr int kQModeF32 = 2;         // fp32
+
+struct QSeg {
+  const uint16_t* w;   // [rows][lda] weights of this segment (+ batch * w_batch)
+  void* out;           // token t: out + t * ldo (+ batch * o_batch), element = segment row
+  int64_t ldo;
+  int rows;            // a multiple of 4
+  int mblocks;         // workgroups along this segment's rows
+  int mode;
+  int period, rope_start;
+};
+
+struct QArgs {
+  const uint16_t* x;   // tokens [n][ldx] (+ batch * x_batch), K contiguous
+  int64_t ldx, x_batch, w_batch, o_batch;
+  int lda, K, n;
+  int n_seg;
+  QSeg seg[3];
+  const int32_t* pos;  // [n] token positions (rope)
+  // absorption: the rope part rides along, copied by the first m-block of
+  // each (head, token block): dst + t * dst_ld + b * dst_batch <- src (64 values)
+  const uint16_t* copy_src;
+  uint16_t* copy_dst;
+  int64_t copy_src_ld, copy_dst_ld, copy_src_batch, copy_dst_batch;
+  double inv_freq[32];   // theta^(-2j / 64)
+};
+
+__device__ __forceinline__ double bf16_bits_to_f64(uint32_t h) { return (double)__uint_as_float(h << 16); }
+
+// The segment of workgroup row-block mb (uniform), and mb within it.
+__device__ __forceinline__ int q_segment(const QArgs& A, int& mb) {
+  int s = 0;
+  if (A.n_seg > 1 && mb >= A.seg[0].mblocks) {
+    mb -= A.seg[0].mblocks;
+    s = 1;
+    if (A.n_seg > 2 && mb >= A.seg[1].mblocks) {
+      mb -= A.seg[1].mblocks;
+      s = 2;
+    }
+  }
+  return s;
+}
+
+// Store rows r .. r + 3 (segment rows, r a multiple of 4) of token t.
+__device__ __forceinline__ void q_store4(const QArgs& A, const QSeg& S, int b, int r, int t, f32x4 v) {
+#pragma clang fp contract(off)
+  if (r >= S.rows || t >= A.n) return;
+  if (S.mode == kQModeF32) {
+    float* o = reinterpret_cast<float*>(S.out) + (int64_t)b * A.o_batch + (int64_t)t * S.ldo + r;
+    *reinterpret_cast<f32x4*>(o) = v;
+    return;
+  }
+  uint16_t* o = reinterpret_cast<uint16_t*>(S.out) + (int64_t)b * A.o_batch + (int64_t)t * S.ldo + r;
+  const int hr = S.mode == kQModeRope ? r % S.period : 0;
+  if (S.mode == kQModeRope && hr >= S.rope_start) {
+    const int p = A.pos[t];
+    const int j = (hr - S.rope_start) >> 1;
+    uint32_t pk[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      double x0 = bf16_bits_to_f64(f32_to_bf16_rne(v[2 * q]));
+      double x1 = bf16_bits_to_f64(f32_to_bf16_rne(v[2 * q + 1]));
+      double sn, cs;
+      turn_sincos(p, A.inv_freq[j + q], sn, cs);
+      rope_pair(x0, x1, sn, cs);
+      pk[q] = pack_bf16x2((float)x0, (float)x1);
+    }
+    *reinterpret_cast<u32x2*>(o) = u32x2{pk[0], pk[1]};
+  } else {
+    *reinterpret_cast<u32x2*>(o) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  }
+}
+
+// The 64-value rope part of each token of the block (absorption only).
+__device__ __forceinline__ void q_copy_rope(const QArgs& A, int b, int n0, int n_tok) {
+  for (int i = threadIdx.x; i < n_tok * 8; i += kQThreads) {
+    const int t = n0 + (i >> 3);
+    if (t >= A.n) continue;
+    const u32x4 v = ld16(A.copy_src + (int64_t)b * A.copy_src_batch + (int64_t)t * A.copy_src_ld + (i & 7) * 8);
+    *reinterpret_cast<u32x4*>(A.copy_dst + (int64_t)b * A.copy_dst_batch + (int64_t)t * A.copy_dst_ld + (i & 7) * 8) = v;
+  }
+}
+
+// ------------------------------------------------------------ decode batches
+// K is consumed in 64-wide blocks dealt to the 4 waves in turn (blocks w,
+// w + 4, ...).  Within a block the two 32-wide MFMA steps take their
+// contraction slots from k = 64 blk + 16 kg + 8 j (j = step, kg = lane / 16),
+// the same order for both operands, so each lane reads 32 contiguous bytes
+// of a row and the 4 lanes of a row read its whole 128-byte line.
+constexpr int kSkBM = 64;            // weight rows per workgroup
+constexpr int kSkTM = kSkBM / 16;
+constexpr int kSkDepth = 3;          // 64-wide blocks in flight per wave
+
+template <int TN>                    // 16 TN tokens per workgroup
+__global__ __launch_bounds__(kQThreads) void qgemm_skinny_kernel(QArgs A) {
+  int mb = blockIdx.x;
+  const int si = q_segment(A, mb);
+  const QSeg& S = si == 0 ? A.seg[0] : (si == 1 ? A.seg[1] : A.seg[2]);
+  const int b = blockIdx.z;
+  const int m0 = mb * kSkBM, n0 = blockIdx.y * 16 * TN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, kg = lane >> 4;
+  if (A.copy_dst && mb == 0) q_copy_rope(A, b, n0, 16 * TN);
+  // operand row pointers: weight row m0 + 16 tm + l16, token n0 + 16 tn + l16
+  // (clamped into range; their results are not stored), lane offset 16 kg
+  const uint16_t* wp[kSkTM];
+  const uint16_t* xp[TN];
+#pragma unroll
+  for (int tm = 0; tm < kSkTM; ++tm)
+    wp[tm] = S.w + (int64_t)b * A.w_batch + (int64_t)min(m0 + 16 * tm + l16, S.rows - 1) * A.lda + 16 * kg;
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn)
+    xp[tn] = A.x + (int64_t)b * A.x_batch + (int64_t)min(n0 + 16 * tn + l16, A.n - 1) * A.ldx + 16 * kg;
+  const int n_blk = A.K / 64;
+  const int n_my = (n_blk - wave + 3) / 4;      // this wave's blocks: wave, wave + 4, ...
+  f32x4 acc[kSkTM][TN];
+#pragma unroll
+  for (int tm = 0; tm < kSkTM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 ra[kSkDepth][kSkTM][2], rb[kSkDepth][TN][2];
+  auto load = [&](int slot, int i) {
+    const int k = 64 * (wave + 4 * i);
+#pragma unroll
+    for (int tm = 0; tm < kSkTM; ++tm)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        ra[slot][tm][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp[tm] + k + 8 * j));
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) rb[slot][tn][j] = ld16(xp[tn] + k + 8 * j);
+  };
+#pragma unroll
+  for (int u = 0; u < kSkDepth; ++u)
+    if (u < n_my) load(u, u);
+  for (int i = 0; i < n_my; i += kSkDepth) {
+#pragma unroll
+    for (int u = 0; u < kSkDepth; ++u) {
+      if (i + u < n_my) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int tm = 0; tm < kSkTM; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+              acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[u][tm][j]), as_bf16x8(rb[u][tn][j]),
+                                                                    acc[tm][tn], 0, 0, 0);
+        if (i + u + kSkDepth < n_my) load(u, i + u + kSkDepth);
+      }
+    }
+  }
+  // sum the 4 waves' partial tiles: wave w finishes tiles tm = w
+  __shared__ f32x4 part[4][kSkTM][TN][64];
+#pragma unroll
+  for (int tm = 0; tm < kSkTM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) part[wave][tm][tn][lane] = acc[tm][tn];
+  __syncthreads();
+  const int tm = wave;
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) {
+    f32x4 v = part[0][tm][tn][lane];
+#pragma unroll
+    for (int w2 = 1; w2 < 4; ++w2) v += part[w2][tm][tn][lane];
+    q_store4(A, S, b, m0 + 16 * tm + 4 * kg, n0 + 16 * tn + l16, v);
+  }
+}
+
+// ----------------------------------------------------------- prefill batches
+constexpr int kTiBM = 128, kTiBN = 128, kTiBK = 64;
+constexpr int kTiPitch = kTiBK * 2 + 16;               // 144 bytes per staged row
+constexpr int kTiTM = kTiBM / 32, kTiTN = kTiBN / 32;  // 16x16 tiles per wave (2 x 2 waves)
+constexpr int kTiAP = kTiBM * 8 / kQThreads;           // 16-byte pieces per thread per chunk
+constexpr int kTiBP = kTiBN * 8 / kQThreads;
+constexpr size_t kTiSmem = 2 * (size_t)(kTiBM + kTiBN) * kTiPitch;   // 73,728 bytes
+
+__global__ __launch_bounds__(kQThreads) void qgemm_tiled_kernel(QArgs A) {
+  extern __shared__ __align__(16) uint8_t qsm[];
+  int mb = blockIdx.x;
+  const int si = q_segment(A, mb);
+  const QSeg& S = si == 0 ? A.seg[0] : (si == 1 ? A.seg[1] : A.seg[2]);
+  const int b = blockIdx.z;
+  const int m0 = mb * kTiBM, n0 = blockIdx.y * kTiBN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int l16 = lane & 15, kg = lane >> 4;
+  if (A.copy_dst && mb == 0) q_copy_rope(A, b, n0, kTiBN);
+  const uint16_t* W = S.w + (int64_t)b * A.w_batch;
+  const uint16_t* X = A.x + (int64_t)b * A.x_batch;
+  u32x4 ga[kTiAP], gb[kTiBP];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int p = 0; p < kTiAP; ++p) {
+      const int f = tid + p * kQThreads;
+      ga[p] = ld16(W + (int64_t)min(m0 + (f >> 3), S.rows - 1) * A.lda + k0 + (f & 7) * 8);
+    }
+#pragma unroll
+    for (int p = 0; p < kTiBP; ++p) {
+      const int f = tid + p * kQThreads;
+      gb[p] = ld16(X + (int64_t)min(n0 + (f >> 3), A.n - 1) * A.ldx + k0 + (f & 7) * 8);
+    }
+  };
+  auto lstore = [&](int buf) {
+    uint8_t* base = qsm + (size_t)buf * (kTiBM + kTiBN) * kTiPitch;
+#pragma unroll
+    for (int p = 0; p < kTiAP; ++p) {
+      const int f = tid + p * kQThreads;
+      *reinterpret_cast<u32x4*>(base + (f >> 3) * kTiPitch + (f & 7) * 16) = ga[p];
+    }
+#pragma unroll
+    for (int p = 0; p < kTiBP; ++p) {
+      const int f = tid + p * kQThreads;
+      *reinterpret_cast<u32x4*>(base + (kTiBM + (f >> 3)) * kTiPitch + (f & 7) * 16) = gb[p];
+    }
+  };
+  f32x4 acc[kTiTM][kTiTN];
+#pragma unroll
+  for (int tm = 0; tm < kTiTM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < kTiTN; ++tn) acc[tm][tn] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nk = A.K / kTiBK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kc = 0; kc < nk; ++kc) {
+    const int buf = kc & 1;
+    if (kc + 1 < nk) gload((kc + 1) * kTiBK);
+    const uint8_t* la = qsm + (size_t)buf * (kTiBM + kTiBN) * kTiPitch;
+    const uint8_t* lb = la + kTiBM * kTiPitch;
+#pragma unroll
+    for (int s = 0; s < kTiBK / 32; ++s) {
+      bf16x8 a[kTiTM], bb[kTiTN];
+#pragma unroll
+      for (int tm = 0; tm < kTiTM; ++tm)
+        a[tm] = *reinterpret_cast<const bf16x8*>(la + (wm * 16 * kTiTM + tm * 16 + l16) * kTiPitch + (s * 32 + 8 * kg) * 2);
+#pragma unroll
+      for (int tn = 0; tn < kTiTN; ++tn)
+        bb[tn] = *reinterpret_cast<const bf16x8*>(lb + (wn * 16 * kTiTN + tn * 16 + l16) * kTiPitch + (s * 32 + 8 * kg) * 2);
+#pragma unroll
+      for (int tm = 0; tm < kTiTM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < kTiTN; ++tn)
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[tm], bb[tn], acc[tm][tn], 0, 0, 0);
+    }
+    if (kc + 1 < nk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int tm = 0; tm < kTiTM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < kTiTN; ++tn)
+      q_store4(A, S, b, m0 + wm * 16 * kTiTM + tm * 16 + 4 * kg, n0 + wn * 16 * kTiTN + tn * 16 + l16, acc[tm][tn]);
+}
+
+}  // namespace sa
+
+namespace sa_host {
+
+static bool q_skinny(int32_t n) { return n <= 64; }
+
+static void fill_inv_freq(double* f) {
+  for (int j = 0; j < 32; ++j) f[j] = std::pow(8.0e6, -(double)(2 * j) / 64.0);
+}
+
+// hipFuncSetAttribute is per device; remember which devices have been set up.
+static std::atomic<uint64_t> g_q_attr_set{0};
+
+static int32_t q_launch(sa::QArgs& A, int n_batch, hipStream_t stream) {
+  const bool sk = q_skinny(A.n);
+  const int sk_tn = A.n <= 16 ? 1 : 2;        // 16 or 32 tokens per skinny workgroup
+  const int bm = sk ? sa::kSkBM : sa::kTiBM, bn = sk ? 16 * sk_tn : sa::kTiBN;
+  int64_t mblocks = 0;
+  for (int s = 0; s < A.n_seg; ++s) {
+    A.seg[s].mblocks = (A.seg[s].rows + bm - 1) / bm;
+    mblocks += A.seg[s].mblocks;
+  }
+  const int64_t nblocks = (A.n + bn - 1) / bn;
+  if (mblocks > 0x7fffffff || nblocks > 65535 || n_batch > 65535) {
+    set_error("query side: grid too large (%lld x %lld x %d)", (long long)mblocks, (long long)nblocks, n_batch);
+    return SA_ERR_UNSUPPORTED;
+  }
+  fill_inv_freq(A.inv_freq);
+  const dim3 grid((unsigned)mblocks, (unsigned)nblocks, (unsigned)n_batch);
+  if (sk) {
+    if (sk_tn == 1)
+      hipLaunchKernelGGL(sa::qgemm_skinny_kernel<1>, grid, dim3(sa::kQThreads), 0, stream, A);
+    else
+      hipLaunchKernelGGL(sa::qgemm_skinny_kernel<2>, grid, dim3(sa::kQThreads), 0, stream, A);
+    return check_launch("qgemm_skinny_kernel");
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    set_error("query side: hipGetDevice failed");
+    return SA_ERR_HIP;
+  }
+  const uint64_t bit = 1ull << (dev & 63);
+  if (!(g_q_attr_set.load() & bit)) {
+    if (hipFuncSetAttribute((const void*)sa::qgemm_tiled_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)sa::kTiSmem) != hipSuccess) {
+      set_error("query side: cannot reserve %zu bytes of LDS", sa::kTiSmem);
+      return SA_ERR_HIP;
+    }
+    g_q_attr_set.fetch_or(bit);
+  }
+  hipLaunchKernelGGL(sa::qgemm_tiled_kernel, grid, dim3(sa::kQThreads), sa::kTiSmem, stream, A);
+  return check_launch("qgemm_tiled_kernel");
+}
+
+int32_t launch_q_project(const void* c_q, const void* w_qb, const void* w_iq, const void* w_iw, const int32_t* pos,
+                         int32_t n, void* q, void* q_idx, float* w, hipStream_t stream) {
+  sa::QArgs A{};
+  A.x = (const uint16_t*)c_q;
+  A.ldx = 2048;
+  A.lda = 2048;
+  A.K = 2048;
+  A.n = n;
+  A.pos = pos;
+  A.seg[0] = sa::QSeg{(const uint16_t*)w_qb, q, sa::kHeads * 256, sa::kHeads * 256, 0, sa::kQModeRope, 256, 192};
+  A.n_seg = 1;
+  if (w_iq) {
+    A.seg[1] = sa::QSeg{(const uint16_t*)w_iq, q_idx, sa::kIdxHeads * sa::kIdxDim, sa::kIdxHeads * sa::kIdxDim, 0,
+                        sa::kQModeRope, sa::kIdxDim, sa::kIdxDim - 64};
+    A.seg[2] = sa::QSeg{(const uint16_t*)w_iw, w, sa::kIdxHeads, sa::kIdxHeads, 0, sa::kQModeF32, 0, 0};
+    A.n_seg = 3;
+  }
+  return q_launch(A, 1, stream);
+}
+
+int32_t launch_q_absorb(const void* q, const void* w_uk_t, int32_t n, void* q_abs, hipStream_t stream) {
+  sa::QArgs A{};
+  A.x = (const uint16_t*)q;
+  A.ldx = sa::kHeads * 256;
+  A.x_batch = 256;
+  A.w_batch = (int64_t)sa::kLatent * 192;
+  A.o_batch = sa::kRow;
+  A.lda = 192;
+  A.K = 192;
+  A.n = n;
+  A.seg[0] = sa::QSeg{(const uint16_t*)w_uk_t, q_abs, (int64_t)sa::kHeads * sa::kRow, sa::kLatent, 0, sa::kQModeBf16, 0, 0};
+  A.n_seg = 1;
+  A.copy_src = (const uint16_t*)q + 192;
+  A.copy_dst = (uint16_t*)q_abs + sa::kLatent;
+  A.copy_src_ld = sa::kHeads * 256;
+  A.copy_dst_ld = (int64_t)sa::kHeads * sa::kRow;
+  A.copy_src_batch = 256;
+  A.copy_dst_batch = sa::kRow;
+  return q_launch(A, sa::kHeads, stream);
+}
+
+}  // namespace sa_host

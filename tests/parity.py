@@ -106,3 +106,64 @@ def check_mla(Lnp, B, idx_gpu, out_gpu, scale, rows=None, lse_gpu=None):
 
 def layer_np(L):
     return {k: to_numpy(getattr(L, k)) for k in ("q_idx", "w", "k_idx", "q_abs", "kv", "w_uv")}
+
+
+# ----------------------------------------------------------------- query side
+# Derived tolerances.  A stored bf16 value y = rnd(sum) where the GPU's fp32
+# sum differs from the exact one by at most eps = projection_error_bound
+# (gamma_{K+1} sum |a_k b_k|); the oracle rounds the exact sum (through fp32).
+# Both roundings move a value by at most half a bf16 ulp (<= 2^-8 |x|), so
+#   |gpu - oracle| <= eps + 2^-7 (|s| + eps) + 2^-23 |s|.
+# A turned pair starts from two such values (errors d0, d1), turns in fp64
+# (error ~1e-16, allowed 2^-20 of the pair's size) and is rounded again:
+#   |gpu - oracle| <= d0 + d1 + 2^-7 (|y| + d0 + d1) + 2^-20 (|x0| + |x1|).
+
+def _bf16_bound(s, eps):
+    return eps + 2.0 ** -7 * (np.abs(s) + eps) + 2.0 ** -23 * np.abs(s) + 1e-30
+
+
+def _check_bf16_part(name, got, exact, eps, rope_first, d, pos, ref_rounded):
+    """got / ref_rounded [n, H, d]; exact / eps [n, H, d] before rounding."""
+    b_pre = _bf16_bound(exact, eps)
+    bound = b_pre.copy()
+    if rope_first is not None:
+        d0, d1 = b_pre[..., rope_first::2], b_pre[..., rope_first + 1::2]
+        x0, x1 = np.abs(exact[..., rope_first::2]), np.abs(exact[..., rope_first + 1::2])
+        for off, y in ((0, ref_rounded[..., rope_first::2]), (1, ref_rounded[..., rope_first + 1::2])):
+            bound[..., rope_first + off::2] = d0 + d1 + 2.0 ** -7 * (np.abs(y) + d0 + d1) + 2.0 ** -20 * (x0 + x1)
+    err = np.abs(got - ref_rounded)
+    bad = np.argwhere(err > bound)
+    assert bad.size == 0, f"{name}: {len(bad)} values outside the derived bound; first {tuple(bad[0])}: " \
+                          f"gpu={got[tuple(bad[0])]} oracle={ref_rounded[tuple(bad[0])]} bound={bound[tuple(bad[0])]}"
+    return float(np.mean(err > 0))
+
+
+def check_q_project(c_q, w_qb, pos, q_gpu, w_iq=None, w_iw=None, qi_gpu=None, w_gpu=None):
+    """All numpy float64 (bf16 values widened); returns the fraction of
+    stored values that differ from the oracle's (a rounding-boundary rate)."""
+    n = c_q.shape[0]
+    if w_iq is None:
+        w_iq, w_iw = np.zeros((32 * 128, 2048)), np.zeros((32, 2048))
+    q_o, qi_o, w_o = ref.q_project(c_q, w_qb, w_iq, w_iw, pos)
+    s = (c_q @ w_qb.T).reshape(n, 64, 256)
+    eps = ref.projection_error_bound(c_q, w_qb).reshape(n, 64, 256)
+    frac = _check_bf16_part("q", q_gpu, s, eps, 192, 256, pos, q_o)
+    if qi_gpu is not None:
+        si = (c_q @ w_iq.T).reshape(n, 32, 128)
+        epsi = ref.projection_error_bound(c_q, w_iq).reshape(n, 32, 128)
+        frac = max(frac, _check_bf16_part("q_idx", qi_gpu, si, epsi, 64, 128, pos, qi_o))
+        epsw = ref.projection_error_bound(c_q, w_iw)
+        err = np.abs(w_gpu - c_q @ w_iw.T)
+        assert np.all(err <= epsw), f"w: max err {err.max()} against bound {epsw[err > epsw][:4]}"
+    return frac
+
+
+def check_q_absorb(q_gpu, w_uk, qa_gpu):
+    """q_abs on the GPU's own q (the absorption alone); w_uk [64, 192, 512]."""
+    qa_o = ref.q_absorb(q_gpu, w_uk)
+    n = q_gpu.shape[0]
+    exact = np.einsum("nhd,hdc->nhc", q_gpu[:, :, :192], w_uk)
+    eps = np.stack([ref.projection_error_bound(q_gpu[:, h, :192], w_uk[h].T) for h in range(64)], axis=1)
+    frac = _check_bf16_part("q_abs", qa_gpu[:, :, :512], exact, eps, None, 512, None, qa_o[:, :, :512])
+    assert np.array_equal(qa_gpu[:, :, 512:], q_gpu[:, :, 192:]), "q_abs rope part is not q's rope part"
+    return frac
