@@ -44,6 +44,10 @@ under ``tests/`` marked ``not gpu``):
                      the relative-position property of the turned query
                      against keys turned by the cache write, the indexer
                      query's unturned first half.
+  e4m3_value,        the format's published values (0x7E = 448, 0x08 = 2^-6,
+  e4m3_encode,       0x01 = 2^-9, 0x38 = 1), 127 finite magnitudes in order,
+  quantize_rows_fp8  round trips, midpoints to the even code, saturation, the
+                     row maximum at +-448, the per-element error bound.
   share_selection,   hand example, dense additive-mask attention over the
   layer_stack_mtp    shared selection cut at each token's position, and the
                      take-all case (sharing changes nothing when every causal
@@ -603,3 +607,72 @@ def projection_error_bound(a, b):
     u = 2.0 ** -24
     g = (K + 1) * u / (1 - (K + 1) * u)
     return g * (np.abs(_f64(a)) @ np.abs(_f64(b)).T)
+
+
+# --------------------------------------------------------------------------
+# FP8 caches.
+#
+# [GLM-5.2 techniques map] "inference quantization": FP8 inference;
+# [GLM-5.2 llm-atlas] "Faits clés": precision fp8.  The pages name FP8 only.
+# Readings taken (each stated again in the design notes):
+#   * The format is OCP 8-bit E4M3 ("fn"): 1 sign bit, 4 exponent bits (bias
+#     7), 3 mantissa bits; exponent field 0 holds the subnormals m * 2^-9; the
+#     largest finite magnitude is 448 (code 0x7E); 0x7F and 0xFF are NaN and
+#     never produced.
+#   * Each cache row (a 576-wide latent + rope row, or a 128-wide indexer key)
+#     is stored as codes with one fp32 scale: scale = amax / 448 computed in
+#     fp32 (1 for an all-zero row); code_i = the E4M3 value nearest to
+#     x_i / scale (the division in fp32), ties to the even code, magnitudes
+#     above 448 saturating to 448.  The stored row means scale * value(code).
+#   * What gets quantized is the bf16 row the cache write produces.
+#   * The queries stay bf16; the path computes on the exactly dequantized rows,
+#     so the indexer, top-k and attention oracles above apply unchanged to
+#     dequantize_rows_fp8's output.
+
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code):
+    """The value of an E4M3 code (0..255), from the format's definition."""
+    code = int(code)
+    sign = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * m * 2.0 ** -9
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)])
+
+
+def e4m3_encode(y):
+    """Nearest E4M3 code of each value (float64 array), ties to the even code,
+    saturating at +-448.  Brute force over the 127 finite magnitudes."""
+    y = np.asarray(y, dtype=np.float64)
+    mags = E4M3_TABLE[:127]                       # codes 0x00..0x7E, increasing
+    a = np.minimum(np.abs(y), E4M3_MAX)
+    d = np.abs(a[..., None] - mags)               # distance to every magnitude
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best                              # one or two nearest codes
+    codes = np.arange(127)
+    even = cand & (codes % 2 == 0)
+    pick = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(cand, axis=-1))
+    neg = np.signbit(y) & (pick > 0)              # -0 encodes as 0x00
+    return (pick | (neg.astype(np.int64) << 7)).astype(np.uint8)
+
+
+def quantize_rows_fp8(x):
+    """Codes (uint8 [n, d]) and scales (float32-valued [n]) of rows x [n, d]
+    (bf16 values)."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    amax = np.max(np.abs(x32), axis=1)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    y = (x32 / scale[:, None]).astype(np.float32)
+    return e4m3_encode(y.astype(np.float64)), scale.astype(np.float64)
+
+
+def dequantize_rows_fp8(codes, scales):
+    """The rows the path computes on: scale * value(code), exact in float64."""
+    return np.asarray(scales, dtype=np.float64)[:, None] * E4M3_TABLE[np.asarray(codes, dtype=np.int64)]

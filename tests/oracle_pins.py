@@ -772,4 +772,68 @@ def check_projection_error_bound_covers_fp32(ref):
     assert err > 2000 * 2.0 ** -24 and err <= ref.projection_error_bound(a1, a1)[0, 0]
 
 
+# ------------------------------------------------------------------ FP8 caches
+# [GLM-5.2 techniques map] "inference quantization" (FP8 inference); the
+# format facts below are the OCP 8-bit floating point specification's E4M3.
+
+def check_e4m3_published_values(ref):
+    v = ref.e4m3_value
+    assert v(0x7E) == 448.0 and v(0xFE) == -448.0          # largest finite magnitude
+    assert v(0x08) == 2.0 ** -6 and v(0x07) == 7 * 2.0 ** -9 and v(0x01) == 2.0 ** -9   # smallest normal, subnormals
+    assert v(0x38) == 1.0 and v(0x3F) == 1.875 and v(0x40) == 2.0
+    assert v(0x00) == 0.0 and np.isnan(v(0x7F)) and np.isnan(v(0xFF))
+    mags = np.array([v(c) for c in range(127)])
+    assert np.all(np.diff(mags) > 0)                       # 127 finite magnitudes, increasing
+
+
+def check_e4m3_encode_rounding(ref):
+    enc = ref.e4m3_encode
+    codes = np.arange(127)
+    vals = np.array([ref.e4m3_value(c) for c in codes])
+    assert np.array_equal(enc(vals), codes) and np.array_equal(enc(-vals[1:]), codes[1:] | 0x80)
+    # midpoints between neighbours go to the even code
+    mid = (vals[:-1] + vals[1:]) / 2
+    got = enc(mid).astype(np.int64)
+    assert np.all(got % 2 == 0) and np.all((got == codes[:-1]) | (got == codes[1:]))
+    # just above / below a midpoint go to the nearer code
+    assert np.array_equal(enc(mid * (1 + 1e-9)), codes[1:]) and np.array_equal(enc(mid * (1 - 1e-9)), codes[:-1])
+    assert enc(np.array([1e6]))[0] == 0x7E and enc(np.array([-500.0]))[0] == 0xFE and enc(np.array([449.0]))[0] == 0x7E
+    assert enc(np.array([2.0 ** -11]))[0] == 0 and enc(np.array([3 * 2.0 ** -11]))[0] == 1   # 2^-10 ties to 0; 1.5 * 2^-10 up
+
+
+def check_quantize_rows_fp8(ref):
+    rng = _rng(91)
+    x = _bf16_grid(rng.standard_normal((6, 576)) * np.array([[1e-3], [1], [30], [1], [1], [0]]))
+    x[3, 7] = 100.0                                        # a spike sets the scale
+    x[4] = -x[4]
+    codes, scales = ref.quantize_rows_fp8(x)
+    deq = ref.dequantize_rows_fp8(codes, scales)
+    for r in range(5):
+        am = np.max(np.abs(x[r]))
+        assert np.float32(scales[r]) == np.float32(np.float32(am) / np.float32(448))
+        i = np.argmax(np.abs(x[r]))
+        assert codes[r, i] & 0x7F == 0x7E                  # the row maximum lands on +-448
+        # per element: at most half a step of the format at the element's size
+        # (relative 2^-4 for normal codes, 2^-10 scale for subnormals), plus the
+        # fp32 division's rounding
+        err = np.abs(deq[r] - x[r])
+        assert np.all(err <= 2.0 ** -4 * np.abs(x[r]) + 2.0 ** -10 * scales[r] + 1e-6 * np.abs(x[r]))
+    assert np.all(codes[5] == 0) and scales[5] == 1.0 and np.all(deq[5] == 0)
+    assert np.array_equal(ref.quantize_rows_fp8(deq[:5])[0], codes[:5])   # quantizing the decoded rows is stable
+
+
+def check_fp8_indexer_scores_scale_out(ref):
+    """ReLU commutes with a positive scale: the score of a key stored as
+    (codes, scale) is scale times the score of the decoded codes alone."""
+    rng = _rng(93)
+    T = 50
+    k = _bf16_grid(rng.standard_normal((T, 128)))
+    codes, scales = ref.quantize_rows_fp8(k)
+    q = _bf16_grid(rng.standard_normal((2, 32, 128)) / 11)
+    w = rng.standard_normal((2, 32))
+    full = ref.indexer_scores(q, w, ref.dequantize_rows_fp8(codes, scales), [0], [0, 0], [49, 30])
+    unit = ref.indexer_scores(q, w, ref.E4M3_TABLE[codes.astype(np.int64)], [0], [0, 0], [49, 30])
+    np.testing.assert_allclose(full[:, :31], unit[:, :31] * scales[None, :31], rtol=1e-12, atol=1e-300)
+
+
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

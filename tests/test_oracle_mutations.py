@@ -71,6 +71,14 @@ MUTATIONS = [
     ("head_weights_wrong_matrix", "w = (c_q @ _f64(w_iw).T).astype(np.float32).astype(np.float64)",
      "w = (c_q @ _f64(w_iw).T)[:, ::-1].astype(np.float32).astype(np.float64)"),
     ("projection_bound_too_small", "g = (K + 1) * u / (1 - (K + 1) * u)", "g = 8 * u"),
+    ("e4m3_wrong_bias", "return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)", "return sign * (1.0 + m / 8.0) * 2.0 ** (e - 8)"),
+    ("e4m3_subnormal_scale", "return sign * m * 2.0 ** -9", "return sign * m * 2.0 ** -10"),
+    ("e4m3_ties_to_lower", "pick = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(cand, axis=-1))",
+     "pick = np.argmax(cand, axis=-1)"),
+    ("e4m3_drops_sign", "return (pick | (neg.astype(np.int64) << 7)).astype(np.uint8)", "return pick.astype(np.uint8)"),
+    ("fp8_scale_over_max_code", "amax / np.float32(E4M3_MAX)", "amax / np.float32(240.0)"),
+    ("fp8_scale_not_applied", "return np.asarray(scales, dtype=np.float64)[:, None] * E4M3_TABLE",
+     "return 1.0 * E4M3_TABLE"),
     ("cache_row_latent_not_normalised", "lat = rms_norm(kv_a[:, :KV_LORA_RANK], gamma)", "lat = kv_a[:, :KV_LORA_RANK] * _f64(gamma)"),
 ]
 
