@@ -42,6 +42,7 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill indexer and cache-write measurements")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-query", action="store_true", help="skip the query-side (projection and absorption) legs")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-cache leg of the decode step")
     ap.add_argument("--cpu-sample", type=int, default=16, help="queries in the CPU oracle sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="repeat the CPU sample for at least this long")
     ap.add_argument("--copies", type=int, default=2,
@@ -291,6 +292,61 @@ def query_side_leg(seed, n, reps=15, warmup=10):
     return out
 
 
+def step_bytes_fp8(wl, k=2048):
+    """step_bytes for FP8 caches: 128 code bytes + a 4-byte scale per indexer
+    key, 576 + 4 per gathered row; queries, W_UV and outputs unchanged."""
+    n_q = wl.n_q
+    keys = sum(p + 1 for p in wl.q_pos)
+    idx_bytes = keys * 132 + n_q * (32 * 128 * 2 + 32 * 4)
+    k_eff = sum(min(k, p + 1) for p in wl.q_pos)
+    per_layer = k_eff * 580 + n_q * 64 * 576 * 2 + 64 * 256 * 512 * 2 + n_q * 64 * 256 * 2
+    n_full = sum(wl.full)
+    return idx_bytes * n_full + per_layer * wl.n_layers + n_full * n_q * k * 4
+
+
+def fp8_leg(batches, wl, steps, warmup):
+    """The same step with both caches stored as FP8 (quantized on the GPU from
+    the bf16 inputs), HIP-graph replays rotating through the input sets."""
+    import torch
+    from sparse_attention_relu_amd import api, synth
+    stacks = []
+    for b in batches:
+        layers = []
+        for L in b.layers:
+            kv8, kvs = api.quantize_rows_fp8(L.kv)
+            L8 = synth.LayerInputs(q_abs=L.q_abs, kv=kv8, w_uv=L.w_uv, q_idx=L.q_idx, w=L.w, kv_scale=kvs)
+            if L.k_idx is not None:
+                L8.k_idx, L8.k_scale = api.quantize_rows_fp8(L.k_idx)
+            layers.append(L8)
+        stacks.append(api.LayerStack(layers, b.seq_start, b.seq_len, b.q_seq, b.q_pos, wl.ld, full=wl.full))
+        stacks[-1]()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    for st_ in stacks:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                st_()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    nb = step_bytes_fp8(wl)
+    gbs = nb / (ms * 1e-3) / 1e9
+    return {"workload": wl.name + "_fp8_caches", "ms_per_step": round(ms, 5),
+            "value": round(wl.n_q / (ms * 1e-3), 1), "unit": "queries/s", "step_bytes": nb,
+            "hbm_gbs_step": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "timing": "%d graph replays after %d warm-up" % (steps, warmup)}
+
+
 class HipEvents:
     """Raw hipEvents (the library records them on its stream)."""
 
@@ -437,6 +493,9 @@ def main():
         out["prefill_indexer"] = prefill_indexer(args.seed)
         print("[bench] cache write", file=sys.stderr, flush=True)
         out["cache_write"] = cache_write_leg(args.seed)
+    if not args.no_fp8 and not prefill:
+        print("[bench] fp8 caches", file=sys.stderr, flush=True)
+        out["decode_fp8"] = fp8_leg(batches, wl, args.steps, args.warmup)
     if not args.no_query:
         print("[bench] query side", file=sys.stderr, flush=True)
         out["query_side"] = {"decode_16_tokens": query_side_leg(args.seed, 16),

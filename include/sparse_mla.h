@@ -201,6 +201,8 @@ int32_t sa_mla_sparse_attn(const void* q_abs, const void* kv, const int64_t* seq
  *                     idx int32 [n_q, k] (output: this layer's selection)
  *   every layer:      q_abs bf16 [n_q,64,576], kv bf16 [rows,576], w_uv bf16 [64,256,512],
  *                     out bf16 [n_q,64,256] (output)
+ *   FP8 caches:       k_scale / kv_scale non-NULL: k_idx / kv hold E4M3 codes (see the
+ *                     FP8 calls below) and these are their per-row scales; NULL: bf16.
  * sa_batch_desc: seq_start int64 [n_seq], seq_len int32 [n_seq], q_seq int32 [n_q],
  * q_pos int32 [n_q], the counts, and ld (score row length, > max q_pos; at most
  * SA_MAX_SEQ_LEN, so every selected position is one the gather can address).
@@ -232,6 +234,8 @@ typedef struct sa_layer_desc {
   const void* kv;
   const void* w_uv;
   void* out;
+  const float* k_scale;     /* non-NULL: k_idx holds FP8 codes [rows, 128] with these scales [rows] */
+  const float* kv_scale;    /* non-NULL: kv holds FP8 codes [rows, 576] with these scales [rows] */
 } sa_layer_desc;
 
 typedef struct sa_batch_desc {
@@ -353,6 +357,57 @@ int32_t sa_q_project(const void* c_q, const void* w_qb, const void* w_iq, const 
  *   q_abs   bf16 [n, 64, 576]   output (sa_mla_sparse_attn's q_abs)
  */
 int32_t sa_q_absorb(const void* q, const void* w_uk_t, int32_t n, void* q_abs, sa_stream_t stream);
+
+/*
+ * FP8 caches (models.inteligile.com techniques map, "inference quantization":
+ * FP8 inference; llm-atlas "GLM-5.2", "Faits clés": precision fp8).  The pages
+ * give no format or scaling; the reading taken: OCP E4M3 codes (1 sign, 4
+ * exponent bits with bias 7, 3 mantissa bits, subnormals m * 2^-9, largest
+ * finite magnitude 448 = code 0x7E) with one fp32 scale per cache row (per
+ * 576-wide latent row, per 128-wide indexer key).  A stored row means
+ * scale * value(code); it halves the bytes the decode path streams.
+ *
+ * sa_quantize_rows_fp8 -- rows of bf16 values to codes and scales:
+ *     scale = max_i |x_i| / 448 (fp32, correctly rounded; 1 for an all-zero row)
+ *     code_i = E4M3 nearest to x_i / scale (fp32 quotient, ties to the even
+ *              code, magnitudes above 448 saturating to 448; zero is 0x00)
+ *   src       bf16 [n_rows, d], d = 576 (cache rows) or 128 (indexer keys)
+ *   dst_rows  int64 [n_rows] or NULL: row i goes to row dst_rows[i] of codes/scales
+ *   codes     uint8 [*, d], scales fp32 [*]
+ * Bit-exact integer decisions (the same fp32 quotient on any conforming
+ * implementation).
+ *
+ * sa_fp8_decode -- n codes (n a multiple of 16) to their bf16 values (exact,
+ * unscaled): the decoder the FP8 kernels use.
+ *
+ * sa_indexer_score_fp8 / sa_indexer_score_fp8_algo -- sa_indexer_score (and its
+ * algo variant) over keys stored as codes k_codes uint8 [rows, 128] with
+ * k_scale fp32 [rows]: the key of row r is k_scale[r] * value(k_codes[r]).
+ * Computed as k_scale[r] times the score of the decoded codes (ReLU commutes
+ * with a positive scale), the codes exact in bf16.
+ *
+ * sa_mla_sparse_attn_fp8 -- sa_mla_sparse_attn over cache rows stored as codes
+ * kv_codes uint8 [rows, 576] with kv_scale fp32 [rows]: row r is
+ * kv_scale[r] * value(kv_codes[r]).  Each logit is the decoded row's logit
+ * times the row's scale, and the softmax weight enters the value product
+ * multiplied by the scale (bf16), the normaliser summing the weights alone.
+ * Same workspace as sa_mla_sparse_attn.
+ */
+int32_t sa_quantize_rows_fp8(const void* src, int64_t n_rows, int32_t d, const int64_t* dst_rows,
+                             void* codes, float* scales, sa_stream_t stream);
+int32_t sa_fp8_decode(const void* codes, int64_t n, void* out, sa_stream_t stream);
+int32_t sa_indexer_score_fp8(const void* q_idx, const float* w, const void* k_codes, const float* k_scale,
+                             const int64_t* seq_start, const int32_t* seq_len, const int32_t* q_seq,
+                             const int32_t* q_pos, int32_t n_q, int32_t n_seq, float* scores, int64_t ld,
+                             sa_stream_t stream);
+int32_t sa_indexer_score_fp8_algo(const void* q_idx, const float* w, const void* k_codes, const float* k_scale,
+                                  const int64_t* seq_start, const int32_t* seq_len, const int32_t* q_seq,
+                                  const int32_t* q_pos, int32_t n_q, int32_t n_seq, float* scores, int64_t ld,
+                                  int32_t algo, sa_stream_t stream);
+int32_t sa_mla_sparse_attn_fp8(const void* q_abs, const void* kv_codes, const float* kv_scale,
+                               const int64_t* seq_start, const int32_t* q_seq, const int32_t* idx, int32_t n_q,
+                               int32_t k, const void* w_uv, float scale, void* out, float* lse, void* ws,
+                               size_t ws_bytes, sa_stream_t stream);
 
 /* IndexShare pattern of the 78-layer model: 1 if layer runs its own indexer
  * (layers 0-2, then every layer l with l mod 4 == 2), else 0; -1 if layer < 0. */

@@ -16,7 +16,7 @@ c_i32, c_i64, c_f32, c_sz, c_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
 
 class LayerDesc(ctypes.Structure):
     _fields_ = [("is_full", c_i32), ("q_idx", c_p), ("w", c_p), ("k_idx", c_p), ("idx", c_p),
-                ("q_abs", c_p), ("kv", c_p), ("w_uv", c_p), ("out", c_p)]
+                ("q_abs", c_p), ("kv", c_p), ("w_uv", c_p), ("out", c_p), ("k_scale", c_p), ("kv_scale", c_p)]
 
 
 class BatchDesc(ctypes.Structure):
@@ -48,6 +48,13 @@ SIGNATURES = {
     "sa_share_selection": (c_i32, [c_p, c_i32, c_i32, c_p, c_p, c_i32, c_p, c_p]),
     "sa_q_project": (c_i32, [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_p, c_p, c_p]),
     "sa_q_absorb": (c_i32, [c_p, c_p, c_i32, c_p, c_p]),
+    "sa_quantize_rows_fp8": (c_i32, [c_p, c_i64, c_i32, c_p, c_p, c_p, c_p]),
+    "sa_fp8_decode": (c_i32, [c_p, c_i64, c_p, c_p]),
+    "sa_indexer_score_fp8": (c_i32, [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_i32, c_i32, c_p, c_i64, c_p]),
+    "sa_indexer_score_fp8_algo": (c_i32, [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_i32, c_i32, c_p, c_i64, c_i32,
+                                          c_p]),
+    "sa_mla_sparse_attn_fp8": (c_i32, [c_p, c_p, c_p, c_p, c_p, c_p, c_i32, c_i32, c_p, c_f32, c_p, c_p, c_p, c_sz,
+                                       c_p]),
     "sa_layer_stack_noalloc_max_bytes": (c_sz, []),
     "sa_layer_stack_noalloc": (c_i32, [ctypes.POINTER(LayerDesc), c_i32, ctypes.POINTER(BatchDesc), c_i32, c_f32,
                                        ctypes.POINTER(StageEvents), c_p]),

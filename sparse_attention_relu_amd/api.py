@@ -128,6 +128,86 @@ def share_selection(sel_idx, sel_of, q_pos, idx=None, stream=None):
     return idx
 
 
+def quantize_rows_fp8(src, codes=None, scales=None, dst_rows=None, stream=None):
+    """sa_quantize_rows_fp8: bf16 rows [n, d] (d = 576 or 128) to E4M3 codes
+    (uint8 [*, d]) and one fp32 scale per row."""
+    n, d = src.shape
+    _need(src, "src", torch.bfloat16, (n, d))
+    dev = src.device
+    if codes is None:
+        codes = torch.empty((n, d), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((codes.shape[0],), dtype=torch.float32, device=dev)
+    _need(codes, "codes", torch.uint8, (None, d))
+    _need(scales, "scales", torch.float32, (codes.shape[0],))
+    if dst_rows is not None:
+        _need(dst_rows, "dst_rows", torch.int64, (n,))
+    elif codes.shape[0] != n:
+        raise ValueError("codes must have one row per source row when dst_rows is not given")
+    L = _lib.lib()
+    st = L.sa_quantize_rows_fp8(_ptr(src), n, d, _ptr(dst_rows), _ptr(codes), _ptr(scales), _stream(stream))
+    _lib.check("sa_quantize_rows_fp8", st)
+    return codes, scales
+
+
+def fp8_decode(codes, out=None, stream=None):
+    """sa_fp8_decode: E4M3 codes (uint8, a multiple of 16) to bf16 values."""
+    _need(codes, "codes", torch.uint8)
+    if out is None:
+        out = torch.empty(codes.shape, dtype=torch.bfloat16, device=codes.device)
+    _need(out, "out", torch.bfloat16, tuple(codes.shape))
+    L = _lib.lib()
+    _lib.check("sa_fp8_decode", L.sa_fp8_decode(_ptr(codes), codes.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
+def indexer_score_fp8(q_idx, w, k_codes, k_scale, seq_start, seq_len, q_seq, q_pos, ld: int, scores=None,
+                      algo: int = 0, stream=None):
+    n_q = q_idx.shape[0]
+    _need(q_idx, "q_idx", torch.bfloat16, (n_q, IDX_HEADS, IDX_DIM))
+    _need(w, "w", torch.float32, (n_q, IDX_HEADS))
+    _need(k_codes, "k_codes", torch.uint8, (None, IDX_DIM))
+    _need(k_scale, "k_scale", torch.float32, (k_codes.shape[0],))
+    _need(seq_start, "seq_start", torch.int64, (None,))
+    _need(seq_len, "seq_len", torch.int32, (seq_start.shape[0],))
+    _need(q_seq, "q_seq", torch.int32, (n_q,))
+    _need(q_pos, "q_pos", torch.int32, (n_q,))
+    if scores is None:
+        scores = torch.empty((n_q, ld), dtype=torch.float32, device=q_idx.device)
+    _need(scores, "scores", torch.float32, (n_q, ld))
+    L = _lib.lib()
+    st = L.sa_indexer_score_fp8_algo(_ptr(q_idx), _ptr(w), _ptr(k_codes), _ptr(k_scale), _ptr(seq_start),
+                                     _ptr(seq_len), _ptr(q_seq), _ptr(q_pos), n_q, seq_start.shape[0], _ptr(scores),
+                                     ld, algo, _stream(stream))
+    _lib.check("sa_indexer_score_fp8", st)
+    return scores
+
+
+def mla_sparse_attn_fp8(q_abs, kv_codes, kv_scale, seq_start, q_seq, idx, w_uv, scale: float = 1.0 / 16, out=None,
+                        lse=None, ws=None, stream=None):
+    n_q, k = idx.shape
+    _need(q_abs, "q_abs", torch.bfloat16, (n_q, HEADS, ROW))
+    _need(kv_codes, "kv_codes", torch.uint8, (None, ROW))
+    _need(kv_scale, "kv_scale", torch.float32, (kv_codes.shape[0],))
+    _need(seq_start, "seq_start", torch.int64, (None,))
+    _need(q_seq, "q_seq", torch.int32, (n_q,))
+    _need(idx, "idx", torch.int32, (n_q, k))
+    _need(w_uv, "w_uv", torch.bfloat16, (HEADS, VDIM, LATENT))
+    if out is None:
+        out = torch.empty((n_q, HEADS, VDIM), dtype=torch.bfloat16, device=q_abs.device)
+    _need(out, "out", torch.bfloat16, (n_q, HEADS, VDIM))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (n_q, HEADS))
+    L = _lib.lib()
+    if ws is None:
+        ws = workspace(L.sa_mla_workspace_size(n_q, k), q_abs.device)
+    st = L.sa_mla_sparse_attn_fp8(_ptr(q_abs), _ptr(kv_codes), _ptr(kv_scale), _ptr(seq_start), _ptr(q_seq),
+                                  _ptr(idx), n_q, k, _ptr(w_uv), float(scale), _ptr(out), _ptr(lse), _ptr(ws),
+                                  ws.numel(), _stream(stream))
+    _lib.check("sa_mla_sparse_attn_fp8", st)
+    return out
+
+
 QLORA = 2048
 
 
@@ -227,13 +307,25 @@ class LayerStack:
         for l, (L, f) in enumerate(zip(layers, full)):
             d = descs[l]
             d.is_full = 1 if f else 0
+            k_scale = getattr(L, "k_scale", None)
+            kv_scale = getattr(L, "kv_scale", None)
             if f:
                 _need(L.q_idx, "q_idx", torch.bfloat16, (n_rows, IDX_HEADS, IDX_DIM))
                 _need(L.w, "w", torch.float32, (n_rows, IDX_HEADS))
-                _need(L.k_idx, "k_idx", torch.bfloat16, (None, IDX_DIM))
+                if k_scale is not None:           # FP8 indexer keys: codes + one scale per key
+                    _need(L.k_idx, "k_idx", torch.uint8, (None, IDX_DIM))
+                    _need(k_scale, "k_scale", torch.float32, (L.k_idx.shape[0],))
+                    d.k_scale = _ptr(k_scale)
+                else:
+                    _need(L.k_idx, "k_idx", torch.bfloat16, (None, IDX_DIM))
                 d.q_idx, d.w, d.k_idx, d.idx = _ptr(L.q_idx), _ptr(L.w), _ptr(L.k_idx), _ptr(self.idxs[l])
             _need(L.q_abs, "q_abs", torch.bfloat16, (n_q, HEADS, ROW))
-            _need(L.kv, "kv", torch.bfloat16, (None, ROW))
+            if kv_scale is not None:              # FP8 cache rows: codes + one scale per row
+                _need(L.kv, "kv", torch.uint8, (None, ROW))
+                _need(kv_scale, "kv_scale", torch.float32, (L.kv.shape[0],))
+                d.kv_scale = _ptr(kv_scale)
+            else:
+                _need(L.kv, "kv", torch.bfloat16, (None, ROW))
             _need(L.w_uv, "w_uv", torch.bfloat16, (HEADS, VDIM, LATENT))
             d.q_abs, d.kv, d.w_uv, d.out = _ptr(L.q_abs), _ptr(L.kv), _ptr(L.w_uv), _ptr(self.outs[l])
         self._descs = descs

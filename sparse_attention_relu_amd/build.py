@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsparse_mla.so")
 DEBUG_LIB = os.path.join(HERE, "libsparse_mla_debug.so")
-SOURCES = ["abi.hip", "indexer.hip", "topk.hip", "mla.hip", "cache.hip", "share.hip", "qproj.hip", "debug.hip"]
+SOURCES = ["abi.hip", "indexer.hip", "topk.hip", "mla.hip", "cache.hip", "share.hip", "qproj.hip", "quant.hip", "debug.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -37,18 +37,22 @@ int32_t check_launch(const char* what) {
 }
 
 int indexer_algo(int32_t n_q, int32_t n_seq, int algo);
-int32_t launch_indexer(const void* q_idx, const float* w, const void* k_idx, const int64_t* seq_start,
-                       const int32_t* seq_len, const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, int32_t n_seq,
-                       float* scores, int64_t ld, int algo, hipStream_t stream, uint32_t* clear, int64_t n_clear);
+int32_t launch_indexer(const void* q_idx, const float* w, const void* k_idx, const float* k_scale,
+                       const int64_t* seq_start, const int32_t* seq_len, const int32_t* q_seq, const int32_t* q_pos,
+                       int32_t n_q, int32_t n_seq, float* scores, int64_t ld, int algo, hipStream_t stream,
+                       uint32_t* clear, int64_t n_clear);
 void topk_clear_range(void* ws, int32_t n_q, int64_t ld, uint32_t** p, int64_t* n);
 
 size_t topk_workspace_size(int32_t n_q, int64_t ld, int32_t k);
 int32_t launch_topk(const float* scores, int64_t ld, const int32_t* q_pos, int32_t n_q, int32_t k, int32_t* idx,
                     void* ws, int algo, hipStream_t stream, bool cleared);
 size_t mla_workspace_size(int32_t n_q, int32_t k);
-int32_t launch_mla(const void* q_abs, const void* kv, const int64_t* seq_start, const int32_t* q_seq,
-                   const int32_t* idx, int32_t n_q, int32_t k, const void* w_uv, float scale, void* out, float* lse,
-                   void* ws, hipStream_t stream);
+int32_t launch_mla(const void* q_abs, const void* kv, const float* kv_scale, const int64_t* seq_start,
+                   const int32_t* q_seq, const int32_t* idx, int32_t n_q, int32_t k, const void* w_uv, float scale,
+                   void* out, float* lse, void* ws, hipStream_t stream);
+int32_t launch_quantize(const void* src, int64_t n_rows, int32_t d, const int64_t* dst_rows, void* codes, float* scales,
+                        hipStream_t stream);
+int32_t launch_fp8_decode(const void* codes, int64_t n, void* out, hipStream_t stream);
 
 int32_t launch_cache_write(const void* kv_a, const void* gamma, const void* k_raw, const void* ln_w, const void* ln_b,
                            const int32_t* pos, const int64_t* dst, int32_t n, void* kv_cache, void* k_cache,
@@ -159,7 +163,7 @@ int32_t sa_indexer_score_algo(const void* q_idx, const float* w, const void* k_i
   SA_REQUIRE(algo >= 0 && algo <= 2, SA_ERR_INVALID_ARG, "indexer: unknown algo %d", algo);
   if (n_q == 0) return SA_OK;
   if ((rc = debug_batch(seq_start, seq_len, q_seq, q_pos, n_q, n_seq, ld, (hipStream_t)stream))) return rc;
-  return launch_indexer(q_idx, w, k_idx, seq_start, seq_len, q_seq, q_pos, n_q, n_seq, scores, ld, algo,
+  return launch_indexer(q_idx, w, k_idx, nullptr, seq_start, seq_len, q_seq, q_pos, n_q, n_seq, scores, ld, algo,
                         (hipStream_t)stream, nullptr, 0);
 }
 
@@ -167,6 +171,47 @@ int32_t sa_indexer_score(const void* q_idx, const float* w, const void* k_idx, c
                          const int32_t* seq_len, const int32_t* q_seq, const int32_t* q_pos, int32_t n_q,
                          int32_t n_seq, float* scores, int64_t ld, sa_stream_t stream) {
   return sa_indexer_score_algo(q_idx, w, k_idx, seq_start, seq_len, q_seq, q_pos, n_q, n_seq, scores, ld, 0, stream);
+}
+
+int32_t sa_indexer_score_fp8_algo(const void* q_idx, const float* w, const void* k_codes, const float* k_scale,
+                                  const int64_t* seq_start, const int32_t* seq_len, const int32_t* q_seq,
+                                  const int32_t* q_pos, int32_t n_q, int32_t n_seq, float* scores, int64_t ld,
+                                  int32_t algo, sa_stream_t stream) {
+  int32_t rc = check_indexer_args(q_idx, w, k_codes, seq_start, seq_len, q_seq, q_pos, n_q, n_seq, scores, ld);
+  if (rc) return rc;
+  SA_REQUIRE(algo >= 0 && algo <= 2, SA_ERR_INVALID_ARG, "indexer: unknown algo %d", algo);
+  if (n_q == 0) return SA_OK;
+  SA_REQUIRE(k_scale, SA_ERR_INVALID_ARG, "indexer: FP8 keys without k_scale");
+  if ((rc = debug_batch(seq_start, seq_len, q_seq, q_pos, n_q, n_seq, ld, (hipStream_t)stream))) return rc;
+  return launch_indexer(q_idx, w, k_codes, k_scale, seq_start, seq_len, q_seq, q_pos, n_q, n_seq, scores, ld, algo,
+                        (hipStream_t)stream, nullptr, 0);
+}
+
+int32_t sa_indexer_score_fp8(const void* q_idx, const float* w, const void* k_codes, const float* k_scale,
+                             const int64_t* seq_start, const int32_t* seq_len, const int32_t* q_seq,
+                             const int32_t* q_pos, int32_t n_q, int32_t n_seq, float* scores, int64_t ld,
+                             sa_stream_t stream) {
+  return sa_indexer_score_fp8_algo(q_idx, w, k_codes, k_scale, seq_start, seq_len, q_seq, q_pos, n_q, n_seq, scores,
+                                   ld, 0, stream);
+}
+
+int32_t sa_quantize_rows_fp8(const void* src, int64_t n_rows, int32_t d, const int64_t* dst_rows, void* codes,
+                             float* scales, sa_stream_t stream) {
+  SA_REQUIRE(n_rows >= 0, SA_ERR_INVALID_ARG, "quantize: negative n_rows");
+  SA_REQUIRE(d == SA_ROW || d == SA_INDEX_DIM, SA_ERR_UNSUPPORTED, "quantize: d=%d is neither %d nor %d", d, SA_ROW,
+             SA_INDEX_DIM);
+  if (n_rows == 0) return SA_OK;
+  SA_REQUIRE(src && codes && scales, SA_ERR_INVALID_ARG, "quantize: null pointer argument");
+  SA_REQUIRE(aligned16(src) && aligned16(codes), SA_ERR_INVALID_ARG, "quantize: src/codes not 16-byte aligned");
+  return launch_quantize(src, n_rows, d, dst_rows, codes, scales, (hipStream_t)stream);
+}
+
+int32_t sa_fp8_decode(const void* codes, int64_t n, void* out, sa_stream_t stream) {
+  SA_REQUIRE(n >= 0 && n % 16 == 0, SA_ERR_INVALID_ARG, "fp8_decode: n=%lld is not a multiple of 16", (long long)n);
+  if (n == 0) return SA_OK;
+  SA_REQUIRE(codes && out, SA_ERR_INVALID_ARG, "fp8_decode: null pointer argument");
+  SA_REQUIRE(aligned16(codes) && aligned16(out), SA_ERR_INVALID_ARG, "fp8_decode: pointers not 16-byte aligned");
+  return launch_fp8_decode(codes, n, out, (hipStream_t)stream);
 }
 
 size_t sa_topk_workspace_size(int32_t n_q, int64_t ld, int32_t k) {
@@ -207,7 +252,23 @@ int32_t sa_mla_sparse_attn(const void* q_abs, const void* kv, const int64_t* seq
   SA_REQUIRE(ws && ws_bytes >= need, SA_ERR_WORKSPACE, "mla: workspace of %zu bytes, %zu needed", ws_bytes, need);
   SA_REQUIRE(((uintptr_t)ws & 255u) == 0, SA_ERR_INVALID_ARG, "mla: workspace not 256-byte aligned");
   if ((rc = debug_idx(idx, n_q, k, nullptr, q_seq, (hipStream_t)stream))) return rc;
-  return launch_mla(q_abs, kv, seq_start, q_seq, idx, n_q, k, w_uv, scale, out, lse, ws, (hipStream_t)stream);
+  return launch_mla(q_abs, kv, nullptr, seq_start, q_seq, idx, n_q, k, w_uv, scale, out, lse, ws,
+                    (hipStream_t)stream);
+}
+
+int32_t sa_mla_sparse_attn_fp8(const void* q_abs, const void* kv_codes, const float* kv_scale, const int64_t* seq_start,
+                               const int32_t* q_seq, const int32_t* idx, int32_t n_q, int32_t k, const void* w_uv,
+                               float scale, void* out, float* lse, void* ws, size_t ws_bytes, sa_stream_t stream) {
+  int32_t rc = check_mla_args(q_abs, kv_codes, seq_start, q_seq, idx, n_q, k, w_uv, scale, out);
+  if (rc) return rc;
+  if (n_q == 0) return SA_OK;
+  SA_REQUIRE(kv_scale, SA_ERR_INVALID_ARG, "mla: FP8 rows without kv_scale");
+  const size_t need = mla_workspace_size(n_q, k);
+  SA_REQUIRE(ws && ws_bytes >= need, SA_ERR_WORKSPACE, "mla: workspace of %zu bytes, %zu needed", ws_bytes, need);
+  SA_REQUIRE(((uintptr_t)ws & 255u) == 0, SA_ERR_INVALID_ARG, "mla: workspace not 256-byte aligned");
+  if ((rc = debug_idx(idx, n_q, k, nullptr, q_seq, (hipStream_t)stream))) return rc;
+  return launch_mla(q_abs, kv_codes, kv_scale, seq_start, q_seq, idx, n_q, k, w_uv, scale, out, lse, ws,
+                    (hipStream_t)stream);
 }
 
 // Layout: scores [n_q, ld] fp32, the top-k workspace, the attention
@@ -301,7 +362,7 @@ int32_t sa_layer_stack(const sa_layer_desc* layers, int32_t n_layers, const sa_b
     if (L.is_full) {
       const bool ev = events && !rec_idx && events->indexer_begin && events->indexer_end;
       if (ev && (rc = record(events->indexer_begin, st))) return rc;
-      rc = launch_indexer(L.q_idx, L.w, L.k_idx, batch->seq_start, batch->seq_len, r_seq, r_pos, n_rows,
+      rc = launch_indexer(L.q_idx, L.w, L.k_idx, L.k_scale, batch->seq_start, batch->seq_len, r_seq, r_pos, n_rows,
                           batch->n_seq, scores, ld, ialgo, st, clear, n_clear);
       if (rc) return rc;
       if (ev && (rc = record(events->indexer_end, st))) return rc;
@@ -319,8 +380,8 @@ int32_t sa_layer_stack(const sa_layer_desc* layers, int32_t n_layers, const sa_b
     }
     const bool eva = events && !rec_attn && events->attn_begin && events->attn_end;
     if (eva && (rc = record(events->attn_begin, st))) return rc;
-    rc = launch_mla(L.q_abs, L.kv, batch->seq_start, batch->q_seq, cur_idx, n_q, k, L.w_uv, scale, L.out, nullptr,
-                    mla_ws, st);
+    rc = launch_mla(L.q_abs, L.kv, L.kv_scale, batch->seq_start, batch->q_seq, cur_idx, n_q, k, L.w_uv, scale, L.out,
+                    nullptr, mla_ws, st);
     if (rc) return rc;
     if (eva && (rc = record(events->attn_end, st))) return rc;
     rec_attn |= eva;

@@ -20,6 +20,7 @@
 //                           sequence).  HBM-bound: 256 B of keys per 8 KFLOP.
 //   indexer_prefill_kernel  16 queries of one sequence share each key tile staged
 //                           in LDS: the dense contraction of chunked prefill.
+#include "fp8.h"
 #include "sa_common.h"
 
 namespace sa {
@@ -64,7 +65,8 @@ constexpr int kKeyPitch = 272;                            // LDS bytes per key r
 struct DecArgs {
   const uint16_t* q_idx;
   const float* w;
-  const uint16_t* k_idx;
+  const uint16_t* k_idx;    // bf16 keys [rows][128], or E4M3 codes [rows][128] (FP8)
+  const float* k_scale;     // FP8: one scale per key row
   const int64_t* seq_start;
   const int32_t* seq_len;
   const int32_t* q_seq;
@@ -85,7 +87,12 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// FP8: the keys are E4M3 codes with one fp32 scale per key; they are decoded
+// to bf16 (exact) on their way into the staging LDS, and each score is the
+// codes' score times the key's scale (ReLU commutes with a positive scale).
+template <bool FP8>
 __global__ __launch_bounds__(kDecThreads) void indexer_decode_kernel(DecArgs A) {
+  constexpr int kG = FP8 ? 4 : 8;          // 16-byte key pieces per lane per step
   // side job: clear the caller's words (a grid-stride loop over all workgroups)
   for (int64_t i = (int64_t)blockIdx.x * kDecThreads + threadIdx.x; i < A.n_clear; i += (int64_t)gridDim.x * kDecThreads)
     A.clear[i] = 0u;
@@ -111,7 +118,9 @@ __global__ __launch_bounds__(kDecThreads) void indexer_decode_kernel(DecArgs A) 
   // and score columns are handled relative to c0 in 32 bits
   const int wlast = (int)min(pos - c0, (int64_t)kDecChunk - 1);       // last valid key
   const int wend = (int)min(A.ld - c0, (int64_t)kDecChunk);          // columns of this chunk in the row
-  const uint16_t* kb = A.k_idx + (A.seq_start[seq] + c0) * kIdxDim;
+  const int64_t row0 = A.seq_start[seq] + c0;
+  const uint16_t* kb = A.k_idx + row0 * kIdxDim;
+  const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(A.k_idx) + row0 * kIdxDim;
   float* sc0 = srow + c0;
   const int n_it = kDecSteps;
   uint8_t* my = lds[wave];
@@ -120,11 +129,20 @@ __global__ __launch_bounds__(kDecThreads) void indexer_decode_kernel(DecArgs A) 
   // Loads past the causal bound re-read the last valid key (always in bounds);
   // their scores are replaced by -inf, so no load needs a branch.  Keys are
   // read once: streaming loads keep them from displacing cached data.
-  auto load = [&](u32x4 (&g)[8], int it) {
+  auto load = [&](u32x4 (&g)[kG], float& ks, int it) {
+    if (FP8) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int key = min(key_of(it) + 4 * j + (lane >> 4), wlast);
-      g[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + key * kIdxDim + (lane & 15) * 8));
+      for (int j = 0; j < kG; ++j) {       // 8 keys of 128 codes per piece index j
+        const int key = min(key_of(it) + 8 * j + (lane >> 3), wlast);
+        g[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb8 + key * kIdxDim + (lane & 7) * 16));
+      }
+      ks = A.k_scale[row0 + min(key_of(it) + (lane & 31), wlast)];
+    } else {
+#pragma unroll
+      for (int j = 0; j < kG; ++j) {
+        const int key = min(key_of(it) + 4 * j + (lane >> 4), wlast);
+        g[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + key * kIdxDim + (lane & 15) * 8));
+      }
     }
   };
 
@@ -145,9 +163,10 @@ __global__ __launch_bounds__(kDecThreads) void indexer_decode_kernel(DecArgs A) 
   const float wv = A.w[(int64_t)t * kIdxHeads + (threadIdx.x & (kIdxHeads - 1))];
   // Prefetches are unconditional (clamped to the last valid step) so the
   // loads stay in order and each step waits only for its own data.
-  u32x4 g0[8], g1[8];
-  load(g0, 0);
-  load(g1, 1);
+  u32x4 g0[kG], g1[kG];
+  float ks0 = 1.f, ks1 = 1.f;
+  load(g0, ks0, 0);
+  load(g1, ks1, 1);
 #pragma unroll
   for (int u = 0; u < kQPieces; ++u) {
     const int f = (int)threadIdx.x + kDecThreads * u;
@@ -166,10 +185,21 @@ __global__ __launch_bounds__(kDecThreads) void indexer_decode_kernel(DecArgs A) 
   // wave 0 stages keys in lds[0] from here on
   lds_barrier();
 
-  auto step = [&](const u32x4 (&g)[8], int it) {
+  auto step = [&](const u32x4 (&g)[kG], float ks, int it) {
+    if (FP8) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      *reinterpret_cast<u32x4*>(my + (4 * j + (lane >> 4)) * kKeyPitch + (lane & 15) * 16) = g[j];
+      for (int j = 0; j < kG; ++j) {       // codes 16c .. 16c + 15 -> bf16 chunks 2c, 2c + 1
+        u32x4 lo, hi;
+        e4m3x16_to_bf16x16(g[j], lo, hi);
+        uint8_t* dst = my + (8 * j + (lane >> 3)) * kKeyPitch + (lane & 7) * 32;
+        *reinterpret_cast<u32x4*>(dst) = lo;
+        *reinterpret_cast<u32x4*>(dst + 16) = hi;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kG; ++j)
+        *reinterpret_cast<u32x4*>(my + (4 * j + (lane >> 4)) * kKeyPitch + (lane & 15) * 16) = g[j];
+    }
     wave_lds_fence();
     f32x16 acc = {};
 #pragma unroll
@@ -178,7 +208,7 @@ __global__ __launch_bounds__(kDecThreads) void indexer_decode_kernel(DecArgs A) 
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], as_bf16x8(b), acc, 0, 0, 0);
     }
     wave_lds_fence();
-    const float sc = relu_weighted_sum(acc, wr);
+    const float sc = FP8 ? relu_weighted_sum(acc, wr) * ks : relu_weighted_sum(acc, wr);
     const int key = key_of(it) + (lane & 31);
     if (lane < 32 && key < wend) sc0[key] = key <= wlast ? sc : -INFINITY;
   };
@@ -186,10 +216,10 @@ __global__ __launch_bounds__(kDecThreads) void indexer_decode_kernel(DecArgs A) 
   static_assert(kDecSteps % 2 == 0, "steps alternate between two register sets");
 #pragma unroll
   for (int it = 0; it < n_it; it += 2) {
-    step(g0, it);
-    if (it + 2 < n_it) load(g0, it + 2);
-    step(g1, it + 1);
-    if (it + 3 < n_it) load(g1, it + 3);
+    step(g0, ks0, it);
+    if (it + 2 < n_it) load(g0, ks0, it + 2);
+    step(g1, ks1, it + 1);
+    if (it + 3 < n_it) load(g1, ks1, it + 3);
   }
 }
 
@@ -200,9 +230,13 @@ constexpr int kPfKT = 128;         // keys per tile
 constexpr int kKeyBytes = kIdxDim * 2;
 constexpr int kPfSplit = 16384;    // keys per workgroup
 
+// FP8: E4M3 key codes with one fp32 scale per key; a tile's codes are
+// decoded to bf16 (exact) when stored to LDS, its scales staged beside it,
+// and each score multiplied by its key's scale.
+template <bool FP8>
 __global__ __launch_bounds__(kPfThreads, 512 / kPfThreads) void indexer_prefill_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
-    const int64_t* __restrict__ seq_start, const int32_t* __restrict__ seq_len, const int32_t* __restrict__ q_seq,
+    const float* __restrict__ k_scale, const int64_t* __restrict__ seq_start, const int32_t* __restrict__ seq_len, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_pos, int n_q, float* __restrict__ scores, int64_t ld, int n_splits) {
   // Workgroups are dealt to the 8 XCDs round-robin (bid % 8).  Give each XCD a
   // contiguous run of the split-major work list, so the workgroups resident on
@@ -219,6 +253,7 @@ __global__ __launch_bounds__(kPfThreads, 512 / kPfThreads) void indexer_prefill_
   const int t_base = qb * kPfQ;
 
   __shared__ __align__(16) uint8_t lds[2][kPfKT * kKeyPitch];
+  __shared__ float sh_ks[FP8 ? 2 : 1][FP8 ? kPfKT : 1];   // FP8: the tiles' key scales
   __shared__ int sh_seq[kPfQ];
   __shared__ int sh_pos[kPfQ];
   __shared__ int sh_done[kPfQ];
@@ -286,27 +321,45 @@ __global__ __launch_bounds__(kPfThreads, 512 / kPfThreads) void indexer_prefill_
     const int rpos1 = (int)max(min(pos[1] - s0, (int64_t)kPfSplit), (int64_t)-1);
     const int rmax = (int)max(min(maxpos - s0, (int64_t)kPfSplit), (int64_t)-1);
     const uint16_t* kseg = kbase + s0 * kIdxDim;
+    const uint8_t* kseg8 = reinterpret_cast<const uint8_t*>(k_idx) + (seq_start[cur] + s0) * kIdxDim;
+    const float* kssg = FP8 ? k_scale + seq_start[cur] + s0 : nullptr;
 
     // Key tiles go global -> registers -> LDS (double-buffered): the loads of
     // tile i + 1 are issued before the products of tile i and stored to LDS
     // after them.
-    constexpr int kPieces = kPfKT * kKeyBytes / 16 / kPfThreads;     // 16-byte pieces per thread
+    constexpr int kPieces = kPfKT * (FP8 ? kIdxDim : kKeyBytes) / 16 / kPfThreads;   // 16-byte pieces per thread
     u32x4 ga[kPieces];
+    float gks = 1.f;                   // FP8: the scale of key threadIdx.x of the tile
     auto load_tile = [&](u32x4 (&g)[kPieces], int tile) {
 #pragma unroll
       for (int j = 0; j < kPieces; ++j) {
         const int flat = j * kPfThreads + threadIdx.x;     // 16-byte piece within the tile
         // keys past the last needed one re-read that key (their scores are -inf)
-        const int rkey = min(tile * kPfKT + (flat >> 4), rmax);
-        g[j] = ld16(kseg + rkey * kIdxDim + (flat & 15) * 8);
+        if (FP8) {
+          const int rkey = min(tile * kPfKT + (flat >> 3), rmax);
+          g[j] = ld16(kseg8 + rkey * kIdxDim + (flat & 7) * 16);
+        } else {
+          const int rkey = min(tile * kPfKT + (flat >> 4), rmax);
+          g[j] = ld16(kseg + rkey * kIdxDim + (flat & 15) * 8);
+        }
       }
+      if (FP8 && threadIdx.x < kPfKT) gks = kssg[min(tile * kPfKT + (int)threadIdx.x, rmax)];
     };
     auto store_tile = [&](const u32x4 (&g)[kPieces], int buf) {
 #pragma unroll
       for (int j = 0; j < kPieces; ++j) {
         const int flat = j * kPfThreads + threadIdx.x;
-        *reinterpret_cast<u32x4*>(lds[buf] + (flat >> 4) * kKeyPitch + (flat & 15) * 16) = g[j];
+        if (FP8) {                     // codes 16c .. 16c + 15 -> bf16 chunks 2c, 2c + 1
+          u32x4 lo, hi;
+          e4m3x16_to_bf16x16(g[j], lo, hi);
+          uint8_t* dst = lds[buf] + (flat >> 3) * kKeyPitch + (flat & 7) * 32;
+          *reinterpret_cast<u32x4*>(dst) = lo;
+          *reinterpret_cast<u32x4*>(dst + 16) = hi;
+        } else {
+          *reinterpret_cast<u32x4*>(lds[buf] + (flat >> 4) * kKeyPitch + (flat & 15) * 16) = g[j];
+        }
       }
+      if (FP8 && threadIdx.x < kPfKT) sh_ks[buf][threadIdx.x] = gks;
     };
     // Products of key column n (32 keys) of the tile in LDS buffer buf, for
     // both queries.
@@ -332,7 +385,8 @@ __global__ __launch_bounds__(kPfThreads, 512 / kPfThreads) void indexer_prefill_
     const int rpos_l = hi ? rpos1 : rpos0;
     float* srow_l = hi ? srow1 : srow0;
     auto finish = [&](const f32x16 (&acc)[2], int tile, int n) {
-      const float sc = sum_halves(relu_weighted_part(acc[0], wr[0]), relu_weighted_part(acc[1], wr[1]));
+      float sc = sum_halves(relu_weighted_part(acc[0], wr[0]), relu_weighted_part(acc[1], wr[1]));
+      if (FP8) sc *= sh_ks[tile & 1][n * 32 + (lane & 31)];
       const int rkey = tile * kPfKT + n * 32 + (lane & 31);
       if (act_l && tile >= 0 && rkey < span) srow_l[rkey] = rkey <= rpos_l ? sc : -INFINITY;
     };
@@ -394,9 +448,11 @@ int indexer_algo(int32_t n_q, int32_t n_seq, int algo) {
 
 // clear / n_clear: words the decode kernel (algo 1) sets to zero on the side;
 // the caller passes none with algo 2.
-int32_t launch_indexer(const void* q_idx, const float* w, const void* k_idx, const int64_t* seq_start,
-                       const int32_t* seq_len, const int32_t* q_seq, const int32_t* q_pos, int32_t n_q, int32_t n_seq,
-                       float* scores, int64_t ld, int algo, hipStream_t stream, uint32_t* clear, int64_t n_clear) {
+// k_scale != NULL: k_idx holds E4M3 codes with one scale per key.
+int32_t launch_indexer(const void* q_idx, const float* w, const void* k_idx, const float* k_scale,
+                       const int64_t* seq_start, const int32_t* seq_len, const int32_t* q_seq, const int32_t* q_pos,
+                       int32_t n_q, int32_t n_seq, float* scores, int64_t ld, int algo, hipStream_t stream,
+                       uint32_t* clear, int64_t n_clear) {
   algo = indexer_algo(n_q, n_seq, algo);
   if (algo != 1 && n_clear > 0) {
     set_error("indexer: only the decode kernel clears words on the side");
@@ -409,9 +465,12 @@ int32_t launch_indexer(const void* q_idx, const float* w, const void* k_idx, con
       set_error("indexer: grid of %lld workgroups is too large", (long long)grid);
       return SA_ERR_UNSUPPORTED;
     }
-    sa::DecArgs A{(const uint16_t*)q_idx, w, (const uint16_t*)k_idx, seq_start, seq_len, q_seq, q_pos, scores, ld,
-                  n_chunks, clear, n_clear > 0 ? n_clear : 0};
-    hipLaunchKernelGGL(sa::indexer_decode_kernel, dim3((unsigned)grid), dim3(sa::kDecThreads), 0, stream, A);
+    sa::DecArgs A{(const uint16_t*)q_idx, w, (const uint16_t*)k_idx, k_scale, seq_start, seq_len, q_seq, q_pos,
+                  scores, ld, n_chunks, clear, n_clear > 0 ? n_clear : 0};
+    if (k_scale)
+      hipLaunchKernelGGL(sa::indexer_decode_kernel<true>, dim3((unsigned)grid), dim3(sa::kDecThreads), 0, stream, A);
+    else
+      hipLaunchKernelGGL(sa::indexer_decode_kernel<false>, dim3((unsigned)grid), dim3(sa::kDecThreads), 0, stream, A);
     return check_launch("indexer_decode_kernel");
   }
   const int n_splits = (int)((ld + sa::kPfSplit - 1) / sa::kPfSplit);
@@ -421,9 +480,14 @@ int32_t launch_indexer(const void* q_idx, const float* w, const void* k_idx, con
     set_error("indexer: grid of %lld workgroups is too large", (long long)grid);
     return SA_ERR_UNSUPPORTED;
   }
-  hipLaunchKernelGGL(sa::indexer_prefill_kernel, dim3((unsigned)grid), dim3(sa::kPfThreads), 0, stream,
-                     (const uint16_t*)q_idx, w, (const uint16_t*)k_idx, seq_start, seq_len, q_seq, q_pos, n_q, scores,
-                     ld, n_splits);
+  if (k_scale)
+    hipLaunchKernelGGL(sa::indexer_prefill_kernel<true>, dim3((unsigned)grid), dim3(sa::kPfThreads), 0, stream,
+                       (const uint16_t*)q_idx, w, (const uint16_t*)k_idx, k_scale, seq_start, seq_len, q_seq, q_pos,
+                       n_q, scores, ld, n_splits);
+  else
+    hipLaunchKernelGGL(sa::indexer_prefill_kernel<false>, dim3((unsigned)grid), dim3(sa::kPfThreads), 0, stream,
+                       (const uint16_t*)q_idx, w, (const uint16_t*)k_idx, k_scale, seq_start, seq_len, q_seq, q_pos,
+                       n_q, scores, ld, n_splits);
   return check_launch("indexer_prefill_kernel");
 }
 

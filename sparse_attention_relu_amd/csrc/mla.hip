@@ -44,6 +44,7 @@
 // v_mfma_f32_16x16x32_bf16 column block, rounding the output to bf16.
 #include <atomic>
 
+#include "fp8.h"
 #include "sa_common.h"
 
 namespace sa {
@@ -84,6 +85,7 @@ struct AttnArgs {
   float* part_ml;        // [n_q][n_sp][64][2]     (max in log2 units, sum)
   uint16_t* obar;        // [n_q][64][512] bf16 latent average
   float* lse;            // [n_q][64] or null
+  const float* kv_scale; // FP8 rows: kv holds E4M3 codes [rows][576] and this one scale per row
 };
 
 constexpr int kMaxSlice = 2048;
@@ -96,11 +98,13 @@ constexpr size_t kAlphaBytes = 2 * kHeadGroup * 4;                        // res
 constexpr size_t kMlBytes = kHeadGroup * 2 * 4;                           // (m, l) per head at the end
 constexpr size_t kFlagBytes = 2 * 4 * 4;
 // LDS of a workgroup with NB blocks of 32 heads (NB = 2: 162,848 bytes)
-template <int NB>
+constexpr size_t kScBytes = (size_t)kRing * kTile * 4;                      // FP8 rows: each staged row's scale
+template <int NB, bool FP8 = false>
 constexpr size_t attn_smem() {
-  return kRingBytes + NB * (kSBytes + kPBytes + kAlphaBytes + kMlBytes) + kFlagBytes + kMaxSlice * 4;
+  return kRingBytes + NB * (kSBytes + kPBytes + kAlphaBytes + kMlBytes) + kFlagBytes + kMaxSlice * 4 +
+         (FP8 ? kScBytes : 0);
 }
-static_assert(attn_smem<2>() <= 160 * 1024, "two head blocks fit the LDS of a CU");
+static_assert(attn_smem<2, true>() <= 160 * 1024, "two head blocks fit the LDS of a CU");
 constexpr int kAttnThreads = 512;          // 4 score waves + 4 output waves
 
 // Slot of the 4-row group p (rows 4p..4p+3) in a head's weight entry: the
@@ -121,7 +125,14 @@ __device__ __forceinline__ float reduce8(float x, Op op) {
 // (query, slice) for all 64 heads, the two blocks of 32 heads sharing every
 // gathered tile (half the gathers and steps per head, twice the products per
 // step).  Head block blk of a workgroup is head group hg + blk.
-template <int NB>
+//
+// FP8 (kv holds E4M3 codes, one fp32 scale per row): the output waves gather
+// 576-byte code rows and their scales into registers one step ahead and land
+// them in the same tile buffers decoded to bf16 (exact), with the scales in
+// sclds; the score waves scale each logit by its row's scale and feed
+// p_j * scale_j to the value product, while the softmax sum keeps p_j: the
+// attention of the rows scale_j * value(codes_j).
+template <int NB, bool FP8>
 __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
   // Workgroups are dealt to the 8 XCDs round-robin (bid % 8): give each XCD a
   // contiguous run of (query, slice, head group) items, so the two head
@@ -147,6 +158,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
   int* flds = reinterpret_cast<int*>(sm2 + NB * (kPBytes + kAlphaBytes));  // [2][4 score waves]
   float* mlds = reinterpret_cast<float*>(sm2 + NB * (kPBytes + kAlphaBytes) + kFlagBytes);   // [NB * 32][2]
   int32_t* spos = reinterpret_cast<int32_t*>(sm2 + NB * (kPBytes + kAlphaBytes + kMlBytes) + kFlagBytes);
+  float* sclds = reinterpret_cast<float*>(spos + kMaxSlice);                 // FP8: [kRing][32] row scales
 
   const int j0 = sp * A.kps;
   const int j1 = min(A.k, j0 + A.kps);
@@ -242,6 +254,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
         // (the swizzle puts the 16 lanes of a read on 16 bank groups)
         const int src_sw = src_lane ^ (2 * pq);
         const u32x4 pos4 = *reinterpret_cast<const u32x4*>(spos + jt + 4 * pq);
+        f32x4 rs4 = {1.f, 1.f, 1.f, 1.f};        // FP8: the scales of this lane's 4 rows
+        if constexpr (FP8) rs4 = *reinterpret_cast<const f32x4*>(sclds + (tile % kRing) * kTile + 4 * pq);
         float x[NB][4];
         float tmax[NB];
         bool bump[NB];
@@ -255,7 +269,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
           tmax[blk] = -INFINITY;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            x[blk][j] = (int)pos4[j] >= 0 ? s4[j] * A.scale_log2 : -INFINITY;
+            x[blk][j] = (int)pos4[j] >= 0 ? (FP8 ? s4[j] * (rs4[j] * A.scale_log2) : s4[j] * A.scale_log2) : -INFINITY;
             tmax[blk] = fmaxf(tmax[blk], x[blk][j]);
           }
           tmax[blk] = reduce8(tmax[blk], [](float a, float b) { return fmaxf(a, b); });
@@ -286,8 +300,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
             p[j] = fast_exp2(x[blk][j] - m_use);
             l_run[blk] += p[j];
           }
-          plds[((pb_i * NB + blk) * kHeadGroup + hloc) * 10 + p_slot(pq)] =
-              u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+          if constexpr (FP8)
+            plds[((pb_i * NB + blk) * kHeadGroup + hloc) * 10 + p_slot(pq)] =
+                u32x2{pack_bf16x2(p[0] * rs4[0], p[1] * rs4[1]), pack_bf16x2(p[2] * rs4[2], p[3] * rs4[3])};
+          else
+            plds[((pb_i * NB + blk) * kHeadGroup + hloc) * 10 + p_slot(pq)] =
+                u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
         }
       }
       lds_barrier();                                                   // BAR_p
@@ -369,11 +387,66 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
   for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) o[blk][mt] = f32x16{};
+  // FP8 gather: per tile this wave loads quarter w of every row's latent
+  // codes (rows 8u + lane / 8, 16 codes at 16 (lane % 8), u = 0..3), the rope
+  // codes of rows 8w .. 8w + 7 (row 8w + (lane % 32) / 4, 16 codes at
+  // 16 (lane % 4); the upper half-wave repeats the lower) and the scales of
+  // rows 8w .. 8w + 7 (every lane loads row 8w + lane % 8), one step ahead,
+  // into registers; land8 decodes them into the tile buffer.
+  const uint8_t* rows8 = reinterpret_cast<const uint8_t*>(A.kv) + A.seq_start[A.q_seq[t]] * kRow;
+  const float* scl = FP8 ? A.kv_scale + A.seq_start[A.q_seq[t]] : nullptr;
+  u32x4 g8l[4], g8r;
+  float g8s = 1.f;
+  auto issue8 = [&](int tile) {
+    const int jt = tile * kTile;
+    int pl[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) pl[u] = spos[jt + 8 * u + (lane >> 3)];
+    const int pr = spos[jt + 8 * w + ((lane & 31) >> 2)];
+    const int ps = spos[jt + 8 * w + (lane & 7)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      g8l[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+          rows8 + (uint32_t)max(pl[u], 0) * (uint32_t)kRow + (uint32_t)(128 * w + 16 * (lane & 7))));
+    g8r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+        rows8 + (uint32_t)max(pr, 0) * (uint32_t)kRow + (uint32_t)(kLatent + 16 * (lane & 3))));
+    g8s = scl[max(ps, 0)];
+  };
+  auto land8 = [&](int tile) {
+    uint8_t* b = ring + (tile % kRing) * kTileBytes;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {           // codes 16c .. 16c + 15 -> bf16 chunks 2c, 2c + 1 of quarter w
+      const int r = 8 * u + (lane >> 3);
+      const int c = 16 * w + 2 * (lane & 7);
+      u32x4 lo, hi;
+      e4m3x16_to_bf16x16(g8l[u], lo, hi);
+      *reinterpret_cast<u32x4*>(b + tile_chunk_offset(r, c)) = lo;
+      *reinterpret_cast<u32x4*>(b + tile_chunk_offset(r, c + 1)) = hi;
+    }
+    if (lane < 32) {
+      const int r = 8 * w + (lane >> 2);
+      const int c = 64 + 2 * (lane & 3);
+      u32x4 lo, hi;
+      e4m3x16_to_bf16x16(g8r, lo, hi);
+      *reinterpret_cast<u32x4*>(b + tile_chunk_offset(r, c)) = lo;
+      *reinterpret_cast<u32x4*>(b + tile_chunk_offset(r, c + 1)) = hi;
+    }
+    if (lane < 8) sclds[(tile % kRing) * kTile + 8 * w + lane] = g8s;
+  };
   store_positions();
   lds_barrier();                                                       // B0
-  issue(0);
-  issue(1);
-  SA_WAIT_VMCNT(kLoadsPerWave);          // tile 0 is in (tile 1 may still be in flight)
+  if constexpr (FP8) {
+    if (n_tiles > 0) {
+      issue8(0);
+      __builtin_amdgcn_s_waitcnt(0);      // (vmcnt(0): tile 0's codes are in)
+      land8(0);
+      if (n_tiles > 1) issue8(1);
+    }
+  } else {
+    issue(0);
+    issue(1);
+    SA_WAIT_VMCNT(kLoadsPerWave);        // tile 0 is in (tile 1 may still be in flight)
+  }
   lds_barrier();                                                       // B1
   // weights / rescale of head l32 come from score wave l32 / 8
   const int pw = l32 >> 3;
@@ -408,7 +481,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
       }
       fl = flds[pb_i * 4 + pw];
     }
-    if (step < n_tiles) {
+    if (!FP8 && step < n_tiles) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       issue(step + 2);
     }
@@ -446,7 +519,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
       }
     }
     // tile step + 1 must be in before the next step's QK (step + 2 stays in flight)
-    if (step < n_tiles) SA_WAIT_VMCNT(kLoadsPerWave);
+    if constexpr (FP8) {
+      // its buffer held tile step - 2, whose last reads (this wave's V operands)
+      // were at step - 1; then tile step + 2's loads go out behind it
+      if (step + 1 < n_tiles) {
+        __builtin_amdgcn_s_waitcnt(0);    // (vmcnt(0): tile step + 1's codes are in)
+        land8(step + 1);
+        if (step + 2 < n_tiles) issue8(step + 2);
+      }
+    } else {
+      if (step < n_tiles) SA_WAIT_VMCNT(kLoadsPerWave);
+    }
     lds_barrier();                                                     // BAR_p
   }
   // Partial accumulators in register-tile order: [t][sp][hg][w][mt][a][lane]
@@ -786,9 +869,10 @@ size_t mla_workspace_size(int32_t n_q, int32_t k) {
 // hipFuncSetAttribute is per device; remember which devices have been set up.
 static std::atomic<uint64_t> g_attr_set{0};
 
-int32_t launch_mla(const void* q_abs, const void* kv, const int64_t* seq_start, const int32_t* q_seq,
-                   const int32_t* idx, int32_t n_q, int32_t k, const void* w_uv, float scale, void* out, float* lse,
-                   void* ws, hipStream_t stream) {
+// kv_scale != NULL: kv holds E4M3 codes [rows][576] with one scale per row.
+int32_t launch_mla(const void* q_abs, const void* kv, const float* kv_scale, const int64_t* seq_start,
+                   const int32_t* q_seq, const int32_t* idx, int32_t n_q, int32_t k, const void* w_uv, float scale,
+                   void* out, float* lse, void* ws, hipStream_t stream) {
   const int n_sp = mla_n_splits(n_q, k);
   int kps = (k + n_sp - 1) / n_sp;
   kps = (kps + sa::kTile - 1) / sa::kTile * sa::kTile;
@@ -808,8 +892,11 @@ int32_t launch_mla(const void* q_abs, const void* kv, const int64_t* seq_start, 
   A.part_ml = m.part_ml;
   A.obar = m.obar;
   A.lse = lse;
+  A.kv_scale = kv_scale;
   const int nb = mla_head_blocks(n_q);
-  const size_t smem = nb == 2 ? sa::attn_smem<2>() : sa::attn_smem<1>();
+  const bool fp8 = kv_scale != nullptr;
+  const size_t smem = nb == 2 ? (fp8 ? sa::attn_smem<2, true>() : sa::attn_smem<2>())
+                              : (fp8 ? sa::attn_smem<1, true>() : sa::attn_smem<1>());
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
     set_error("mla: hipGetDevice failed");
@@ -817,10 +904,14 @@ int32_t launch_mla(const void* q_abs, const void* kv, const int64_t* seq_start, 
   }
   const uint64_t bit = 1ull << (dev & 63);
   if (!(g_attr_set.load() & bit)) {
-    if (hipFuncSetAttribute((const void*)sa::mla_attn_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    if (hipFuncSetAttribute((const void*)sa::mla_attn_kernel<1, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)sa::attn_smem<1>()) != hipSuccess ||
-        hipFuncSetAttribute((const void*)sa::mla_attn_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize,
+        hipFuncSetAttribute((const void*)sa::mla_attn_kernel<2, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)sa::attn_smem<2>()) != hipSuccess ||
+        hipFuncSetAttribute((const void*)sa::mla_attn_kernel<1, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)sa::attn_smem<1, true>()) != hipSuccess ||
+        hipFuncSetAttribute((const void*)sa::mla_attn_kernel<2, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)sa::attn_smem<2, true>()) != hipSuccess ||
         hipFuncSetAttribute((const void*)sa::mla_wuv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)sa::kWuvSmem) != hipSuccess) {
       set_error("mla: cannot reserve %zu bytes of LDS", smem);
@@ -835,10 +926,14 @@ int32_t launch_mla(const void* q_abs, const void* kv, const int64_t* seq_start, 
     set_error("mla: grid too large");
     return SA_ERR_UNSUPPORTED;
   }
-  if (nb == 2)
-    hipLaunchKernelGGL(sa::mla_attn_kernel<2>, dim3((unsigned)grid), dim3(sa::kAttnThreads), smem, stream, A);
+  if (nb == 2 && fp8)
+    hipLaunchKernelGGL((sa::mla_attn_kernel<2, true>), dim3((unsigned)grid), dim3(sa::kAttnThreads), smem, stream, A);
+  else if (nb == 2)
+    hipLaunchKernelGGL((sa::mla_attn_kernel<2, false>), dim3((unsigned)grid), dim3(sa::kAttnThreads), smem, stream, A);
+  else if (fp8)
+    hipLaunchKernelGGL((sa::mla_attn_kernel<1, true>), dim3((unsigned)grid), dim3(sa::kAttnThreads), smem, stream, A);
   else
-    hipLaunchKernelGGL(sa::mla_attn_kernel<1>, dim3((unsigned)grid), dim3(sa::kAttnThreads), smem, stream, A);
+    hipLaunchKernelGGL((sa::mla_attn_kernel<1, false>), dim3((unsigned)grid), dim3(sa::kAttnThreads), smem, stream, A);
   int32_t rc = check_launch("mla_attn_kernel");
   if (rc) return rc;
   if (n_sp > 1) {

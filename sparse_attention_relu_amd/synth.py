@@ -172,6 +172,8 @@ class LayerInputs:
     q_idx: Optional[torch.Tensor] = None
     w: Optional[torch.Tensor] = None
     k_idx: Optional[torch.Tensor] = None
+    kv_scale: Optional[torch.Tensor] = None     # set when kv holds FP8 codes
+    k_scale: Optional[torch.Tensor] = None      # set when k_idx holds FP8 codes
 
 
 @dataclasses.dataclass

@@ -25,8 +25,10 @@ def np_batch(batch):
     return dict(seq_start=to_numpy(batch.seq_start), q_seq=to_numpy(batch.q_seq), q_pos=to_numpy(batch.q_pos))
 
 
-def check_scores(L, B, scores_gpu, rows=None):
-    """L: numpy layer dict (q_idx, w, k_idx); B: numpy batch dict; scores_gpu float64 [n_q, ld]."""
+def check_scores(L, B, scores_gpu, rows=None, extra_rel=0.0):
+    """L: numpy layer dict (q_idx, w, k_idx); B: numpy batch dict; scores_gpu float64 [n_q, ld].
+    extra_rel: one more fp32 rounding of the score (FP8 keys: the codes' score
+    times the key's scale), added as extra_rel * |exact|."""
     n_q, ld = scores_gpu.shape
     rows = range(n_q) if rows is None else rows
     worst = 0.0
@@ -35,7 +37,7 @@ def check_scores(L, B, scores_gpu, rows=None):
         exact = ref.indexer_scores_at(L["q_idx"], L["w"], L["k_idx"], B["seq_start"], B["q_seq"], B["q_pos"], t,
                                       np.arange(p + 1))
         base = int(B["seq_start"][B["q_seq"][t]])
-        bound = ref.score_error_bound(L["q_idx"][t], L["w"][t], L["k_idx"][base:base + p + 1])
+        bound = ref.score_error_bound(L["q_idx"][t], L["w"][t], L["k_idx"][base:base + p + 1]) + extra_rel * np.abs(exact)
         err = np.abs(scores_gpu[t, :p + 1] - exact)
         bad = np.nonzero(err > bound)[0]
         assert bad.size == 0, f"row {t}: {bad.size} scores outside the fp32 bound, first at s={bad[0]}: " \
@@ -57,7 +59,7 @@ def check_topk_exact(scores_gpu, q_pos, k, idx_gpu, rows=None):
                                  f"({d.size} positions differ, first {d[:8]}); got head {got[:8]} tail {got[-4:]}")
 
 
-def check_topk_band(L, B, idx_gpu, k, rows=None):
+def check_topk_band(L, B, idx_gpu, k, rows=None, extra_rel=0.0):
     """The GPU's selection against the oracle's exact scores, with the tie band."""
     n_q = idx_gpu.shape[0]
     rows = range(n_q) if rows is None else rows
@@ -79,7 +81,8 @@ def check_topk_band(L, B, idx_gpu, k, rows=None):
         sigma = sel[np.lexsort((-sel, exact[sel]))[0]]      # the oracle's k-th pick
         base = int(B["seq_start"][B["q_seq"][t]])
         keys = L["k_idx"][base:base + p + 1]
-        eps = ref.score_error_bound(L["q_idx"][t], L["w"][t], keys[np.concatenate([[sigma], diff])])
+        pts = np.concatenate([[sigma], diff])
+        eps = ref.score_error_bound(L["q_idx"][t], L["w"][t], keys[pts]) + extra_rel * np.abs(exact[pts])
         tau = 1e-3 * abs(exact[sigma]) + eps[0] + eps[1:]
         gap = np.abs(exact[diff] - exact[sigma])
         assert np.all(gap <= tau), f"row {t}: swapped positions outside the tie band: {diff[gap > tau][:8]}"
