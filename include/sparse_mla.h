@@ -180,6 +180,12 @@ int32_t sa_topk_select(const float* scores, int64_t ld, const int32_t* q_pos, in
  *   ws      workspace of at least sa_mla_workspace_size(n_q, k) bytes
  */
 size_t sa_mla_workspace_size(int32_t n_q, int32_t k);
+/* How sa_mla_sparse_attn (and its FP8 variant) slices each query's selection
+ * for n_q queries of k entries: *n_sp slices of *kps entries (the last may be
+ * shorter, none is empty); with *n_sp > 1 the slices' partial softmax states
+ * (fp32) are combined by a log-sum-exp merge.  For workspace planning and
+ * error analysis. */
+int32_t sa_mla_split_info(int32_t n_q, int32_t k, int32_t* n_sp, int32_t* kps);
 int32_t sa_mla_sparse_attn(const void* q_abs, const void* kv, const int64_t* seq_start,
                            const int32_t* q_seq, const int32_t* idx, int32_t n_q, int32_t k,
                            const void* w_uv, float scale, void* out, float* lse,

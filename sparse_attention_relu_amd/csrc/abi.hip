@@ -47,6 +47,7 @@ size_t topk_workspace_size(int32_t n_q, int64_t ld, int32_t k);
 int32_t launch_topk(const float* scores, int64_t ld, const int32_t* q_pos, int32_t n_q, int32_t k, int32_t* idx,
                     void* ws, int algo, hipStream_t stream, bool cleared);
 size_t mla_workspace_size(int32_t n_q, int32_t k);
+void mla_split(int32_t n_q, int32_t k, int* n_sp, int* kps);
 int32_t launch_mla(const void* q_abs, const void* kv, const float* kv_scale, const int64_t* seq_start,
                    const int32_t* q_seq, const int32_t* idx, int32_t n_q, int32_t k, const void* w_uv, float scale,
                    void* out, float* lse, void* ws, hipStream_t stream);
@@ -235,6 +236,16 @@ int32_t sa_topk_select_algo(const float* scores, int64_t ld, const int32_t* q_po
 int32_t sa_topk_select(const float* scores, int64_t ld, const int32_t* q_pos, int32_t n_q, int32_t k, int32_t* idx,
                        void* ws, size_t ws_bytes, sa_stream_t stream) {
   return sa_topk_select_algo(scores, ld, q_pos, n_q, k, idx, ws, ws_bytes, 0, stream);
+}
+
+int32_t sa_mla_split_info(int32_t n_q, int32_t k, int32_t* n_sp, int32_t* kps) {
+  SA_REQUIRE(n_q >= 1 && k >= 1 && k <= SA_MAX_TOPK && n_sp && kps, SA_ERR_INVALID_ARG,
+             "mla_split_info: n_q=%d, k=%d", n_q, k);
+  int a, b;
+  mla_split(n_q, k, &a, &b);
+  *n_sp = a;
+  *kps = b;
+  return SA_OK;
 }
 
 size_t sa_mla_workspace_size(int32_t n_q, int32_t k) {

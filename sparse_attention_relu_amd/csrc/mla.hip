@@ -831,14 +831,26 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 constexpr int kTwoBlockMinQ = 64;
 int mla_head_blocks(int32_t n_q) { return n_q >= kTwoBlockMinQ ? 2 : 1; }
 
-int mla_n_splits(int32_t n_q, int32_t k) {
-  // About one workgroup per CU; a slice keeps at least two 32-row tiles.
+// The slicing of each query's selection: n_sp slices of kps entries (a
+// multiple of the 32-row tile; the last slice may be shorter).  About one
+// workgroup per CU; a slice keeps at least two tiles; the slice count is
+// recomputed from the rounded slice length so no slice is empty.
+void mla_split(int32_t n_q, int32_t k, int* n_sp_out, int* kps_out) {
   const int target = mla_head_blocks(n_q) == 2 ? 256 : 128;
   int n_sp = (target + n_q - 1) / n_q;
   const int max_sp = (k + 63) / 64;
   if (n_sp > max_sp) n_sp = max_sp;
   if (n_sp > sa::kMaxSp) n_sp = sa::kMaxSp;
   if (n_sp < 1) n_sp = 1;
+  int kps = (k + n_sp - 1) / n_sp;
+  kps = (kps + sa::kTile - 1) / sa::kTile * sa::kTile;
+  *n_sp_out = (k + kps - 1) / kps;
+  *kps_out = kps;
+}
+
+int mla_n_splits(int32_t n_q, int32_t k) {
+  int n_sp, kps;
+  mla_split(n_q, k, &n_sp, &kps);
   return n_sp;
 }
 
@@ -873,9 +885,8 @@ static std::atomic<uint64_t> g_attr_set{0};
 int32_t launch_mla(const void* q_abs, const void* kv, const float* kv_scale, const int64_t* seq_start,
                    const int32_t* q_seq, const int32_t* idx, int32_t n_q, int32_t k, const void* w_uv, float scale,
                    void* out, float* lse, void* ws, hipStream_t stream) {
-  const int n_sp = mla_n_splits(n_q, k);
-  int kps = (k + n_sp - 1) / n_sp;
-  kps = (kps + sa::kTile - 1) / sa::kTile * sa::kTile;
+  int n_sp, kps;
+  mla_split(n_q, k, &n_sp, &kps);
   MlaWs m = mla_carve(ws, n_q, n_sp);
   sa::AttnArgs A;
   A.q_abs = (const uint16_t*)q_abs;

@@ -162,3 +162,17 @@ def test_layer_stack_rejects_bad_shared_selection(L):
     assert rc == -1 and b"sel_of" in L.sa_last_error_message()
     batch.n_sel = -1
     assert L.sa_layer_stack(descs, 1, ctypes.byref(batch), 2048, 1.0 / 16, FAKE, big, None, None) == -1
+
+
+def test_mla_split_has_no_empty_slice(L):
+    """The selection's slicing: whole 32-row tiles per slice, at most 32
+    slices, every slice non-empty (the rounded slice length sets the count)."""
+    n_sp, kps = ctypes.c_int32(), ctypes.c_int32()
+    for n_q in (1, 3, 5, 7, 9, 16, 63, 64, 130, 300, 4096):
+        for k in (1, 7, 64, 300, 1000, 2047, 2048):
+            assert L.sa_mla_split_info(n_q, k, ctypes.byref(n_sp), ctypes.byref(kps)) == 0
+            s, p = n_sp.value, kps.value
+            assert 1 <= s <= 32 and p % 32 == 0 and p >= 32, (n_q, k, s, p)
+            assert (s - 1) * p < k <= s * p, (n_q, k, s, p)     # the last slice holds at least one entry
+    assert L.sa_mla_split_info(0, 16, ctypes.byref(n_sp), ctypes.byref(kps)) == -1
+    assert L.sa_mla_split_info(4, 4096, ctypes.byref(n_sp), ctypes.byref(kps)) == -1
