@@ -164,6 +164,7 @@ def cpu_baseline(b, wl, n_sample, min_seconds):
             break
     total = t_idx + t_mla
     return {"value": reps * len(S) / total, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{len(S)} of {wl.n_q} queries of the same workload through all {wl.n_layers} layers, "
                       f"repeated {reps}x (indexer + top-k {t_idx:.2f} s, attention {t_mla:.2f} s); "
                       f"gathering rows from device memory untimed",
@@ -197,12 +198,14 @@ def cache_write_leg(seed, reps=15, warmup=5, n=4096, rows=131072):
         call(s)
         c.record(s)
     torch.cuda.synchronize()
-    ms = sorted(a.elapsed_time(c) for a, c in ev)[len(ev) // 2]
+    spread = sorted(a.elapsed_time(c) for a, c in ev)
+    ms = spread[len(ev) // 2]
     # inputs read and rows written (bf16), positions and row indices, weights
     nbytes = n * (576 + 128) * 2 * 2 + n * (4 + 8) + (512 + 2 * 128) * 2
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"workload": "cache_write_4096_tokens_at_126976", "ms": round(ms, 5), "bytes": nbytes,
             "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm",
+            "ms_min": round(spread[0], 5), "ms_max": round(spread[-1], 5),
             "timing": "median of %d HIP-event-timed launches" % reps}
 
 
@@ -214,7 +217,7 @@ def prefill_indexer(seed, reps=9, warmup=20):
     g = synth._gen(dev, seed, 0, 4)
     q = synth._randn((wl.n_q, 32, 128), g, dev, std=1 / 128 ** 0.5, dtype=torch.bfloat16)
     w = synth._randn((wl.n_q, 32), synth._gen(dev, seed, 0, 5), dev, std=1 / 32 ** 0.5)
-    kI = synth.indexer_keys(wl.total_tokens, synth._gen(dev, seed, 0, 6), dev)
+    _, kI = synth.law_rows(wl.seq_lens, synth._gen(dev, seed, 0, 2), synth._gen(dev, seed, 0, 6), dev)
     seq_start = torch.zeros(1, dtype=torch.int64, device=dev)
     seq_len = torch.tensor(wl.seq_lens, dtype=torch.int32, device=dev)
     q_seq = torch.zeros(wl.n_q, dtype=torch.int32, device=dev)
@@ -231,12 +234,14 @@ def prefill_indexer(seed, reps=9, warmup=20):
         api.indexer_score(q, w, kI, seq_start, seq_len, q_seq, q_pos, wl.ld, scores=scores, stream=s)
         c.record(s)
     torch.cuda.synchronize()
-    ms = sorted(a.elapsed_time(c) for a, c in ev)[len(ev) // 2]
+    spread = sorted(a.elapsed_time(c) for a, c in ev)
+    ms = spread[len(ev) // 2]
     causal_flops = sum(2.0 * 32 * 128 * (p + 1) for p in wl.q_pos)
     tflops = causal_flops / (ms * 1e-3) / 1e12
     return {"workload": wl.name, "tflops": round(tflops, 1), "ms": round(ms, 4), "unit": "TFLOP/s",
             "flops": causal_flops, "frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
-            "peak": BF16_PEAK_TFLOPS, "timing": "median of %d HIP-event-timed launches" % reps}
+            "peak": BF16_PEAK_TFLOPS, "ms_min": round(spread[0], 5), "ms_max": round(spread[-1], 5),
+            "timing": "median of %d HIP-event-timed launches" % reps}
 
 
 def query_side_leg(seed, n, reps=15, warmup=10):
@@ -339,12 +344,86 @@ def fp8_leg(batches, wl, steps, warmup):
         graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
+    spread = replay_spread(graphs, steps)
     nb = step_bytes_fp8(wl)
     gbs = nb / (ms * 1e-3) / 1e9
     return {"workload": wl.name + "_fp8_caches", "ms_per_step": round(ms, 5),
             "value": round(wl.n_q / (ms * 1e-3), 1), "unit": "queries/s", "step_bytes": nb,
             "hbm_gbs_step": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-            "timing": "%d graph replays after %d warm-up" % (steps, warmup)}
+            "replay_ms": spread, "timing": "%d graph replays after %d warm-up" % (steps, warmup)}
+
+
+def replay_spread(graphs, n):
+    """Median, min and max of n graph replays, each between its own pair of
+    HIP events (a second pass after the timed region; the headline figure is
+    the wall-clock mean of the timed region)."""
+    import torch
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i, (a, c) in enumerate(ev):
+        a.record(s)
+        graphs[i % len(graphs)].replay()
+        c.record(s)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(c) for a, c in ev)
+    return {"median": round(ms[len(ms) // 2], 5), "min": round(ms[0], 5), "max": round(ms[-1], 5), "n": n,
+            "timing": "HIP events around each replay"}
+
+
+def stage_fractions(kern_ms, eager_ms):
+    rest = max(eager_ms - kern_ms["indexer"] - kern_ms["topk"], 0.0)
+    return {"indexer": round(kern_ms["indexer"] / eager_ms, 4), "topk": round(kern_ms["topk"] / eager_ms, 4),
+            "attention_all_layers": round(rest / eager_ms, 4), "attention_all_layers_ms": round(rest, 5)}
+
+
+def gpu_sclk_mhz():
+    """(current, highest) shader clock levels in MHz from the driver's sysfs
+    table (the current level is marked '*'), or (None, None) where it cannot
+    be read."""
+    import glob
+    import re
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(f) as fh:
+                lines = fh.read().splitlines()
+        except OSError:
+            continue
+        cur, levels = None, []
+        for line in lines:
+            m = re.search(r"(\d+)\s*mhz", line.lower())
+            if not m:
+                continue
+            levels.append(int(m.group(1)))
+            if line.rstrip().endswith("*"):
+                cur = int(m.group(1))
+        if levels:
+            return cur, max(levels)
+    return None, None
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def environment(torch, sclk_after):
+    p = torch.cuda.get_device_properties(0)
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as fh:
+            rocm = fh.read().strip()
+    except OSError:
+        pass
+    return {"gpu": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "sclk_mhz_after_timed_region": sclk_after[0], "sclk_mhz_top_level": sclk_after[1],
+            "rocm": rocm, "hip_runtime": torch.version.hip, "torch": torch.__version__,
+            "host_cpu": cpu_model()}
 
 
 class HipEvents:
@@ -425,7 +504,9 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
+    sclk_after = gpu_sclk_mhz()
     print(f"[bench] timed {args.steps} graph replays: {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
+    replay_ms = replay_spread(graphs, args.steps)
 
     # Per-kernel HIP-event timing: eager steps rotating through the same input
     # sets, issued back to back (each step has its own events) and read after
@@ -449,6 +530,7 @@ def main():
         steps_ms.append(step_ev[i][0].elapsed_time(step_ev[i][1]))
     hev.close()
     kern_ms = {n: sum(v) / len(v) for n, v in acc.items()}
+    eager_ms = sum(steps_ms) / len(steps_ms)
     total_bytes, idx_bytes = step_bytes(wl)
     attn_bytes = layer_attn_bytes(wl)
     prefill = args.workload == "c3"
@@ -483,10 +565,21 @@ def main():
         "hbm_gbs_step": None if prefill else round(total_bytes / (ms_step * 1e-3) / 1e9, 1),
         "step_bytes": None if prefill else total_bytes,
         "roofline": roofline,
+        # the whole step against the HBM roofline: algorithmic bytes of one
+        # step over the graph-replay time
+        "step_roofline": None if prefill else {
+            "bound": "hbm", "achieved": round(total_bytes / (ms_step * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(total_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes_per_step": total_bytes, "ms_per_step": round(ms_step, 5)},
+        "replay_ms": replay_ms,
         "kernel_ms_first_layer": {n: round(v, 5) for n, v in kern_ms.items()},
+        # where an eager step's time goes: the indexer and top-k of the full
+        # layer, and everything after them (attention + W_UV of all layers)
+        "stage_fractions_eager": stage_fractions(kern_ms, eager_ms),
         "attn_layer_gbs": None if prefill else round(attn_bytes / (kern_ms["attn"] * 1e-3) / 1e9, 1),
-        "eager_ms_per_step": round(sum(steps_ms) / len(steps_ms), 5),
+        "eager_ms_per_step": round(eager_ms, 5),
         "input_copies": len(stacks),
+        "env": environment(torch, sclk_after),
     }
     if not args.no_prefill:
         print("[bench] prefill indexer", file=sys.stderr, flush=True)

@@ -388,7 +388,8 @@ __global__ __launch_bounds__(kPfThreads, 512 / kPfThreads) void indexer_prefill_
       float sc = sum_halves(relu_weighted_part(acc[0], wr[0]), relu_weighted_part(acc[1], wr[1]));
       if (FP8) sc *= sh_ks[tile & 1][n * 32 + (lane & 31)];
       const int rkey = tile * kPfKT + n * 32 + (lane & 31);
-      if (act_l && tile >= 0 && rkey < span) srow_l[rkey] = rkey <= rpos_l ? sc : -INFINITY;
+      // streaming store: the score rows are read back only by the next kernel
+      if (act_l && tile >= 0 && rkey < span) __builtin_nontemporal_store(rkey <= rpos_l ? sc : -INFINITY, &srow_l[rkey]);
     };
     // Software pipeline over the key columns of a tile: each column is
     // finished during the products of the next one (the last column of a tile

@@ -8,16 +8,22 @@ Shapes and distributions follow the model the pages describe
 (models.inteligile.com "GLM-5.2 / Model techniques map", section "Checked in
 its code"; llm-atlas "GLM-5.2", section "Champs bruts du config.json"):
 
-  indexer key  k_idx  [T, 128]        LayerNorm(N(0,1)^128), gamma 1, beta 0,
-                                      eps 1e-5 -> bf16 (the indexer key is the
-                                      LayerNorm of a projection)
+  indexer key  k_idx  [T, 128]        LayerNorm(N(0,1)^128), weight 1, bias 0,
+                                      eps 1e-5, dims 64..127 turned by RoPE at
+                                      the row's position -> bf16
   indexer q    q_idx  [n_q, 32, 128]  N(0, 1/128) -> bf16
   head weights w      [n_q, 32]       N(0, 1/32), fp32
-  cache row    kv     [T, 576]        [RMSNorm(N(0,1)^512), eps 1e-5 ;
+  cache row    kv     [T, 576]        [RMSNorm(N(0,1)^512), weight 1, eps 1e-5 ;
                                        RoPE(N(0,1)^64, position, theta 8e6,
                                        interleaved pairs)] -> bf16
   folded query q_abs  [n_q, 64, 576]  N(0, 1/576) -> bf16
   up-projection w_uv  [64, 256, 512]  N(0, 1/512) -> bf16
+
+The cache rows and indexer keys are made the way a model makes them: raw
+N(0, 1) projections are drawn here and the library's cache write
+(sa_cache_write, whose own parity against the oracle is tested element by
+element) normalises and rotates them into rows on the device.  A caller may
+pass another row writer (make_batch's write_rows).
 
 Sequences are packed: row seq_start[b] + s of a cache holds position s of
 sequence b.  No dataset or trained weight is involved; these seeded tensors
@@ -129,39 +135,59 @@ def _randn(shape, g, device, std=1.0, dtype=torch.float32):
     return x.to(dtype)
 
 
-def _fill_rows(out: torch.Tensor, g, device, make_chunk, chunk_rows: int):
-    n = out.shape[0]
-    for r0 in range(0, n, chunk_rows):
-        r1 = min(n, r0 + chunk_rows)
-        out[r0:r1] = make_chunk(r1 - r0, r0, g)
+def norm_params(device):
+    """kv_a_layernorm weight, k_norm weight and k_norm bias at their initial
+    values (1, 1, 0): the written rows are the normalised projections."""
+    dev = torch.device(device)
+    return (torch.ones(LATENT, dtype=torch.bfloat16, device=dev), torch.ones(IDX_DIM, dtype=torch.bfloat16, device=dev),
+            torch.zeros(IDX_DIM, dtype=torch.bfloat16, device=dev))
 
 
-def indexer_keys(total_tokens: int, g, device, chunk_rows=1 << 16) -> torch.Tensor:
-    """[T, 128] indexer keys drawn i.i.d. N(0, 1): the law of a normalised key
-    (zero mean and unit variance per row in expectation), without computing
-    any normalisation here."""
-    out = torch.empty((total_tokens, IDX_DIM), dtype=torch.bfloat16, device=device)
-
-    def mk(n, r0, gg):
-        return torch.randn((n, IDX_DIM), generator=gg, device=device).to(torch.bfloat16)
-
-    _fill_rows(out, g, device, mk, chunk_rows)
-    return out
+def positions(seq_lens, device) -> torch.Tensor:
+    """int32 [T]: the position of each packed cache row within its sequence."""
+    dev = torch.device(device)
+    if not seq_lens:
+        return torch.empty(0, dtype=torch.int32, device=dev)
+    return torch.cat([torch.arange(int(n), dtype=torch.int32, device=dev) for n in seq_lens])
 
 
-def cache_rows(seq_lens, g, device, chunk_rows=1 << 16) -> torch.Tensor:
-    """Packed [T, 576] rows drawn i.i.d. N(0, 1): a 512-d latent of unit RMS in
-    expectation, then a 64-d rope key whose pairs are isotropic Gaussians, a law
-    no rotation changes.  The arithmetic that turns projections into rows is
-    the cache-write kernel's, not this module's."""
+def raw_projection_chunks(seq_lens, g_kv, g_key, device, chunk_rows=1 << 16):
+    """Chunks of the raw projections of every cached token, in packed row
+    order: (kv_a [n, 576], k_raw [n, 128] or None, pos int32 [n], dst int64 [n])
+    with kv_a and k_raw drawn i.i.d. N(0, 1) (k_raw only when g_key is given).
+    Nothing is normalised or rotated here."""
+    dev = torch.device(device)
+    pos = positions(seq_lens, dev)
+    T = pos.shape[0]
+    for r0 in range(0, T, chunk_rows):
+        n = min(T, r0 + chunk_rows) - r0
+        kv_a = torch.randn((n, ROW), generator=g_kv, device=dev).to(torch.bfloat16)
+        k_raw = None if g_key is None else torch.randn((n, IDX_DIM), generator=g_key, device=dev).to(torch.bfloat16)
+        yield kv_a, k_raw, pos[r0:r0 + n], torch.arange(r0, r0 + n, dtype=torch.int64, device=dev)
+
+
+def cache_write_rows(kv_a, k_raw, pos, dst, kv, k_idx, params):
+    """The default row writer: the library's cache write (sa_cache_write) turns
+    the raw projections into cache rows and indexer keys on the device."""
+    from sparse_attention_relu_amd import api
+    gamma, ln_w, ln_b = params
+    api.cache_write(kv_a, gamma, pos, dst, kv, k_raw=k_raw, ln_w=ln_w if k_raw is not None else None,
+                    ln_b=ln_b if k_raw is not None else None, k_cache=k_idx if k_raw is not None else None)
+
+
+def law_rows(seq_lens, g_kv, g_key, device, write_rows=None, chunk_rows=1 << 16):
+    """Cache rows kv [T, 576] (and indexer keys k_idx [T, 128] when g_key is
+    given) of the stated law: raw N(0, 1) projections drawn here, written into
+    rows by write_rows (default: the library's cache write)."""
+    dev = torch.device(device)
     T = int(sum(seq_lens))
-    out = torch.empty((T, ROW), dtype=torch.bfloat16, device=device)
-
-    def mk(n, r0, gg):
-        return torch.randn((n, ROW), generator=gg, device=device).to(torch.bfloat16)
-
-    _fill_rows(out, g, device, mk, chunk_rows)
-    return out
+    kv = torch.empty((T, ROW), dtype=torch.bfloat16, device=dev)
+    k_idx = None if g_key is None else torch.empty((T, IDX_DIM), dtype=torch.bfloat16, device=dev)
+    params = norm_params(dev)
+    write = write_rows or cache_write_rows
+    for kv_a, k_raw, pos, dst in raw_projection_chunks(seq_lens, g_kv, g_key, dev, chunk_rows):
+        write(kv_a, k_raw, pos, dst, kv, k_idx, params)
+    return kv, k_idx
 
 
 @dataclasses.dataclass
@@ -186,13 +212,15 @@ class Batch:
     layers: List[LayerInputs]
 
 
-def make_layer(wl: Workload, layer: int, device, seed: int = 0) -> LayerInputs:
+def make_layer(wl: Workload, layer: int, device, seed: int = 0, write_rows=None) -> LayerInputs:
     dev = torch.device(device)
-    n_q, T = wl.n_q, wl.total_tokens
+    n_q = wl.n_q
+    kv, k_idx = law_rows(wl.seq_lens, _gen(dev, seed, layer, 2), _gen(dev, seed, layer, 6) if wl.full[layer] else None,
+                         dev, write_rows)
     L = LayerInputs(
         q_abs=_randn((n_q, HEADS, ROW), _gen(dev, seed, layer, 1), dev, std=1 / math.sqrt(ROW),
                      dtype=torch.bfloat16),
-        kv=cache_rows(wl.seq_lens, _gen(dev, seed, layer, 2), dev),
+        kv=kv,
         w_uv=_randn((HEADS, VDIM, LATENT), _gen(dev, seed, layer, 3), dev, std=1 / math.sqrt(LATENT),
                     dtype=torch.bfloat16),
     )
@@ -200,11 +228,11 @@ def make_layer(wl: Workload, layer: int, device, seed: int = 0) -> LayerInputs:
         L.q_idx = _randn((n_q, IDX_HEADS, IDX_DIM), _gen(dev, seed, layer, 4), dev,
                          std=1 / math.sqrt(IDX_DIM), dtype=torch.bfloat16)
         L.w = _randn((n_q, IDX_HEADS), _gen(dev, seed, layer, 5), dev, std=1 / math.sqrt(IDX_HEADS))
-        L.k_idx = indexer_keys(T, _gen(dev, seed, layer, 6), dev)
+        L.k_idx = k_idx
     return L
 
 
-def make_batch(wl: Workload, device, seed: int = 0, layers=None) -> Batch:
+def make_batch(wl: Workload, device, seed: int = 0, layers=None, write_rows=None) -> Batch:
     dev = torch.device(device)
     layer_ids = range(wl.n_layers) if layers is None else layers
     return Batch(
@@ -213,7 +241,7 @@ def make_batch(wl: Workload, device, seed: int = 0, layers=None) -> Batch:
         seq_len=torch.tensor(wl.seq_lens, dtype=torch.int32, device=dev),
         q_seq=torch.tensor(wl.q_seq, dtype=torch.int32, device=dev),
         q_pos=torch.tensor(wl.q_pos, dtype=torch.int32, device=dev),
-        layers=[make_layer(wl, l, dev, seed) for l in layer_ids],
+        layers=[make_layer(wl, l, dev, seed, write_rows) for l in layer_ids],
     )
 
 

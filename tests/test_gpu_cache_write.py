@@ -106,3 +106,39 @@ def test_cache_write_prefill_chunk_sampled(gpu_lib):
     pick = np.random.default_rng(5).choice(n, size=96, replace=False)
     _assert_ulp_close(kv[dst[pick]], want_rows[pick], "cache rows")
     _assert_ulp_close(kc[dst[pick]], want_keys[pick], "indexer keys")
+
+
+def test_synthetic_rows_follow_the_stated_law(gpu_lib):
+    """The seeded batches' cache rows and indexer keys are the oracle's cache
+    write of the raw N(0, 1) projections drawn for them (weight 1, bias 0):
+    RMS-normalised latents with rotated rope keys, LayerNorm'd indexer keys."""
+    from sparse_attention_relu_amd import synth
+    wl = synth.ragged_workload([300, 70000, 5], [(0, 299), (1, 69999), (2, 4)], n_layers=1)
+    seed = 11
+    b = synth.make_batch(wl, DEV, seed=seed)
+    kv, k_idx = to_numpy(b.layers[0].kv), to_numpy(b.layers[0].k_idx)
+    dev = torch.device(DEV)
+    chunks = synth.raw_projection_chunks(wl.seq_lens, synth._gen(dev, seed, 0, 2), synth._gen(dev, seed, 0, 6), dev)
+    starts = wl.seq_start
+    checked = 0
+    for kv_a, k_raw, pos, dst in chunks:
+        d = to_numpy(dst)
+        # rows at each sequence's start and end, and a spread in between
+        pick = np.unique(np.concatenate([np.arange(0, len(d), 997), [len(d) - 1]] +
+                                        [np.nonzero((d >= s0) & (d < s0 + 3))[0] for s0 in starts]))
+        p = to_numpy(pos)[pick]
+        assert np.array_equal(p, d[pick] - np.array([starts[np.searchsorted(starts, r, side="right") - 1]
+                                                     for r in d[pick]]))
+        want_rows = ref.cache_rows_from_projection(to_numpy(kv_a)[pick], np.ones(512), p)
+        want_keys = ref.indexer_keys_from_projection(to_numpy(k_raw)[pick], np.ones(128), np.zeros(128), p)
+        _assert_ulp_close(kv[d[pick]], want_rows, "synthetic cache rows", max_frac=0.02)
+        _assert_ulp_close(k_idx[d[pick]], want_keys, "synthetic indexer keys", max_frac=0.02)
+        checked += len(pick)
+    assert checked >= 70
+    lat = kv[:, :512]
+    rms = np.sqrt(np.mean(lat * lat, axis=1))
+    assert np.all(np.abs(rms - 1.0) < 0.01), "latents are not RMS-normalised"
+    # LayerNorm gives each key a unit mean square, which the rotation of its
+    # pairs keeps
+    ms = np.mean(k_idx * k_idx, axis=1)
+    assert np.all(np.abs(ms - 1.0) < 0.01), "indexer keys are not LayerNorm'd"
