@@ -6,6 +6,7 @@ raises on a non-zero status.  All arithmetic happens in the HIP kernels.
 """
 from __future__ import annotations
 
+import ctypes
 from typing import List, Optional, Sequence
 
 import torch
@@ -86,6 +87,14 @@ def topk_select(scores, q_pos, k: int = MAX_TOPK, idx=None, ws=None, algo: int =
                                _stream(stream))
     _lib.check("sa_topk_select", st)
     return idx
+
+
+def mla_split_info(n_q: int, k: int):
+    """sa_mla_split_info: (slices per query, selection entries per slice) of
+    the attention's split of each query's selection."""
+    n_sp, kps = ctypes.c_int32(), ctypes.c_int32()
+    _lib.check("sa_mla_split_info", _lib.lib().sa_mla_split_info(n_q, k, ctypes.byref(n_sp), ctypes.byref(kps)))
+    return n_sp.value, kps.value
 
 
 def mla_sparse_attn(q_abs, kv, seq_start, q_seq, idx, w_uv, scale: float = 1.0 / 16, out=None, lse=None, ws=None,

@@ -133,6 +133,23 @@ def test_mla_slice_counts(gpu_lib, n_q):
                      lse_gpu=to_numpy(lse))
 
 
+@pytest.mark.parametrize("k", [100, 600, 2048])
+def test_mla_single_query(gpu_lib, k):
+    # one query: the merge and W_UV run as one kernel (2, 10 and 32 slices)
+    wl = synth.ragged_workload([5000], [(0, 4321)], k=k, name=f"single_{k}")
+    b = _batch(wl, seed=40 + k)
+    L = b.layers[0]
+    sc = api.indexer_score(L.q_idx, L.w, L.k_idx, b.seq_start, b.seq_len, b.q_seq, b.q_pos, wl.ld)
+    idx = api.topk_select(sc, b.q_pos, k=k)
+    n_sp, _ = api.mla_split_info(1, k)
+    assert n_sp > 1
+    lse = torch.empty((1, 64), dtype=torch.float32, device=DEV)
+    out = api.mla_sparse_attn(L.q_abs, L.kv, b.seq_start, b.q_seq, idx, L.w_uv, wl.scale, lse=lse)
+    torch.cuda.synchronize()
+    parity.check_mla(parity.layer_np(L), parity.np_batch(b), to_numpy(idx), to_numpy(out), wl.scale,
+                     lse_gpu=to_numpy(lse))
+
+
 @pytest.mark.parametrize("n_q", [130, 300])
 def test_mla_all_heads_per_workgroup(gpu_lib, n_q):
     # from 64 queries on, one attention workgroup takes all 64 heads of a
