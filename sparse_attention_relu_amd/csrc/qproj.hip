@@ -140,42 +140,47 @@ __device__ __forceinline__ void q_copy_rope(const QArgs& A, int b, int n0, int n
 // contraction slots from k = 64 blk + 16 kg + 8 j (j = step, kg = lane / 16),
 // the same order for both operands, so each lane reads 32 contiguous bytes
 // of a row and the 4 lanes of a row read its whole 128-byte line.
-constexpr int kSkBM = 64;            // weight rows per workgroup
-constexpr int kSkTM = kSkBM / 16;
+constexpr int kSkTM = 2;             // 16-row weight tiles per workgroup (fastest of 1, 2, 4 at 16 tokens)
 constexpr int kSkDepth = 3;          // 64-wide blocks in flight per wave
 
-template <int TN>                    // 16 TN tokens per workgroup
+// KPW > 0: K is exactly 4 KPW blocks (every wave has KPW of them) and the
+// block loop is unrolled at compile time, so every load is unconditional and
+// the compiler waits for each block's loads alone.  With a runtime count
+// (KPW = 0) the loads sit behind branches, and the compiler, unable to count
+// what is outstanding, waits for everything before each block: one block in
+// flight instead of kSkDepth.
+template <int TN, int KPW, int TM>   // 16 TN tokens and 16 TM weight rows per workgroup
 __global__ __launch_bounds__(kQThreads) void qgemm_skinny_kernel(QArgs A) {
   int mb = blockIdx.x;
   const int si = q_segment(A, mb);
   const QSeg& S = si == 0 ? A.seg[0] : (si == 1 ? A.seg[1] : A.seg[2]);
   const int b = blockIdx.z;
-  const int m0 = mb * kSkBM, n0 = blockIdx.y * 16 * TN;
+  const int m0 = mb * 16 * TM, n0 = blockIdx.y * 16 * TN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, kg = lane >> 4;
   if (A.copy_dst && mb == 0) q_copy_rope(A, b, n0, 16 * TN);
   // operand row pointers: weight row m0 + 16 tm + l16, token n0 + 16 tn + l16
   // (clamped into range; their results are not stored), lane offset 16 kg
-  const uint16_t* wp[kSkTM];
+  const uint16_t* wp[TM];
   const uint16_t* xp[TN];
 #pragma unroll
-  for (int tm = 0; tm < kSkTM; ++tm)
+  for (int tm = 0; tm < TM; ++tm)
     wp[tm] = S.w + (int64_t)b * A.w_batch + (int64_t)min(m0 + 16 * tm + l16, S.rows - 1) * A.lda + 16 * kg;
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn)
     xp[tn] = A.x + (int64_t)b * A.x_batch + (int64_t)min(n0 + 16 * tn + l16, A.n - 1) * A.ldx + 16 * kg;
   const int n_blk = A.K / 64;
   const int n_my = (n_blk - wave + 3) / 4;      // this wave's blocks: wave, wave + 4, ...
-  f32x4 acc[kSkTM][TN];
+  f32x4 acc[TM][TN];
 #pragma unroll
-  for (int tm = 0; tm < kSkTM; ++tm)
+  for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = f32x4{0.f, 0.f, 0.f, 0.f};
-  u32x4 ra[kSkDepth][kSkTM][2], rb[kSkDepth][TN][2];
+  u32x4 ra[kSkDepth][TM][2], rb[kSkDepth][TN][2];
   auto load = [&](int slot, int i) {
     const int k = 64 * (wave + 4 * i);
 #pragma unroll
-    for (int tm = 0; tm < kSkTM; ++tm)
+    for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         ra[slot][tm][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp[tm] + k + 8 * j));
@@ -184,39 +189,58 @@ __global__ __launch_bounds__(kQThreads) void qgemm_skinny_kernel(QArgs A) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) rb[slot][tn][j] = ld16(xp[tn] + k + 8 * j);
   };
+  auto products = [&](int u) {
 #pragma unroll
-  for (int u = 0; u < kSkDepth; ++u)
-    if (u < n_my) load(u, u);
-  for (int i = 0; i < n_my; i += kSkDepth) {
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int u = 0; u < kSkDepth; ++u) {
-      if (i + u < n_my) {
+      for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int tn = 0; tn < TN; ++tn)
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[u][tm][j]), as_bf16x8(rb[u][tn][j]),
+                                                                acc[tm][tn], 0, 0, 0);
+  };
+  if constexpr (KPW > 0) {
+    static_assert(KPW >= kSkDepth, "the unrolled loop starts with kSkDepth blocks in flight");
+    // (the scheduling barriers keep each block's loads where they are
+    // written; left free, the scheduler sinks them next to their use)
 #pragma unroll
-          for (int tm = 0; tm < kSkTM; ++tm)
+    for (int u = 0; u < kSkDepth; ++u) load(u, u);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int tn = 0; tn < TN; ++tn)
-              acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[u][tm][j]), as_bf16x8(rb[u][tn][j]),
-                                                                    acc[tm][tn], 0, 0, 0);
-        if (i + u + kSkDepth < n_my) load(u, i + u + kSkDepth);
+    for (int i = 0; i < KPW; ++i) {
+      products(i % kSkDepth);
+      if (i + kSkDepth < KPW) load(i % kSkDepth, i + kSkDepth);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < kSkDepth; ++u)
+      if (u < n_my) load(u, u);
+    for (int i = 0; i < n_my; i += kSkDepth) {
+#pragma unroll
+      for (int u = 0; u < kSkDepth; ++u) {
+        if (i + u < n_my) {
+          products(u);
+          if (i + u + kSkDepth < n_my) load(u, i + u + kSkDepth);
+        }
       }
     }
   }
-  // sum the 4 waves' partial tiles: wave w finishes tiles tm = w
-  __shared__ f32x4 part[4][kSkTM][TN][64];
+  // sum the 4 waves' partial tiles: wave w finishes tiles tm = w, w + 4, ...
+  __shared__ f32x4 part[4][TM][TN][64];
 #pragma unroll
-  for (int tm = 0; tm < kSkTM; ++tm)
+  for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) part[wave][tm][tn][lane] = acc[tm][tn];
   __syncthreads();
-  const int tm = wave;
+  for (int tm = wave; tm < TM; tm += 4) {
 #pragma unroll
-  for (int tn = 0; tn < TN; ++tn) {
-    f32x4 v = part[0][tm][tn][lane];
+    for (int tn = 0; tn < TN; ++tn) {
+      f32x4 v = part[0][tm][tn][lane];
 #pragma unroll
-    for (int w2 = 1; w2 < 4; ++w2) v += part[w2][tm][tn][lane];
-    q_store4(A, S, b, m0 + 16 * tm + 4 * kg, n0 + 16 * tn + l16, v);
+      for (int w2 = 1; w2 < 4; ++w2) v += part[w2][tm][tn][lane];
+      q_store4(A, S, b, m0 + 16 * tm + 4 * kg, n0 + 16 * tn + l16, v);
+    }
   }
 }
 
@@ -322,7 +346,7 @@ static std::atomic<uint64_t> g_q_attr_set{0};
 static int32_t q_launch(sa::QArgs& A, int n_batch, hipStream_t stream) {
   const bool sk = q_skinny(A.n);
   const int sk_tn = A.n <= 16 ? 1 : 2;        // 16 or 32 tokens per skinny workgroup
-  const int bm = sk ? sa::kSkBM : sa::kTiBM, bn = sk ? 16 * sk_tn : sa::kTiBN;
+  const int bm = sk ? 16 * sa::kSkTM : sa::kTiBM, bn = sk ? 16 * sk_tn : sa::kTiBN;
   int64_t mblocks = 0;
   for (int s = 0; s < A.n_seg; ++s) {
     A.seg[s].mblocks = (A.seg[s].rows + bm - 1) / bm;
@@ -336,10 +360,16 @@ static int32_t q_launch(sa::QArgs& A, int n_batch, hipStream_t stream) {
   fill_inv_freq(A.inv_freq);
   const dim3 grid((unsigned)mblocks, (unsigned)nblocks, (unsigned)n_batch);
   if (sk) {
-    if (sk_tn == 1)
-      hipLaunchKernelGGL(sa::qgemm_skinny_kernel<1>, grid, dim3(sa::kQThreads), 0, stream, A);
+    const bool k2048 = A.K == 2048;      // q_lora_rank: 8 blocks per wave, unrolled
+    constexpr int TM = sa::kSkTM;
+    if (sk_tn == 1 && k2048)
+      hipLaunchKernelGGL((sa::qgemm_skinny_kernel<1, 8, TM>), grid, dim3(sa::kQThreads), 0, stream, A);
+    else if (k2048)
+      hipLaunchKernelGGL((sa::qgemm_skinny_kernel<2, 8, TM>), grid, dim3(sa::kQThreads), 0, stream, A);
+    else if (sk_tn == 1)
+      hipLaunchKernelGGL((sa::qgemm_skinny_kernel<1, 0, TM>), grid, dim3(sa::kQThreads), 0, stream, A);
     else
-      hipLaunchKernelGGL(sa::qgemm_skinny_kernel<2>, grid, dim3(sa::kQThreads), 0, stream, A);
+      hipLaunchKernelGGL((sa::qgemm_skinny_kernel<2, 0, TM>), grid, dim3(sa::kQThreads), 0, stream, A);
     return check_launch("qgemm_skinny_kernel");
   }
   int dev = 0;
