@@ -91,6 +91,21 @@ def test_topk_ties_and_edges(gpu_lib, kind, algo):
         parity.check_topk_exact(to_numpy(sc), to_numpy(q_pos), k, to_numpy(idx))
 
 
+@pytest.mark.parametrize("kind", ["normal", "quantised", "spiky"])
+def test_topk_rows_longer_than_the_bitmap(gpu_lib, kind):
+    # rows of 262,145..900,000 positions: longer than the finish kernel's LDS
+    # bitmap, so the kept positions are put in order by sorting; the exact
+    # path must agree bitwise
+    ld = 900000
+    sc = _synthetic_scores(kind, 5, ld, 13)
+    q_pos = torch.tensor([262144, 262143 + 2048, 524290, 786431, ld - 1], dtype=torch.int32, device=DEV)
+    for k in (2048, 700):
+        idx = api.topk_select(sc, q_pos, k=k, algo=1)
+        torch.cuda.synchronize()
+        parity.check_topk_exact(to_numpy(sc), to_numpy(q_pos), k, to_numpy(idx))
+        assert torch.equal(idx, api.topk_select(sc, q_pos, k=k, algo=2))
+
+
 def test_topk_paths_agree_bitwise(gpu_lib):
     sc = _synthetic_scores("normal", 40, 131072, 3)
     q_pos = torch.randint(0, 131072, (40,), dtype=torch.int32, device=DEV)
