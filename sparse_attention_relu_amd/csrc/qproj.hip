@@ -37,8 +37,8 @@
 //                        summed through LDS at the end.  HBM-bound on the
 //                        weights.
 //   qgemm_tiled_kernel   prefill batches: 128 weight rows x 128 tokens per
-//                        workgroup, 64-wide K chunks staged in LDS (two
-//                        buffers, global -> registers -> LDS one chunk ahead),
+//                        workgroup, 64-wide K chunks staged in LDS by direct
+//                        global -> LDS loads (two stages, one chunk ahead),
 //                        2 x 2 waves of 64 x 64.  MFMA-bound.
 #include <atomic>
 #include <cmath>
@@ -245,12 +245,22 @@ __global__ __launch_bounds__(kQThreads) void qgemm_skinny_kernel(QArgs A) {
 }
 
 // ----------------------------------------------------------- prefill batches
+// 128 weight rows x 128 tokens per workgroup (4 waves of 64 x 64), K in
+// kTiBK-wide chunks through a ring of kTiStages LDS stages filled by direct
+// global -> LDS loads, kTiStages - 1 chunks ahead of the products.  A stage
+// holds each row's kTiBK values as 16-byte chunks, chunk c of row r at slot
+// ti_slot(r, c): the 8 lanes of each 128-byte phase of an operand read hit
+// 32 different banks.
 constexpr int kTiBM = 128, kTiBN = 128, kTiBK = 64;
-constexpr int kTiPitch = kTiBK * 2 + 16;               // 144 bytes per staged row
+constexpr int kTiStages = 2;                           // two workgroups per CU beat deeper rings (fewer waves)
 constexpr int kTiTM = kTiBM / 32, kTiTN = kTiBN / 32;  // 16x16 tiles per wave (2 x 2 waves)
-constexpr int kTiAP = kTiBM * 8 / kQThreads;           // 16-byte pieces per thread per chunk
-constexpr int kTiBP = kTiBN * 8 / kQThreads;
-constexpr size_t kTiSmem = 2 * (size_t)(kTiBM + kTiBN) * kTiPitch;   // 73,728 bytes
+constexpr int kTiRowB = kTiBK * 2;                     // bytes per staged row
+constexpr int kTiChunks = kTiRowB / 16;                // 16-byte chunks per staged row
+constexpr int kTiStageB = (kTiBM + kTiBN) * kTiRowB;
+constexpr int kTiLoads = kTiStageB / 16 / kQThreads;   // 16-byte direct loads per thread per stage
+constexpr size_t kTiSmem = (size_t)kTiStages * kTiStageB;   // 64 KB: two workgroups per CU
+static_assert(kTiChunks == 4 || kTiChunks == 8, "64- or 128-byte rows");
+__device__ __forceinline__ int ti_slot(int r, int c) { return kTiChunks == 8 ? c ^ (r & 7) : c ^ ((r >> 1) & 3); }
 
 __global__ __launch_bounds__(kQThreads) void qgemm_tiled_kernel(QArgs A) {
   extern __shared__ __align__(16) uint8_t qsm[];
@@ -265,64 +275,69 @@ __global__ __launch_bounds__(kQThreads) void qgemm_tiled_kernel(QArgs A) {
   if (A.copy_dst && mb == 0) q_copy_rope(A, b, n0, kTiBN);
   const uint16_t* W = S.w + (int64_t)b * A.w_batch;
   const uint16_t* X = A.x + (int64_t)b * A.x_batch;
-  u32x4 ga[kTiAP], gb[kTiBP];
-  auto gload = [&](int k0) {
+  // Load u of this wave fills the 1 KB of staged rows from row
+  // (1024 / kTiRowB) (4 u + wave) on (rows 0..127 weights, 128..255 tokens):
+  // lane p -> row + p / kTiChunks, slot p % kTiChunks, which holds the chunk
+  // that ti_slot maps there.
+  const uint16_t* src[kTiLoads];
+  int dst[kTiLoads];
 #pragma unroll
-    for (int p = 0; p < kTiAP; ++p) {
-      const int f = tid + p * kQThreads;
-      ga[p] = ld16(W + (int64_t)min(m0 + (f >> 3), S.rows - 1) * A.lda + k0 + (f & 7) * 8);
-    }
+  for (int u = 0; u < kTiLoads; ++u) {
+    const int row = (1024 / kTiRowB) * (4 * u + wave) + lane / kTiChunks;
+    const int chunk = ti_slot(row, lane % kTiChunks);      // (the mapping is its own inverse)
+    src[u] = row < kTiBM ? W + (int64_t)min(m0 + row, S.rows - 1) * A.lda + 8 * chunk
+                         : X + (int64_t)min(n0 + row - kTiBM, A.n - 1) * A.ldx + 8 * chunk;
+    dst[u] = 1024 * (4 * u + wave);                      // the instruction's 1 KB, lane p at + 16 p
+  }
+  const int nk = A.K / kTiBK;
+  auto issue = [&](int kc) {                             // chunk kc (clamped) into its stage
+    const int kk = min(kc, nk - 1);
+    uint8_t* st = qsm + (size_t)(kc % kTiStages) * kTiStageB;
 #pragma unroll
-    for (int p = 0; p < kTiBP; ++p) {
-      const int f = tid + p * kQThreads;
-      gb[p] = ld16(X + (int64_t)min(n0 + (f >> 3), A.n - 1) * A.ldx + k0 + (f & 7) * 8);
-    }
-  };
-  auto lstore = [&](int buf) {
-    uint8_t* base = qsm + (size_t)buf * (kTiBM + kTiBN) * kTiPitch;
-#pragma unroll
-    for (int p = 0; p < kTiAP; ++p) {
-      const int f = tid + p * kQThreads;
-      *reinterpret_cast<u32x4*>(base + (f >> 3) * kTiPitch + (f & 7) * 16) = ga[p];
-    }
-#pragma unroll
-    for (int p = 0; p < kTiBP; ++p) {
-      const int f = tid + p * kQThreads;
-      *reinterpret_cast<u32x4*>(base + (kTiBM + (f >> 3)) * kTiPitch + (f & 7) * 16) = gb[p];
-    }
+    for (int u = 0; u < kTiLoads; ++u)
+      __builtin_amdgcn_global_load_lds((const void*)(src[u] + kk * kTiBK),
+                                       (__attribute__((address_space(3))) void*)(st + dst[u]), 16, 0, 0);
   };
   f32x4 acc[kTiTM][kTiTN];
 #pragma unroll
   for (int tm = 0; tm < kTiTM; ++tm)
 #pragma unroll
     for (int tn = 0; tn < kTiTN; ++tn) acc[tm][tn] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nk = A.K / kTiBK;
-  gload(0);
-  lstore(0);
+#pragma unroll
+  for (int c = 0; c < kTiStages - 1; ++c) issue(c);
+  SA_WAIT_VMCNT(kTiLoads * (kTiStages - 2));            // chunk 0 is in
   __syncthreads();
+  // operand rows of this lane: weight row wm 64 + 16 tm + l16, token row
+  // 128 + wn 64 + 16 tn + l16; chunk 4 s + kg
+  const int rA = wm * 16 * kTiTM + l16, rB = kTiBM + wn * 16 * kTiTN + l16;
+#pragma unroll 1
   for (int kc = 0; kc < nk; ++kc) {
-    const int buf = kc & 1;
-    if (kc + 1 < nk) gload((kc + 1) * kTiBK);
-    const uint8_t* la = qsm + (size_t)buf * (kTiBM + kTiBN) * kTiPitch;
-    const uint8_t* lb = la + kTiBM * kTiPitch;
+    issue(kc + kTiStages - 1);                           // into the stage read at kc - 1
+    const uint8_t* st = qsm + (size_t)(kc % kTiStages) * kTiStageB;
 #pragma unroll
     for (int s = 0; s < kTiBK / 32; ++s) {
+      const int c = 4 * s + kg;
       bf16x8 a[kTiTM], bb[kTiTN];
 #pragma unroll
-      for (int tm = 0; tm < kTiTM; ++tm)
-        a[tm] = *reinterpret_cast<const bf16x8*>(la + (wm * 16 * kTiTM + tm * 16 + l16) * kTiPitch + (s * 32 + 8 * kg) * 2);
+      for (int tm = 0; tm < kTiTM; ++tm) {
+        const int r = rA + 16 * tm;
+        a[tm] = *reinterpret_cast<const bf16x8*>(st + r * kTiRowB + 16 * ti_slot(r, c));
+      }
 #pragma unroll
-      for (int tn = 0; tn < kTiTN; ++tn)
-        bb[tn] = *reinterpret_cast<const bf16x8*>(lb + (wn * 16 * kTiTN + tn * 16 + l16) * kTiPitch + (s * 32 + 8 * kg) * 2);
+      for (int tn = 0; tn < kTiTN; ++tn) {
+        const int r = rB + 16 * tn;
+        bb[tn] = *reinterpret_cast<const bf16x8*>(st + r * kTiRowB + 16 * ti_slot(r, c));
+      }
 #pragma unroll
       for (int tm = 0; tm < kTiTM; ++tm)
 #pragma unroll
         for (int tn = 0; tn < kTiTN; ++tn)
           acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[tm], bb[tn], acc[tm][tn], 0, 0, 0);
     }
-    if (kc + 1 < nk) lstore(buf ^ 1);
-    __syncthreads();
+    SA_WAIT_VMCNT(kTiLoads * (kTiStages - 2));          // chunk kc + 1 is in
+    __syncthreads();                                     // and every wave is done with chunk kc's stage
   }
+  SA_WAIT_VMCNT(0);                                      // (the clamped trailing loads land before the end)
 #pragma unroll
   for (int tm = 0; tm < kTiTM; ++tm)
 #pragma unroll
