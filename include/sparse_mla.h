@@ -464,7 +464,8 @@ int32_t sa_cache_write(const void* kv_a, const void* gamma, const void* k_raw, c
  *            automatic picks 2 when n_q >= 64 and n_q >= 16 * n_seq (at least
  *            16 queries per sequence on average), else 1.
  *   topk:    1 = rows split over many workgroups with candidate compaction,
- *            2 = one workgroup per row, full radix passes (the exact fallback).
+ *            2 = one workgroup per row, full radix passes (the exact fallback);
+ *            automatic picks 2 for rows of at most 12,288 scores (ld), else 1.
  * Returns SA_ERR_INVALID_ARG for an unknown algo.
  */
 int32_t sa_indexer_score_algo(const void* q_idx, const float* w, const void* k_idx,

@@ -12,7 +12,8 @@
 // k_eff largest composites: composites are unique, so the tie rule is built
 // in and every step below is an exact integer radix select.
 //
-// Path 1 (many workgroups per row, used by default):
+// Path 1 (many workgroups per row, the automatic choice for rows longer than
+// kPath2MaxLd):
 //   hist     rows x chunks: 4096-bin histogram of the top 12 key bits (LDS,
 //            then global atomics).  Inside sa_layer_stack the decode
 //            indexer zeroes the histograms and counters on the side.
@@ -25,8 +26,9 @@
 //   finish   one workgroup per row: the candidates go to LDS, a radix select
 //            finds the remaining count among them, and a bitonic sort puts the
 //            kept positions in ascending order.
-// Path 2 (one workgroup per row; also the exact fallback of path 1 when the
-//   candidates overflow their capacity): three radix passes over the row give
+// Path 2 (one workgroup per row; the automatic choice for short rows, and the
+//   exact fallback of path 1 when the candidates overflow their capacity):
+//   three radix passes over the row give
 //   the exact k_eff-th largest key K*, then one ordered pass keeps every
 //   key > K* and the lowest-positioned keys == K*, writing them in order.
 #include "topk_common.h"
@@ -40,6 +42,7 @@ constexpr int kFinThreads = 1024;
 constexpr int kLdsCand = 8192;         // candidates staged in LDS by the finish kernel
 constexpr int kFinBins = 2048;         // 11-bit digits in the finish kernel
 constexpr int kBitmapBits = 1 << 18;   // rows up to this length are emitted in order from an LDS bitmap
+constexpr int64_t kPath2MaxLd = 12288; // the automatic choice takes path 2 for rows up to this length
 static_assert(kMaxTopk % kFinThreads == 0, "the finish kernel loads the kept positions in whole rounds");
 
 // ----------------------------------------------------------------- path 1
@@ -450,7 +453,11 @@ void topk_clear_range(void* ws, int32_t n_q, int64_t ld, uint32_t** p, int64_t* 
 // cleared: path 1's words (topk_clear_range) are already zero in stream order.
 int32_t launch_topk(const float* scores, int64_t ld, const int32_t* q_pos, int32_t n_q, int32_t k, int32_t* idx,
                     void* ws, int algo, hipStream_t stream, bool cleared) {
-  if (algo == 0) algo = 1;
+  // Automatic choice: one kernel and one workgroup per row (path 2) for short
+  // rows, whose three radix passes over at most 12,288 scores cost less than
+  // path 1's three launches (4 rows of 4096: 10.8 against 20.7 us; 16 of 8192:
+  // 15.4 against 22.6 us; even at 16,384); path 1 from there on.
+  if (algo == 0) algo = ld <= sa::kPath2MaxLd ? 2 : 1;
   sa::TopkWs w = topk_carve(ws, n_q, ld);
   const int n_chunks = (int)((ld + sa::kChunk - 1) / sa::kChunk);
   if ((int64_t)n_chunks * n_q > 0x7fffffff) {
