@@ -37,8 +37,9 @@
 // 16 lanes of one operand read hit 16 different bank groups.
 // With one slice per query the workgroup normalises and writes the latent
 // average obar (bf16); with several, each writes its partial state and
-// mla_merge_kernel (up to 8 slices) or mla_merge_wide_kernel (more slices,
-// i.e. few queries) combines them.
+// mla_merge_kernel (up to 8 slices), mla_merge_wide_kernel (more slices,
+// i.e. few queries) or mla_merge_split_kernel (more slices and at most two
+// queries) combines them.
 // mla_wuv_kernel: one workgroup per (head, 64 value rows) holds that 64 x 512
 // slice of W_UV in registers and multiplies it with obar^T, 16 queries per
 // v_mfma_f32_16x16x32_bf16 column block, rounding the output to bf16.
@@ -741,6 +742,87 @@ __global__ __launch_bounds__(kMergeWaves * 64) void mla_merge_wide_kernel(AttnAr
     A.lse[(int64_t)t * kHeads + head] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
+// The merge for one or two queries with many slices (the decode of one long
+// sequence): 64 items per query are too few workgroups to stream the partial
+// states at the chip's rate, so each item is split 4 ways by lane.  Workgroup
+// (item, quarter q) takes lanes 16q .. 16q + 15 of the item; thread (g, i)
+// (i = lane within the quarter, g = 0..15) merges slices g, g + 16, and the 16
+// groups of a lane are combined through LDS.  Same dims per lane and the same
+// arithmetic as the merges above.
+constexpr int kSplitMaxQ = 2;          // queries up to which this merge is used
+static_assert(kMaxSp <= 32, "two slices per thread cover every slice");
+
+__global__ __launch_bounds__(256) void mla_merge_split_kernel(AttnArgs A) {
+  const int n_wg = (int)gridDim.x;
+  const int wg = (n_wg & 7) ? (int)blockIdx.x : (int)(blockIdx.x & 7) * (n_wg >> 3) + (int)(blockIdx.x >> 3);
+  const int t = wg >> 8;                          // 64 items x 4 quarters per query
+  const int qb = (wg >> 2) & 63, qq = wg & 3;
+  const int hg = qb >> 5, w = (qb >> 3) & 3, mp = (qb >> 2) & 1, a = qb & 3;
+  const int i = threadIdx.x & 15, g = threadIdx.x >> 4;
+  const int lane = 16 * qq + i;                   // lane of the item (the attention's register lane)
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int head = kHeadGroup * hg + l32;
+  const int n_sp = A.n_sp;
+  const f32x4* src = reinterpret_cast<const f32x4*>(A.part_o) + (((int64_t)t * n_sp * 2 + hg) * 4 + w) * 1024 +
+                     (2 * mp * 4 + a) * 64 + lane;
+  const float2* mlp = reinterpret_cast<const float2*>(A.part_ml) + (int64_t)t * n_sp * kHeads + head;
+  f32x4 v0[2], v1[2];
+  float2 ml[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int s = g + 16 * u;
+    ml[u] = float2{-INFINITY, 0.f};
+    v0[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    v1[u] = v0[u];
+    if (s < n_sp) {
+      ml[u] = mlp[(int64_t)s * kHeads];
+      v0[u] = src[(int64_t)s * 8192];
+      v1[u] = src[(int64_t)s * 8192 + 256];
+    }
+  }
+  float M = fmaxf(ml[0].x, ml[1].x), L = 0.f;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const float wt = ml[u].x != -INFINITY ? fast_exp2(ml[u].x - M) : 0.f;
+    L = fmaf(wt, ml[u].y, L);
+    acc0 += wt * v0[u];
+    acc1 += wt * v1[u];
+  }
+  __shared__ float part[10][16][16];              // [field][group][lane in quarter]
+  part[0][g][i] = M;
+  part[1][g][i] = L;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    part[2 + b][g][i] = acc0[b];
+    part[6 + b][g][i] = acc1[b];
+  }
+  __syncthreads();
+  if (g != 0) return;
+  float Mt = -INFINITY;
+  for (int q = 0; q < 16; ++q) Mt = fmaxf(Mt, part[0][q][i]);
+  float Lt = 0.f;
+  f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < 16; ++q) {
+    const float mq = part[0][q][i];
+    const float c = mq != -INFINITY ? fast_exp2(mq - Mt) : 0.f;   // groups without slices have M = -inf
+    Lt = fmaf(c, part[1][q][i], Lt);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      o0[b] = fmaf(c, part[2 + b][q][i], o0[b]);
+      o1[b] = fmaf(c, part[6 + b][q][i], o1[b]);
+    }
+  }
+  const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+  // o0[b] is dim 128w + 32a + 16hl + 4b + 2mp, o1[b] the next dim
+  uint16_t* ob = A.obar + ((int64_t)t * kHeads + head) * kLatent + 128 * w + 32 * a + 16 * hl + 2 * mp;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+    *reinterpret_cast<uint32_t*>(ob + 4 * b) = pack_bf16x2(o0[b] * inv, o1[b] * inv);
+  if (A.lse && w == 0 && mp == 0 && a == 0 && hl == 0)
+    A.lse[(int64_t)t * kHeads + head] = Lt > 0.f ? (Mt + __log2f(Lt)) * 0.69314718055994531f : -INFINITY;
+}
+
 // ------------------------------------------------------------------ W_UV
 struct WuvArgs {
   const uint16_t* obar;     // [n_q][64][512] bf16
@@ -948,11 +1030,17 @@ int32_t launch_mla(const void* q_abs, const void* kv, const float* kv_scale, con
   int32_t rc = check_launch("mla_attn_kernel");
   if (rc) return rc;
   if (n_sp > 1) {
-    if (wide)
-      hipLaunchKernelGGL(sa::mla_merge_wide_kernel, dim3((unsigned)merge_grid), dim3(sa::kMergeWaves * 64), 0, stream, A);
-    else
-      hipLaunchKernelGGL(sa::mla_merge_kernel, dim3((unsigned)merge_grid), dim3(256), 0, stream, A);
-    if ((rc = check_launch(wide ? "mla_merge_wide_kernel" : "mla_merge_kernel"))) return rc;
+    if (wide && n_q <= sa::kSplitMaxQ) {
+      hipLaunchKernelGGL(sa::mla_merge_split_kernel, dim3((unsigned)(n_q * 256)), dim3(256), 0, stream, A);
+      if ((rc = check_launch("mla_merge_split_kernel"))) return rc;
+    } else {
+      if (wide)
+        hipLaunchKernelGGL(sa::mla_merge_wide_kernel, dim3((unsigned)merge_grid), dim3(sa::kMergeWaves * 64), 0, stream,
+                           A);
+      else
+        hipLaunchKernelGGL(sa::mla_merge_kernel, dim3((unsigned)merge_grid), dim3(256), 0, stream, A);
+      if ((rc = check_launch(wide ? "mla_merge_wide_kernel" : "mla_merge_kernel"))) return rc;
+    }
   }
   sa::WuvArgs W{m.obar, (const uint16_t*)w_uv, (uint16_t*)out, n_q};
   hipLaunchKernelGGL(sa::mla_wuv_kernel, dim3(sa::kHeads * 4), dim3(256), sa::kWuvSmem, stream, W);
