@@ -35,9 +35,14 @@
 
 namespace sa {
 
-constexpr int kChunk = 8192;           // elements per workgroup in path 1
 constexpr int kHistThreads = 1024;
-constexpr int kPer = kChunk / kHistThreads;
+// Path 1 reads PER scores per thread, a chunk of PER x 1024 per workgroup:
+// 8 (8192-score chunks) for decode batches, 32 when the rows would give more
+// than kManyChunks workgroups (chunked prefill: 4096 rows of 131,072), where
+// each workgroup's fixed chain (its row's histogram, the bin search, the
+// slot reservation) would otherwise outweigh its share of the scores.
+constexpr int kPerSmall = 8, kPerLarge = 32;
+constexpr int64_t kManyChunks = 4096;
 constexpr int kFinThreads = 1024;
 constexpr int kLdsCand = 8192;         // candidates staged in LDS by the finish kernel
 constexpr int kFinBins = 2048;         // 11-bit digits in the finish kernel
@@ -52,13 +57,14 @@ __global__ void topk_zero_kernel(uint32_t* __restrict__ a, int64_t n_a, int32_t*
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_b; i += stride) b[i] = 0;
 }
 
+template <int kPer>
 __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(const float* __restrict__ scores, int64_t ld,
                                                                    const int32_t* __restrict__ q_pos, int k,
                                                                    int n_chunks, TopkWs ws) {
   const int t = blockIdx.x / n_chunks;
   const int chunk = blockIdx.x - t * n_chunks;
   const int64_t n_t = (int64_t)q_pos[t] + 1;
-  const int64_t b0 = (int64_t)chunk * kChunk;
+  const int64_t b0 = (int64_t)chunk * (kPer * kHistThreads);
   if (n_t <= k || b0 >= n_t) return;      // take-all rows need no histogram
   __shared__ uint32_t h[kBins1];
   for (int i = threadIdx.x; i < kBins1; i += kHistThreads) h[i] = 0u;
@@ -79,13 +85,14 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(const float* __
     if (h[i]) atomicAdd(&gh[i], h[i]);
 }
 
+template <int kPer>
 __global__ __launch_bounds__(kHistThreads) void topk_compact_kernel(const float* __restrict__ scores, int64_t ld,
                                                                       const int32_t* __restrict__ q_pos, int k,
                                                                       int n_chunks, TopkWs ws) {
   const int t = blockIdx.x / n_chunks;
   const int chunk = blockIdx.x - t * n_chunks;
   const int64_t n_t = (int64_t)q_pos[t] + 1;
-  const int64_t b0 = (int64_t)chunk * kChunk;
+  const int64_t b0 = (int64_t)chunk * (kPer * kHistThreads);
   if (n_t <= k || b0 >= n_t) return;
   __shared__ __align__(16) uint32_t h[kBins1];
   __shared__ int sh_wave[kHistThreads / 64];
@@ -429,12 +436,22 @@ int32_t topk_zero_words(int32_t* p, int64_t n, hipStream_t stream) {
   return check_launch("topk_zero_kernel");
 }
 
+// Scores per thread of path 1's chunks for a batch of n_q rows of ld.
+static int topk_per(int32_t n_q, int64_t ld) {
+  const int64_t small = (ld + sa::kPerSmall * sa::kHistThreads - 1) / (sa::kPerSmall * sa::kHistThreads);
+  return small * n_q > sa::kManyChunks ? sa::kPerLarge : sa::kPerSmall;
+}
+
 // Everything after the first-digit histogram: compaction and finish.
-int32_t topk_after_hist(const float* scores, int64_t ld, const int32_t* q_pos, int32_t n_q, int32_t k, int32_t* idx,
-                        const sa::TopkWs& w, hipStream_t stream) {
-  const int n_chunks = (int)((ld + sa::kChunk - 1) / sa::kChunk);
-  hipLaunchKernelGGL(sa::topk_compact_kernel, dim3(n_chunks * n_q), dim3(sa::kHistThreads), 0, stream, scores, ld,
-                     q_pos, k, n_chunks, w);
+static int32_t topk_after_hist(const float* scores, int64_t ld, const int32_t* q_pos, int32_t n_q, int32_t k,
+                               int32_t* idx, const sa::TopkWs& w, int per, hipStream_t stream) {
+  const int n_chunks = (int)((ld + per * sa::kHistThreads - 1) / (per * sa::kHistThreads));
+  if (per == sa::kPerLarge)
+    hipLaunchKernelGGL(sa::topk_compact_kernel<sa::kPerLarge>, dim3(n_chunks * n_q), dim3(sa::kHistThreads), 0, stream,
+                       scores, ld, q_pos, k, n_chunks, w);
+  else
+    hipLaunchKernelGGL(sa::topk_compact_kernel<sa::kPerSmall>, dim3(n_chunks * n_q), dim3(sa::kHistThreads), 0, stream,
+                       scores, ld, q_pos, k, n_chunks, w);
   int32_t rc = check_launch("topk_compact_kernel");
   if (rc) return rc;
   hipLaunchKernelGGL(sa::topk_finish_kernel, dim3(n_q), dim3(sa::kFinThreads), 0, stream, scores, ld, q_pos, k, idx, w,
@@ -459,18 +476,23 @@ int32_t launch_topk(const float* scores, int64_t ld, const int32_t* q_pos, int32
   // 15.4 against 22.6 us; even at 16,384); path 1 from there on.
   if (algo == 0) algo = ld <= sa::kPath2MaxLd ? 2 : 1;
   sa::TopkWs w = topk_carve(ws, n_q, ld);
-  const int n_chunks = (int)((ld + sa::kChunk - 1) / sa::kChunk);
-  if ((int64_t)n_chunks * n_q > 0x7fffffff) {
+  const int per = topk_per(n_q, ld);
+  const int64_t n_chunks = (ld + per * sa::kHistThreads - 1) / (per * sa::kHistThreads);
+  if (n_chunks * n_q > 0x7fffffff) {
     set_error("topk: too many chunks");
     return SA_ERR_UNSUPPORTED;
   }
   if (algo == 1) {
     int32_t rc = cleared ? SA_OK : topk_zero(w, nullptr, 0, stream);
     if (rc) return rc;
-    hipLaunchKernelGGL(sa::topk_hist_kernel, dim3(n_chunks * n_q), dim3(sa::kHistThreads), 0, stream, scores, ld,
-                       q_pos, k, n_chunks, w);
+    if (per == sa::kPerLarge)
+      hipLaunchKernelGGL(sa::topk_hist_kernel<sa::kPerLarge>, dim3((unsigned)(n_chunks * n_q)), dim3(sa::kHistThreads),
+                         0, stream, scores, ld, q_pos, k, (int)n_chunks, w);
+    else
+      hipLaunchKernelGGL(sa::topk_hist_kernel<sa::kPerSmall>, dim3((unsigned)(n_chunks * n_q)), dim3(sa::kHistThreads),
+                         0, stream, scores, ld, q_pos, k, (int)n_chunks, w);
     if ((rc = check_launch("topk_hist_kernel"))) return rc;
-    return topk_after_hist(scores, ld, q_pos, n_q, k, idx, w, stream);
+    return topk_after_hist(scores, ld, q_pos, n_q, k, idx, w, per, stream);
   }
   hipLaunchKernelGGL(sa::topk_finish_kernel, dim3(n_q), dim3(sa::kFinThreads), 0, stream, scores, ld, q_pos, k, idx,
                      w, 1);

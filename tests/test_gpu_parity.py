@@ -106,6 +106,21 @@ def test_topk_rows_longer_than_the_bitmap(gpu_lib, kind):
         assert torch.equal(idx, api.topk_select(sc, q_pos, k=k, algo=2))
 
 
+@pytest.mark.parametrize("kind", ["normal", "quantised"])
+def test_topk_many_rows_large_chunks(gpu_lib, kind):
+    # 600 rows of 60,000: more than 4096 chunks of 8192, so path 1 reads 32
+    # scores per thread (chunks of 32,768, the last one ragged)
+    ld = 60000
+    sc = _synthetic_scores(kind, 600, ld, 29)
+    g = torch.Generator(device=DEV).manual_seed(31)
+    q_pos = torch.randint(20000, ld, (600,), generator=g, device=DEV, dtype=torch.int32)
+    q_pos[:3] = torch.tensor([ld - 1, 32767, 32768], dtype=torch.int32, device=DEV)
+    idx = api.topk_select(sc, q_pos, k=2048, algo=1)
+    assert torch.equal(idx, api.topk_select(sc, q_pos, k=2048, algo=2))
+    rows = [0, 1, 2, 100, 333, 599]
+    parity.check_topk_exact(to_numpy(sc), to_numpy(q_pos), 2048, to_numpy(idx), rows=rows)
+
+
 def test_topk_paths_agree_bitwise(gpu_lib):
     sc = _synthetic_scores("normal", 40, 131072, 3)
     q_pos = torch.randint(0, 131072, (40,), dtype=torch.int32, device=DEV)
