@@ -31,7 +31,7 @@
 //
 //   qgemm_skinny_kernel  decode batches (16 or 32 tokens per token block):
 //                        each wave streams its share of K (64-wide blocks w,
-//                        w + 4, ...) for 64 weight rows straight into MFMA
+//                        w + 4, ...) for 32 weight rows straight into MFMA
 //                        operand registers, 3 blocks in flight, no LDS and no
 //                        barrier in the loop; the 4 waves' partial tiles are
 //                        summed through LDS at the end.  HBM-bound on the

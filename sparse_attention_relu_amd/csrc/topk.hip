@@ -24,8 +24,9 @@
 //            candidates (composite keys); one atomic per workgroup and counter
 //            reserves the output slots.
 //   finish   one workgroup per row: the candidates go to LDS, a radix select
-//            finds the remaining count among them, and a bitonic sort puts the
-//            kept positions in ascending order.
+//            finds the remaining count among them, and the kept positions are
+//            put in ascending order by an LDS bitmap (rows up to 2^18
+//            positions) or a bitonic sort (longer rows).
 // Path 2 (one workgroup per row; the automatic choice for short rows, and the
 //   exact fallback of path 1 when the candidates overflow their capacity):
 //   three radix passes over the row give
