@@ -140,7 +140,8 @@ int32_t sa_indexer_score(const void* q_idx, const float* w, const void* k_idx,
  * idx[t, 0 .. k_eff) in ascending order and idx[t, k_eff .. k) = -1.
  * The result is deterministic.  NaN scores are not allowed.
  *
- *   scores  fp32  [n_q, ld]   (entries beyond q_pos[t] are not read)
+ *   scores  fp32  [n_q, ld]   (entries beyond q_pos[t] may hold anything: they
+ *                             may be read but never affect the result)
  *   q_pos   int32 [n_q]       0 <= q_pos[t] < ld
  *   k       1 .. 2048
  *   idx     int32 [n_q, k]    output

@@ -38,11 +38,13 @@ namespace sa {
 
 constexpr int kHistThreads = 1024;
 // Path 1 reads PER scores per thread, a chunk of PER x 1024 per workgroup:
-// 8 (8192-score chunks) for decode batches, 32 when the rows would give more
-// than kManyChunks workgroups (chunked prefill: 4096 rows of 131,072), where
-// each workgroup's fixed chain (its row's histogram, the bin search, the
-// slot reservation) would otherwise outweigh its share of the scores.
-constexpr int kPerSmall = 8, kPerLarge = 32;
+// 8 (8192-score chunks) for decode batches; when the rows would give more
+// than kManyChunks such workgroups (chunked prefill: 4096 rows of 131,072),
+// where each workgroup's fixed chain (its row's histogram, the bin search,
+// the slot reservation) would otherwise outweigh its share of the scores,
+// 32 in the histogram and 16 in the compaction (whose registers at 32 would
+// leave room for one workgroup per CU instead of two).
+constexpr int kPerSmall = 8, kPerLargeHist = 32, kPerLargeCompact = 16;
 constexpr int64_t kManyChunks = 4096;
 constexpr int kFinThreads = 1024;
 constexpr int kLdsCand = 8192;         // candidates staged in LDS by the finish kernel
@@ -58,25 +60,53 @@ __global__ void topk_zero_kernel(uint32_t* __restrict__ a, int64_t n_a, int32_t*
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_b; i += stride) b[i] = 0;
 }
 
+// Path 1's chunk loads: v[j] = row[b0 + threadIdx.x + kHistThreads j];
+// returns the row's length q_pos[t] + 1.  Small chunks (decode batches, one or
+// two workgroups per CU, each a chain of round trips) are requested beside the
+// length, one round trip instead of two: entries past the row's end are read
+// within the row stride and ignored.  Large chunks (many workgroups per CU
+// hide the chain) load after the length, as registers for 32 early loads
+// would halve the workgroups a CU holds.
+template <int kPer>
+__device__ __forceinline__ int64_t load_chunk(const float* row, int64_t b0, int64_t ld, const int32_t* qp_ptr,
+                                              float (&v)[kPer]) {
+  if constexpr (kPer == kPerSmall) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) v[j] = row[min(b0 + threadIdx.x + kHistThreads * j, ld - 1)];
+    const int qp = *qp_ptr;
+    // (the empty statements keep the compiler from sinking the loads behind
+    // the caller's branch on the length)
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) asm volatile("" ::"v"(v[j]));
+    asm volatile("" ::"s"(qp));
+    return (int64_t)qp + 1;
+  } else {
+    const int64_t n_t = (int64_t)*qp_ptr + 1;
+    if (b0 < n_t) {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int64_t s = b0 + threadIdx.x + kHistThreads * j;
+        v[j] = s < n_t ? row[s] : 0.f;
+      }
+    }
+    return n_t;
+  }
+}
+
 template <int kPer>
 __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(const float* __restrict__ scores, int64_t ld,
                                                                    const int32_t* __restrict__ q_pos, int k,
                                                                    int n_chunks, TopkWs ws) {
   const int t = blockIdx.x / n_chunks;
   const int chunk = blockIdx.x - t * n_chunks;
-  const int64_t n_t = (int64_t)q_pos[t] + 1;
   const int64_t b0 = (int64_t)chunk * (kPer * kHistThreads);
+  const float* row = scores + (int64_t)t * ld;
+  float v[kPer];
+  const int64_t n_t = load_chunk<kPer>(row, b0, ld, q_pos + t, v);
   if (n_t <= k || b0 >= n_t) return;      // take-all rows need no histogram
   __shared__ uint32_t h[kBins1];
   for (int i = threadIdx.x; i < kBins1; i += kHistThreads) h[i] = 0u;
   __syncthreads();
-  const float* row = scores + (int64_t)t * ld;
-  float v[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int64_t s = b0 + threadIdx.x + kHistThreads * j;
-    v[j] = s < n_t ? row[s] : 0.f;
-  }
 #pragma unroll
   for (int j = 0; j < kPer; ++j)
     if (b0 + threadIdx.x + kHistThreads * j < n_t) atomicAdd(&h[score_key(v[j]) >> 20], 1u);
@@ -92,25 +122,23 @@ __global__ __launch_bounds__(kHistThreads) void topk_compact_kernel(const float*
                                                                       int n_chunks, TopkWs ws) {
   const int t = blockIdx.x / n_chunks;
   const int chunk = blockIdx.x - t * n_chunks;
-  const int64_t n_t = (int64_t)q_pos[t] + 1;
   const int64_t b0 = (int64_t)chunk * (kPer * kHistThreads);
+  const float* row = scores + (int64_t)t * ld;
+  float v[kPer];
+  FirstHist<kHistThreads> fh;
+  if constexpr (kPer == kPerSmall) fh = load_first_hist<kHistThreads>(ws, t);   // beside the chunk
+  const int64_t n_t = load_chunk<kPer>(row, b0, ld, q_pos + t, v);
   if (n_t <= k || b0 >= n_t) return;
+  if constexpr (kPer != kPerSmall) fh = load_first_hist<kHistThreads>(ws, t);
   __shared__ __align__(16) uint32_t h[kBins1];
   __shared__ int sh_wave[kHistThreads / 64];
   __shared__ int sh_res[2];
   __shared__ int sh_base[2];
   int32_t* st = ws.state + (int64_t)t * ST_WORDS;
-  const float* row = scores + (int64_t)t * ld;
-  float v[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int64_t s = b0 + threadIdx.x + kHistThreads * j;
-    v[j] = s < n_t ? row[s] : 0.f;
-  }
   // Every workgroup of the row finds the bin of the k-th largest key from the
   // row's histogram (cheaper than a cross-workgroup handoff); chunk 0 records it.
   int above, n_cand;
-  const uint32_t bin = (uint32_t)first_digit_bin<kHistThreads>(ws, t, k, h, sh_wave, sh_res, &above, &n_cand);
+  const uint32_t bin = (uint32_t)first_digit_bin<kHistThreads>(fh, k, h, sh_wave, sh_res, &above, &n_cand);
   if (chunk == 0 && threadIdx.x == 0) {
     st[ST_B1] = (int)bin;
     st[ST_ABOVE] = above;
@@ -306,7 +334,26 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
                                                                     int32_t* __restrict__ idx, TopkWs ws,
                                                                     int force_exact) {
   const int t = blockIdx.x;
-  const int64_t n_t = (int64_t)q_pos[t] + 1;
+  // After path 1, everything the row may need is requested in one round
+  // trip, beside its length and counts: all kMaxTopk kept-position slots and
+  // the first kFinThreads candidate slots (cap >= kFinThreads); what lies
+  // past the counts is ignored.
+  const int32_t* sel = ws.sel + (int64_t)t * kMaxTopk;
+  const uint64_t* gcand = ws.cand + (int64_t)t * ws.cap;
+  int sv[kMaxTopk / kFinThreads] = {};
+  uint64_t cv0 = 0;
+  if (!force_exact) {
+#pragma unroll
+    for (int u = 0; u < kMaxTopk / kFinThreads; ++u) sv[u] = sel[threadIdx.x + kFinThreads * u];
+    cv0 = gcand[threadIdx.x];
+  }
+  const int32_t* st = ws.state + (int64_t)t * ST_WORDS;
+  const int st_ncand = st[ST_NCAND], st_above = st[ST_ABOVE], st_b1 = st[ST_B1];
+  const int qp = q_pos[t];
+  // (the empty statement keeps the compiler from sinking the count loads
+  // behind the branch on the row's length: all four arrive together)
+  asm volatile("" ::"s"(st_ncand), "s"(st_above), "s"(st_b1), "s"(qp));
+  const int64_t n_t = (int64_t)qp + 1;
   int32_t* out = idx + (int64_t)t * k;
   __shared__ __align__(16) uint32_t h[kBins1];
   __shared__ int v[2 * kFinThreads];
@@ -321,28 +368,21 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
   }
   const int k_eff = k;
   const float* row = scores + (int64_t)t * ld;
-  const int32_t* st = ws.state + (int64_t)t * ST_WORDS;
-  if (force_exact || st[ST_NCAND] > ws.cap) {
+  if (force_exact || st_ncand > ws.cap) {
     select_row_exact(row, n_t, k_eff, out, h, sh_wave, sh_res);
     return;
   }
   // Counts come from the compaction; clamped so that inconsistent workspace
   // contents cannot index out of range.
-  const int n_above = min(max(st[ST_ABOVE], 0), k_eff - 1);
-  const int n_cand = (int)min((int64_t)max(st[ST_NCAND], 0), ws.cap);
+  const int n_above = min(max(st_above, 0), k_eff - 1);
+  const int n_cand = (int)min((int64_t)max(st_ncand, 0), ws.cap);
   const bool in_lds = n_cand <= kLdsCand;
   const bool ordered_by_bitmap = n_t <= kBitmapBits;
-  const int32_t* sel = ws.sel + (int64_t)t * kMaxTopk;
-  const uint64_t* gcand = ws.cand + (int64_t)t * ws.cap;
   const int n_words = (int)((n_t + 31) >> 5);
-  // The kept positions (n_above < kMaxTopk = 2 x kFinThreads) are loaded
-  // beside the candidates, in one round trip.
-  int sv[kMaxTopk / kFinThreads];
+  // kept positions: n_above < kMaxTopk = 2 x kFinThreads
 #pragma unroll
-  for (int u = 0; u < kMaxTopk / kFinThreads; ++u) {
-    const int i = (int)threadIdx.x + kFinThreads * u;
-    sv[u] = i < n_above ? sel[i] : -1;
-  }
+  for (int u = 0; u < kMaxTopk / kFinThreads; ++u)
+    if ((int)threadIdx.x + kFinThreads * u >= n_above) sv[u] = -1;
   if (ordered_by_bitmap) {
     for (int i = threadIdx.x; i < n_words; i += kFinThreads) bm[i] = 0u;
   } else {
@@ -353,7 +393,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
     }
   }
   if (in_lds)
-    for (int i = threadIdx.x; i < n_cand; i += kFinThreads) lc[i] = gcand[i];
+    for (int i = threadIdx.x; i < n_cand; i += kFinThreads) lc[i] = i < kFinThreads ? cv0 : gcand[i];
   __syncthreads();
   if (ordered_by_bitmap)
 #pragma unroll
@@ -362,7 +402,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
       if (s >= 0 && s < n_t) atomicOr(&bm[s >> 5], 1u << (s & 31));
     }
   const uint64_t* cand = in_lds ? lc : gcand;
-  const Kept kept = select_candidates(cand, n_cand, (uint32_t)st[ST_B1], k_eff - n_above, h, sh_wave, sh_res);
+  const Kept kept = select_candidates(cand, n_cand, (uint32_t)st_b1, k_eff - n_above, h, sh_wave, sh_res);
   if (threadIdx.x == 0) sh_cnt = 0;
   __syncthreads();
   for (int i = threadIdx.x; i < n_cand; i += kFinThreads) {
@@ -391,6 +431,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
 namespace sa_host {
 
 static int64_t topk_cap(int64_t ld) {
+  static_assert(sa::kFinThreads <= 4096, "the finish kernel reads kFinThreads candidate slots unconditionally");
   int64_t cap = ld / 16;
   if (cap < 4096) cap = 4096;
   if (cap > 65536) cap = 65536;
@@ -437,22 +478,26 @@ int32_t topk_zero_words(int32_t* p, int64_t n, hipStream_t stream) {
   return check_launch("topk_zero_kernel");
 }
 
-// Scores per thread of path 1's chunks for a batch of n_q rows of ld.
-static int topk_per(int32_t n_q, int64_t ld) {
+// Whether a batch of n_q rows of ld takes path 1's large chunks.
+static bool topk_large_chunks(int32_t n_q, int64_t ld) {
   const int64_t small = (ld + sa::kPerSmall * sa::kHistThreads - 1) / (sa::kPerSmall * sa::kHistThreads);
-  return small * n_q > sa::kManyChunks ? sa::kPerLarge : sa::kPerSmall;
+  return small * n_q > sa::kManyChunks;
 }
+
+static int64_t topk_chunks(int64_t ld, int per) { return (ld + per * sa::kHistThreads - 1) / (per * sa::kHistThreads); }
 
 // Everything after the first-digit histogram: compaction and finish.
 static int32_t topk_after_hist(const float* scores, int64_t ld, const int32_t* q_pos, int32_t n_q, int32_t k,
-                               int32_t* idx, const sa::TopkWs& w, int per, hipStream_t stream) {
-  const int n_chunks = (int)((ld + per * sa::kHistThreads - 1) / (per * sa::kHistThreads));
-  if (per == sa::kPerLarge)
-    hipLaunchKernelGGL(sa::topk_compact_kernel<sa::kPerLarge>, dim3(n_chunks * n_q), dim3(sa::kHistThreads), 0, stream,
-                       scores, ld, q_pos, k, n_chunks, w);
-  else
+                               int32_t* idx, const sa::TopkWs& w, bool large, hipStream_t stream) {
+  if (large) {
+    const int n_chunks = (int)topk_chunks(ld, sa::kPerLargeCompact);
+    hipLaunchKernelGGL(sa::topk_compact_kernel<sa::kPerLargeCompact>, dim3(n_chunks * n_q), dim3(sa::kHistThreads), 0,
+                       stream, scores, ld, q_pos, k, n_chunks, w);
+  } else {
+    const int n_chunks = (int)topk_chunks(ld, sa::kPerSmall);
     hipLaunchKernelGGL(sa::topk_compact_kernel<sa::kPerSmall>, dim3(n_chunks * n_q), dim3(sa::kHistThreads), 0, stream,
                        scores, ld, q_pos, k, n_chunks, w);
+  }
   int32_t rc = check_launch("topk_compact_kernel");
   if (rc) return rc;
   hipLaunchKernelGGL(sa::topk_finish_kernel, dim3(n_q), dim3(sa::kFinThreads), 0, stream, scores, ld, q_pos, k, idx, w,
@@ -477,23 +522,26 @@ int32_t launch_topk(const float* scores, int64_t ld, const int32_t* q_pos, int32
   // 15.4 against 22.6 us; even at 16,384); path 1 from there on.
   if (algo == 0) algo = ld <= sa::kPath2MaxLd ? 2 : 1;
   sa::TopkWs w = topk_carve(ws, n_q, ld);
-  const int per = topk_per(n_q, ld);
-  const int64_t n_chunks = (ld + per * sa::kHistThreads - 1) / (per * sa::kHistThreads);
-  if (n_chunks * n_q > 0x7fffffff) {
+  const bool large = topk_large_chunks(n_q, ld);
+  // (the compaction's chunks are the smaller ones)
+  if (topk_chunks(ld, large ? sa::kPerLargeCompact : sa::kPerSmall) * n_q > 0x7fffffff) {
     set_error("topk: too many chunks");
     return SA_ERR_UNSUPPORTED;
   }
   if (algo == 1) {
     int32_t rc = cleared ? SA_OK : topk_zero(w, nullptr, 0, stream);
     if (rc) return rc;
-    if (per == sa::kPerLarge)
-      hipLaunchKernelGGL(sa::topk_hist_kernel<sa::kPerLarge>, dim3((unsigned)(n_chunks * n_q)), dim3(sa::kHistThreads),
-                         0, stream, scores, ld, q_pos, k, (int)n_chunks, w);
-    else
+    if (large) {
+      const int64_t n_chunks = topk_chunks(ld, sa::kPerLargeHist);
+      hipLaunchKernelGGL(sa::topk_hist_kernel<sa::kPerLargeHist>, dim3((unsigned)(n_chunks * n_q)),
+                         dim3(sa::kHistThreads), 0, stream, scores, ld, q_pos, k, (int)n_chunks, w);
+    } else {
+      const int64_t n_chunks = topk_chunks(ld, sa::kPerSmall);
       hipLaunchKernelGGL(sa::topk_hist_kernel<sa::kPerSmall>, dim3((unsigned)(n_chunks * n_q)), dim3(sa::kHistThreads),
                          0, stream, scores, ld, q_pos, k, (int)n_chunks, w);
+    }
     if ((rc = check_launch("topk_hist_kernel"))) return rc;
-    return topk_after_hist(scores, ld, q_pos, n_q, k, idx, w, per, stream);
+    return topk_after_hist(scores, ld, q_pos, n_q, k, idx, w, large, stream);
   }
   hipLaunchKernelGGL(sa::topk_finish_kernel, dim3(n_q), dim3(sa::kFinThreads), 0, stream, scores, ld, q_pos, k, idx,
                      w, 1);

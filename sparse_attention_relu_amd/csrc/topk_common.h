@@ -95,18 +95,30 @@ __device__ int find_bin(const uint32_t* hist, int need, int* above_out, int* sh_
 
 // Locate the bin of the k-th largest key from a row's complete first-digit
 // histogram (built by an earlier kernel, so plain loads see it).  NT threads;
-// h (kBins1 entries of LDS) receives the histogram.  Returns the bin; *above =
-// keys in higher bins, *n_cand = keys in the bin.
+// each holds kBins1 / 4 / NT groups of four bins, requested by
+// load_first_hist; first_digit_bin puts them in h (kBins1 entries of LDS),
+// returns the bin and writes *above = keys in higher bins, *n_cand = keys in
+// the bin.
 template <int NT>
-__device__ int first_digit_bin(const TopkWs& ws, int t, int k, uint32_t* h, int* sh_wave, int* sh_res, int* above,
-                               int* n_cand) {
+struct FirstHist {
+  u32x4 q[kBins1 / 4 / NT];
+};
+
+template <int NT>
+__device__ __forceinline__ FirstHist<NT> load_first_hist(const TopkWs& ws, int t) {
   const u32x4* gh = reinterpret_cast<const u32x4*>(ws.hist + (int64_t)t * kBins1);
+  FirstHist<NT> r;
+#pragma unroll
+  for (int i = 0; i < kBins1 / 4 / NT; ++i) r.q[i] = gh[threadIdx.x + NT * i];
+  return r;
+}
+
+template <int NT>
+__device__ int first_digit_bin(const FirstHist<NT>& fh, int k, uint32_t* h, int* sh_wave, int* sh_res, int* above,
+                               int* n_cand) {
   u32x4* hh = reinterpret_cast<u32x4*>(h);
-  u32x4 tmp[kBins1 / 4 / NT];
 #pragma unroll
-  for (int i = 0; i < kBins1 / 4 / NT; ++i) tmp[i] = gh[threadIdx.x + NT * i];
-#pragma unroll
-  for (int i = 0; i < kBins1 / 4 / NT; ++i) hh[threadIdx.x + NT * i] = tmp[i];
+  for (int i = 0; i < kBins1 / 4 / NT; ++i) hh[threadIdx.x + NT * i] = fh.q[i];
   __syncthreads();
   const int d = find_bin<NT, kBins1>(h, k, above, sh_wave, sh_res);
   *n_cand = (int)h[d];
