@@ -92,9 +92,21 @@ __global__ __launch_bounds__(kCwWaves * 64) void cache_write_kernel(CacheWriteAr
   const int t = blockIdx.x * kCwWaves + (threadIdx.x >> 6);
   if (t >= A.n) return;                    // whole waves leave together
   const int lane = threadIdx.x & 63;
+  const uint16_t* src = A.kv_a + (int64_t)t * kRow;
+  // Every load is issued first, so the token costs one round trip (the
+  // stores below could alias the inputs as far as the compiler knows, so it
+  // would not move later loads above them).
   const int p = A.pos[t];
   const int64_t row = A.dst[t];
-  const uint16_t* src = A.kv_a + (int64_t)t * kRow;
+  const u32x4 xv = ld16(src + 8 * lane);                                      // latent 8l .. 8l + 7
+  const u32x4 gv = ld16(A.gamma + 8 * lane);
+  const uint32_t kv = *reinterpret_cast<const uint32_t*>(src + kLatent + 2 * (lane & 31));   // rope pair l % 32
+  uint32_t kr = 0, wv = 0, bv = 0;                                            // indexer dims 2l, 2l + 1
+  if (A.k_raw) {
+    kr = *reinterpret_cast<const uint32_t*>(A.k_raw + (int64_t)t * kIdxDim + 2 * lane);
+    wv = *reinterpret_cast<const uint32_t*>(A.ln_w + 2 * lane);
+    bv = *reinterpret_cast<const uint32_t*>(A.ln_b + 2 * lane);
+  }
   uint16_t* out = A.kv_cache + row * kRow;
   // Lane l turns pair l % 32: lanes 0..31 for the rope key, 32..63 for the
   // indexer key's last 64 dims; one sine and cosine per lane.
@@ -102,8 +114,6 @@ __global__ __launch_bounds__(kCwWaves * 64) void cache_write_kernel(CacheWriteAr
   turn_sincos(p, A.inv_freq[lane & 31], sn, cs);
 
   // Latent: lane l holds values 8l .. 8l + 7.
-  const u32x4 xv = ld16(src + 8 * lane);
-  const u32x4 gv = ld16(A.gamma + 8 * lane);
   double x[8], g[8];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -123,18 +133,14 @@ __global__ __launch_bounds__(kCwWaves * 64) void cache_write_kernel(CacheWriteAr
 
   // Rope key: lane i < 32 turns pair i.
   if (lane < kRope / 2) {
-    const uint32_t kv = *reinterpret_cast<const uint32_t*>(src + kLatent + 2 * lane);
     double k0 = bf16_to_f64(kv & 0xffffu), k1 = bf16_to_f64(kv >> 16);
     rope_pair(k0, k1, sn, cs);
     *reinterpret_cast<uint32_t*>(out + kLatent + 2 * lane) = pack2(k0, k1);
   }
 
-  // Indexer key: lane l holds dims 2l, 2l + 1; lanes 32..63 (dims 64..127) turn
-  // pair l - 32.
+  // Indexer key: LayerNorm over the 128 dims, then lanes 32..63 (dims
+  // 64..127) turn pair l - 32.
   if (A.k_raw) {
-    const uint32_t kr = *reinterpret_cast<const uint32_t*>(A.k_raw + (int64_t)t * kIdxDim + 2 * lane);
-    const uint32_t wv = *reinterpret_cast<const uint32_t*>(A.ln_w + 2 * lane);
-    const uint32_t bv = *reinterpret_cast<const uint32_t*>(A.ln_b + 2 * lane);
     const double a0 = bf16_to_f64(kr & 0xffffu), a1 = bf16_to_f64(kr >> 16);
     const double mean = wave_sum(a0 + a1) / (double)kIdxDim;
     const double d0 = a0 - mean, d1 = a1 - mean;
