@@ -26,7 +26,9 @@
 //   finish   one workgroup per row: the candidates go to LDS, a radix select
 //            finds the remaining count among them, and the kept positions are
 //            put in ascending order by an LDS bitmap (rows up to 2^18
-//            positions) or a bitonic sort (longer rows).
+//            positions), a two-level bitmap (one 128-bit map per occupied
+//            bucket of 128 positions, rows up to 2^20) or a bitonic sort
+//            (longer rows).
 // Path 2 (one workgroup per row; the automatic choice for short rows, and the
 //   exact fallback of path 1 when the candidates overflow their capacity):
 //   three radix passes over the row give
@@ -48,10 +50,17 @@ constexpr int kPerSmall = 8, kPerLargeHist = 32, kPerLargeCompact = 16;
 constexpr int64_t kManyChunks = 4096;
 constexpr int kFinThreads = 1024;
 constexpr int kLdsCand = 8192;         // candidates staged in LDS by the finish kernel
+constexpr int kPreCand = 1024;         // candidate slots the finish kernel requests with the counts
 constexpr int kFinBins = 2048;         // 11-bit digits in the finish kernel
 constexpr int kBitmapBits = 1 << 18;   // rows up to this length are emitted in order from an LDS bitmap
+constexpr int kSparseSpan = 128;       // longer rows, up to kSparseBits: buckets of 128 positions,
+constexpr int kSparseWords = kSparseSpan / 32;
+constexpr int kSparseBits = 1 << 20;   // one 4-word bitmap per occupied bucket
+constexpr int kSparseBuckets = kSparseBits / kSparseSpan;
 constexpr int64_t kPath2MaxLd = 12288; // the automatic choice takes path 2 for rows up to this length
 static_assert(kMaxTopk % kFinThreads == 0, "the finish kernel loads the kept positions in whole rounds");
+static_assert(kSparseBuckets <= kBitmapBits / 32 && kSparseWords * kMaxTopk <= 2 * kLdsCand && kMaxTopk <= kBins1,
+              "the two-level bitmap reuses the bitmap, candidate and histogram arrays");
 
 // ----------------------------------------------------------------- path 1
 __global__ void topk_zero_kernel(uint32_t* __restrict__ a, int64_t n_a, int32_t* __restrict__ b, int64_t n_b) {
@@ -307,26 +316,73 @@ __device__ Kept select_candidates(const uint64_t* cand, int n_cand, uint32_t b1,
   return Kept{prefix, mask};
 }
 
-// Ascending emission of the positions set in bm[0 .. n_words): thread i owns a
-// run of words; a prefix sum of their popcounts gives its first output slot.
-// Slots past the set bits (up to k) get -1.
-__device__ void emit_bitmap(const uint32_t* bm, int n_words, int32_t* __restrict__ out, int k, int* sh_wave) {
+// Ascending emission of the positions set in words[0 .. n_words), bit j of
+// word i standing for position base(i) + j (base increasing with i): thread i
+// owns a run of words; a prefix sum of their popcounts gives its first output
+// slot.  Slots past the set bits (up to k) get -1.
+template <class Base>
+__device__ void emit_words(const uint32_t* words, int n_words, Base base, int32_t* __restrict__ out, int k,
+                           int* sh_wave) {
   const int per = (n_words + kFinThreads - 1) / kFinThreads;
   const int w0 = min((int)threadIdx.x * per, n_words), w1 = min(w0 + per, n_words);
   int cnt = 0;
-  for (int i = w0; i < w1; ++i) cnt += __popc(bm[i]);
+  for (int i = w0; i < w1; ++i) cnt += __popc(words[i]);
   int total;
   int slot = block_inclusive_scan<kFinThreads>(cnt, sh_wave, &total) - cnt;
   for (int i = w0; i < w1; ++i) {
-    uint32_t bits = bm[i];
+    uint32_t bits = words[i];
+    const int b0 = base(i);
     while (bits) {
       const int b = __ffs(bits) - 1;
       bits &= bits - 1;
-      if (slot >= 0 && slot < k) out[slot] = (i << 5) + b;
+      if (slot >= 0 && slot < k) out[slot] = b0 + b;
       ++slot;
     }
   }
   for (int i = total + threadIdx.x; i < k; i += kFinThreads) out[i] = -1;
+}
+
+// Ascending emission of the distinct positions v[0 .. n_v) (n_v <= kMaxTopk)
+// of a row of n_t <= kSparseBits positions, through a two-level bitmap: the
+// 128-position buckets that hold a position are flagged (flag: kSparseBuckets
+// words), numbered in order by a prefix sum (bucket_of: the bucket of each
+// number, at most n_v of them), and each position sets its bit in the 4-word
+// bitmap of its bucket's number (words: 4 kMaxTopk words); the words are then
+// emitted in order.  Entries outside [0, n_t) are dropped.
+__device__ void emit_sparse(const int* v, int n_v, int64_t n_t, uint32_t* flag, uint32_t* words, int* bucket_of,
+                            int32_t* __restrict__ out, int k, int* sh_wave) {
+  const int n_b = (int)((n_t + kSparseSpan - 1) / kSparseSpan);
+  for (int i = threadIdx.x; i < n_b; i += kFinThreads) flag[i] = 0u;
+  for (int i = threadIdx.x; i < kSparseWords * kMaxTopk; i += kFinThreads) words[i] = 0u;
+  __syncthreads();
+  for (int i = threadIdx.x; i < n_v; i += kFinThreads) {
+    const int p = v[i];
+    if (p >= 0 && p < n_t) flag[p / kSparseSpan] = 1u;
+  }
+  __syncthreads();
+  // thread i numbers a run of buckets; a flag becomes its bucket's number
+  const int per = (n_b + kFinThreads - 1) / kFinThreads;
+  const int b0 = min((int)threadIdx.x * per, n_b), b1 = min(b0 + per, n_b);
+  int cnt = 0;
+  for (int b = b0; b < b1; ++b) cnt += (int)flag[b];
+  int n_used;
+  int num = block_inclusive_scan<kFinThreads>(cnt, sh_wave, &n_used) - cnt;
+  for (int b = b0; b < b1; ++b)
+    if (flag[b]) {
+      flag[b] = (uint32_t)num;
+      bucket_of[num] = b;
+      ++num;
+    }
+  __syncthreads();
+  for (int i = threadIdx.x; i < n_v; i += kFinThreads) {
+    const int p = v[i];
+    if (p >= 0 && p < n_t)
+      atomicOr(&words[kSparseWords * flag[p / kSparseSpan] + (p % kSparseSpan) / 32], 1u << (p & 31));
+  }
+  __syncthreads();
+  emit_words(words, kSparseWords * n_used,
+             [&](int i) { return bucket_of[i / kSparseWords] * kSparseSpan + (i % kSparseWords) * 32; }, out, k,
+             sh_wave);
 }
 
 __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* __restrict__ scores, int64_t ld,
@@ -336,16 +392,17 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
   const int t = blockIdx.x;
   // After path 1, everything the row may need is requested in one round
   // trip, beside its length and counts: all kMaxTopk kept-position slots and
-  // the first kFinThreads candidate slots (cap >= kFinThreads); what lies
-  // past the counts is ignored.
+  // the first kPreCand candidate slots (cap >= kPreCand); what lies past the
+  // counts is ignored.
   const int32_t* sel = ws.sel + (int64_t)t * kMaxTopk;
   const uint64_t* gcand = ws.cand + (int64_t)t * ws.cap;
   int sv[kMaxTopk / kFinThreads] = {};
-  uint64_t cv0 = 0;
+  uint64_t cv[kPreCand / kFinThreads] = {};
   if (!force_exact) {
 #pragma unroll
     for (int u = 0; u < kMaxTopk / kFinThreads; ++u) sv[u] = sel[threadIdx.x + kFinThreads * u];
-    cv0 = gcand[threadIdx.x];
+#pragma unroll
+    for (int u = 0; u < kPreCand / kFinThreads; ++u) cv[u] = gcand[threadIdx.x + kFinThreads * u];
   }
   const int32_t* st = ws.state + (int64_t)t * ST_WORDS;
   const int st_ncand = st[ST_NCAND], st_above = st[ST_ABOVE], st_b1 = st[ST_B1];
@@ -392,8 +449,14 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
       if (i < n_above) v[i] = sv[u];
     }
   }
-  if (in_lds)
-    for (int i = threadIdx.x; i < n_cand; i += kFinThreads) lc[i] = i < kFinThreads ? cv0 : gcand[i];
+  if (in_lds) {
+#pragma unroll
+    for (int u = 0; u < kPreCand / kFinThreads; ++u) {
+      const int i = (int)threadIdx.x + kFinThreads * u;
+      if (i < n_cand) lc[i] = cv[u];
+    }
+    for (int i = kPreCand + threadIdx.x; i < n_cand; i += kFinThreads) lc[i] = gcand[i];
+  }
   __syncthreads();
   if (ordered_by_bitmap)
 #pragma unroll
@@ -418,12 +481,17 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
     }
   }
   __syncthreads();
+  if (!ordered_by_bitmap && n_t <= kSparseBits) {
+    const int n_v = min(n_above + sh_cnt, k_eff);
+    emit_sparse(v, n_v, n_t, bm, reinterpret_cast<uint32_t*>(lc), reinterpret_cast<int*>(h), out, k, sh_wave);
+    return;
+  }
   if (!ordered_by_bitmap) {
     bitonic_sort_2048(v, k_eff);
     for (int i = threadIdx.x; i < k; i += kFinThreads) out[i] = i < k_eff ? v[i] : -1;
     return;
   }
-  emit_bitmap(bm, n_words, out, k, sh_wave);
+  emit_words(bm, n_words, [](int i) { return i << 5; }, out, k, sh_wave);
 }
 
 }  // namespace sa
@@ -431,7 +499,8 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
 namespace sa_host {
 
 static int64_t topk_cap(int64_t ld) {
-  static_assert(sa::kFinThreads <= 4096, "the finish kernel reads kFinThreads candidate slots unconditionally");
+  static_assert(sa::kPreCand <= 4096 && sa::kPreCand % sa::kFinThreads == 0,
+                "the finish kernel reads kPreCand candidate slots unconditionally");
   int64_t cap = ld / 16;
   if (cap < 4096) cap = 4096;
   if (cap > 65536) cap = 65536;

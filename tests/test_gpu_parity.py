@@ -93,9 +93,9 @@ def test_topk_ties_and_edges(gpu_lib, kind, algo):
 
 @pytest.mark.parametrize("kind", ["normal", "quantised", "spiky"])
 def test_topk_rows_longer_than_the_bitmap(gpu_lib, kind):
-    # rows of 262,145..900,000 positions: longer than the finish kernel's LDS
-    # bitmap, so the kept positions are put in order by sorting; the exact
-    # path must agree bitwise
+    # rows of 262,145..900,000 positions: longer than the finish kernel's
+    # one-level LDS bitmap, so the kept positions are put in order through the
+    # two-level one (128-position buckets); the exact path must agree bitwise
     ld = 900000
     sc = _synthetic_scores(kind, 5, ld, 13)
     q_pos = torch.tensor([262144, 262143 + 2048, 524290, 786431, ld - 1], dtype=torch.int32, device=DEV)
@@ -106,10 +106,43 @@ def test_topk_rows_longer_than_the_bitmap(gpu_lib, kind):
         assert torch.equal(idx, api.topk_select(sc, q_pos, k=k, algo=2))
 
 
+def test_topk_rows_beyond_the_two_level_bitmap(gpu_lib):
+    # rows longer than 2^20 positions: the kept positions are sorted instead
+    ld = 1200000
+    sc = _synthetic_scores("normal", 2, ld, 17)
+    q_pos = torch.tensor([1048576, ld - 1], dtype=torch.int32, device=DEV)
+    idx = api.topk_select(sc, q_pos, k=2048, algo=1)
+    torch.cuda.synchronize()
+    parity.check_topk_exact(to_numpy(sc), to_numpy(q_pos), 2048, to_numpy(idx))
+    assert torch.equal(idx, api.topk_select(sc, q_pos, k=2048, algo=2))
+
+
+def test_topk_clustered_selection(gpu_lib):
+    # selections made of dense windows (whole 128-position buckets kept, a
+    # window across a bucket boundary, one at the row's start and one ending
+    # at its last position) plus scattered positions, for rows on both sides
+    # of 2^18 and up to 2^20 positions
+    ld = 1048576
+    g = torch.Generator(device=DEV).manual_seed(41)
+    sc = torch.randn((4, ld), generator=g, device=DEV)
+    q_pos = torch.tensor([200000, 700000, ld - 1, 300000], dtype=torch.int32, device=DEV)
+    windows = [(0, [(0, 1500)]), (1, [(300000, 301500)]), (2, [(ld - 1200, ld), (128 * 1000 - 37, 128 * 1000 + 500)]),
+               (3, [(299000 - 1700, 299000)])]
+    for r, ws in windows:
+        for a, b in ws:
+            sc[r, a:b] += 10.0
+    for k in (2048, 1600):
+        idx = api.topk_select(sc, q_pos, k=k, algo=1)
+        torch.cuda.synchronize()
+        parity.check_topk_exact(to_numpy(sc), to_numpy(q_pos), k, to_numpy(idx))
+        assert torch.equal(idx, api.topk_select(sc, q_pos, k=k, algo=2))
+
+
 @pytest.mark.parametrize("kind", ["normal", "quantised"])
 def test_topk_many_rows_large_chunks(gpu_lib, kind):
     # 600 rows of 60,000: more than 4096 chunks of 8192, so path 1 reads 32
-    # scores per thread (chunks of 32,768, the last one ragged)
+    # scores per thread in the histogram (chunks of 32,768) and 16 in the
+    # compaction (16,384), the last chunk of each row ragged
     ld = 60000
     sc = _synthetic_scores(kind, 600, ld, 29)
     g = torch.Generator(device=DEV).manual_seed(31)
