@@ -36,10 +36,12 @@
 //                        barrier in the loop; the 4 waves' partial tiles are
 //                        summed through LDS at the end.  HBM-bound on the
 //                        weights.
-//   qgemm_tiled_kernel   prefill batches: 128 weight rows x 128 tokens per
-//                        workgroup, 64-wide K chunks staged in LDS by direct
-//                        global -> LDS loads (two stages, one chunk ahead),
-//                        2 x 2 waves of 64 x 64.  MFMA-bound.
+//   qgemm_tiled_kernel   prefill batches: 128 or 256 weight rows x 128 tokens
+//                        per workgroup, K chunks staged in LDS by direct
+//                        global -> LDS loads (a ring of stages), waves of
+//                        64 x 64: 128 x 128 tiles and 64-wide chunks in two
+//                        stages for the projection, 256 x 128 tiles and
+//                        32-wide chunks in three stages for the absorption.
 #include <atomic>
 #include <cmath>
 
@@ -126,7 +128,7 @@ __device__ __forceinline__ void q_store4(const QArgs& A, const QSeg& S, int b, i
 
 // The 64-value rope part of each token of the block (absorption only).
 __device__ __forceinline__ void q_copy_rope(const QArgs& A, int b, int n0, int n_tok) {
-  for (int i = threadIdx.x; i < n_tok * 8; i += kQThreads) {
+  for (int i = threadIdx.x; i < n_tok * 8; i += blockDim.x) {
     const int t = n0 + (i >> 3);
     if (t >= A.n) continue;
     const u32x4 v = ld16(A.copy_src + (int64_t)b * A.copy_src_batch + (int64_t)t * A.copy_src_ld + (i & 7) * 8);
@@ -245,57 +247,89 @@ __global__ __launch_bounds__(kQThreads) void qgemm_skinny_kernel(QArgs A) {
 }
 
 // ----------------------------------------------------------- prefill batches
-// 128 weight rows x 128 tokens per workgroup (4 waves of 64 x 64), K in
-// kTiBK-wide chunks through a ring of kTiStages LDS stages filled by direct
-// global -> LDS loads, kTiStages - 1 chunks ahead of the products.  A stage
-// holds each row's kTiBK values as 16-byte chunks, chunk c of row r at slot
-// ti_slot(r, c): the 8 lanes of each 128-byte phase of an operand read hit
-// 32 different banks.
-constexpr int kTiBM = 128, kTiBN = 128, kTiBK = 64;
-constexpr int kTiStages = 2;                           // two workgroups per CU beat deeper rings (fewer waves)
-constexpr int kTiTM = kTiBM / 32, kTiTN = kTiBN / 32;  // 16x16 tiles per wave (2 x 2 waves)
-constexpr int kTiRowB = kTiBK * 2;                     // bytes per staged row
-constexpr int kTiChunks = kTiRowB / 16;                // 16-byte chunks per staged row
-constexpr int kTiStageB = (kTiBM + kTiBN) * kTiRowB;
-constexpr int kTiLoads = kTiStageB / 16 / kQThreads;   // 16-byte direct loads per thread per stage
-constexpr size_t kTiSmem = (size_t)kTiStages * kTiStageB;   // 64 KB: two workgroups per CU
-static_assert(kTiChunks == 4 || kTiChunks == 8, "64- or 128-byte rows");
-__device__ __forceinline__ int ti_slot(int r, int c) { return kTiChunks == 8 ? c ^ (r & 7) : c ^ ((r >> 1) & 3); }
+// BM weight rows x 128 tokens per workgroup (BM / 64 x 2 waves of 64 x 64), K
+// in BK-wide chunks through a ring of STAGES LDS stages filled by direct
+// global -> LDS loads, STAGES - 1 chunks ahead of the products.  A stage
+// holds each row's BK values as 16-byte chunks, chunk c of row r at slot
+// ti_slot(r, c): the lanes of each 128-byte phase of an operand read hit 32
+// different banks.
+// (launch bounds: WPC workgroups of (BM / 64) x 2 waves per CU)
+template <int BM>
+constexpr int ti_threads() { return 64 * (BM / 64) * 2; }
+template <int BM, int WPC>
+constexpr int ti_waves_per_simd() { return (BM / 64) * 2 * WPC / 4; }
 
-__global__ __launch_bounds__(kQThreads) void qgemm_tiled_kernel(QArgs A) {
+template <int BM, int BK, int STAGES>
+struct TiCfg {
+  static constexpr int kBN = 128;
+  static constexpr int kWM = BM / 64;                  // wave rows
+  static constexpr int kWaves = kWM * (kBN / 64);
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kRowB = BK * 2;                 // bytes per staged row
+  static constexpr int kChunks = kRowB / 16;           // 16-byte chunks per staged row
+  static constexpr int kStageB = (BM + kBN) * kRowB;
+  static constexpr int kLoads = kStageB / 16 / kThreads;   // 16-byte direct loads per thread per stage
+  static constexpr size_t kSmem = (size_t)STAGES * kStageB;
+  static_assert(kChunks == 4 || kChunks == 8, "64- or 128-byte rows");
+  static_assert(kStageB % (1024 * kWaves) == 0, "whole 1 KB loads per wave");
+  static_assert(STAGES >= 2, "at least one chunk ahead");
+  static_assert(kThreads == ti_threads<BM>(), "launch bounds");
+};
+constexpr int kTiTM = 4, kTiTN = 4;                     // 16x16 tiles per wave (64 x 64)
+
+// Configurations (interleaved A/B at 4096 tokens, identical outputs):
+// the projection (K = 2048) takes 128 x 128 tiles, 64-wide chunks in two
+// stages, two workgroups per CU: 473 us, against 520-723 us for 32-wide chunks
+// (2-4 stages, 2-4 workgroups per CU) or 256-row tiles.  The absorption
+// (K = 192 per head, three chunks: the tile's fixed costs dominate) takes
+// 256 x 128 tiles, 32-wide chunks in three stages, two workgroups per CU:
+// 222 against 253 us.
+struct TiProject {
+  static constexpr int kBM = 128, kBK = 64, kStages = 2, kWpc = 2;
+};
+struct TiAbsorb {
+  static constexpr int kBM = 256, kBK = 32, kStages = 3, kWpc = 2;
+};
+
+template <int BM, int BK, int STAGES, int WPC>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, ti_threads<BM>()),
+                          amdgpu_waves_per_eu(ti_waves_per_simd<BM, WPC>()))) void qgemm_tiled_kernel(QArgs A) {
+  using C = TiCfg<BM, BK, STAGES>;
+  constexpr int kCh = C::kChunks;
+  auto ti_slot = [](int r, int c) { return kCh == 8 ? c ^ (r & 7) : c ^ ((r >> 1) & 3); };
   extern __shared__ __align__(16) uint8_t qsm[];
   int mb = blockIdx.x;
   const int si = q_segment(A, mb);
   const QSeg& S = si == 0 ? A.seg[0] : (si == 1 ? A.seg[1] : A.seg[2]);
   const int b = blockIdx.z;
-  const int m0 = mb * kTiBM, n0 = blockIdx.y * kTiBN;
+  const int m0 = mb * BM, n0 = blockIdx.y * C::kBN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % C::kWM, wn = wave / C::kWM;
   const int l16 = lane & 15, kg = lane >> 4;
-  if (A.copy_dst && mb == 0) q_copy_rope(A, b, n0, kTiBN);
+  if (A.copy_dst && mb == 0) q_copy_rope(A, b, n0, C::kBN);
   const uint16_t* W = S.w + (int64_t)b * A.w_batch;
   const uint16_t* X = A.x + (int64_t)b * A.x_batch;
   // Load u of this wave fills the 1 KB of staged rows from row
-  // (1024 / kTiRowB) (4 u + wave) on (rows 0..127 weights, 128..255 tokens):
-  // lane p -> row + p / kTiChunks, slot p % kTiChunks, which holds the chunk
-  // that ti_slot maps there.
-  const uint16_t* src[kTiLoads];
-  int dst[kTiLoads];
+  // (1024 / kRowB) (kWaves u + wave) on (rows 0..BM-1 weights, then tokens):
+  // lane p -> row + p / kChunks, slot p % kChunks, which holds the chunk that
+  // ti_slot maps there.
+  const uint16_t* src[C::kLoads];
+  int dst[C::kLoads];
 #pragma unroll
-  for (int u = 0; u < kTiLoads; ++u) {
-    const int row = (1024 / kTiRowB) * (4 * u + wave) + lane / kTiChunks;
-    const int chunk = ti_slot(row, lane % kTiChunks);      // (the mapping is its own inverse)
-    src[u] = row < kTiBM ? W + (int64_t)min(m0 + row, S.rows - 1) * A.lda + 8 * chunk
-                         : X + (int64_t)min(n0 + row - kTiBM, A.n - 1) * A.ldx + 8 * chunk;
-    dst[u] = 1024 * (4 * u + wave);                      // the instruction's 1 KB, lane p at + 16 p
+  for (int u = 0; u < C::kLoads; ++u) {
+    const int row = (1024 / C::kRowB) * (C::kWaves * u + wave) + lane / kCh;
+    const int chunk = ti_slot(row, lane % kCh);          // (the mapping is its own inverse)
+    src[u] = row < BM ? W + (int64_t)min(m0 + row, S.rows - 1) * A.lda + 8 * chunk
+                      : X + (int64_t)min(n0 + row - BM, A.n - 1) * A.ldx + 8 * chunk;
+    dst[u] = 1024 * (C::kWaves * u + wave);              // the instruction's 1 KB, lane p at + 16 p
   }
-  const int nk = A.K / kTiBK;
+  const int nk = A.K / BK;
   auto issue = [&](int kc) {                             // chunk kc (clamped) into its stage
     const int kk = min(kc, nk - 1);
-    uint8_t* st = qsm + (size_t)(kc % kTiStages) * kTiStageB;
+    uint8_t* st = qsm + (size_t)(kc % STAGES) * C::kStageB;
 #pragma unroll
-    for (int u = 0; u < kTiLoads; ++u)
-      __builtin_amdgcn_global_load_lds((const void*)(src[u] + kk * kTiBK),
+    for (int u = 0; u < C::kLoads; ++u)
+      __builtin_amdgcn_global_load_lds((const void*)(src[u] + kk * BK),
                                        (__attribute__((address_space(3))) void*)(st + dst[u]), 16, 0, 0);
   };
   f32x4 acc[kTiTM][kTiTN];
@@ -304,29 +338,29 @@ __global__ __launch_bounds__(kQThreads) void qgemm_tiled_kernel(QArgs A) {
 #pragma unroll
     for (int tn = 0; tn < kTiTN; ++tn) acc[tm][tn] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int c = 0; c < kTiStages - 1; ++c) issue(c);
-  SA_WAIT_VMCNT(kTiLoads * (kTiStages - 2));            // chunk 0 is in
+  for (int c = 0; c < STAGES - 1; ++c) issue(c);
+  SA_WAIT_VMCNT(C::kLoads * (STAGES - 2));               // chunk 0 is in
   __syncthreads();
-  // operand rows of this lane: weight row wm 64 + 16 tm + l16, token row
-  // 128 + wn 64 + 16 tn + l16; chunk 4 s + kg
-  const int rA = wm * 16 * kTiTM + l16, rB = kTiBM + wn * 16 * kTiTN + l16;
+  // operand rows of this lane: weight row 64 wm + 16 tm + l16, token row
+  // BM + 64 wn + 16 tn + l16; chunk 4 s + kg
+  const int rA = 64 * wm + l16, rB = BM + 64 * wn + l16;
 #pragma unroll 1
   for (int kc = 0; kc < nk; ++kc) {
-    issue(kc + kTiStages - 1);                           // into the stage read at kc - 1
-    const uint8_t* st = qsm + (size_t)(kc % kTiStages) * kTiStageB;
+    issue(kc + STAGES - 1);                              // into the stage read at kc - 1
+    const uint8_t* st = qsm + (size_t)(kc % STAGES) * C::kStageB;
 #pragma unroll
-    for (int s = 0; s < kTiBK / 32; ++s) {
+    for (int s = 0; s < BK / 32; ++s) {
       const int c = 4 * s + kg;
       bf16x8 a[kTiTM], bb[kTiTN];
 #pragma unroll
       for (int tm = 0; tm < kTiTM; ++tm) {
         const int r = rA + 16 * tm;
-        a[tm] = *reinterpret_cast<const bf16x8*>(st + r * kTiRowB + 16 * ti_slot(r, c));
+        a[tm] = *reinterpret_cast<const bf16x8*>(st + r * C::kRowB + 16 * ti_slot(r, c));
       }
 #pragma unroll
       for (int tn = 0; tn < kTiTN; ++tn) {
         const int r = rB + 16 * tn;
-        bb[tn] = *reinterpret_cast<const bf16x8*>(st + r * kTiRowB + 16 * ti_slot(r, c));
+        bb[tn] = *reinterpret_cast<const bf16x8*>(st + r * C::kRowB + 16 * ti_slot(r, c));
       }
 #pragma unroll
       for (int tm = 0; tm < kTiTM; ++tm)
@@ -334,7 +368,7 @@ __global__ __launch_bounds__(kQThreads) void qgemm_tiled_kernel(QArgs A) {
         for (int tn = 0; tn < kTiTN; ++tn)
           acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[tm], bb[tn], acc[tm][tn], 0, 0, 0);
     }
-    SA_WAIT_VMCNT(kTiLoads * (kTiStages - 2));          // chunk kc + 1 is in
+    SA_WAIT_VMCNT(C::kLoads * (STAGES - 2));             // chunk kc + 1 is in
     __syncthreads();                                     // and every wave is done with chunk kc's stage
   }
   SA_WAIT_VMCNT(0);                                      // (the clamped trailing loads land before the end)
@@ -342,7 +376,7 @@ __global__ __launch_bounds__(kQThreads) void qgemm_tiled_kernel(QArgs A) {
   for (int tm = 0; tm < kTiTM; ++tm)
 #pragma unroll
     for (int tn = 0; tn < kTiTN; ++tn)
-      q_store4(A, S, b, m0 + wm * 16 * kTiTM + tm * 16 + 4 * kg, n0 + wn * 16 * kTiTN + tn * 16 + l16, acc[tm][tn]);
+      q_store4(A, S, b, m0 + 64 * wm + tm * 16 + 4 * kg, n0 + 64 * wn + tn * 16 + l16, acc[tm][tn]);
 }
 
 }  // namespace sa
@@ -355,13 +389,42 @@ static void fill_inv_freq(double* f) {
   for (int j = 0; j < 32; ++j) f[j] = std::pow(8.0e6, -(double)(2 * j) / 64.0);
 }
 
+template <class T>
+using TiOf = sa::TiCfg<T::kBM, T::kBK, T::kStages>;
+
+template <class T>
+static const void* ti_kernel() {
+  return (const void*)sa::qgemm_tiled_kernel<T::kBM, T::kBK, T::kStages, T::kWpc>;
+}
+
 // hipFuncSetAttribute is per device; remember which devices have been set up.
 static std::atomic<uint64_t> g_q_attr_set{0};
 
+static int32_t q_reserve_lds() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    set_error("query side: hipGetDevice failed");
+    return SA_ERR_HIP;
+  }
+  const uint64_t bit = 1ull << (dev & 63);
+  if (g_q_attr_set.load() & bit) return SA_OK;
+  if (hipFuncSetAttribute(ti_kernel<sa::TiProject>(), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)TiOf<sa::TiProject>::kSmem) != hipSuccess ||
+      hipFuncSetAttribute(ti_kernel<sa::TiAbsorb>(), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)TiOf<sa::TiAbsorb>::kSmem) != hipSuccess) {
+    set_error("query side: cannot reserve the tiled product's LDS");
+    return SA_ERR_HIP;
+  }
+  g_q_attr_set.fetch_or(bit);
+  return SA_OK;
+}
+
+// T: the tiled product's configuration for batches above the skinny limit.
+template <class T>
 static int32_t q_launch(sa::QArgs& A, int n_batch, hipStream_t stream) {
   const bool sk = q_skinny(A.n);
   const int sk_tn = A.n <= 16 ? 1 : 2;        // 16 or 32 tokens per skinny workgroup
-  const int bm = sk ? 16 * sa::kSkTM : sa::kTiBM, bn = sk ? 16 * sk_tn : sa::kTiBN;
+  const int bm = sk ? 16 * sa::kSkTM : T::kBM, bn = sk ? 16 * sk_tn : TiOf<T>::kBN;
   int64_t mblocks = 0;
   for (int s = 0; s < A.n_seg; ++s) {
     A.seg[s].mblocks = (A.seg[s].rows + bm - 1) / bm;
@@ -387,21 +450,10 @@ static int32_t q_launch(sa::QArgs& A, int n_batch, hipStream_t stream) {
       hipLaunchKernelGGL((sa::qgemm_skinny_kernel<2, 0, TM>), grid, dim3(sa::kQThreads), 0, stream, A);
     return check_launch("qgemm_skinny_kernel");
   }
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) {
-    set_error("query side: hipGetDevice failed");
-    return SA_ERR_HIP;
-  }
-  const uint64_t bit = 1ull << (dev & 63);
-  if (!(g_q_attr_set.load() & bit)) {
-    if (hipFuncSetAttribute((const void*)sa::qgemm_tiled_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)sa::kTiSmem) != hipSuccess) {
-      set_error("query side: cannot reserve %zu bytes of LDS", sa::kTiSmem);
-      return SA_ERR_HIP;
-    }
-    g_q_attr_set.fetch_or(bit);
-  }
-  hipLaunchKernelGGL(sa::qgemm_tiled_kernel, grid, dim3(sa::kQThreads), sa::kTiSmem, stream, A);
+  const int32_t rc = q_reserve_lds();
+  if (rc) return rc;
+  hipLaunchKernelGGL((sa::qgemm_tiled_kernel<T::kBM, T::kBK, T::kStages, T::kWpc>), grid, dim3(TiOf<T>::kThreads),
+                     TiOf<T>::kSmem, stream, A);
   return check_launch("qgemm_tiled_kernel");
 }
 
@@ -422,7 +474,7 @@ int32_t launch_q_project(const void* c_q, const void* w_qb, const void* w_iq, co
     A.seg[2] = sa::QSeg{(const uint16_t*)w_iw, w, sa::kIdxHeads, sa::kIdxHeads, 0, sa::kQModeF32, 0, 0};
     A.n_seg = 3;
   }
-  return q_launch(A, 1, stream);
+  return q_launch<sa::TiProject>(A, 1, stream);
 }
 
 int32_t launch_q_absorb(const void* q, const void* w_uk_t, int32_t n, void* q_abs, hipStream_t stream) {
@@ -443,7 +495,7 @@ int32_t launch_q_absorb(const void* q, const void* w_uk_t, int32_t n, void* q_ab
   A.copy_dst_ld = (int64_t)sa::kHeads * sa::kRow;
   A.copy_src_batch = 256;
   A.copy_dst_batch = sa::kRow;
-  return q_launch(A, sa::kHeads, stream);
+  return q_launch<sa::TiAbsorb>(A, sa::kHeads, stream);
 }
 
 }  // namespace sa_host
