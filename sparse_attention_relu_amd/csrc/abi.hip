@@ -50,7 +50,7 @@ size_t mla_workspace_size(int32_t n_q, int32_t k);
 void mla_split(int32_t n_q, int32_t k, int* n_sp, int* kps);
 int32_t launch_mla(const void* q_abs, const void* kv, const float* kv_scale, const int64_t* seq_start,
                    const int32_t* q_seq, const int32_t* idx, int32_t n_q, int32_t k, const void* w_uv, float scale,
-                   void* out, float* lse, void* ws, hipStream_t stream);
+                   void* out, float* lse, void* ws, hipStream_t stream, bool shared_rows);
 int32_t launch_quantize(const void* src, int64_t n_rows, int32_t d, const int64_t* dst_rows, void* codes, float* scales,
                         hipStream_t stream);
 int32_t launch_fp8_decode(const void* codes, int64_t n, void* out, hipStream_t stream);
@@ -263,8 +263,9 @@ int32_t sa_mla_sparse_attn(const void* q_abs, const void* kv, const int64_t* seq
   SA_REQUIRE(ws && ws_bytes >= need, SA_ERR_WORKSPACE, "mla: workspace of %zu bytes, %zu needed", ws_bytes, need);
   SA_REQUIRE(((uintptr_t)ws & 255u) == 0, SA_ERR_INVALID_ARG, "mla: workspace not 256-byte aligned");
   if ((rc = debug_idx(idx, n_q, k, nullptr, q_seq, (hipStream_t)stream))) return rc;
+  // (no sequence count here: the gathers stream, as for decode batches)
   return launch_mla(q_abs, kv, nullptr, seq_start, q_seq, idx, n_q, k, w_uv, scale, out, lse, ws,
-                    (hipStream_t)stream);
+                    (hipStream_t)stream, false);
 }
 
 int32_t sa_mla_sparse_attn_fp8(const void* q_abs, const void* kv_codes, const float* kv_scale, const int64_t* seq_start,
@@ -279,7 +280,7 @@ int32_t sa_mla_sparse_attn_fp8(const void* q_abs, const void* kv_codes, const fl
   SA_REQUIRE(((uintptr_t)ws & 255u) == 0, SA_ERR_INVALID_ARG, "mla: workspace not 256-byte aligned");
   if ((rc = debug_idx(idx, n_q, k, nullptr, q_seq, (hipStream_t)stream))) return rc;
   return launch_mla(q_abs, kv_codes, kv_scale, seq_start, q_seq, idx, n_q, k, w_uv, scale, out, lse, ws,
-                    (hipStream_t)stream);
+                    (hipStream_t)stream, false);
 }
 
 // Layout: scores [n_q, ld] fp32, the top-k workspace, the attention
@@ -359,6 +360,9 @@ int32_t sa_layer_stack(const sa_layer_desc* layers, int32_t n_layers, const sa_b
   // scores.  The decode indexer also clears the top-k's histograms and
   // counters on the side, which saves the top-k a launch of its own for that.
   const int ialgo = indexer_algo(n_rows, batch->n_seq, 0);
+  // Queries that share their sequences' rows (chunked prefill, the same test
+  // as the indexer's choice): the attention's gathers keep the rows cached.
+  const bool shared_rows = indexer_algo(n_q, batch->n_seq, 0) == 2;
   uint32_t* clear = nullptr;
   int64_t n_clear = 0;
   if (ialgo == 1) topk_clear_range(topk_ws, n_rows, ld, &clear, &n_clear);
@@ -392,7 +396,7 @@ int32_t sa_layer_stack(const sa_layer_desc* layers, int32_t n_layers, const sa_b
     const bool eva = events && !rec_attn && events->attn_begin && events->attn_end;
     if (eva && (rc = record(events->attn_begin, st))) return rc;
     rc = launch_mla(L.q_abs, L.kv, L.kv_scale, batch->seq_start, batch->q_seq, cur_idx, n_q, k, L.w_uv, scale, L.out,
-                    nullptr, mla_ws, st);
+                    nullptr, mla_ws, st, shared_rows);
     if (rc) return rc;
     if (eva && (rc = record(events->attn_end, st))) return rc;
     rec_attn |= eva;

@@ -133,7 +133,12 @@ __device__ __forceinline__ float reduce8(float x, Op op) {
 // sclds; the score waves scale each logit by its row's scale and feed
 // p_j * scale_j to the value product, while the softmax sum keeps p_j: the
 // attention of the rows scale_j * value(codes_j).
-template <int NB, bool FP8>
+//
+// CACHED: the row gathers use the default cache policy instead of streaming
+// loads, for batches whose queries share their sequences' rows (chunked
+// prefill: 4096 queries of one sequence gather each of its rows about 64
+// times per layer, and these repeats then hit in the caches).
+template <int NB, bool FP8, bool CACHED>
 __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
   // Workgroups are dealt to the 8 XCDs round-robin (bid % 8): give each XCD a
   // contiguous run of (query, slice, head group) items, so the two head
@@ -368,13 +373,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
     for (int u = 0; u < kLoadsPerWave; ++u) {
       // padding entries read row 0; byte offsets within the sequence stay
       // below 2^32 for sequences below 3.7M rows.  Cache policy: streaming
-      // (non-temporal), the rows are dead after this step's two head groups
-      // (-1.5 us per launch against the default policy).
+      // (non-temporal) unless CACHED, as in decode batches the rows are dead
+      // after this step's two head groups (-1.5 us per launch against the
+      // default policy).
       const int p = pos[u] >= 0 ? pos[u] : 0;
       const uint32_t off = (uint32_t)p * (uint32_t)kRowBytes + (uint32_t)lcol[u];
       uint8_t* dst = b + (u < 8 ? w * kQuarterBytes + 1024 * u : kRopeOff + 1024 * w);
       __builtin_amdgcn_global_load_lds((const void*)(rows_b + off), (__attribute__((address_space(3))) void*)dst, 16,
-                                       0, kCpolNt);
+                                       0, CACHED ? 0 : kCpolNt);
     }
   };
   // V^T operand: 8-byte read of row rho = 16ks + 8(e >> 2) + 4hl + (e & 3),
@@ -405,12 +411,15 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
     for (int u = 0; u < 4; ++u) pl[u] = spos[jt + 8 * u + (lane >> 3)];
     const int pr = spos[jt + 8 * w + ((lane & 31) >> 2)];
     const int ps = spos[jt + 8 * w + (lane & 7)];
+    // (streaming loads unless CACHED, as for the bf16 rows)
+    auto ld_row = [](const uint8_t* p) {
+      if constexpr (CACHED) return *reinterpret_cast<const u32x4*>(p);
+      else return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    };
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      g8l[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-          rows8 + (uint32_t)max(pl[u], 0) * (uint32_t)kRow + (uint32_t)(128 * w + 16 * (lane & 7))));
-    g8r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-        rows8 + (uint32_t)max(pr, 0) * (uint32_t)kRow + (uint32_t)(kLatent + 16 * (lane & 3))));
+      g8l[u] = ld_row(rows8 + (uint32_t)max(pl[u], 0) * (uint32_t)kRow + (uint32_t)(128 * w + 16 * (lane & 7)));
+    g8r = ld_row(rows8 + (uint32_t)max(pr, 0) * (uint32_t)kRow + (uint32_t)(kLatent + 16 * (lane & 3)));
     g8s = scl[max(ps, 0)];
   };
   auto land8 = [&](int tile) {
@@ -964,9 +973,32 @@ size_t mla_workspace_size(int32_t n_q, int32_t k) {
 static std::atomic<uint64_t> g_attr_set{0};
 
 // kv_scale != NULL: kv holds E4M3 codes [rows][576] with one scale per row.
+// shared_rows: the batch's queries share their sequences' rows (the caller
+// knows the sequence count), so the gathers keep them in the caches.
+template <int NB, bool FP8>
+static void launch_attn(bool cached, int64_t grid, size_t smem, hipStream_t stream, const sa::AttnArgs& A) {
+  if (cached)
+    hipLaunchKernelGGL((sa::mla_attn_kernel<NB, FP8, true>), dim3((unsigned)grid), dim3(sa::kAttnThreads), smem,
+                       stream, A);
+  else
+    hipLaunchKernelGGL((sa::mla_attn_kernel<NB, FP8, false>), dim3((unsigned)grid), dim3(sa::kAttnThreads), smem,
+                       stream, A);
+}
+
+template <int NB, bool FP8>
+static hipError_t reserve_attn_lds() {
+  const int smem = (int)sa::attn_smem<NB, FP8>();
+  hipError_t e = hipFuncSetAttribute((const void*)sa::mla_attn_kernel<NB, FP8, false>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute((const void*)sa::mla_attn_kernel<NB, FP8, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            smem);
+  return e;
+}
+
 int32_t launch_mla(const void* q_abs, const void* kv, const float* kv_scale, const int64_t* seq_start,
                    const int32_t* q_seq, const int32_t* idx, int32_t n_q, int32_t k, const void* w_uv, float scale,
-                   void* out, float* lse, void* ws, hipStream_t stream) {
+                   void* out, float* lse, void* ws, hipStream_t stream, bool shared_rows) {
   int n_sp, kps;
   mla_split(n_q, k, &n_sp, &kps);
   MlaWs m = mla_carve(ws, n_q, n_sp);
@@ -997,14 +1029,8 @@ int32_t launch_mla(const void* q_abs, const void* kv, const float* kv_scale, con
   }
   const uint64_t bit = 1ull << (dev & 63);
   if (!(g_attr_set.load() & bit)) {
-    if (hipFuncSetAttribute((const void*)sa::mla_attn_kernel<1, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)sa::attn_smem<1>()) != hipSuccess ||
-        hipFuncSetAttribute((const void*)sa::mla_attn_kernel<2, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)sa::attn_smem<2>()) != hipSuccess ||
-        hipFuncSetAttribute((const void*)sa::mla_attn_kernel<1, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)sa::attn_smem<1, true>()) != hipSuccess ||
-        hipFuncSetAttribute((const void*)sa::mla_attn_kernel<2, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)sa::attn_smem<2, true>()) != hipSuccess ||
+    if (reserve_attn_lds<1, false>() != hipSuccess || reserve_attn_lds<2, false>() != hipSuccess ||
+        reserve_attn_lds<1, true>() != hipSuccess || reserve_attn_lds<2, true>() != hipSuccess ||
         hipFuncSetAttribute((const void*)sa::mla_wuv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)sa::kWuvSmem) != hipSuccess) {
       set_error("mla: cannot reserve %zu bytes of LDS", smem);
@@ -1020,13 +1046,13 @@ int32_t launch_mla(const void* q_abs, const void* kv, const float* kv_scale, con
     return SA_ERR_UNSUPPORTED;
   }
   if (nb == 2 && fp8)
-    hipLaunchKernelGGL((sa::mla_attn_kernel<2, true>), dim3((unsigned)grid), dim3(sa::kAttnThreads), smem, stream, A);
+    launch_attn<2, true>(shared_rows, grid, smem, stream, A);
   else if (nb == 2)
-    hipLaunchKernelGGL((sa::mla_attn_kernel<2, false>), dim3((unsigned)grid), dim3(sa::kAttnThreads), smem, stream, A);
+    launch_attn<2, false>(shared_rows, grid, smem, stream, A);
   else if (fp8)
-    hipLaunchKernelGGL((sa::mla_attn_kernel<1, true>), dim3((unsigned)grid), dim3(sa::kAttnThreads), smem, stream, A);
+    launch_attn<1, true>(shared_rows, grid, smem, stream, A);
   else
-    hipLaunchKernelGGL((sa::mla_attn_kernel<1, false>), dim3((unsigned)grid), dim3(sa::kAttnThreads), smem, stream, A);
+    launch_attn<1, false>(shared_rows, grid, smem, stream, A);
   int32_t rc = check_launch("mla_attn_kernel");
   if (rc) return rc;
   if (n_sp > 1) {
