@@ -840,22 +840,41 @@ struct WuvArgs {
   int n_q;
 };
 
-constexpr int kWuvRows = 64;                    // value rows per workgroup
 constexpr int kWuvQ = 16;                       // queries per block (MFMA N)
-constexpr size_t kWuvSmem = (size_t)(kWuvRows + 2 * kWuvQ) * kLatent * 2;   // 96 KB
+// ROWS value rows per workgroup (ROWS / 16 waves), the query blocks split
+// QSPLIT ways: 64 x 1 for decode batches (the W_UV slice dominates a
+// workgroup's bytes); 128 x 2 from kWuvWideQ queries on, where each
+// workgroup streams every obar row of its head and the per-CU rate bounds
+// the kernel, so twice the value rows per obar byte halve those bytes.
+template <int ROWS>
+constexpr size_t wuv_smem() { return (size_t)(ROWS + 2 * kWuvQ) * kLatent * 2; }   // 96 or 160 KB
+constexpr int kWuvWideQ = 512;
 
-// One workgroup per (head, 64 value rows).  Its W_UV rows and, block by block,
-// the obar rows of 16 queries are staged in LDS with 1 KB direct-to-LDS loads
-// (one 512-wide row each, chunks swizzled by row so the MFMA operand reads are
-// conflict-free).  Wave w multiplies value rows 16w..16w+15 with each block.
-__global__ __launch_bounds__(256) void mla_wuv_kernel(WuvArgs W) {
+// One workgroup per (head, ROWS value rows, 1 / QSPLIT of the query blocks).
+// Its W_UV rows and, block by block, the obar rows of 16 queries are staged in
+// LDS with 1 KB direct-to-LDS loads (one 512-wide row each, chunks swizzled by
+// row so the MFMA operand reads are conflict-free).  Wave w multiplies value
+// rows 16w..16w+15 with each block.
+template <int ROWS, int QSPLIT>
+__global__ __launch_bounds__(ROWS * 4) void mla_wuv_kernel(WuvArgs W) {
+  constexpr int kWaves = ROWS / 16;
+  constexpr int kRowBlocks = kVdim / ROWS;
+  constexpr int kBlkLoads = kWuvQ / kWaves;            // obar rows each wave stages per block
+  static_assert(kVdim % ROWS == 0 && kWuvQ % kWaves == 0, "value-row blocks and staging shares");
   extern __shared__ __align__(16) uint8_t smem[];
-  const int h = blockIdx.x >> 2;
-  const int vb = (blockIdx.x & 3) * kWuvRows;
+  const int bx = (int)blockIdx.x;
+  const int h = bx / (kRowBlocks * QSPLIT);
+  const int rest = bx - h * (kRowBlocks * QSPLIT);
+  const int vb = (rest / QSPLIT) * ROWS;
+  const int qs = rest % QSPLIT;
+  const int n_blk_all = (W.n_q + kWuvQ - 1) / kWuvQ;
+  const int per = (n_blk_all + QSPLIT - 1) / QSPLIT;
+  const int b0 = qs * per, b1 = min(b0 + per, n_blk_all);
+  if (b0 >= b1) return;                                 // (before any load)
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  uint8_t* wl = smem;                                   // [64 rows][1 KB]
-  uint8_t* ol = smem + kWuvRows * 1024;                 // [2 buffers][16 rows][1 KB]
+  uint8_t* wl = smem;                                   // [ROWS rows][1 KB]
+  uint8_t* ol = smem + ROWS * 1024;                     // [2 buffers][16 rows][1 KB]
   // Row r of a staged block: lane p fills slot p with chunk p ^ (r & 15).
   auto stage_row = [&](uint8_t* dst_row, const uint16_t* src_row, int r) {
     const uint8_t* src = reinterpret_cast<const uint8_t*>(src_row) + 16 * (lane ^ (r & 15));
@@ -864,34 +883,33 @@ __global__ __launch_bounds__(256) void mla_wuv_kernel(WuvArgs W) {
   const uint16_t* wsrc = W.w_uv + ((int64_t)h * kVdim + vb) * kLatent;
 #pragma unroll
   for (int u = 0; u < 16; ++u) stage_row(wl + (16 * w + u) * 1024, wsrc + (int64_t)(16 * w + u) * kLatent, u);
-  const int n_blk = (W.n_q + kWuvQ - 1) / kWuvQ;
   auto stage_block = [&](int b) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = 4 * w + u;
+    for (int u = 0; u < kBlkLoads; ++u) {
+      const int r = kBlkLoads * w + u;
       const int tq = min(b * kWuvQ + r, W.n_q - 1);
-      stage_row(ol + ((b & 1) * kWuvQ + r) * 1024, W.obar + ((int64_t)tq * kHeads + h) * kLatent, r);
+      stage_row(ol + (((b - b0) & 1) * kWuvQ + r) * 1024, W.obar + ((int64_t)tq * kHeads + h) * kLatent, r);
     }
   };
-  stage_block(0);
+  stage_block(b0);
   // Operand reads: row l16 (value row 16w + l16, or query l16), chunk 4s + g.
   // Byte offset of chunk 4s + g of row l16: 16 ((4s + g) ^ l16) = 64 s ^ rd.
   const int rd = 16 * (g ^ l16);
   bf16x8 wa[16];
-  for (int b = 0; b < n_blk; ++b) {
-    if (b + 1 < n_blk) {
+  for (int b = b0; b < b1; ++b) {
+    if (b + 1 < b1) {
       stage_block(b + 1);
-      SA_WAIT_VMCNT(4);
+      SA_WAIT_VMCNT(kBlkLoads);
     } else {
       SA_WAIT_VMCNT(0);
     }
     lds_barrier();
-    if (b == 0) {
+    if (b == b0) {
 #pragma unroll
       for (int s = 0; s < 16; ++s)
         wa[s] = *reinterpret_cast<const bf16x8*>(wl + (16 * w + l16) * 1024 + ((16 * (4 * s)) ^ rd));
     }
-    const uint8_t* orow = ol + ((b & 1) * kWuvQ + l16) * 1024;
+    const uint8_t* orow = ol + (((b - b0) & 1) * kWuvQ + l16) * 1024;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 16; ++s)
@@ -903,7 +921,7 @@ __global__ __launch_bounds__(256) void mla_wuv_kernel(WuvArgs W) {
       const u32x2 pk = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
       *reinterpret_cast<u32x2*>(W.out + ((int64_t)tq * kHeads + h) * kVdim + vb + 16 * w + 4 * g) = pk;
     }
-    lds_barrier();                      // buffer b & 1 is refilled by the next iteration's staging
+    lds_barrier();                      // buffer (b - b0) & 1 is refilled by the next iteration's staging
   }
 }
 
@@ -1031,8 +1049,10 @@ int32_t launch_mla(const void* q_abs, const void* kv, const float* kv_scale, con
   if (!(g_attr_set.load() & bit)) {
     if (reserve_attn_lds<1, false>() != hipSuccess || reserve_attn_lds<2, false>() != hipSuccess ||
         reserve_attn_lds<1, true>() != hipSuccess || reserve_attn_lds<2, true>() != hipSuccess ||
-        hipFuncSetAttribute((const void*)sa::mla_wuv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)sa::kWuvSmem) != hipSuccess) {
+        hipFuncSetAttribute((const void*)sa::mla_wuv_kernel<64, 1>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)sa::wuv_smem<64>()) != hipSuccess ||
+        hipFuncSetAttribute((const void*)sa::mla_wuv_kernel<128, 2>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)sa::wuv_smem<128>()) != hipSuccess) {
       set_error("mla: cannot reserve %zu bytes of LDS", smem);
       return SA_ERR_HIP;
     }
@@ -1069,7 +1089,11 @@ int32_t launch_mla(const void* q_abs, const void* kv, const float* kv_scale, con
     }
   }
   sa::WuvArgs W{m.obar, (const uint16_t*)w_uv, (uint16_t*)out, n_q};
-  hipLaunchKernelGGL(sa::mla_wuv_kernel, dim3(sa::kHeads * 4), dim3(256), sa::kWuvSmem, stream, W);
+  if (n_q >= sa::kWuvWideQ)
+    hipLaunchKernelGGL((sa::mla_wuv_kernel<128, 2>), dim3(sa::kHeads * 2 * 2), dim3(512), sa::wuv_smem<128>(), stream,
+                       W);
+  else
+    hipLaunchKernelGGL((sa::mla_wuv_kernel<64, 1>), dim3(sa::kHeads * 4), dim3(256), sa::wuv_smem<64>(), stream, W);
   return check_launch("mla_wuv_kernel");
 }
 
