@@ -179,6 +179,30 @@ def test_fp8_layer_stack_mixed(gpu_lib):
         parity.check_mla(Lm, B, to_numpy(cur), to_numpy(outs[l]), wl.scale)
 
 
+def test_fp8_layer_stack_shared_rows(gpu_lib):
+    """96 queries of one sequence with FP8 caches: the stack's attention
+    gathers the codes with cached loads (queries sharing their sequence's
+    rows), the separate FP8 call streams them; outputs identical bit for bit,
+    and sampled queries against the oracle on the dequantized rows."""
+    wl = synth.ragged_workload([5000], [(0, 4904 + i) for i in range(96)], n_layers=2, name="fp8_shared_rows")
+    wl.full = [True, False]
+    b = synth.make_batch(wl, DEV, seed=21)
+    layers, deqs = [], []
+    for L in b.layers:
+        L8, deq = _fp8_layer(L)
+        layers.append(L8)
+        deqs.append(deq)
+    outs, idxs = api.layer_stack(layers, b.seq_start, b.seq_len, b.q_seq, b.q_pos, wl.ld, full=wl.full)
+    torch.cuda.synchronize()
+    B = parity.np_batch(b)
+    for l, L in enumerate(layers):
+        o = api.mla_sparse_attn_fp8(L.q_abs, L.kv, L.kv_scale, b.seq_start, b.q_seq, idxs[0], L.w_uv, wl.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(o, outs[l]), f"layer {l}"
+        Lm = {"q_abs": to_numpy(L.q_abs), "kv": deqs[l]["kv"], "w_uv": to_numpy(L.w_uv)}
+        parity.check_mla(Lm, B, to_numpy(idxs[0]), to_numpy(outs[l]), wl.scale, rows=[0, 47, 95])
+
+
 def test_fp8_decode_config_full(gpu_lib):
     """The 16-query, 65,536..131,072-token, 4-layer decode configuration with
     FP8 caches, in the launch configuration the benchmark times."""

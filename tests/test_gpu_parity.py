@@ -286,6 +286,29 @@ def test_layer_stack_matches_separate_calls(gpu_lib):
     parity.check_topk_band(parity.layer_np(b.layers[3]), B, to_numpy(idxs[3]), 2048)
 
 
+def test_layer_stack_shared_rows_matches_separate_calls(gpu_lib):
+    # 600 queries of one sequence: the stack's attention gathers with cached
+    # loads (queries sharing their sequence's rows) and W_UV takes its
+    # 128-row, two-way query split; the separate call streams its gathers,
+    # and the outputs must be identical bit for bit
+    lens = [9000]
+    queries = [(0, 8400 + i) for i in range(600)]
+    wl = synth.ragged_workload(lens, queries, n_layers=2, name="shared_rows")
+    wl.full = [True, False]
+    b = _batch(wl, seed=19)
+    outs, idxs = api.layer_stack(b.layers, b.seq_start, b.seq_len, b.q_seq, b.q_pos, wl.ld, full=wl.full)
+    torch.cuda.synchronize()
+    for l, L in enumerate(b.layers):
+        o = api.mla_sparse_attn(L.q_abs, L.kv, b.seq_start, b.q_seq, idxs[0], L.w_uv, wl.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(o, outs[l]), f"layer {l}"
+    B = parity.np_batch(b)
+    rows = [0, 1, 299, 598, 599]
+    sel = to_numpy(idxs[0])
+    for l in range(2):
+        parity.check_mla(parity.layer_np(b.layers[l]), B, sel, to_numpy(outs[l]), wl.scale, rows=rows)
+
+
 def test_deterministic(gpu_lib):
     wl = ragged_wl(n_layers=2)
     b = _batch(wl, seed=13)
