@@ -577,6 +577,11 @@ def main():
         # layer, and everything after them (attention + W_UV of all layers)
         "stage_fractions_eager": stage_fractions(kern_ms, eager_ms),
         "attn_layer_gbs": None if prefill else round(attn_bytes / (kern_ms["attn"] * 1e-3) / 1e9, 1),
+        # query tokens x layers per second over the graph replays, and the
+        # rate of one layer's attention stage alone (sa_mla_sparse_attn's
+        # work: attention + merge + W_UV, from the first layer's events)
+        "layer_queries_per_s": round(wl.n_q * wl.n_layers / (ms_step * 1e-3), 1),
+        "attn_stage_queries_per_s": round(wl.n_q / (kern_ms["attn"] * 1e-3), 1),
         "eager_ms_per_step": round(eager_ms, 5),
         "input_copies": len(stacks),
         "env": environment(torch, sclk_after),
