@@ -142,7 +142,9 @@ __device__ __forceinline__ void q_copy_rope(const QArgs& A, int b, int n0, int n
 // contraction slots from k = 64 blk + 16 kg + 8 j (j = step, kg = lane / 16),
 // the same order for both operands, so each lane reads 32 contiguous bytes
 // of a row and the 4 lanes of a row read its whole 128-byte line.
-constexpr int kSkTM = 2;             // 16-row weight tiles per workgroup (fastest of 1, 2, 4 at 16 tokens)
+// 16-row weight tiles per workgroup: the projection takes 6 (96 rows: its
+// 20,512 rows make 215 workgroups, one per CU), the absorption 2.
+constexpr int kSkTMProject = 6, kSkTMAbsorb = 2;
 constexpr int kSkDepth = 3;          // 64-wide blocks in flight per wave
 
 // KPW > 0: K is exactly 4 KPW blocks (every wave has KPW of them) and the
@@ -285,9 +287,11 @@ constexpr int kTiTM = 4, kTiTN = 4;                     // 16x16 tiles per wave 
 // 256 x 128 tiles, 32-wide chunks in three stages, two workgroups per CU:
 // 222 against 253 us.
 struct TiProject {
+  static constexpr int kSkTM = kSkTMProject;
   static constexpr int kBM = 128, kBK = 64, kStages = 2, kWpc = 2;
 };
 struct TiAbsorb {
+  static constexpr int kSkTM = kSkTMAbsorb;
   static constexpr int kBM = 256, kBK = 32, kStages = 3, kWpc = 2;
 };
 
@@ -424,7 +428,7 @@ template <class T>
 static int32_t q_launch(sa::QArgs& A, int n_batch, hipStream_t stream) {
   const bool sk = q_skinny(A.n);
   const int sk_tn = A.n <= 16 ? 1 : 2;        // 16 or 32 tokens per skinny workgroup
-  const int bm = sk ? 16 * sa::kSkTM : T::kBM, bn = sk ? 16 * sk_tn : TiOf<T>::kBN;
+  const int bm = sk ? 16 * T::kSkTM : T::kBM, bn = sk ? 16 * sk_tn : TiOf<T>::kBN;
   int64_t mblocks = 0;
   for (int s = 0; s < A.n_seg; ++s) {
     A.seg[s].mblocks = (A.seg[s].rows + bm - 1) / bm;
@@ -439,7 +443,7 @@ static int32_t q_launch(sa::QArgs& A, int n_batch, hipStream_t stream) {
   const dim3 grid((unsigned)mblocks, (unsigned)nblocks, (unsigned)n_batch);
   if (sk) {
     const bool k2048 = A.K == 2048;      // q_lora_rank: 8 blocks per wave, unrolled
-    constexpr int TM = sa::kSkTM;
+    constexpr int TM = T::kSkTM;
     if (sk_tn == 1 && k2048)
       hipLaunchKernelGGL((sa::qgemm_skinny_kernel<1, 8, TM>), grid, dim3(sa::kQThreads), 0, stream, A);
     else if (k2048)
