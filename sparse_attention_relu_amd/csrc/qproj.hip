@@ -143,8 +143,10 @@ __device__ __forceinline__ void q_copy_rope(const QArgs& A, int b, int n0, int n
 // the same order for both operands, so each lane reads 32 contiguous bytes
 // of a row and the 4 lanes of a row read its whole 128-byte line.
 // 16-row weight tiles per workgroup: the projection takes 6 (96 rows: its
-// 20,512 rows make 215 workgroups, one per CU), the absorption 2.
-constexpr int kSkTMProject = 6, kSkTMAbsorb = 2;
+// 20,512 rows make 215 workgroups, one per CU), the absorption 4 (64 rows
+// per head block, 512 workgroups: 7.36 against 7.66 us for 2 and 7.68 for 8
+// at 16 tokens).
+constexpr int kSkTMProject = 6, kSkTMAbsorb = 4;
 constexpr int kSkDepth = 3;          // 64-wide blocks in flight per wave
 
 // KPW > 0: K is exactly 4 KPW blocks (every wave has KPW of them) and the
