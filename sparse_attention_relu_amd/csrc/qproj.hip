@@ -31,11 +31,11 @@
 //
 //   qgemm_skinny_kernel  decode batches (16 or 32 tokens per token block):
 //                        each wave streams its share of K (64-wide blocks w,
-//                        w + 4, ...) for 32 weight rows straight into MFMA
-//                        operand registers, 3 blocks in flight, no LDS and no
-//                        barrier in the loop; the 4 waves' partial tiles are
-//                        summed through LDS at the end.  HBM-bound on the
-//                        weights.
+//                        w + 4, ...) for 96 (projection) or 64 (absorption)
+//                        weight rows straight into MFMA operand registers,
+//                        3 blocks in flight, no LDS and no barrier in the
+//                        loop; the 4 waves' partial tiles are summed through
+//                        LDS at the end.  HBM-bound on the weights.
 //   qgemm_tiled_kernel   prefill batches: 128 or 256 weight rows x 128 tokens
 //                        per workgroup, K chunks staged in LDS by direct
 //                        global -> LDS loads (a ring of stages), waves of
