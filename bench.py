@@ -233,6 +233,14 @@ def prefill_indexer(seed, reps=9, warmup=20):
         a.record(s)
         api.indexer_score(q, w, kI, seq_start, seq_len, q_seq, q_pos, wl.ld, scores=scores, stream=s)
         c.record(s)
+    # the shader clock level while the launches run (they are queued; the
+    # host samples the driver's table during their ~30 ms)
+    sclk = []
+    for _ in range(6):
+        time.sleep(0.004)
+        cur, _top = gpu_sclk_mhz()
+        if cur is not None:
+            sclk.append(cur)
     torch.cuda.synchronize()
     spread = sorted(a.elapsed_time(c) for a, c in ev)
     ms = spread[len(ev) // 2]
@@ -241,6 +249,7 @@ def prefill_indexer(seed, reps=9, warmup=20):
     return {"workload": wl.name, "tflops": round(tflops, 1), "ms": round(ms, 4), "unit": "TFLOP/s",
             "flops": causal_flops, "frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
             "peak": BF16_PEAK_TFLOPS, "ms_min": round(spread[0], 5), "ms_max": round(spread[-1], 5),
+            "sclk_mhz_during": sorted(sclk)[len(sclk) // 2] if sclk else None,
             "timing": "median of %d HIP-event-timed launches" % reps}
 
 
