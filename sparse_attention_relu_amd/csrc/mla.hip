@@ -253,6 +253,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
             slds[((blk * 4 + w) * 4 + g) * 64 + (lane ^ (2 * (2 * g + hl)))] =
                 f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
         }
+        // Issue order: the 9 operand reads, then the products, then the
+        // partial stores.  Left alone, the scheduler interleaves the reads
+        // with the products and keeps only one or two of them in flight.
+        __builtin_amdgcn_sched_group_barrier(0x100, 9, 0);        // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 9 * NB, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x200, 4 * NB, 0);   // LDS writes
       }
       lds_barrier();                                                   // BAR_s
       if (active) {
@@ -262,15 +268,20 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
         const u32x4 pos4 = *reinterpret_cast<const u32x4*>(spos + jt + 4 * pq);
         f32x4 rs4 = {1.f, 1.f, 1.f, 1.f};        // FP8: the scales of this lane's 4 rows
         if constexpr (FP8) rs4 = *reinterpret_cast<const f32x4*>(sclds + (tile % kRing) * kTile + 4 * pq);
+        f32x4 sp4[NB][4];
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+          for (int w2 = 0; w2 < 4; ++w2) sp4[blk][w2] = slds[((blk * 4 + w2) * 4 + ig) * 64 + src_sw];
+        // every read above goes out before the first sum: one LDS round trip
+        __builtin_amdgcn_sched_barrier(0);
         float x[NB][4];
         float tmax[NB];
         bool bump[NB];
         bool bump_any = false;
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) {
-          f32x4 s4 = slds[((blk * 4 + 0) * 4 + ig) * 64 + src_sw];
-#pragma unroll
-          for (int w2 = 1; w2 < 4; ++w2) s4 += slds[((blk * 4 + w2) * 4 + ig) * 64 + src_sw];
+          const f32x4 s4 = ((sp4[blk][0] + sp4[blk][1]) + sp4[blk][2]) + sp4[blk][3];
           // ---- online softmax of head hloc of the block over rows jt + 4pq .. +3
           tmax[blk] = -INFINITY;
 #pragma unroll
@@ -362,12 +373,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
     lrow[8] = r;
     lcol[8] = 16 * (64 + ((lane & 7) ^ ((r >> 1) & 7)));
   }
-  auto issue = [&](int tile) {
+  auto read_pos = [&](int tile, int (&pos)[kLoadsPerWave]) {
     const int jt = min(tile, max(n_tiles - 1, 0)) * kTile;
-    // every position first (one LDS round trip), then the loads
-    int pos[kLoadsPerWave];
 #pragma unroll
     for (int u = 0; u < kLoadsPerWave; ++u) pos[u] = spos[jt + lrow[u]];
+  };
+  auto issue_at = [&](int tile, const int (&pos)[kLoadsPerWave]) {
     uint8_t* b = ring + (tile % kRing) * kTileBytes;
 #pragma unroll
     for (int u = 0; u < kLoadsPerWave; ++u) {
@@ -383,6 +394,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
                                        0, CACHED ? 0 : kCpolNt);
     }
   };
+  auto issue = [&](int tile) {
+    // every position first (one LDS round trip), then the loads
+    int pos[kLoadsPerWave];
+    read_pos(tile, pos);
+    issue_at(tile, pos);
+  };
+  // Streaming gathers take the positions of the tile they issue from
+  // registers, read one step earlier while the products ran, so the loads go
+  // out as soon as the operand reads are back (about -0.5 us per launch on
+  // 16-query decode steps).  With cached gathers (chunked prefill) that
+  // measured slower, and the positions are read just before the loads.
+  constexpr bool kPosAhead = !FP8 && !CACHED;
   // V^T operand: 8-byte read of row rho = 16ks + 8(e >> 2) + 4hl + (e & 3),
   // dims 128w + 4 l32 .. +3 (chunk 16w + l32 / 2, half l32 & 1); rho & 15 is
   // 8(e >> 2) + 4hl + (e & 3) for every ks.
@@ -460,6 +483,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
   lds_barrier();                                                       // B1
   // weights / rescale of head l32 come from score wave l32 / 8
   const int pw = l32 >> 3;
+  int npos[kLoadsPerWave];        // kPosAhead: positions of the next tile to gather
+  if constexpr (kPosAhead) read_pos(2, npos);
 #pragma unroll 1
   for (int step = 0; step <= n_tiles; ++step) {
     // Operands of tile step - 1 are read before BAR_s; its products run after
@@ -493,7 +518,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
     }
     if (!FP8 && step < n_tiles) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      issue(step + 2);
+      if constexpr (kPosAhead) issue_at(step + 2, npos);
+      else issue(step + 2);
     }
     lds_barrier();                                                     // BAR_s
     if (pv_step) {
@@ -538,6 +564,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
         if (step + 2 < n_tiles) issue8(step + 2);
       }
     } else {
+      if constexpr (kPosAhead)
+        if (step + 1 < n_tiles) read_pos(step + 3, npos);   // issued next step
       if (step < n_tiles) SA_WAIT_VMCNT(kLoadsPerWave);
     }
     lds_barrier();                                                     // BAR_p
