@@ -938,11 +938,15 @@ __global__ __launch_bounds__(ROWS * 4) void mla_wuv_kernel(WuvArgs W) {
         wa[s] = *reinterpret_cast<const bf16x8*>(wl + (16 * w + l16) * 1024 + ((16 * (4 * s)) ^ rd));
     }
     const uint8_t* orow = ol + (((b - b0) & 1) * kWuvQ + l16) * 1024;
+    bf16x8 ob[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) ob[s] = *reinterpret_cast<const bf16x8*>(orow + ((16 * (4 * s)) ^ rd));
+    // every operand read above goes out before the first product: one LDS
+    // round trip per block instead of several
+    __builtin_amdgcn_sched_barrier(0);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 16; ++s)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[s], *reinterpret_cast<const bf16x8*>(orow + ((16 * (4 * s)) ^ rd)),
-                                                    acc, 0, 0, 0);
+    for (int s = 0; s < 16; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[s], ob[s], acc, 0, 0, 0);
     // acc[j] = out[t = 16b + l16][h][vb + 16w + 4g + j]
     const int tq = b * kWuvQ + l16;
     if (tq < W.n_q) {
