@@ -19,7 +19,9 @@
 //            indexer zeroes the histograms and counters on the side.
 //   compact  rows x chunks, one pass with the chunk in registers: every
 //            workgroup reads the finished histogram and finds the bin b1 that
-//            holds the k_eff-th largest key (no hand-off between workgroups);
+//            holds the k_eff-th largest key (no hand-off between workgroups;
+//            with large chunks a one-workgroup-per-row bin kernel finds it
+//            once and the compaction reads it from the row's state words);
 //            positions in bins above b1 are kept outright, those in b1 become
 //            candidates (composite keys); one atomic per workgroup and counter
 //            reserves the output slots.
@@ -125,7 +127,33 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(const float* __
     if (h[i]) atomicAdd(&gh[i], h[i]);
 }
 
-template <int kPer>
+// Large chunks: the bin of the k-th largest key is found once per row, by one
+// workgroup, and recorded in the row's state words (bin, keys above it, keys
+// in it) for the compaction and the finish.
+__global__ __launch_bounds__(kHistThreads) void topk_bin_kernel(const int32_t* __restrict__ q_pos, int k, TopkWs ws) {
+  const int t = blockIdx.x;
+  const FirstHist<kHistThreads> fh = load_first_hist<kHistThreads>(ws, t);   // beside the length
+  const int64_t n_t = (int64_t)q_pos[t] + 1;
+  if (n_t <= k) return;                   // take-all rows have no histogram
+  __shared__ __align__(16) uint32_t h[kBins1];
+  __shared__ int sh_wave[kHistThreads / 64];
+  __shared__ int sh_res[2];
+  int above, n_cand;
+  const int bin = first_digit_bin<kHistThreads>(fh, k, h, sh_wave, sh_res, &above, &n_cand);
+  if (threadIdx.x == 0) {
+    int32_t* st = ws.state + (int64_t)t * ST_WORDS;
+    st[ST_B1] = bin;
+    st[ST_ABOVE] = above;
+    st[ST_NCAND] = n_cand;
+  }
+}
+
+// kBinDone: topk_bin_kernel has recorded the row's bin (large chunks: 8 or
+// more workgroups per row would each repeat the 16 KB histogram read and the
+// workgroup-wide bin search); otherwise every workgroup of the row finds the
+// bin from the row's histogram (cheaper than a cross-workgroup hand-off) and
+// chunk 0 records it.
+template <int kPer, bool kBinDone>
 __global__ __launch_bounds__(kHistThreads) void topk_compact_kernel(const float* __restrict__ scores, int64_t ld,
                                                                       const int32_t* __restrict__ q_pos, int k,
                                                                       int n_chunks, TopkWs ws) {
@@ -133,25 +161,36 @@ __global__ __launch_bounds__(kHistThreads) void topk_compact_kernel(const float*
   const int chunk = blockIdx.x - t * n_chunks;
   const int64_t b0 = (int64_t)chunk * (kPer * kHistThreads);
   const float* row = scores + (int64_t)t * ld;
+  int32_t* st = ws.state + (int64_t)t * ST_WORDS;
   float v[kPer];
   FirstHist<kHistThreads> fh;
-  if constexpr (kPer == kPerSmall) fh = load_first_hist<kHistThreads>(ws, t);   // beside the chunk
+  int rec_bin = 0, rec_cand = 0;
+  if constexpr (kBinDone) {
+    rec_bin = st[ST_B1];
+    rec_cand = st[ST_NCAND];
+  } else if constexpr (kPer == kPerSmall) {
+    fh = load_first_hist<kHistThreads>(ws, t);   // beside the chunk
+  }
   const int64_t n_t = load_chunk<kPer>(row, b0, ld, q_pos + t, v);
   if (n_t <= k || b0 >= n_t) return;
-  if constexpr (kPer != kPerSmall) fh = load_first_hist<kHistThreads>(ws, t);
+  if constexpr (!kBinDone && kPer != kPerSmall) fh = load_first_hist<kHistThreads>(ws, t);
   __shared__ __align__(16) uint32_t h[kBins1];
   __shared__ int sh_wave[kHistThreads / 64];
   __shared__ int sh_res[2];
   __shared__ int sh_base[2];
-  int32_t* st = ws.state + (int64_t)t * ST_WORDS;
-  // Every workgroup of the row finds the bin of the k-th largest key from the
-  // row's histogram (cheaper than a cross-workgroup handoff); chunk 0 records it.
-  int above, n_cand;
-  const uint32_t bin = (uint32_t)first_digit_bin<kHistThreads>(fh, k, h, sh_wave, sh_res, &above, &n_cand);
-  if (chunk == 0 && threadIdx.x == 0) {
-    st[ST_B1] = (int)bin;
-    st[ST_ABOVE] = above;
-    st[ST_NCAND] = n_cand;
+  uint32_t bin;
+  int n_cand;
+  if constexpr (kBinDone) {
+    bin = (uint32_t)rec_bin;
+    n_cand = rec_cand;
+  } else {
+    int above;
+    bin = (uint32_t)first_digit_bin<kHistThreads>(fh, k, h, sh_wave, sh_res, &above, &n_cand);
+    if (chunk == 0 && threadIdx.x == 0) {
+      st[ST_B1] = (int)bin;
+      st[ST_ABOVE] = above;
+      st[ST_NCAND] = n_cand;
+    }
   }
   const bool take_cand = n_cand <= ws.cap;
   uint32_t above_mask = 0, cand_mask = 0;
@@ -559,13 +598,16 @@ static int64_t topk_chunks(int64_t ld, int per) { return (ld + per * sa::kHistTh
 static int32_t topk_after_hist(const float* scores, int64_t ld, const int32_t* q_pos, int32_t n_q, int32_t k,
                                int32_t* idx, const sa::TopkWs& w, bool large, hipStream_t stream) {
   if (large) {
+    hipLaunchKernelGGL(sa::topk_bin_kernel, dim3(n_q), dim3(sa::kHistThreads), 0, stream, q_pos, k, w);
+    int32_t rc = check_launch("topk_bin_kernel");
+    if (rc) return rc;
     const int n_chunks = (int)topk_chunks(ld, sa::kPerLargeCompact);
-    hipLaunchKernelGGL(sa::topk_compact_kernel<sa::kPerLargeCompact>, dim3(n_chunks * n_q), dim3(sa::kHistThreads), 0,
-                       stream, scores, ld, q_pos, k, n_chunks, w);
+    hipLaunchKernelGGL((sa::topk_compact_kernel<sa::kPerLargeCompact, true>), dim3(n_chunks * n_q),
+                       dim3(sa::kHistThreads), 0, stream, scores, ld, q_pos, k, n_chunks, w);
   } else {
     const int n_chunks = (int)topk_chunks(ld, sa::kPerSmall);
-    hipLaunchKernelGGL(sa::topk_compact_kernel<sa::kPerSmall>, dim3(n_chunks * n_q), dim3(sa::kHistThreads), 0, stream,
-                       scores, ld, q_pos, k, n_chunks, w);
+    hipLaunchKernelGGL((sa::topk_compact_kernel<sa::kPerSmall, false>), dim3(n_chunks * n_q), dim3(sa::kHistThreads), 0,
+                       stream, scores, ld, q_pos, k, n_chunks, w);
   }
   int32_t rc = check_launch("topk_compact_kernel");
   if (rc) return rc;
