@@ -183,10 +183,16 @@ int32_t sa_topk_select(const float* scores, int64_t ld, const int32_t* q_pos, in
 size_t sa_mla_workspace_size(int32_t n_q, int32_t k);
 /* How sa_mla_sparse_attn (and its FP8 variant) slices each query's selection
  * for n_q queries of k entries: *n_sp slices of *kps entries (the last may be
- * shorter, none is empty); with *n_sp > 1 the slices' partial softmax states
- * (fp32) are combined by a log-sum-exp merge.  For workspace planning and
- * error analysis. */
+ * shorter, none is empty), slice s taking entries s * kps .. of each idx row;
+ * with *n_sp > 1 the slices' partial softmax states are combined by a
+ * log-sum-exp merge.  For workspace planning and error analysis. */
 int32_t sa_mla_split_info(int32_t n_q, int32_t k, int32_t* n_sp, int32_t* kps);
+/* The precision of those partial states: 0 (one slice, none), 32 (fp32), or
+ * 16 (each slice's unnormalised weighted row sum rounded to bf16, round to
+ * nearest even, before the merge; used for one 32-head block per workgroup and
+ * 2..8 slices, i.e. decode batches of 16..63 queries at k = 2048).  A negative
+ * status for arguments outside the ranges above.  For error analysis. */
+int32_t sa_mla_partial_bits(int32_t n_q, int32_t k);
 int32_t sa_mla_sparse_attn(const void* q_abs, const void* kv, const int64_t* seq_start,
                            const int32_t* q_seq, const int32_t* idx, int32_t n_q, int32_t k,
                            const void* w_uv, float scale, void* out, float* lse,

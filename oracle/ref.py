@@ -260,7 +260,7 @@ def round_to_bf16(x):
 
 
 def mla_error_bound(out, q_abs, w_uv, rows_list, p_list, scale, n_lat=KV_LORA_RANK,
-                    model="probabilistic", lam=8.0):
+                    model="probabilistic", lam=8.0, part_slices=None):
     """Per-element tolerance for the GPU's sparse MLA output, derived from the
     arithmetic the kernels are allowed (not fitted to results).
 
@@ -273,6 +273,12 @@ def mla_error_bound(out, q_abs, w_uv, rows_list, p_list, scale, n_lat=KV_LORA_RA
       * weights fed to the value product in bf16 and the normaliser formed
         from the unrounded fp32 weights: relative 2 ub per weight;
       * fp32 accumulation of up to 2048 weighted rows;
+      * with part_slices (per query, the slice of each gathered row, in the
+        order of rows_list): the selection is processed in slices whose
+        partial weighted row sums are each rounded once to bf16 before they
+        are combined; slice s holds a positive multiple of
+        a_s = sum over its rows of p_j R_j[:512], so the latent average moves
+        by at most ub sum_s |a_s| (worst) or lam ub sqrt(sum_s a_s^2);
       * the latent average fed to the up-projection in bf16 (relative 2 ub)
         and summed in fp32 over 512 terms;
       * the final rounding of the output to bf16 (ub |out|, rigorous).
@@ -308,14 +314,22 @@ def mla_error_bound(out, q_abs, w_uv, rows_list, p_list, scale, n_lat=KV_LORA_RA
         v = rows[:, :n_lat]
         pv_abs = p @ np.abs(v)                                        # [64, 512]: sum_j p_j |R_j[c]|
         obar = p @ v                                                  # [64, 512]
+        a_sl = None
+        if part_slices is not None and n_sel > 0:
+            sl = np.asarray(part_slices[t])
+            a_sl = np.stack([p[:, sl == s] @ v[sl == s] for s in np.unique(sl)])   # [slices, 64, 512]
         if model == "worst":
             d_obar = (2 * ub + rel_z) * pv_abs + gamma(max(n_sel, 1)) * pv_abs
+            if a_sl is not None:
+                d_obar = d_obar + ub * np.abs(a_sl).sum(axis=0)
             for h in range(out.shape[1]):
                 bound[t, h] = wa[h] @ d_obar[h] + (2 * ub + gamma(n_lat)) * (wa[h] @ np.abs(obar[h])) \
                     + ub * np.abs(out[t, h])
         else:
             pv_sq = np.sqrt((p ** 2) @ (v ** 2))                      # [64, 512]
             d_obar = lam * 2 * ub * pv_sq + rel_z * pv_abs + lam * np.sqrt(max(n_sel, 1)) * u * pv_abs
+            if a_sl is not None:
+                d_obar = d_obar + lam * ub * np.sqrt((a_sl ** 2).sum(axis=0))
             for h in range(out.shape[1]):
                 prop = np.sqrt((w[h] ** 2) @ (d_obar[h] ** 2))        # errors of obar through W_UV
                 rnd = lam * 2 * ub * np.sqrt((w[h] ** 2) @ (obar[h] ** 2))

@@ -41,6 +41,7 @@ SIGNATURES = {
     "sa_topk_select_algo": (c_i32, [c_p, c_i64, c_p, c_i32, c_i32, c_p, c_p, c_sz, c_i32, c_p]),
     "sa_mla_workspace_size": (c_sz, [c_i32, c_i32]),
     "sa_mla_split_info": (c_i32, [c_i32, c_i32, ctypes.POINTER(c_i32), ctypes.POINTER(c_i32)]),
+    "sa_mla_partial_bits": (c_i32, [c_i32, c_i32]),
     "sa_mla_sparse_attn": (c_i32, [c_p, c_p, c_p, c_p, c_p, c_i32, c_i32, c_p, c_f32, c_p, c_p, c_p, c_sz, c_p]),
     "sa_cache_write": (c_i32, [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_p, c_p]),
     "sa_layer_stack_workspace_size": (c_sz, [c_i32, c_i64, c_i32]),

@@ -97,6 +97,14 @@ def mla_split_info(n_q: int, k: int):
     return n_sp.value, kps.value
 
 
+def mla_partial_bits(n_q: int, k: int) -> int:
+    """sa_mla_partial_bits: 0 (no partial states), 32 (fp32) or 16 (bf16)."""
+    r = _lib.lib().sa_mla_partial_bits(n_q, k)
+    if r < 0:
+        _lib.check("sa_mla_partial_bits", r)
+    return r
+
+
 def mla_sparse_attn(q_abs, kv, seq_start, q_seq, idx, w_uv, scale: float = 1.0 / 16, out=None, lse=None, ws=None,
                     stream=None):
     n_q, k = idx.shape

@@ -48,9 +48,10 @@ int32_t launch_topk(const float* scores, int64_t ld, const int32_t* q_pos, int32
                     void* ws, int algo, hipStream_t stream, bool cleared);
 size_t mla_workspace_size(int32_t n_q, int32_t k);
 void mla_split(int32_t n_q, int32_t k, int* n_sp, int* kps);
+int mla_partial_bits(int32_t n_q, int32_t k);
 int32_t launch_mla(const void* q_abs, const void* kv, const float* kv_scale, const int64_t* seq_start,
                    const int32_t* q_seq, const int32_t* idx, int32_t n_q, int32_t k, const void* w_uv, float scale,
-                   void* out, float* lse, void* ws, hipStream_t stream, bool shared_rows);
+                   void* out, float* lse, void* ws, hipStream_t stream, bool shared_rows, int part_half = 0);
 int32_t launch_quantize(const void* src, int64_t n_rows, int32_t d, const int64_t* dst_rows, void* codes, float* scales,
                         hipStream_t stream);
 int32_t launch_fp8_decode(const void* codes, int64_t n, void* out, hipStream_t stream);
@@ -248,6 +249,11 @@ int32_t sa_mla_split_info(int32_t n_q, int32_t k, int32_t* n_sp, int32_t* kps) {
   return SA_OK;
 }
 
+int32_t sa_mla_partial_bits(int32_t n_q, int32_t k) {
+  SA_REQUIRE(n_q >= 1 && k >= 1 && k <= SA_MAX_TOPK, SA_ERR_INVALID_ARG, "mla_partial_bits: n_q=%d, k=%d", n_q, k);
+  return mla_partial_bits(n_q, k);
+}
+
 size_t sa_mla_workspace_size(int32_t n_q, int32_t k) {
   if (n_q <= 0 || k <= 0) return 256;
   return mla_workspace_size(n_q, k > SA_MAX_TOPK ? SA_MAX_TOPK : k);
@@ -395,8 +401,11 @@ int32_t sa_layer_stack(const sa_layer_desc* layers, int32_t n_layers, const sa_b
     }
     const bool eva = events && !rec_attn && events->attn_begin && events->attn_end;
     if (eva && (rc = record(events->attn_begin, st))) return rc;
+    // consecutive layers put their bf16 partial states in alternate halves of
+    // the region, so a layer's streaming stores do not land on lines the
+    // previous layer's merge has just read into the L2
     rc = launch_mla(L.q_abs, L.kv, L.kv_scale, batch->seq_start, batch->q_seq, cur_idx, n_q, k, L.w_uv, scale, L.out,
-                    nullptr, mla_ws, st, shared_rows);
+                    nullptr, mla_ws, st, shared_rows, l & 1);
     if (rc) return rc;
     if (eva && (rc = record(events->attn_end, st))) return rc;
     rec_attn |= eva;

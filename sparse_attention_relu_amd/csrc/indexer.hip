@@ -78,15 +78,6 @@ struct DecArgs {
   int64_t n_clear;
 };
 
-// Orders a wave's LDS writes before its reads of other lanes' data (and the
-// reads before the next writes).  LDS-only: in-flight global loads are not
-// waited for.
-__device__ __forceinline__ void wave_lds_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // FP8: the keys are E4M3 codes with one fp32 scale per key; they are decoded
 // to bf16 (exact) on their way into the staging LDS, and each score is the
 // codes' score times the key's scale (ReLU commutes with a positive scale).

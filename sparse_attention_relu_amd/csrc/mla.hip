@@ -82,11 +82,13 @@ struct AttnArgs {
   int n_sp;
   int kps;               // selection entries per slice (multiple of kTile)
   float scale_log2;      // scale * log2(e)
-  float* part_o;         // [n_q][n_sp] blocks of 64 x 512 fp32 in register-tile order (n_sp > 1)
+  float* part_o;         // n_sp > 1: [n_q][n_sp] blocks of 64 x 512 fp32 in register-tile order, or with
+                         // part_bf16 [n_q][n_sp][64][512] bf16 (unnormalised, head-major)
   float* part_ml;        // [n_q][n_sp][64][2]     (max in log2 units, sum)
   uint16_t* obar;        // [n_q][64][512] bf16 latent average
   float* lse;            // [n_q][64] or null
   const float* kv_scale; // FP8 rows: kv holds E4M3 codes [rows][576] and this one scale per row
+  int part_bf16;         // partial states in bf16, head-major (merged by mla_merge_wuv_kernel)
 };
 
 constexpr int kMaxSlice = 2048;
@@ -476,9 +478,15 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
       if (n_tiles > 1) issue8(1);
     }
   } else {
-    issue(0);
-    issue(1);
-    SA_WAIT_VMCNT(kLoadsPerWave);        // tile 0 is in (tile 1 may still be in flight)
+    // Only tiles of the slice are gathered (no clamped re-reads past its
+    // end), so each wait below names exactly the loads still allowed out.
+    if (n_tiles > 0) issue(0);
+    if (n_tiles > 1) {
+      issue(1);
+      SA_WAIT_VMCNT(kLoadsPerWave);      // tile 0 is in (tile 1 may still be in flight)
+    } else {
+      SA_WAIT_VMCNT(0);
+    }
   }
   lds_barrier();                                                       // B1
   // weights / rescale of head l32 come from score wave l32 / 8
@@ -516,7 +524,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
       }
       fl = flds[pb_i * 4 + pw];
     }
-    if (!FP8 && step < n_tiles) {
+    if (!FP8 && step + 2 < n_tiles) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       if constexpr (kPosAhead) issue_at(step + 2, npos);
       else issue(step + 2);
@@ -566,7 +574,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
     } else {
       if constexpr (kPosAhead)
         if (step + 1 < n_tiles) read_pos(step + 3, npos);   // issued next step
-      if (step < n_tiles) SA_WAIT_VMCNT(kLoadsPerWave);
+      // tile step + 1 must be in; tile step + 2, if any, stays in flight
+      if (step + 2 < n_tiles)
+        SA_WAIT_VMCNT(kLoadsPerWave);
+      else if (step + 1 < n_tiles)
+        SA_WAIT_VMCNT(0);
     }
     lds_barrier();                                                     // BAR_p
   }
@@ -576,7 +588,29 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
   // being written back from L2 when the kernel ends (-1 us per launch).  They
   // need no (m, l), so they are issued before BAR_end, beside the score waves'
   // last softmax.
-  if (A.n_sp > 1) {
+  if (A.n_sp > 1 && A.part_bf16) {
+    // Head-major bf16 partials, so the fused merge reads one head's 512
+    // dims as 1 KB.  The four output waves assemble the block's
+    // [32 heads][512 dims] in ring buffer blk (no load targets the ring after
+    // the last step, and every read of it is done), 16-byte chunk q of head r
+    // at slot q ^ (r & 15); after BAR_end each wave stores 8 heads as whole
+    // 1 KB rows.
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      uint8_t* tb = ring + blk * kTileBytes;
+      const f32x16* ot = o[blk];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+#pragma unroll
+        for (int bh = 0; bh < 2; ++bh) {            // dims 128w + 32a + 16hl + 8bh .. +7: chunk 16w + 4a + 2hl + bh
+          const int i0 = 4 * a + 2 * bh;
+          const u32x4 pk = {pack_bf16x2(ot[0][i0], ot[1][i0]), pack_bf16x2(ot[2][i0], ot[3][i0]),
+                            pack_bf16x2(ot[0][i0 + 1], ot[1][i0 + 1]), pack_bf16x2(ot[2][i0 + 1], ot[3][i0 + 1])};
+          *reinterpret_cast<u32x4*>(tb + l32 * 1024 + 16 * ((16 * w + 4 * a + 2 * hl + bh) ^ (l32 & 15))) = pk;
+        }
+      }
+    }
+  } else if (A.n_sp > 1) {
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
       f32x4* po = reinterpret_cast<f32x4*>(A.part_o) + ((((int64_t)t * A.n_sp + sp) * 2 + hg + blk) * 4 + w) * 16 * 64;
@@ -589,8 +623,25 @@ __global__ __launch_bounds__(kAttnThreads, 1) void mla_attn_kernel(AttnArgs A) {
               &po[(mt * 4 + a) * 64 + lane]);
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);         // the trailing (clamped) tile loads land before the workgroup ends
+  __builtin_amdgcn_s_waitcnt(0);         // the partial stores are out before the workgroup ends
   lds_barrier();                                                       // BAR_end: (m, l) of every head
+  if (A.n_sp > 1 && A.part_bf16) {
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      const uint8_t* tb = ring + blk * kTileBytes;
+      uint16_t* pb = reinterpret_cast<uint16_t*>(A.part_o) +
+                     (((int64_t)t * A.n_sp + sp) * kHeads + kHeadGroup * (hg + blk) + 8 * w) * kLatent;
+      u32x4 v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 8 * w + i;
+        v[i] = *reinterpret_cast<const u32x4*>(tb + r * 1024 + 16 * (lane ^ (r & 15)));
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        __builtin_nontemporal_store(v[i], reinterpret_cast<u32x4*>(pb + i * kLatent + 8 * lane));
+    }
+  }
   // Result element 4a + b of tile mt is dim 128w + 32a + 16hl + 4b + mt of
   // head 32hg + l32: for each a a lane holds 16 consecutive dims.
   if (A.n_sp == 1) {
@@ -957,6 +1008,136 @@ __global__ __launch_bounds__(ROWS * 4) void mla_wuv_kernel(WuvArgs W) {
   }
 }
 
+// ------------------------------------------------------- merge + W_UV in one
+// For decode batches whose selections are split into 2..8 slices: the merge
+// of the slices' bf16 head-major partial states is done by the workgroups of
+// the W_UV product itself, one launch per layer instead of two.  One
+// workgroup per (head, 128 value rows): it stages its 128 KB of W_UV in LDS
+// (as mla_wuv_kernel<128>), and for each block of 16 queries thread
+// (query rq, 16-dim chunk c) reads that chunk of the head's partial states
+// for every slice (32 B each, one round trip per 8 slices), combines them
+// with the log-sum-exp weights 2^(m_s - max m) and writes the bf16 latent
+// average into the LDS row the products read.  Each partial state is read by
+// the two workgroups of its head.
+struct MergeWuvArgs {
+  const uint16_t* part_o;   // [n_q][n_sp][64][512] bf16, unnormalised
+  const float* part_ml;     // [n_q][n_sp][64][2]: max (log2 units), sum
+  const uint16_t* w_uv;     // [64][256][512]
+  uint16_t* out;            // [n_q][64][256]
+  float* lse;               // [n_q][64] or null
+  int n_q, n_sp;
+};
+constexpr int kMwRows = 128;
+constexpr int kMwThreads = kMwRows * 4;
+constexpr int kMwMaxSp = kMergeBatch;     // slices merged per round trip (and at most)
+constexpr size_t kMwSmem = (size_t)(kMwRows + kWuvQ) * kLatent * 2;   // 144 KB
+static_assert(kMwThreads == kWuvQ * (kLatent / 16), "one thread per (query of the block, 16-dim chunk)");
+
+__global__ __launch_bounds__(kMwThreads) void mla_merge_wuv_kernel(MergeWuvArgs W) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int h = (int)blockIdx.x >> 1;
+  const int vb = ((int)blockIdx.x & 1) * kMwRows;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  uint8_t* wl = smem;                                   // [128 rows][1 KB]
+  uint8_t* ol = smem + kMwRows * 1024;                  // [16 rows][1 KB]: the block's latent averages
+  // W_UV rows as in mla_wuv_kernel: lane p of row r fills slot p with chunk p ^ (r & 15)
+  const uint16_t* wsrc = W.w_uv + ((int64_t)h * kVdim + vb) * kLatent;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int r = 16 * w + u;
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(wsrc + (int64_t)r * kLatent) + 16 * (lane ^ u);
+    __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(wl + r * 1024), 16,
+                                     0, 0);
+  }
+  const int rq = threadIdx.x >> 5, c = threadIdx.x & 31;
+  const int rd = 16 * (g ^ l16);
+  const int64_t slice_stride = (int64_t)kHeads * kLatent / 8;      // in 16-byte units
+  bf16x8 wa[16];
+  const int n_blk = (W.n_q + kWuvQ - 1) / kWuvQ;
+  for (int b = 0; b < n_blk; ++b) {
+    const int tq = min(b * kWuvQ + rq, W.n_q - 1);
+    const u32x4* src =
+        reinterpret_cast<const u32x4*>(W.part_o + ((int64_t)tq * W.n_sp * kHeads + h) * kLatent + 16 * c);
+    const float2* mlp = reinterpret_cast<const float2*>(W.part_ml) + (int64_t)tq * W.n_sp * kHeads + h;
+    float M = -INFINITY, L = 0.f;
+    float acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    for (int s0 = 0; s0 < W.n_sp; s0 += kMwMaxSp) {
+      u32x4 v[kMwMaxSp][2];
+      float2 ml[kMwMaxSp];
+#pragma unroll
+      for (int u = 0; u < kMwMaxSp; ++u) {
+        ml[u] = float2{-INFINITY, 0.f};
+        v[u][0] = u32x4{0u, 0u, 0u, 0u};
+        v[u][1] = v[u][0];
+        if (s0 + u < W.n_sp) {
+          ml[u] = mlp[(int64_t)(s0 + u) * kHeads];
+          v[u][0] = src[(s0 + u) * slice_stride];
+          v[u][1] = src[(s0 + u) * slice_stride + 1];
+        }
+      }
+      float mb = M;
+#pragma unroll
+      for (int u = 0; u < kMwMaxSp; ++u) mb = fmaxf(mb, ml[u].x);
+      if (mb > M) {                       // new running maximum (never taken while every slice is empty)
+        const float cf = M == -INFINITY ? 0.f : fast_exp2(M - mb);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] *= cf;
+        L *= cf;
+        M = mb;
+      }
+#pragma unroll
+      for (int u = 0; u < kMwMaxSp; ++u) {
+        const float wt = ml[u].x != -INFINITY ? fast_exp2(ml[u].x - M) : 0.f;
+        L = fmaf(wt, ml[u].y, L);
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {         // dims 16c + 8k2 + 2e, +1
+            const uint32_t x = v[u][k2][e];
+            acc[8 * k2 + 2 * e] = fmaf(wt, __uint_as_float(x << 16), acc[8 * k2 + 2 * e]);
+            acc[8 * k2 + 2 * e + 1] = fmaf(wt, __uint_as_float(x & 0xffff0000u), acc[8 * k2 + 2 * e + 1]);
+          }
+      }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    uint8_t* orow = ol + rq * 1024;
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {      // chunk 2c + k2 of row rq at slot (2c + k2) ^ rq
+      const float* x = acc + 8 * k2;
+      const u32x4 pk = {pack_bf16x2(x[0] * inv, x[1] * inv), pack_bf16x2(x[2] * inv, x[3] * inv),
+                        pack_bf16x2(x[4] * inv, x[5] * inv), pack_bf16x2(x[6] * inv, x[7] * inv)};
+      *reinterpret_cast<u32x4*>(orow + 16 * ((2 * c + k2) ^ rq)) = pk;
+    }
+    if (W.lse && vb == 0 && c == 0 && b * kWuvQ + rq < W.n_q)
+      W.lse[(int64_t)(b * kWuvQ + rq) * kHeads + h] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
+    SA_WAIT_VMCNT(0);                     // (the W_UV rows, on the first block)
+    lds_barrier();
+    if (b == 0) {
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+        wa[s] = *reinterpret_cast<const bf16x8*>(wl + (16 * w + l16) * 1024 + ((16 * (4 * s)) ^ rd));
+    }
+    const uint8_t* qrow = ol + l16 * 1024;
+    bf16x8 ob[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) ob[s] = *reinterpret_cast<const bf16x8*>(qrow + ((16 * (4 * s)) ^ rd));
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 o4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 16; ++s) o4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[s], ob[s], o4, 0, 0, 0);
+    // o4[j] = out[16b + l16][h][vb + 16w + 4g + j]
+    const int to = b * kWuvQ + l16;
+    if (to < W.n_q) {
+      const u32x2 pk = {pack_bf16x2(o4[0], o4[1]), pack_bf16x2(o4[2], o4[3])};
+      *reinterpret_cast<u32x2*>(W.out + ((int64_t)to * kHeads + h) * kVdim + vb + 16 * w + 4 * g) = pk;
+    }
+    lds_barrier();                        // the block's rows are rewritten by the next block's merge
+  }
+}
+
 }  // namespace sa
 
 namespace sa_host {
@@ -987,6 +1168,16 @@ void mla_split(int32_t n_q, int32_t k, int* n_sp_out, int* kps_out) {
   kps = (kps + sa::kTile - 1) / sa::kTile * sa::kTile;
   *n_sp_out = (k + kps - 1) / kps;
   *kps_out = kps;
+}
+
+// Partial states: none with one slice; bf16 head-major, merged inside the
+// W_UV launch, for one head block and 2..8 slices (decode batches of 16..63
+// queries); fp32 register-tile order with a merge launch otherwise.
+int mla_partial_bits(int32_t n_q, int32_t k) {
+  int n_sp, kps;
+  mla_split(n_q, k, &n_sp, &kps);
+  if (n_sp == 1) return 0;
+  return (mla_head_blocks(n_q) == 1 && n_sp <= sa::kMwMaxSp) ? 16 : 32;
 }
 
 int mla_n_splits(int32_t n_q, int32_t k) {
@@ -1048,10 +1239,14 @@ static hipError_t reserve_attn_lds() {
 
 int32_t launch_mla(const void* q_abs, const void* kv, const float* kv_scale, const int64_t* seq_start,
                    const int32_t* q_seq, const int32_t* idx, int32_t n_q, int32_t k, const void* w_uv, float scale,
-                   void* out, float* lse, void* ws, hipStream_t stream, bool shared_rows) {
+                   void* out, float* lse, void* ws, hipStream_t stream, bool shared_rows, int part_half) {
   int n_sp, kps;
   mla_split(n_q, k, &n_sp, &kps);
   MlaWs m = mla_carve(ws, n_q, n_sp);
+  const bool part_bf16 = mla_partial_bits(n_q, k) == 16;
+  // bf16 partial states take half of the fp32 region; part_half picks which
+  if (part_bf16 && part_half)
+    m.part_o = reinterpret_cast<float*>(reinterpret_cast<uint16_t*>(m.part_o) + (size_t)n_q * n_sp * sa::kHeads * sa::kLatent);
   sa::AttnArgs A;
   A.q_abs = (const uint16_t*)q_abs;
   A.kv = (const uint16_t*)kv;
@@ -1068,6 +1263,7 @@ int32_t launch_mla(const void* q_abs, const void* kv, const float* kv_scale, con
   A.obar = m.obar;
   A.lse = lse;
   A.kv_scale = kv_scale;
+  A.part_bf16 = part_bf16 ? 1 : 0;
   const int nb = mla_head_blocks(n_q);
   const bool fp8 = kv_scale != nullptr;
   const size_t smem = nb == 2 ? (fp8 ? sa::attn_smem<2, true>() : sa::attn_smem<2>())
@@ -1084,7 +1280,9 @@ int32_t launch_mla(const void* q_abs, const void* kv, const float* kv_scale, con
         hipFuncSetAttribute((const void*)sa::mla_wuv_kernel<64, 1>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)sa::wuv_smem<64>()) != hipSuccess ||
         hipFuncSetAttribute((const void*)sa::mla_wuv_kernel<128, 2>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)sa::wuv_smem<128>()) != hipSuccess) {
+                            (int)sa::wuv_smem<128>()) != hipSuccess ||
+        hipFuncSetAttribute((const void*)sa::mla_merge_wuv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)sa::kMwSmem) != hipSuccess) {
       set_error("mla: cannot reserve %zu bytes of LDS", smem);
       return SA_ERR_HIP;
     }
@@ -1107,6 +1305,12 @@ int32_t launch_mla(const void* q_abs, const void* kv, const float* kv_scale, con
     launch_attn<1, false>(shared_rows, grid, smem, stream, A);
   int32_t rc = check_launch("mla_attn_kernel");
   if (rc) return rc;
+  if (A.part_bf16) {
+    sa::MergeWuvArgs M{(const uint16_t*)m.part_o, m.part_ml, (const uint16_t*)w_uv, (uint16_t*)out, lse, n_q, n_sp};
+    hipLaunchKernelGGL(sa::mla_merge_wuv_kernel, dim3(sa::kHeads * (sa::kVdim / sa::kMwRows)), dim3(sa::kMwThreads),
+                       sa::kMwSmem, stream, M);
+    return check_launch("mla_merge_wuv_kernel");
+  }
   if (n_sp > 1) {
     if (wide && n_q <= sa::kSplitMaxQ) {
       hipLaunchKernelGGL(sa::mla_merge_split_kernel, dim3((unsigned)(n_q * 256)), dim3(256), 0, stream, A);

@@ -67,6 +67,15 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // clobber keeps the compiler from moving memory accesses across the barrier.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Orders a wave's LDS writes before its reads of other lanes' data (and the
+// reads before the next writes).  LDS-only: in-flight global loads are not
+// waited for.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // s_waitcnt vmcnt(n) leaving the other counters unconstrained (gfx9 encoding).
 #define SA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8))
 

@@ -384,6 +384,47 @@ def check_mla_error_bound_sane(ref):
     assert np.max(prob - 2.0 ** -8 * np.abs(out)) < 0.25 * np.sqrt(np.mean(out ** 2))
 
 
+def _simulate_sliced_bf16(ref, q_t, rows, wuv, scale, kps):
+    """Another allowed evaluation: the rows processed in slices of kps, each
+    slice's unnormalised weighted row sum (fp32 weights against its own
+    maximum, bf16 weights in the product) rounded to bf16, the slices
+    combined with fp32 factors exp(m_s - max m), then as above."""
+    r32 = rows.astype(np.float32)
+    z = (q_t.astype(np.float32) @ r32.T) * np.float32(scale)           # [64, k]
+    n = rows.shape[0]
+    parts = []
+    for j0 in range(0, n, kps):
+        zs = z[:, j0:j0 + kps]
+        ms = zs.max(axis=1, keepdims=True)
+        e = np.exp(zs - ms).astype(np.float32)
+        os16 = ref.round_to_bf16(ref.round_to_bf16(e).astype(np.float32) @ r32[j0:j0 + kps, :512]).astype(np.float32)
+        parts.append((ms, e.sum(axis=1, dtype=np.float32)[:, None], os16))
+    M = np.max([m for m, _, _ in parts], axis=0)
+    num = sum(np.exp(m - M).astype(np.float32) * o for m, _, o in parts)
+    den = sum(np.exp(m - M).astype(np.float32) * l for m, l, _ in parts)
+    ob16 = ref.round_to_bf16((num / den).astype(np.float32)).astype(np.float32)
+    o = np.einsum("hvc,hc->hv", wuv.astype(np.float32), ob16)
+    return ref.round_to_bf16(o)
+
+
+def check_mla_error_bound_sliced(ref):
+    """With part_slices the derived tolerances also cover slice partials
+    rounded to bf16 before the merge (8 slices of 256 over k = 2048), and
+    they only grow against the unsliced ones."""
+    q, kv, starts, q_seq, q_pos, idx, wuv = _mla_inputs(59, 2, [3000], 2048)
+    out, obar, m, l, rows, p = ref.sparse_mla(q, kv, starts, q_seq, idx, wuv, 1.0 / 16, return_parts=True)
+    sl = [np.arange(r.shape[0]) // 256 for r in rows]
+    worst = ref.mla_error_bound(out, q, wuv, rows, p, 1.0 / 16, model="worst", part_slices=sl)
+    prob = ref.mla_error_bound(out, q, wuv, rows, p, 1.0 / 16, part_slices=sl)
+    prob0 = ref.mla_error_bound(out, q, wuv, rows, p, 1.0 / 16)
+    for t in range(2):
+        sim = _simulate_sliced_bf16(ref, q[t], rows[t], wuv, 1.0 / 16, 256)
+        assert np.all(np.abs(sim - out[t]) <= prob[t])
+        assert np.all(np.abs(sim - out[t]) <= worst[t])
+    assert np.all(prob >= prob0) and np.any(prob > prob0)
+    assert np.all(prob <= worst)
+
+
 def check_round_to_bf16(ref):
     """Round to nearest, ties to even, on hand-picked binary32 values:
     1 + 2^-8 is a tie between 1 and 1 + 2^-7 and goes to the even 1;

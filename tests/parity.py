@@ -88,17 +88,31 @@ def check_topk_band(L, B, idx_gpu, k, rows=None, extra_rel=0.0):
         assert np.all(gap <= tau), f"row {t}: swapped positions outside the tie band: {diff[gap > tau][:8]}"
 
 
-def check_mla(Lnp, B, idx_gpu, out_gpu, scale, rows=None, lse_gpu=None):
-    """out_gpu float64 [n_q, 64, 256] (bf16 widened); idx_gpu int64 [n_q, k]."""
+def part_slices(idx_rows, n_launch, k):
+    """The slice of each selected entry (valid entries of each idx row, in
+    order) when the attention launch of n_launch queries with k entries
+    rounds its partial states to bf16 (sa_mla_partial_bits), else None."""
+    from sparse_attention_relu_amd import api
+    if api.mla_partial_bits(n_launch, k) != 16:
+        return None
+    kps = api.mla_split_info(n_launch, k)[1]
+    return [np.nonzero(np.asarray(r) >= 0)[0] // kps for r in idx_rows]
+
+
+def check_mla(Lnp, B, idx_gpu, out_gpu, scale, rows=None, lse_gpu=None, n_launch=None):
+    """out_gpu float64 [n_q, 64, 256] (bf16 widened); idx_gpu int64 [n_q, k].
+    n_launch: the query count of the attention launch when idx_gpu holds only
+    some of its rows (default: every row of idx_gpu)."""
     rows = list(range(idx_gpu.shape[0])) if rows is None else list(rows)
     sub = lambda a: a[rows]
     out, obar, m, l, rows_l, p_l = ref.sparse_mla(sub(Lnp["q_abs"]), Lnp["kv"], B["seq_start"], sub(B["q_seq"]),
                                                   sub(idx_gpu), Lnp["w_uv"], scale, return_parts=True)
+    slices = part_slices(sub(idx_gpu), n_launch or idx_gpu.shape[0], idx_gpu.shape[1])
     got = out_gpu[rows]
     err = np.abs(got - out)
     ns = 2e-2 + 1e-2 * np.abs(out)
     assert np.all(err <= ns), f"outside the 2e-2 + 1e-2|x| bar: max err {err.max()}"
-    bound = ref.mla_error_bound(out, sub(Lnp["q_abs"]), Lnp["w_uv"], rows_l, p_l, scale)
+    bound = ref.mla_error_bound(out, sub(Lnp["q_abs"]), Lnp["w_uv"], rows_l, p_l, scale, part_slices=slices)
     bad = np.argwhere(err > bound)
     assert bad.size == 0, f"{len(bad)} outputs outside the derived bound; first {bad[0]}: " \
                           f"gpu={got[tuple(bad[0])]} oracle={out[tuple(bad[0])]} bound={bound[tuple(bad[0])]}"

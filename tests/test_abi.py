@@ -176,3 +176,22 @@ def test_mla_split_has_no_empty_slice(L):
             assert (s - 1) * p < k <= s * p, (n_q, k, s, p)     # the last slice holds at least one entry
     assert L.sa_mla_split_info(0, 16, ctypes.byref(n_sp), ctypes.byref(kps)) == -1
     assert L.sa_mla_split_info(4, 4096, ctypes.byref(n_sp), ctypes.byref(kps)) == -1
+
+
+def test_mla_partial_bits(L):
+    """The partial states' precision follows the slicing: none with one slice,
+    bf16 for one head block (fewer than 64 queries) and 2..8 slices, fp32
+    otherwise; out-of-range arguments give a negative status."""
+    n_sp, kps = ctypes.c_int32(), ctypes.c_int32()
+    for n_q in (1, 2, 3, 15, 16, 24, 63, 64, 130, 4096):
+        for k in (1, 64, 100, 300, 600, 2048):
+            assert L.sa_mla_split_info(n_q, k, ctypes.byref(n_sp), ctypes.byref(kps)) == 0
+            bits = L.sa_mla_partial_bits(n_q, k)
+            if n_sp.value == 1:
+                assert bits == 0, (n_q, k)
+            elif n_q < 64 and n_sp.value <= 8:
+                assert bits == 16, (n_q, k)
+            else:
+                assert bits == 32, (n_q, k)
+    assert L.sa_mla_partial_bits(16, 2048) == 16 and L.sa_mla_partial_bits(64, 2048) == 32
+    assert L.sa_mla_partial_bits(0, 16) < 0 and L.sa_mla_partial_bits(4, 4096) < 0

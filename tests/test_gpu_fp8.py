@@ -243,4 +243,4 @@ def test_fp8_decode_config_full(gpu_lib):
             off += len(sel)
         Lm = {"q_abs": to_numpy(L.q_abs[rows]), "kv": np.concatenate(rows_all), "w_uv": to_numpy(L.w_uv)}
         Bm = {"seq_start": np.array(starts), "q_seq": np.arange(len(rows)), "q_pos": None}
-        parity.check_mla(Lm, Bm, idx_loc, to_numpy(outs[l][rows]), wl.scale)
+        parity.check_mla(Lm, Bm, idx_loc, to_numpy(outs[l][rows]), wl.scale, n_launch=wl.n_q)

@@ -35,7 +35,7 @@ def _check_mla_compact(L, wl, idx, out, queries):
         off += len(rows)
     Lnp = {"q_abs": qa, "kv": np.concatenate(rows_all), "w_uv": wuv}
     B = {"seq_start": np.array(starts), "q_seq": np.arange(len(queries)), "q_pos": None}
-    return parity.check_mla(Lnp, B, idx_loc, out[list(queries)], wl.scale)
+    return parity.check_mla(Lnp, B, idx_loc, out[list(queries)], wl.scale, n_launch=wl.n_q)
 
 
 def _run_stack(wl, seed=0):

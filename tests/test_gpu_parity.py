@@ -196,6 +196,26 @@ def test_mla_slice_counts(gpu_lib, n_q):
                      lse_gpu=to_numpy(lse))
 
 
+@pytest.mark.parametrize("n_q", [16, 24, 40, 63])
+def test_mla_bf16_partials_merged_in_wuv(gpu_lib, n_q):
+    # 16..63 queries at k = 2048: 8, 6, 4 and 3 slices whose bf16 partial
+    # states are merged inside the W_UV launch, over 1..4 blocks of 16 queries
+    # (the last one ragged); the bound includes the slices' rounding
+    assert api.mla_partial_bits(n_q, 2048) == 16
+    lens = [4096, 3000, 2500, 3500]
+    queries = [(i % 4, lens[i % 4] - 1 - 5 * i) for i in range(n_q)]
+    wl = synth.ragged_workload(lens, queries, name=f"bf16parts{n_q}")
+    b = _batch(wl, seed=70 + n_q)
+    L = b.layers[0]
+    sc = api.indexer_score(L.q_idx, L.w, L.k_idx, b.seq_start, b.seq_len, b.q_seq, b.q_pos, wl.ld)
+    idx = api.topk_select(sc, b.q_pos, k=2048)
+    lse = torch.empty((wl.n_q, 64), dtype=torch.float32, device=DEV)
+    out = api.mla_sparse_attn(L.q_abs, L.kv, b.seq_start, b.q_seq, idx, L.w_uv, wl.scale, lse=lse)
+    torch.cuda.synchronize()
+    parity.check_mla(parity.layer_np(L), parity.np_batch(b), to_numpy(idx), to_numpy(out), wl.scale,
+                     lse_gpu=to_numpy(lse))
+
+
 @pytest.mark.parametrize("k", [100, 600, 2048])
 def test_mla_single_query(gpu_lib, k):
     # one query: the merge and W_UV run as one kernel (2, 10 and 32 slices)

@@ -35,6 +35,8 @@ MUTATIONS = [
     ("mla_padding_not_skipped", "sel = idx[t][idx[t] >= 0]", "sel = idx[t]"),
     ("mla_sequence_offset_ignored", "rows = _f64(kv[int(seq_start[q_seq[t]]) + sel])", "rows = _f64(kv[sel])"),
     ("mla_no_normalisation", "p = e / lsum", "p = e"),
+    ("bound_drops_slice_rounding", "d_obar = d_obar + lam * ub * np.sqrt((a_sl ** 2).sum(axis=0))",
+     "d_obar = d_obar + 0.0 * ub * np.sqrt((a_sl ** 2).sum(axis=0))"),
     ("pattern_offset_wrong", "== INDEX_TOPK_FREQ - 1", "== 0"),
     ("pattern_no_prefix", "if layer < INDEX_SKIP_TOPK_OFFSET:\n        return True", "if layer < 1:\n        return True"),
     ("stack_shares_wrong_layer", "            cur = topk_select_rows(sc, q_pos, k)", "            cur = topk_select_rows(sc, q_pos, k - 1)"),
