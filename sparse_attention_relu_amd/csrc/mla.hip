@@ -1035,8 +1035,11 @@ static_assert(kMwThreads == kWuvQ * (kLatent / 16), "one thread per (query of th
 
 __global__ __launch_bounds__(kMwThreads) void mla_merge_wuv_kernel(MergeWuvArgs W) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const int h = (int)blockIdx.x >> 1;
-  const int vb = ((int)blockIdx.x & 1) * kMwRows;
+  // the two workgroups of a head (value rows 0..127 and 128..255) are 64
+  // apart, so the round-robin dealing puts them on one XCD, where the
+  // second read of the head's partial states can hit that XCD's L2
+  const int h = (int)blockIdx.x & (kHeads - 1);
+  const int vb = ((int)blockIdx.x >> 6) * kMwRows;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   uint8_t* wl = smem;                                   // [128 rows][1 KB]
