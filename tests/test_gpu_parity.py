@@ -178,10 +178,11 @@ def test_mla_on_gpu_selection(gpu_lib, case):
     print(f"{case}: worst |err|/bound = {worst:.3g}")
 
 
-@pytest.mark.parametrize("n_q", [1, 3, 5, 10])
+@pytest.mark.parametrize("n_q", [1, 3, 5, 6, 10])
 def test_mla_slice_counts(gpu_lib, n_q):
-    # about 128 / n_q slices per query: 32, 32, 26 and 13, i.e. the merge with
-    # 4 waves per item (even and uneven slice shares) and with 2 waves (uneven)
+    # about 128 / n_q slices per query: 32, 32, 22, 22 and 13, i.e. the split
+    # merge (one query) and the wide merge with 4 waves per item (even and
+    # uneven slice shares) and with 2 waves (uneven)
     lens = [4096, 3000, 2500]
     queries = [(i % 3, lens[i % 3] - 1 - 7 * i) for i in range(n_q)]
     wl = synth.ragged_workload(lens, queries, name=f"slices{n_q}")
@@ -218,7 +219,8 @@ def test_mla_bf16_partials_merged_in_wuv(gpu_lib, n_q):
 
 @pytest.mark.parametrize("k", [100, 600, 2048])
 def test_mla_single_query(gpu_lib, k):
-    # one query: the merge and W_UV run as one kernel (2, 10 and 32 slices)
+    # one query: 2 slices merged inside the W_UV launch (bf16 partial
+    # states), 10 and 32 by the split merge (fp32)
     wl = synth.ragged_workload([5000], [(0, 4321)], k=k, name=f"single_{k}")
     b = _batch(wl, seed=40 + k)
     L = b.layers[0]
