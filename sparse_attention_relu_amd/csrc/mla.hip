@@ -36,12 +36,15 @@
 // c ^ (r & 15), within a rope row (8 chunks) at slot c ^ ((r >> 1) & 7): the
 // 16 lanes of one operand read hit 16 different bank groups.
 // With one slice per query the workgroup normalises and writes the latent
-// average obar (bf16); with several, each writes its partial state and
-// mla_merge_kernel (up to 8 slices), mla_merge_wide_kernel (more slices,
-// i.e. few queries) or mla_merge_split_kernel (more slices and at most two
-// queries) combines them.
-// mla_wuv_kernel: one workgroup per (head, 64 value rows) holds that 64 x 512
-// slice of W_UV in registers and multiplies it with obar^T, 16 queries per
+// average obar (bf16); with several, each writes its partial state.  With
+// one 32-head block per workgroup and 2..8 slices (16..63 decode queries)
+// the partial states are bf16 and head-major, and mla_merge_wuv_kernel
+// merges them inside the W_UV launch; otherwise they are fp32 in register
+// tile order and mla_merge_kernel (up to 8 slices), mla_merge_wide_kernel
+// (more slices, i.e. few queries) or mla_merge_split_kernel (more slices and
+// at most two queries) combines them into obar.
+// mla_wuv_kernel: one workgroup per (head, 64 value rows) stages that 64 x 512
+// slice of W_UV in LDS and multiplies it with obar^T, 16 queries per
 // v_mfma_f32_16x16x32_bf16 column block, rounding the output to bf16.
 #include <atomic>
 
