@@ -101,10 +101,11 @@ def test_fp8_indexer_and_topk(gpu_lib, case, algo):
     print(f"{case} algo {algo}: worst |err| / bound {worst:.3g}")
 
 
-@pytest.mark.parametrize("n_q", [4, 8, 1, 3, 10, 130])
+@pytest.mark.parametrize("n_q", [4, 8, 1, 3, 10, 24, 130])
 def test_fp8_attention(gpu_lib, n_q):
-    # 8: the ragged batch (slices per query as for 16 decode queries); 1, 3, 10:
-    # the wide merge; 130: all 64 heads per workgroup
+    # 8: the ragged batch; 1, 3, 10: the wide merge; 24: 6 slices whose bf16
+    # partial states are merged inside the W_UV launch over two query blocks;
+    # 130: all 64 heads per workgroup
     if n_q == 8:
         wl = _ragged()
     elif n_q == 4:
