@@ -1040,7 +1040,6 @@ static_assert(kMwThreads == kWuvQ * (kLatent / 16), "one thread per (query of th
 constexpr int kMwMaxSp = kMergeBatch;     // slices merged per round trip (and at most)
 constexpr size_t kMwSmem = (size_t)(kMwRows + kWuvQ) * kLatent * 2;   // 80 KB
 
-
 __global__ __launch_bounds__(kMwThreads) void mla_merge_wuv_kernel(MergeWuvArgs W) {
   extern __shared__ __align__(16) uint8_t smem[];
   // the four workgroups of a head (value rows 64j .. 64j + 63) are 64 apart,
