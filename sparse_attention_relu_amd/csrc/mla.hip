@@ -1017,9 +1017,10 @@ __global__ __launch_bounds__(ROWS * 4) void mla_wuv_kernel(WuvArgs W) {
 // For decode batches whose selections are split into 2..8 slices: the merge
 // of the slices' bf16 head-major partial states is done by the workgroups of
 // the W_UV product itself, one launch per layer instead of two.  One
-// workgroup of 512 threads per (head, 64 value rows): its first four waves
-// stage its 64 KB of W_UV in LDS (as mla_wuv_kernel<64>) and run the
-// products; for each block of 16 queries thread (query rq, 16-dim chunk c)
+// workgroup of 512 threads per (head, 64 value rows): all eight waves stage
+// its 64 KB of W_UV in LDS (8 rows each; with 16 rows on each of the first
+// four the step took 0.8 us longer) and the first four run the products;
+// for each block of 16 queries thread (query rq, 16-dim chunk c)
 // reads that chunk of the head's partial states for every slice (32 B each,
 // one round trip per 8 slices), combines them with the log-sum-exp weights
 // 2^(m_s - max m) and writes the bf16 latent average into the LDS row the
@@ -1047,21 +1048,20 @@ __global__ __launch_bounds__(kMwThreads) void mla_merge_wuv_kernel(MergeWuvArgs 
   // reads of the head's partial states can hit that XCD's L2
   const int h = (int)blockIdx.x & (kHeads - 1);
   const int vb = ((int)blockIdx.x >> 6) * kMwRows;
-  constexpr int kWaves = kMwRows / 16;      // waves that stage W_UV rows and run the products
+  constexpr int kWaves = kMwRows / 16;      // waves that run the products
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   uint8_t* wl = smem;                                   // [64 rows][1 KB]
   uint8_t* ol = smem + kMwRows * 1024;                  // [16 rows][1 KB]: the block's latent averages
-  // W_UV rows as in mla_wuv_kernel: lane p of row r fills slot p with chunk p ^ (r & 15)
+  // W_UV rows as in mla_wuv_kernel, kMwRows / 8 per wave: lane p of row r
+  // fills slot p with chunk p ^ (r & 15)
   const uint16_t* wsrc = W.w_uv + ((int64_t)h * kVdim + vb) * kLatent;
-  if (w < kWaves) {
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int r = 16 * w + u;
-      const uint8_t* src = reinterpret_cast<const uint8_t*>(wsrc + (int64_t)r * kLatent) + 16 * (lane ^ u);
-      __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(wl + r * 1024),
-                                       16, 0, 0);
-    }
+  for (int u = 0; u < kMwRows / 8; ++u) {
+    const int r = (kMwRows / 8) * w + u;
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(wsrc + (int64_t)r * kLatent) + 16 * (lane ^ (r & 15));
+    __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(wl + r * 1024),
+                                     16, 0, 0);
   }
   const int rq = threadIdx.x >> 5, c = threadIdx.x & 31;
   const int rd = 16 * (g ^ l16);
